@@ -1,0 +1,315 @@
+"""DSpark draft round on MI355X (gfx950).
+
+Thin ctypes binding of the HIP library `libdspark.so` (C ABI in
+include/dspark.h).  Python only marshals arguments: device buffers and the
+current stream come from PyTorch, every step of the round runs in the
+library's kernels.  There is no CPU fallback: if the library is not built,
+`load_library()` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, List, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+F32, BF16, Q4 = 0, 1, 2
+INPUT_CONTEXT_HIDDEN, INPUT_TARGET_FEATURES = 0, 1
+_KIND = {"f32": F32, "bf16": BF16, "q4": Q4}
+
+EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_aux_bytes", "dspark_model_prepare",
+            "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
+            "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
+            "dspark_last_error")
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dspark status {status}: {msg}")
+        self.status = status
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("hidden_size", ctypes.c_int32), ("num_hidden_layers", ctypes.c_int32),
+                ("num_attention_heads", ctypes.c_int32), ("global_head_dim", ctypes.c_int32),
+                ("num_global_key_value_heads", ctypes.c_int32), ("intermediate_size", ctypes.c_int32),
+                ("vocab_size", ctypes.c_int32), ("block_size", ctypes.c_int32), ("mask_token_id", ctypes.c_int32),
+                ("markov_rank", ctypes.c_int32), ("attention_k_eq_v", ctypes.c_int32),
+                ("markov_head_vanilla", ctypes.c_int32), ("activation_gelu_tanh", ctypes.c_int32),
+                ("fc_in", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+                ("partial_rotary_factor", ctypes.c_double), ("rms_norm_eps", ctypes.c_double),
+                ("final_logit_softcapping", ctypes.c_double), ("weight_dtype", ctypes.c_int32),
+                ("act_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class KernelTime(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("launches", ctypes.c_int32), ("ms", ctypes.c_double)]
+
+
+class Weight(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char_p), ("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p), ("rows", ctypes.c_int64),
+                ("cols", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdspark.so; raises if it is not built (no fallback path)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run block_draft_model_dspark_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I32, SZ, I64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_int64
+    lib.dspark_model_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(Weight), ctypes.c_int,
+                                        ctypes.POINTER(P)]
+    lib.dspark_model_destroy.argtypes = [P]
+    lib.dspark_model_destroy.restype = None
+    lib.dspark_model_aux_bytes.argtypes = [P]
+    lib.dspark_model_aux_bytes.restype = SZ
+    lib.dspark_model_prepare.argtypes = [P, P, SZ, P]
+    lib.dspark_project_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+    lib.dspark_project_workspace_bytes.restype = SZ
+    lib.dspark_project_context_kv.argtypes = [P, ctypes.c_int, P, ctypes.c_int, ctypes.c_int,
+                                              ctypes.POINTER(I32), ctypes.POINTER(P), ctypes.POINTER(P), P, SZ, P]
+    lib.dspark_draft_workspace_bytes.argtypes = [P, ctypes.c_int, ctypes.c_int, I64]
+    lib.dspark_draft_workspace_bytes.restype = SZ
+    lib.dspark_draft_rows.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(I32),
+                                      ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, P, P, SZ, P]
+    lib.dspark_draft_block.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P), I32, I32, I32, P, P, P, P, SZ, P]
+    lib.dspark_profile_enable.argtypes = [ctypes.c_int]
+    lib.dspark_profile_enable.restype = None
+    lib.dspark_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
+    lib.dspark_profile_read.restype = ctypes.c_int
+    lib.dspark_last_error.argtypes = []
+    lib.dspark_last_error.restype = ctypes.c_char_p
+    for fn in ("dspark_model_create", "dspark_model_prepare", "dspark_project_context_kv", "dspark_draft_rows",
+               "dspark_draft_block"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise DsparkError(status, _lib.dspark_last_error().decode())
+
+
+def _stream_handle(stream=None) -> int:
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _torch_dtype(kind: str):
+    import torch
+    return {"f32": torch.float32, "bf16": torch.bfloat16}[kind]
+
+
+def upload(stored: Dict[str, object], device="cuda") -> Dict[str, dict]:
+    """Stored tensors (kind, shape, data, scales, biases) -> device tensors."""
+    import torch
+    out = {}
+    for name, st in stored.items():
+        if st.kind == "f32":
+            d = torch.from_numpy(np.ascontiguousarray(st.data)).to(device)
+            out[name] = {"kind": "f32", "data": d, "shape": st.shape}
+        elif st.kind == "bf16":
+            d = torch.from_numpy(np.ascontiguousarray(st.data).view(np.int16)).to(device).view(torch.bfloat16)
+            out[name] = {"kind": "bf16", "data": d, "shape": st.shape}
+        else:
+            d = torch.from_numpy(np.ascontiguousarray(st.data).view(np.int32)).to(device)
+            s = torch.from_numpy(np.ascontiguousarray(st.scales).view(np.int16)).to(device).view(torch.bfloat16)
+            b = torch.from_numpy(np.ascontiguousarray(st.biases).view(np.int16)).to(device).view(torch.bfloat16)
+            out[name] = {"kind": "q4", "data": d, "scales": s, "biases": b, "shape": st.shape}
+    return out
+
+
+def act_tensor(st, device="cuda"):
+    """A stored activation (f32 or bf16) -> device tensor of the same shape."""
+    import torch
+    if st.kind == "f32":
+        return torch.from_numpy(np.ascontiguousarray(st.data)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(st.data).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+class Model:
+    """A drafter whose weights live in device tensors owned by this object."""
+
+    def __init__(self, cfg, weights: Dict[str, dict]):
+        lib = load_library()
+        self.cfg = cfg
+        self.weights = weights  # keeps the device tensors alive
+        c = Config()
+        c.hidden_size = cfg.hidden_size
+        c.num_hidden_layers = cfg.num_hidden_layers
+        c.num_attention_heads = cfg.num_attention_heads
+        c.global_head_dim = cfg.global_head_dim
+        c.num_global_key_value_heads = cfg.num_global_key_value_heads
+        c.intermediate_size = cfg.intermediate_size
+        c.vocab_size = cfg.vocab_size
+        c.block_size = cfg.block_size
+        c.mask_token_id = cfg.mask_token_id
+        c.markov_rank = cfg.markov_rank
+        c.attention_k_eq_v = int(getattr(cfg, "attention_k_eq_v", True))
+        c.markov_head_vanilla = int(getattr(cfg, "markov_head_type", "vanilla") == "vanilla")
+        c.activation_gelu_tanh = int(getattr(cfg, "hidden_activation", "gelu_pytorch_tanh") == "gelu_pytorch_tanh")
+        c.fc_in = cfg.num_taps * cfg.target_hidden_size if "fc.weight" in weights else 0
+        c.rope_theta = cfg.rope_theta
+        c.partial_rotary_factor = cfg.partial_rotary_factor
+        c.rms_norm_eps = cfg.rms_norm_eps
+        c.final_logit_softcapping = cfg.final_logit_softcapping or 0.0
+        c.weight_dtype = _KIND[cfg.weight_dtype]
+        c.act_dtype = _KIND[cfg.act_dtype]
+        c.group_size = cfg.group_size
+        self._c = c
+        names = list(weights)
+        self._names = [n.encode() for n in names]
+        table = (Weight * len(names))()
+        for i, n in enumerate(names):
+            w = weights[n]
+            shape = w["shape"]
+            table[i].name = self._names[i]
+            table[i].dtype = _KIND[w["kind"]]
+            table[i].data = w["data"].data_ptr()
+            table[i].scales = _ptr(w.get("scales"))
+            table[i].biases = _ptr(w.get("biases"))
+            table[i].rows = shape[0]
+            table[i].cols = shape[1] if len(shape) > 1 else 1
+        h = ctypes.c_void_p()
+        _check(lib.dspark_model_create(ctypes.byref(c), table, len(names), ctypes.byref(h)))
+        self.handle = h
+        self.aux = None
+
+    def __del__(self):
+        if getattr(self, "handle", None) and _lib is not None:
+            _lib.dspark_model_destroy(self.handle)
+            self.handle = None
+
+    def prepare(self, stream=None):
+        import torch
+        n = _lib.dspark_model_aux_bytes(self.handle)
+        self.aux = torch.empty(n, dtype=torch.uint8, device="cuda")
+        _check(_lib.dspark_model_prepare(self.handle, self.aux.data_ptr(), n, _stream_handle(stream)))
+        return self
+
+    @property
+    def act_dtype(self):
+        return _torch_dtype(self.cfg.act_dtype)
+
+
+def profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (timing only)."""
+    load_library().dspark_profile_enable(int(on))
+
+
+def profile_read() -> Dict[str, tuple]:
+    """{kernel role: (launches, total ms)} since the last read."""
+    buf = (KernelTime * 64)()
+    n = load_library().dspark_profile_read(buf, 64)
+    return {buf[i].name.decode(): (buf[i].launches, buf[i].ms) for i in range(n)}
+
+
+def project_workspace_bytes(model: Model, input_kind: int, B: int, L: int) -> int:
+    return int(_lib.dspark_project_workspace_bytes(model.handle, input_kind, B, L))
+
+
+def draft_workspace_bytes(model: Model, A: int, max_ctx: int, total_ctx: int) -> int:
+    return int(_lib.dspark_draft_workspace_bytes(model.handle, A, max_ctx, total_ctx))
+
+
+def project_context_kv(model: Model, x, pos0: Sequence[int], input_kind: int = INPUT_CONTEXT_HIDDEN,
+                       k_out=None, v_out=None, workspace=None, stream=None):
+    """deepspec.ts, #projectContextKVRows.  x [B, L, H] (or [B, L, fc_in] for
+    target features), act dtype, on the GPU.  Returns per-layer (K, V) lists,
+    each [B, nKv, L, hd]."""
+    import torch
+    cfg = model.cfg
+    B, L = int(x.shape[0]), int(x.shape[1])
+    nL = cfg.num_hidden_layers
+    if k_out is None:
+        k_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
+        v_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
+    n = project_workspace_bytes(model, input_kind, B, L)
+    if workspace is None or workspace.numel() < n:
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
+    pos = (ctypes.c_int32 * B)(*[int(p) for p in pos0])
+    kp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in k_out])
+    vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_out])
+    _check(_lib.dspark_project_context_kv(model.handle, input_kind, x.data_ptr(), B, L, pos, kp, vp,
+                                          workspace.data_ptr(), n, _stream_handle(stream)))
+    return k_out, v_out
+
+
+class DraftCall:
+    """Marshalled arguments of one dspark_draft_rows call, reusable so that a
+    timing loop re-issues the same call without Python-side allocation."""
+
+    def __init__(self, model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+                 positions: Sequence[int], collect_logits: bool = False, workspace=None, tokens=None):
+        import torch
+        cfg = model.cfg
+        A = len(anchors)
+        nL = cfg.num_hidden_layers
+        self.model = model
+        self.A = A
+        self.keep = (k_rows, v_rows)
+        self.kp = (ctypes.c_void_p * (nL * A))(*[k_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+        self.vp = (ctypes.c_void_p * (nL * A))(*[v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+        self.lens = (ctypes.c_int32 * A)(*[int(v) for v in ctx_lens])
+        self.anchors = (ctypes.c_int32 * A)(*[int(v) for v in anchors])
+        self.positions = (ctypes.c_int32 * A)(*[int(v) for v in positions])
+        self.tokens = tokens if tokens is not None else torch.empty(A, cfg.gamma, dtype=torch.int32, device="cuda")
+        self.logits = (torch.empty(A, cfg.gamma, cfg.V, dtype=torch.float32, device="cuda")
+                       if collect_logits else None)
+        n = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
+        self.ws = workspace if workspace is not None and workspace.numel() >= n else torch.empty(
+            n, dtype=torch.uint8, device="cuda")
+        self.nbytes = n
+
+    def __call__(self, stream=None):
+        m = self.model
+        _check(_lib.dspark_draft_rows(m.handle, self.A, self.kp, self.vp, self.lens, self.anchors, self.positions,
+                                      self.tokens.data_ptr(), _ptr(self.logits),
+                                      _ptr(m.aux), self.ws.data_ptr(), self.nbytes, _stream_handle(stream)))
+        return self.tokens
+
+
+def draft_rows(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+               positions: Sequence[int], collect_logits: bool = False, stream=None):
+    """deepspec.ts, draftRows.  k_rows[l][a], v_rows[l][a]: row a's layer-l
+    context K/V [nKv, ctx_len[a], hd] on the GPU.  Returns (tokens [A, gamma]
+    int32 on the GPU, logits [A, gamma, V] fp32 or None)."""
+    call = DraftCall(model, k_rows, v_rows, ctx_lens, anchors, positions, collect_logits)
+    call(stream)
+    return call.tokens, call.logits
+
+
+def draft_block(model: Model, k_ctx, v_ctx, anchor: int, position: int, collect_logits: bool = True,
+                stream=None):
+    """deepspec-module.ts, draftBlock: one row.  k_ctx[l], v_ctx[l]:
+    [nKv, ctx_len, hd].  Returns (tokens [gamma], logits [gamma, V] or None)."""
+    import torch
+    cfg = model.cfg
+    nL = cfg.num_hidden_layers
+    L = int(k_ctx[0].shape[1])
+    tokens = torch.empty(cfg.gamma, dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.gamma, cfg.V, dtype=torch.float32, device="cuda") if collect_logits else None
+    n = draft_workspace_bytes(model, 1, L, L)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    kp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in k_ctx])
+    vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_ctx])
+    _check(_lib.dspark_draft_block(model.handle, kp, vp, L, int(anchor), int(position), tokens.data_ptr(),
+                                   _ptr(logits), _ptr(model.aux), ws.data_ptr(), n, _stream_handle(stream)))
+    return tokens, logits

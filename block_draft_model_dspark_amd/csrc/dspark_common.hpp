@@ -1,0 +1,132 @@
+// Shared device helpers for the gfx950 DSpark kernels: bf16 conversion, the
+// hi/lo bf16 split that carries fp32 activations through bf16 MFMA, the
+// 16x16x32 bf16 MFMA, and wave64 reductions.
+//
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16, wave64), lane l, g = l >> 4:
+//   A (16 rows x 32 k): row l & 15, k = 8g .. 8g+7 (eight bf16)
+//   B (32 k x 16 cols): col l & 15, k = 8g .. 8g+7
+//   D (16 x 16 f32):    col l & 15, rows 4g .. 4g+3
+// Any permutation of k applied identically to A and B leaves D unchanged; the
+// kernels use that freedom to match operands to natural memory order.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  __bf16 b = (__bf16)f;  // round to nearest even (v_cvt_pk_bf16_f32)
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// load one activation/norm element stored as f32 (bf16 == false) or bf16
+__device__ __forceinline__ float ld_act(const void* p, int64_t i, bool bf16) {
+  return bf16 ? bf2f(((const uint16_t*)p)[i]) : ((const float*)p)[i];
+}
+__device__ __forceinline__ void st_act(void* p, int64_t i, float v, bool bf16) {
+  if (bf16) ((uint16_t*)p)[i] = f2bf(v);
+  else ((float*)p)[i] = v;
+}
+
+// x ~= hi + lo with both bf16: hi = rne(x), lo = rne(x - hi)
+__device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __bf16 h = (__bf16)v[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(v[i] - (float)h);
+  }
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* v) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)v[i];
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+// block-wide sum; `red` holds >= blockDim/64 floats; all threads get the result
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+__device__ __forceinline__ float block_max(float v, float* red) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = (blockDim.x + 63) >> 6;
+  v = wave_max(v);
+  __syncthreads();
+  if (l == 0) red[w] = v;
+  __syncthreads();
+  float t = -INFINITY;
+  for (int i = 0; i < nw; ++i) t = fmaxf(t, red[i]);
+  return t;
+}
+
+// (value, index) argmax: larger value wins, lower index on equal values
+__device__ __forceinline__ bool better(float u, int i, float bu, int bi) {
+  return u > bu || (u == bu && i < bi);
+}
+__device__ __forceinline__ void wave_argmax(float& u, int& i) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float ou = __shfl_xor(u, o);
+    int oi = __shfl_xor(i, o);
+    if (better(ou, oi, u, i)) { u = ou; i = oi; }
+  }
+}
+__device__ __forceinline__ void block_argmax(float& u, int& i, float* redu, int* redi) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = (blockDim.x + 63) >> 6;
+  wave_argmax(u, i);
+  __syncthreads();
+  if (l == 0) { redu[w] = u; redi[w] = i; }
+  __syncthreads();
+  u = redu[0];
+  i = redi[0];
+  for (int k = 1; k < nw; ++k)
+    if (better(redu[k], redi[k], u, i)) { u = redu[k]; i = redi[k]; }
+}
+
+// RoPE angle for pair k at integer position pos, in double: pos divided by the
+// wavelength theta^(2k/hd) for the first nrot pairs, 0 (identity) beyond
+__device__ __forceinline__ void rope_cs(int64_t pos, int k, int hd, double theta, int nrot, float& c, float& s) {
+  if (k >= nrot) { c = 1.f; s = 0.f; return; }
+  double ang = (double)pos / pow(theta, (2.0 * k) / (double)hd);
+  double sd, cd;
+  sincos(ang, &sd, &cd);
+  c = (float)cd;
+  s = (float)sd;
+}
+
+// gelu_pytorch_tanh in fp32
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * x * (1.f + tanhf(k0 * (x + 0.044715f * x * x * x)));
+}
+
+}  // namespace dsp

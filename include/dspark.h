@@ -1,0 +1,182 @@
+/*
+ * dspark.h -- C ABI of the MI355X (gfx950) DSpark draft-round library.
+ *
+ * One draft round of the DeepSpec DSpark semi-autoregressive drafter, as the
+ * page "@mlx-bun/inference 0.0.0-stage -> 1.0.0,
+ * package/src/models/speculative/deepspec.ts" (cited "deepspec.ts") and its
+ * earlier revision "mlx-bun 0.2.0 -> 0.4.0,
+ * package/src/spec/dspark/deepspec-module.ts" (cited "deepspec-module.ts")
+ * transcribe it:
+ *   context rows -> per-layer context K/V   (dspark_project_context_kv)
+ *   [anchor, MASK x (gamma-1)] -> backbone -> softcapped logits -> greedy
+ *   Markov walk                              (dspark_draft_rows / _block)
+ *
+ * Conventions for every call:
+ *  - Pointers named *_dev are device pointers on the current HIP device;
+ *    *_host are host pointers read before the call returns.
+ *  - Every check runs on the host before any HIP call.  A non-OK status
+ *    means nothing was enqueued and no output was touched;
+ *    dspark_last_error() then describes the problem (thread-local).
+ *  - Work is enqueued on `stream` and is asynchronous; device faults surface
+ *    at the caller's next synchronisation of that stream.
+ *  - The library allocates no device memory.  Weights are borrowed for the
+ *    model's lifetime; every other pointer only for the duration of the call
+ *    and the work it enqueues.  No C++ exception crosses this boundary.
+ *  - Calls on one model may overlap only if they use distinct workspaces.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSPARK_OK = 0,
+  DSPARK_ERR_INVALID_ARG = 1, /* null pointer, non-positive size, id or position out of range */
+  DSPARK_ERR_SHAPE = 2,       /* sizes that disagree with the model or with each other */
+  DSPARK_ERR_UNSUPPORTED = 3, /* config variant the drafter refuses, or a dtype/shape not built */
+  DSPARK_ERR_WORKSPACE = 4,   /* workspace or aux buffer too small / misaligned */
+  DSPARK_ERR_HIP = 5          /* a HIP launch error, with hipGetErrorString in the message */
+} dspark_status;
+
+typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1, DSPARK_Q4 = 2 } dspark_dtype;
+
+/* Drafter config: the config.json fields of deepspec.ts, DeepspecConfig and
+ * readConfig.  readConfig refuses attention_k_eq_v == 0, a Markov head other
+ * than "vanilla" when markov_rank > 0, and any activation other than
+ * gelu_pytorch_tanh; dspark_model_create refuses the same with
+ * DSPARK_ERR_UNSUPPORTED. */
+typedef struct {
+  int32_t hidden_size;                /* H */
+  int32_t num_hidden_layers;
+  int32_t num_attention_heads;        /* nH */
+  int32_t global_head_dim;            /* hd: 64, 128 or 256 */
+  int32_t num_global_key_value_heads; /* nKv, divides nH */
+  int32_t intermediate_size;          /* I */
+  int32_t vocab_size;                 /* V */
+  int32_t block_size;                 /* gamma, 1..32 */
+  int32_t mask_token_id;
+  int32_t markov_rank;                /* r; 0 = no Markov head (plain argmax) */
+  int32_t attention_k_eq_v;           /* must be 1 */
+  int32_t markov_head_vanilla;        /* must be 1 when markov_rank > 0 */
+  int32_t activation_gelu_tanh;       /* must be 1 */
+  int32_t fc_in;                      /* taps * target hidden; 0 = no fc / hidden_norm */
+  double rope_theta;
+  double partial_rotary_factor;
+  double rms_norm_eps;
+  double final_logit_softcapping;     /* <= 0: no softcap */
+  int32_t weight_dtype;               /* matmul weights and gather tables: F32, BF16 or Q4 */
+  int32_t act_dtype;                  /* norm vectors, layer_scalar, context K/V, X inputs: F32 or BF16 */
+  int32_t group_size;                 /* Q4 group along the input axis (64) */
+} dspark_config;
+
+/* One checkpoint tensor (deepspec.ts, DeepspecDrafter constructor keys, e.g.
+ * "layers.0.self_attn.q_proj.weight", "markov_head.markov_w1.weight").
+ * Matrices are [rows=out, cols=in] row-major and are read in that storage
+ * order, never transposed or copied.  Vectors ([n]) use rows = n, cols = 1.
+ * Q4: data = uint32 [rows, cols/8], code j of a word in bits 4j..4j+3;
+ * scales, biases = bf16 [rows, cols/group]; value = scale * code + bias. */
+typedef struct {
+  const char* name;
+  int32_t dtype;
+  const void* data;
+  const void* scales;
+  const void* biases;
+  int64_t rows;
+  int64_t cols;
+} dspark_weight;
+
+typedef struct dspark_model dspark_model;
+
+/* Validate the config and the weight table and build a model handle that
+ * borrows the device pointers.  Missing, misshapen or mistyped tensors give
+ * DSPARK_ERR_SHAPE; refused variants DSPARK_ERR_UNSUPPORTED. */
+dspark_status dspark_model_create(const dspark_config* cfg, const dspark_weight* table, int n,
+                                  dspark_model** out);
+void dspark_model_destroy(dspark_model* m);
+
+/* Per-model derived data the Markov walk uses to skip vocabulary entries that
+ * cannot win a step (row norms of markov_w2 and the largest markov_w1 row
+ * norm).  The caller allocates `aux_bytes` of device memory, calls prepare
+ * once (asynchronously on `stream`), and keeps the buffer alive and unchanged
+ * while the model is used. */
+size_t dspark_model_aux_bytes(const dspark_model* m);
+dspark_status dspark_model_prepare(dspark_model* m, void* aux_dev, size_t aux_bytes, hipStream_t stream);
+
+/* Input of dspark_project_context_kv. */
+typedef enum {
+  DSPARK_INPUT_CONTEXT_HIDDEN = 0, /* x [B, L, H] (act dtype): already projected context rows */
+  DSPARK_INPUT_TARGET_FEATURES = 1 /* x [B, L, fc_in] (act dtype): concatenated target taps;
+                                      runs fc then hidden_norm first (deepspec.ts, #projectContext) */
+} dspark_input_kind;
+
+size_t dspark_project_workspace_bytes(const dspark_model* m, int input_kind, int B, int L);
+
+/* deepspec.ts, #projectContextKVRows (and deepspec-module.ts,
+ * projectContextKV): for every layer, k = k_proj(ctx); V = weightless
+ * RMSNorm(k); K = RoPE(RMSNorm(k; k_norm)) at positions pos0[b] + i.
+ *   x_dev        input per `input_kind`, row-major, act dtype
+ *   pos0_host[B] first absolute position of each batch row (>= 0)
+ *   k_out_dev[l], v_out_dev[l]  per layer, [B, nKv, L, hd] act dtype
+ * Workspace: dspark_project_workspace_bytes(m, input_kind, B, L) bytes,
+ * 256-byte aligned. */
+dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, const void* x_dev, int B, int L,
+                                        const int32_t* pos0_host, void* const* k_out_dev, void* const* v_out_dev,
+                                        void* ws_dev, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace for dspark_draft_rows with A rows whose context lengths sum to at
+ * most total_ctx and none exceeds max_ctx. */
+size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, int64_t total_ctx);
+
+/* deepspec.ts, draftRows at temperature 0 with confidence truncation off
+ * (every row keeps its full block):
+ *   ids = [anchor_a, MASK x (gamma-1)] -> #forwardBackbone over each row's own
+ *   context K/V ++ its block -> #computeLogits -> sequential Markov walk.
+ *   k_ctx_dev[l*A + a], v_ctx_dev[l*A + a]  row a's layer-l context K/V,
+ *       [nKv, ctx_len[a], hd] act dtype (rows stored independently; each
+ *       row attends only its own context)
+ *   ctx_len_host[A]    0 <= ctx_len[a] <= max_ctx of the workspace
+ *   anchors_host[A]    0 <= anchor < V
+ *   positions_host[A]  absolute position of each block's first slot (>= 0)
+ *   tokens_dev[A*gamma] int32 output, row-major [A, gamma]
+ *   logits_dev          NULL, or float [A, gamma, V] base logits (after
+ *                       softcap, before the Markov bias)
+ *   aux_dev             the buffer filled by dspark_model_prepare
+ * A is at most 64. */
+dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
+                                float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
+                                hipStream_t stream);
+
+/* deepspec-module.ts, draftBlock: draftRows with one row. */
+dspark_status dspark_draft_block(const dspark_model* m, const void* const* k_ctx_dev, const void* const* v_ctx_dev,
+                                 int32_t ctx_len, int32_t anchor, int32_t position, int32_t* tokens_dev,
+                                 float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Optional per-kernel timing (benchmarks and diagnostics).  While enabled,
+ * each kernel launch is bracketed by two HIP events recorded on the launch
+ * stream.  dspark_profile_read waits for those events, writes up to `max`
+ * records (one per kernel role, e.g. "gemm.lm_head", "attn"), returns the
+ * number written and clears the log.  Process-wide; not for concurrent use. */
+typedef struct {
+  const char* name;  /* static string owned by the library */
+  int32_t launches;
+  double ms;         /* summed event-to-event time */
+} dspark_kernel_time;
+void dspark_profile_enable(int on);
+int dspark_profile_read(dspark_kernel_time* out, int max);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char* dspark_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DSPARK_H */

@@ -1,0 +1,158 @@
+"""CPU-side checks of the C ABI: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any HIP call
+(no compute runs here; the device pointers given are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dspark.h")
+
+
+@pytest.fixture(scope="module")
+def dsp():
+    import block_draft_model_dspark_amd as dsp
+    if not os.path.exists(dsp.LIB_PATH):
+        from block_draft_model_dspark_amd import build
+        build.build()
+    dsp.load_library()
+    return dsp
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(dspark_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_binding_agree(dsp):
+    decl = declared_functions()
+    assert set(decl) == set(dsp.EXPORTED), decl
+
+
+def test_every_declared_symbol_is_exported(dsp):
+    lib = ctypes.CDLL(dsp.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+FAKE = 0x10000  # never dereferenced: all paths below fail validation first
+
+
+def fake_table(dsp, cfg, drop=None, bad_shape=None):
+    names = synth.tensor_names(cfg, with_fc=False)
+    table = (dsp.Weight * len(names))()
+    keep = []
+    n = 0
+    for name in names:
+        if name == drop:
+            continue
+        shape = list(synth.tensor_shape(cfg, name))
+        if name == bad_shape:
+            shape[0] += 16
+        kind = cfg.weight_dtype if synth.gen.is_matrix(name) else cfg.act_dtype
+        b = name.encode()
+        keep.append(b)
+        table[n].name = b
+        table[n].dtype = {"f32": 0, "bf16": 1, "q4": 2}[kind]
+        table[n].data = FAKE
+        table[n].scales = FAKE
+        table[n].biases = FAKE
+        table[n].rows = shape[0]
+        table[n].cols = shape[1] if len(shape) > 1 else 1
+        n += 1
+    return table, n, keep
+
+
+def make_config(dsp, cfg, **over):
+    c = dsp.Config()
+    for f, _ in dsp.Config._fields_:
+        if hasattr(cfg, f) and getattr(cfg, f) is not None and not isinstance(getattr(cfg, f), str):
+            setattr(c, f, getattr(cfg, f))
+    c.attention_k_eq_v = 1
+    c.markov_head_vanilla = 1
+    c.activation_gelu_tanh = 1
+    c.fc_in = 0
+    c.final_logit_softcapping = cfg.final_logit_softcapping or 0.0
+    c.weight_dtype = {"f32": 0, "bf16": 1, "q4": 2}[cfg.weight_dtype]
+    c.act_dtype = {"f32": 0, "bf16": 1, "q4": 2}[cfg.act_dtype]
+    for k, v in over.items():
+        setattr(c, k, v)
+    return c
+
+
+def create(dsp, c, table, n):
+    h = ctypes.c_void_p()
+    st = dsp._lib.dspark_model_create(ctypes.byref(c), table, n, ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("attention_k_eq_v", 0, 3), ("markov_head_vanilla", 0, 3), ("activation_gelu_tanh", 0, 3),
+    ("global_head_dim", 96, 3), ("num_global_key_value_heads", 3, 2), ("block_size", 0, 1),
+    ("mask_token_id", 5000, 1), ("vocab_size", 1000, 3)])
+def test_config_guards(dsp, field, value, status):
+    cfg = synth.TINY
+    table, n, keep = fake_table(dsp, cfg)
+    c = make_config(dsp, cfg, **{field: value})
+    st, _ = create(dsp, c, table, n)
+    assert st == status, dsp._lib.dspark_last_error()
+    assert dsp._lib.dspark_last_error()
+
+
+def test_missing_and_misshapen_tensors(dsp):
+    cfg = synth.TINY
+    c = make_config(dsp, cfg)
+    table, n, keep = fake_table(dsp, cfg, drop="layers.0.mlp.up_proj.weight")
+    st, _ = create(dsp, c, table, n)
+    assert st == 2 and b"up_proj" in dsp._lib.dspark_last_error()
+    table, n, keep = fake_table(dsp, cfg, bad_shape="lm_head.weight")
+    st, _ = create(dsp, c, table, n)
+    assert st == 2 and b"lm_head" in dsp._lib.dspark_last_error()
+
+
+def test_draft_rows_host_validation(dsp):
+    """A model over fake pointers validates calls without touching the GPU."""
+    cfg = synth.TINY
+    c = make_config(dsp, cfg)
+    table, n, keep = fake_table(dsp, cfg)
+    st, h = create(dsp, c, table, n)
+    assert st == 0
+    lib = dsp._lib
+    P = ctypes.c_void_p
+    kp = (P * 1)(FAKE)
+    lens = (ctypes.c_int32 * 1)(32)
+    pos = (ctypes.c_int32 * 1)(32)
+    ws_need = lib.dspark_draft_workspace_bytes(h, 1, 32, 32)
+    assert ws_need > 0
+
+    def call(anchor=5, A=1, ws=ws_need, ws_ptr=FAKE * 16, aux=FAKE, tok=FAKE):
+        anc = (ctypes.c_int32 * 1)(anchor)
+        return lib.dspark_draft_rows(h, A, kp, kp, lens, anc, pos, tok, None, aux, ws_ptr, ws, None)
+
+    assert call(anchor=-1) == 1
+    assert call(anchor=cfg.V) == 1
+    assert call(A=0) == 1
+    assert call(A=65) == 3
+    assert call(ws=ws_need - 1) == 4
+    assert call(ws_ptr=FAKE * 16 + 8) == 4
+    assert call(aux=None) == 1
+    assert call(tok=None) == 1
+    bad_lens = (ctypes.c_int32 * 1)(-1)
+    anc = (ctypes.c_int32 * 1)(5)
+    assert lib.dspark_draft_rows(h, 1, kp, kp, bad_lens, anc, pos, FAKE, None, FAKE, FAKE * 16, ws_need, None) == 1
+    nullk = (P * 1)(None)
+    assert lib.dspark_draft_rows(h, 1, nullk, nullk, lens, anc, pos, FAKE, None, FAKE, FAKE * 16, ws_need, None) == 1
+    # projection
+    n_ws = lib.dspark_project_workspace_bytes(h, 0, 1, 32)
+    p0 = (ctypes.c_int32 * 1)(-3)
+    outs = (P * 1)(FAKE)
+    assert lib.dspark_project_context_kv(h, 0, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws, None) == 1
+    p0[0] = 0
+    assert lib.dspark_project_context_kv(h, 1, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws, None) == 3  # no fc
+    assert lib.dspark_project_context_kv(h, 0, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws - 1, None) == 4
+    assert lib.dspark_project_context_kv(h, 7, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws, None) == 1
+    lib.dspark_model_destroy(h)
