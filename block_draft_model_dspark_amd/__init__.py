@@ -59,11 +59,12 @@ class Weight(ctypes.Structure):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libdspark.so; raises if it is not built (no fallback path)."""
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libdspark.so (or `path`); raises if it is not built (no fallback path)."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run block_draft_model_dspark_amd/build.py")
     lib = ctypes.CDLL(path)

@@ -112,39 +112,42 @@ RopeCfg rope_of(const dspark_model* m) {
 
 // ---- GEMM planning --------------------------------------------------------
 struct GemmPlan {
-  int mt, kc, S, kslice;
-  size_t pbytes;
+  int mt, kc, S, kslice, xmode;
+  size_t pbytes;   // split-K partials
+  size_t cwords;   // reduction counters
 };
 
-GemmPlan plan_gemm(int wk, bool xbf, int M, int N, int K) {
+GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   GemmPlan p;
   // row tiles per workgroup: 1 for M <= 16, else 4 (2 and 3 are not enabled)
   p.mt = M <= 16 ? 1 : 4;
   int kc = wk == WK_F32 ? 256 : 512;
-  while (kc > 128 && gemm_lds_bytes(wk, xbf, p.mt, kc) > 65536) kc /= 2;
+  while (kc > 128 && gemm_lds_bytes(wk, xmode, p.mt, kc) > 65536) kc /= 2;
   const int mblocks = ceil_div(M, 16 * p.mt);
-  const int ntw = ceil_div(N / 16, 4);
-  if (M <= 64) {
-    // split K so the weight stream spreads over >= 512 workgroups
-    while (kc > 128 && (int64_t)ntw * mblocks * ceil_div(K, kc) < 512) kc /= 2;
-    if (kc > K) kc = K;
-    p.kc = kc;
-    p.kslice = kc;
-    p.S = ceil_div(K, kc);
-  } else {
-    if (kc > K) kc = K;
-    p.kc = kc;
-    p.S = 1;
-    p.kslice = ceil_div(K, kc) * kc;
+  const int wgs = (N / 64) * mblocks;
+  // split K only when the grid is too small to keep HBM busy (a weight
+  // stream needs many workgroups in flight); slices are multiples of 64 and
+  // at most 16 per column block (one batch of partial loads in the reduction)
+  const int target = 512;
+  int kslice = ceil_div(K, 64) * 64;
+  if (wgs < target) {
+    const int st = std::min(16, ceil_div(target, wgs));
+    kslice = std::max(128, ceil_div(ceil_div(K, st), 64) * 64);
+    kslice = std::min(kslice, ceil_div(K, 64) * 64);
   }
-  p.pbytes = (size_t)p.S * M * N * 4;
+  p.S = ceil_div(K, kslice);
+  p.kslice = kslice;
+  p.kc = std::min(kc, kslice);
+  p.xmode = xmode;
+  p.pbytes = p.S > 1 ? (size_t)p.S * M * N * 4 : 0;
+  p.cwords = gemm_counter_words(M, N, p.mt, group_cols);
   return p;
 }
 
-hipError_t run_gemm(const GemmPlan& p, GemmArgs a, int wk, bool xbf, hipStream_t st) {
+hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st) {
   a.kslice = p.kslice;
   a.kc = p.kc;
-  return launch_gemm(a, wk, xbf, p.mt, p.S, st);
+  return launch_gemm(a, e, epi, wk, p.xmode, p.mt, p.S, st);
 }
 
 GemmSeg seg_of(const Mat& w, int n0) {
@@ -159,29 +162,34 @@ GemmSeg seg_of(const Mat& w, int n0) {
 
 // ---- draft workspace layout ---------------------------------------------
 struct DraftLayout {
-  size_t h, x, P, q, kb, vb, opart, ml, z, lo, top, total;
+  size_t hA, hB, Y, sums, rt, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, top, total;
   GemmPlan qk, o, gu, dn, lm;
+  size_t cwords;
+  int nsplit_max;
 };
 
-int attn_split(int64_t total_keys) {
-  int64_t s = (total_keys + 511) / 512;
-  s = (s + 31) / 32 * 32;
-  return (int)std::max<int64_t>(64, s);
+// context keys per attention split: a multiple of the 32-key staging chunk,
+// grown with the total context so that at most ~512 context splits exist
+int attn_split(int64_t total_ctx) {
+  int64_t s = (total_ctx + 511) / 512;
+  s = (s + ATT_KEYS - 1) / ATT_KEYS * ATT_KEYS;
+  return (int)std::max<int64_t>(ATT_KEYS, s);
 }
 
 DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   const dspark_config& c = m->c;
   const int M = A * c.block_size, H = c.hidden_size, I = c.intermediate_size, hd = c.global_head_dim;
+  const int nH = c.num_attention_heads, nKv = c.num_global_key_value_heads;
   const int wk = c.weight_dtype;
   DraftLayout d;
-  d.qk = plan_gemm(wk, false, M, (c.num_attention_heads + c.num_global_key_value_heads) * hd, H);
-  d.o = plan_gemm(wk, false, M, H, c.num_attention_heads * hd);
-  d.gu = plan_gemm(wk, false, M, 2 * I, H);
-  d.dn = plan_gemm(wk, false, M, H, I);
-  d.lm = plan_gemm(wk, false, M, c.vocab_size, H);
-  const size_t pmax = std::max({d.qk.pbytes, d.o.pbytes, d.gu.pbytes, d.dn.pbytes, d.lm.pbytes});
-  const int xw = std::max({H, I, c.num_attention_heads * hd});
-  const int nsplit_max = 512 + A;
+  d.qk = plan_gemm(wk, XM_NORM, M, (nH + nKv) * hd, H, 0);
+  d.o = plan_gemm(wk, XM_F32, M, H, nH * hd, 0);
+  d.gu = plan_gemm(wk, XM_NORM, M, 2 * I, H, 0);
+  d.dn = plan_gemm(wk, XM_F32, M, H, I, 0);
+  d.lm = plan_gemm(wk, XM_NORM, M, c.vocab_size, H, 0);
+  const size_t pmax = std::max({d.qk.pbytes, d.o.pbytes, d.gu.pbytes, d.dn.pbytes, d.lm.pbytes, (size_t)4});
+  d.cwords = std::max({d.qk.cwords, d.o.cwords, d.gu.cwords, d.dn.cwords, d.lm.cwords});
+  d.nsplit_max = 512 + 2 * A;
   const int NC = nc_of(m);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -189,16 +197,23 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
     off = align256(off + bytes);
     return o;
   };
-  d.h = take((size_t)M * H * 4);
-  d.x = take((size_t)M * xw * 4);
+  d.hA = take((size_t)M * H * 4);
+  d.hB = take((size_t)M * H * 4);
+  d.Y = take((size_t)M * H * 4);
+  d.sums = take((size_t)(H / 64) * M * 16);
+  d.rt = take((size_t)M * (hd / 2) * 8);
+  d.O = take((size_t)M * nH * hd * 4);
+  d.act = take((size_t)M * I * 4);
   d.P = take(pmax);
-  d.q = take((size_t)A * c.num_global_key_value_heads * m->nq * hd * 4);
-  d.kb = take((size_t)A * c.num_global_key_value_heads * c.block_size * hd * 4);
-  d.vb = take((size_t)A * c.num_global_key_value_heads * c.block_size * hd * 4);
-  d.opart = take((size_t)nsplit_max * c.num_global_key_value_heads * m->nq * hd * 4);
-  d.ml = take((size_t)nsplit_max * c.num_global_key_value_heads * m->nq * 2 * 4);
+  d.cnt = take(d.cwords * 4);
+  d.q = take((size_t)A * nKv * m->nq * hd * 4);
+  d.kb = take((size_t)A * nKv * c.block_size * hd * 4);
+  d.vb = take((size_t)A * nKv * c.block_size * hd * 4);
+  d.ssq = take((size_t)(nH + nKv) * (hd / 64) * M * 4);
+  d.opart = take((size_t)d.nsplit_max * nKv * m->nq * hd * 4);
+  d.ml = take((size_t)d.nsplit_max * nKv * m->nq * 2 * 4);
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
-  d.lo = take((size_t)M * NC * 4);
+  d.lohi = take((size_t)M * NC * 8);
   d.top = take((size_t)M * NC * WALK_TOP * 8);
   d.total = off;
   return d;
@@ -206,32 +221,42 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
 
 // ---- projection workspace layout -----------------------------------------
 struct ProjLayout {
-  size_t P1, C, P2, total;
+  size_t P, Y, C, sums, rt, cnt, total;
   GemmPlan fc, kp;
+  size_t cwords;
   int lay_per_gemm;
 };
 
+int xmode_in(const dspark_model* m) { return m->c.act_dtype == DSPARK_BF16 ? XM_BF16 : XM_F32; }
+
 ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   const dspark_config& c = m->c;
-  const int M = B * L, H = c.hidden_size;
+  const int M = B * L, H = c.hidden_size, hd = c.global_head_dim, nKv = c.num_global_key_value_heads;
   ProjLayout p{};
   p.lay_per_gemm = std::min(c.num_hidden_layers, MAX_SEG);
+  const int Nk = p.lay_per_gemm * nKv * hd;
+  const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
+  size_t pbytes = 4;
+  if (feats) {
+    p.fc = plan_gemm(c.weight_dtype, xmode_in(m), M, H, c.fc_in, 0);
+    pbytes = std::max(pbytes, p.fc.pbytes);
+    p.cwords = p.fc.cwords;
+  }
+  p.kp = plan_gemm(c.weight_dtype, feats ? XM_NORM : xmode_in(m), M, Nk, H, hd);
+  pbytes = std::max(pbytes, p.kp.pbytes);
+  p.cwords = std::max(p.cwords, p.kp.cwords);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;
     off = align256(off + bytes);
     return o;
   };
-  const bool in_bf16 = c.act_dtype == DSPARK_BF16;
-  if (input_kind == DSPARK_INPUT_TARGET_FEATURES) {
-    p.fc = plan_gemm(c.weight_dtype, in_bf16, M, H, c.fc_in);
-    p.P1 = take(p.fc.pbytes);
-    p.C = take((size_t)M * H * 4);
-    p.kp = plan_gemm(c.weight_dtype, false, M, p.lay_per_gemm * c.num_global_key_value_heads * c.global_head_dim, H);
-  } else {
-    p.kp = plan_gemm(c.weight_dtype, in_bf16, M, p.lay_per_gemm * c.num_global_key_value_heads * c.global_head_dim, H);
-  }
-  p.P2 = take(p.kp.pbytes);
+  p.P = take(pbytes);
+  p.Y = take((size_t)M * Nk * 4);
+  p.C = feats ? take((size_t)M * H * 4) : 0;
+  p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
+  p.rt = take((size_t)M * (hd / 2) * 8);
+  p.cnt = take(p.cwords * 4);
   p.total = off;
   return p;
 }
@@ -256,8 +281,8 @@ dspark_status check_config(const dspark_config& c) {
     return fail(DSPARK_ERR_UNSUPPORTED, "hidden, intermediate and fc input sizes must be multiples of 64");
   if (c.hidden_size > 8192 || c.intermediate_size > (1 << 20))
     return fail(DSPARK_ERR_UNSUPPORTED, "hidden_size > 8192 not built");
-  if (c.vocab_size % 16 || c.vocab_size > 1024 * WALK_CHUNK)
-    return fail(DSPARK_ERR_UNSUPPORTED, "vocab_size must be a multiple of 16 and at most %d", 1024 * WALK_CHUNK);
+  if (c.vocab_size % 64 || c.vocab_size > 1024 * WALK_CHUNK)
+    return fail(DSPARK_ERR_UNSUPPORTED, "vocab_size must be a multiple of 64 and at most %d", 1024 * WALK_CHUNK);
   if (c.block_size > 32) return fail(DSPARK_ERR_UNSUPPORTED, "block_size > 32 not built");
   if ((c.num_attention_heads / c.num_global_key_value_heads) * c.block_size > 128)
     return fail(DSPARK_ERR_UNSUPPORTED, "more than 128 query rows per kv head not built");
@@ -453,10 +478,21 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
 
   char* ws = (char*)ws_dev;
   const int M = B * L, H = c.hidden_size, hd = c.global_head_dim, nKv = c.num_global_key_value_heads;
-  const bool in_bf16 = c.act_dtype == DSPARK_BF16;
-  const void* X = x_dev;
-  bool xbf = in_bf16;
-  if (input_kind == DSPARK_INPUT_TARGET_FEATURES) {
+  unsigned* cnt = (unsigned*)(ws + p.cnt);
+  float2* rt = (float2*)(ws + p.rt);
+  PrepArgs pr{};
+  pr.cnt = cnt;
+  pr.ncnt = (int)p.cwords;
+  pr.rt = rt;
+  pr.B = B;
+  pr.L = L;
+  pr.rope = rope_of(m);
+  for (int b = 0; b < B; ++b) pr.pos0[b] = pos0_host[b];
+  HIPCHECK(timed("prep", stream, [&] { return launch_prep(pr, stream); }));
+  const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
+  NormIn nin{};
+  if (feats) {
+    // fc rows and their statistics; k_proj reads hidden_norm(fc x)
     GemmArgs g{};
     g.X = x_dev;
     g.ldx = c.fc_in;
@@ -465,56 +501,53 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     g.K = c.fc_in;
     g.nseg = 1;
     g.seg[0] = seg_of(m->fc, 0);
-    g.P = (float*)(ws + p.P1);
-    HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, m->fc.kind, in_bf16, stream); }));
-    RowEpiArgs r{};
-    r.P = g.P;
-    r.S = p.fc.S;
-    r.M = M;
-    r.N = H;
-    r.w1 = m->hidden_norm;
-    r.act_bf16 = act_bf16(m);
-    r.eps = (float)c.rms_norm_eps;
-    r.x = (float*)(ws + p.C);
-    r.mode = 2;
-    HIPCHECK(timed("norm.hidden", stream, [&] { return launch_row_epi(r, stream); }));
-    X = r.x;
-    xbf = false;
+    g.P = (float*)(ws + p.P);
+    EpiArgs e{};
+    e.Y = (float*)(ws + p.C);
+    e.cnt = cnt;
+    e.act_bf16 = act_bf16(m);
+    e.h = nullptr;
+    e.w1 = m->hidden_norm;
+    e.sums = (float4*)(ws + p.sums);
+    HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream); }));
+    nin.y = e.Y;
+    nin.sums = e.sums;
+    nin.nparts = H / 64;
+    nin.w1 = m->hidden_norm;
+    nin.eps = (float)c.rms_norm_eps;
+    nin.act_bf16 = act_bf16(m);
   }
   for (int l0 = 0; l0 < c.num_hidden_layers; l0 += p.lay_per_gemm) {
     const int nl = std::min(p.lay_per_gemm, c.num_hidden_layers - l0);
     GemmArgs g{};
-    g.X = X;
+    g.X = x_dev;
     g.ldx = H;
     g.M = M;
     g.N = nl * nKv * hd;
     g.K = H;
     g.nseg = nl;
     for (int i = 0; i < nl; ++i) g.seg[i] = seg_of(m->L[l0 + i].k, i * nKv * hd);
-    g.P = (float*)(ws + p.P2);
+    g.P = (float*)(ws + p.P);
+    g.nin = nin;
     GemmPlan gp = p.kp;
-    if (nl != p.lay_per_gemm) gp = plan_gemm(c.weight_dtype, xbf, M, g.N, H);
-    HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, m->L[l0].k.kind, xbf, stream); }));
-    KvEpiArgs e{};
-    e.P = g.P;
-    e.S = gp.S;
-    e.M = M;
-    e.N = g.N;
-    e.B = B;
-    e.L = L;
-    e.layers = nl;
-    e.nKv = nKv;
-    e.hd = hd;
+    if (nl != p.lay_per_gemm) gp = plan_gemm(c.weight_dtype, p.kp.xmode, M, g.N, H, hd);
+    EpiArgs e{};
+    e.Y = (float*)(ws + p.Y);
+    e.cnt = cnt;
+    e.group_cols = hd;
     e.eps = (float)c.rms_norm_eps;
     e.act_bf16 = act_bf16(m);
-    e.rope = rope_of(m);
-    for (int b = 0; b < B; ++b) e.pos0[b] = pos0_host[b];
+    e.nH = c.num_attention_heads;
+    e.nKv = nKv;
+    e.hd = hd;
+    e.rt = rt;
+    e.L = L;
     for (int i = 0; i < nl; ++i) {
-      e.kn[i] = m->L[l0 + i].kn;
+      e.kn_l[i] = m->L[l0 + i].kn;
       e.kout[i] = k_out_dev[l0 + i];
       e.vout[i] = v_out_dev[l0 + i];
     }
-    HIPCHECK(timed("kv_epilogue", stream, [&] { return launch_kv_epi(e, stream); }));
+    HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream); }));
   }
   return DSPARK_OK;
 }
@@ -565,31 +598,45 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   const int M = A * G, H = c.hidden_size, I = c.intermediate_size, hd = c.global_head_dim;
   const int nH = c.num_attention_heads, nKv = c.num_global_key_value_heads;
   const float eps = (float)c.rms_norm_eps;
-  float* h = (float*)(ws + d.h);
-  float* x = (float*)(ws + d.x);
+  const int abf = act_bf16(m);
+  float* hA = (float*)(ws + d.hA);  // the embedding, then each layer's post-attention residual
+  float* hB = (float*)(ws + d.hB);  // the residual entering each layer
+  float* Y = (float*)(ws + d.Y);
+  float4* sums = (float4*)(ws + d.sums);
+  float2* rt = (float2*)(ws + d.rt);
+  float* O = (float*)(ws + d.O);
+  float* act = (float*)(ws + d.act);
   float* P = (float*)(ws + d.P);
+  unsigned* cnt = (unsigned*)(ws + d.cnt);
   const int wk = m->lm.kind;
+  const int NC = nc_of(m);
 
-  // attention split plan
-  const int split = attn_split(total_keys);
+  // attention split plan: context splits of `split` keys, then the block split
+  const int split = attn_split(total_keys - (int64_t)A * G);
   AttnArgs at{};
   MergeArgs mg{};
   int nsplit = 0;
   for (int a = 0; a < A; ++a) {
     at.split_off[a] = nsplit;
-    nsplit += ceil_div(ctx_len_host[a] + G, split);
+    nsplit += ceil_div(ctx_len_host[a], split) + 1;
     at.len[a] = ctx_len_host[a];
   }
   at.split_off[A] = nsplit;
+  if (nsplit > d.nsplit_max) return fail(DSPARK_ERR_SHAPE, "attention splits %d exceed the plan", nsplit);
   std::memcpy(mg.split_off, at.split_off, sizeof at.split_off);
   at.A = A;
   at.gamma = G;
   at.nKv = nKv;
+  at.nH = nH;
   at.nq = m->nq;
   at.split = split;
+  at.M = M;
+  at.hd = hd;
+  at.eps = eps;
   at.q = (const float*)(ws + d.q);
   at.kb = (const float*)(ws + d.kb);
   at.vb = (const float*)(ws + d.vb);
+  at.ssq = (const float*)(ws + d.ssq);
   at.opart = (float*)(ws + d.opart);
   at.ml = (float*)(ws + d.ml);
   mg.A = A;
@@ -600,29 +647,67 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   mg.hd = hd;
   mg.opart = at.opart;
   mg.ml = at.ml;
-  mg.O = x;
+  mg.O = O;
 
-  EmbedArgs e{};
-  e.E = m->embed.w;
-  e.Es = m->embed.s;
-  e.Eb = m->embed.b;
-  e.ekind = m->embed.kind;
-  e.group = c.group_size;
-  e.w_in = m->L[0].in;
-  e.act_bf16 = act_bf16(m);
-  e.H = H;
+  EmbedArgs em{};
+  em.E = m->embed.w;
+  em.Es = m->embed.s;
+  em.Eb = m->embed.b;
+  em.ekind = m->embed.kind;
+  em.group = c.group_size;
+  em.H = H;
+  em.scale = (float)std::sqrt((double)H);
+  em.mask_id = c.mask_token_id;
+  em.h = hA;
+  em.sums = sums;
+  em.rt = rt;
+  em.rope = rope_of(m);
+  em.cnt = cnt;
+  em.ncnt = (int)d.cwords;
+  em.rows = rows;
+  HIPCHECK(timed("embed", stream, [&] { return launch_embed(em, M, stream); }));
+
+  // input rows of a GEMM: x = rms((h + rms(y) w1) sc) w2 from the statistics
+  auto norm_in = [&](const float* h, const float* y, const void* w1, const void* sc, const void* w2, float* hout) {
+    NormIn n{};
+    n.h = h;
+    n.y = y;
+    n.sums = sums;
+    n.nparts = H / 64;
+    n.w1 = w1;
+    n.w2 = w2;
+    n.sc = sc;
+    n.hout = hout;
+    n.eps = eps;
+    n.act_bf16 = abf;
+    return n;
+  };
+
+  EpiArgs e{};
+  e.cnt = cnt;
   e.eps = eps;
-  e.scale = (float)std::sqrt((double)H);
-  e.mask_id = c.mask_token_id;
-  e.h = h;
-  e.x = x;
-  e.rows = rows;
-  HIPCHECK(timed("embed", stream, [&] { return launch_embed(e, M, stream); }));
+  e.act_bf16 = abf;
+  e.nH = nH;
+  e.nKv = nKv;
+  e.hd = hd;
+  e.gamma = G;
+  e.rt = rt;
+  e.q = (float*)(ws + d.q);
+  e.kb = (float*)(ws + d.kb);
+  e.vb = (float*)(ws + d.vb);
+  e.ssq = (float*)(ws + d.ssq);
+  e.act = act;
+  e.sums = sums;
 
+  // The residual stream is formed lazily: a sublayer output y stays in Y
+  // with its row statistics, and the next GEMM's staging adds it to the
+  // residual it read and writes the sum (q|k writes hB, gate|up writes hA).
+  const float* y_prev = nullptr;  // pending sublayer output folded into the next input norm
+  const void* w1_prev = nullptr;
+  const void* sc_prev = nullptr;
   for (int l = 0; l < nL; ++l) {
     const LayerW& W = m->L[l];
     GemmArgs g{};
-    g.X = x;
     g.ldx = H;
     g.M = M;
     g.N = (nH + nKv) * hd;
@@ -631,36 +716,20 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.seg[0] = seg_of(W.q, 0);
     g.seg[1] = seg_of(W.k, nH * hd);
     g.P = P;
-    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, wk, false, stream); }));
-
-    QkEpiArgs q{};
-    q.P = P;
-    q.S = d.qk.S;
-    q.M = M;
-    q.N = g.N;
-    q.qn = W.qn;
-    q.kn = W.kn;
-    q.act_bf16 = act_bf16(m);
-    q.nH = nH;
-    q.nKv = nKv;
-    q.hd = hd;
-    q.eps = eps;
-    q.rope = rope_of(m);
-    q.q = (float*)(ws + d.q);
-    q.kb = (float*)(ws + d.kb);
-    q.vb = (float*)(ws + d.vb);
-    q.rows = rows;
-    HIPCHECK(timed("qk_epilogue", stream, [&] { return launch_qk_epi(q, stream); }));
+    g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, W.in, hB);
+    e.qn = W.qn;
+    e.kn = W.kn;
+    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream); }));
 
     for (int a = 0; a < A; ++a) {
       at.row[a].k = k_ctx_dev[l * A + a];
       at.row[a].v = v_ctx_dev[l * A + a];
     }
-    HIPCHECK(timed("attn", stream, [&] { return launch_attn(at, hd, c.act_dtype == DSPARK_BF16, nsplit, stream); }));
+    HIPCHECK(timed("attn", stream, [&] { return launch_attn(at, c.act_dtype == DSPARK_BF16, nsplit, stream); }));
     HIPCHECK(timed("attn_merge", stream, [&] { return launch_merge(mg, stream); }));
 
     g = GemmArgs{};
-    g.X = x;
+    g.X = O;
     g.ldx = nH * hd;
     g.M = M;
     g.N = H;
@@ -668,23 +737,12 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.nseg = 1;
     g.seg[0] = seg_of(W.o, 0);
     g.P = P;
-    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, wk, false, stream); }));
-    RowEpiArgs r{};
-    r.P = P;
-    r.S = d.o.S;
-    r.M = M;
-    r.N = H;
-    r.w1 = W.pa;
-    r.w2 = W.pf;
-    r.act_bf16 = act_bf16(m);
-    r.eps = eps;
-    r.h = h;
-    r.x = x;
-    r.mode = 0;
-    HIPCHECK(timed("attn_out_epilogue", stream, [&] { return launch_row_epi(r, stream); }));
+    e.Y = Y;
+    e.h = hB;
+    e.w1 = W.pa;
+    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream); }));
 
     g = GemmArgs{};
-    g.X = x;
     g.ldx = H;
     g.M = M;
     g.N = 2 * I;
@@ -693,17 +751,11 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.seg[0] = seg_of(W.g, 0);
     g.seg[1] = seg_of(W.u, I);
     g.P = P;
-    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, wk, false, stream); }));
-    GateUpArgs gu{};
-    gu.P = P;
-    gu.S = d.gu.S;
-    gu.M = M;
-    gu.I = I;
-    gu.x = x;
-    HIPCHECK(timed("gelu_gate", stream, [&] { return launch_gateup(gu, stream); }));
+    g.nin = norm_in(hB, Y, W.pa, nullptr, W.pf, hA);
+    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream); }));
 
     g = GemmArgs{};
-    g.X = x;
+    g.X = act;
     g.ldx = I;
     g.M = M;
     g.N = H;
@@ -711,25 +763,16 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.nseg = 1;
     g.seg[0] = seg_of(W.d, 0);
     g.P = P;
-    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, wk, false, stream); }));
-    r = RowEpiArgs{};
-    r.P = P;
-    r.S = d.dn.S;
-    r.M = M;
-    r.N = H;
-    r.w1 = W.pff;
-    r.w2 = l + 1 < nL ? m->L[l + 1].in : m->norm;
-    r.scalar = W.scalar;
-    r.act_bf16 = act_bf16(m);
-    r.eps = eps;
-    r.h = h;
-    r.x = x;
-    r.mode = 1;
-    HIPCHECK(timed("mlp_out_epilogue", stream, [&] { return launch_row_epi(r, stream); }));
+    e.Y = Y;
+    e.h = hA;
+    e.w1 = W.pff;
+    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream); }));
+    y_prev = Y;
+    w1_prev = W.pff;
+    sc_prev = W.scalar;
   }
 
   GemmArgs g{};
-  g.X = x;
   g.ldx = H;
   g.M = M;
   g.N = c.vocab_size;
@@ -737,21 +780,15 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   g.nseg = 1;
   g.seg[0] = seg_of(m->lm, 0);
   g.P = P;
-  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, wk, false, stream); }));
-
-  const int NC = nc_of(m);
-  LmEpiArgs le{};
-  le.P = P;
-  le.S = d.lm.S;
-  le.M = M;
-  le.V = c.vocab_size;
-  le.cap = c.final_logit_softcapping > 0 ? (float)c.final_logit_softcapping : 0.f;
-  le.aux = c.markov_rank > 0 ? (const float*)aux_dev : nullptr;
-  le.z = logits_dev ? logits_dev : (float*)(ws + d.z);
-  le.lo = (float*)(ws + d.lo);
-  le.top = (float2*)(ws + d.top);
-  le.NC = NC;
-  HIPCHECK(timed("logits_epilogue", stream, [&] { return launch_lm_epi(le, stream); }));
+  g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, m->norm, nullptr);
+  float* z = logits_dev ? logits_dev : (float*)(ws + d.z);
+  e.Y = z;
+  e.cap = c.final_logit_softcapping > 0 ? (float)c.final_logit_softcapping : 0.f;
+  e.aux = c.markov_rank > 0 ? (const float*)aux_dev : nullptr;
+  e.lohi = (float2*)(ws + d.lohi);
+  e.top = (float2*)(ws + d.top);
+  e.NC = NC;
+  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream); }));
 
   WalkArgs w{};
   w.rows = rows;
@@ -760,9 +797,9 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   w.rank = c.markov_rank;
   w.wkind = m->w1.kind;
   w.group = c.group_size;
-  w.z = le.z;
-  w.lo = le.lo;
-  w.top = le.top;
+  w.z = z;
+  w.lohi = e.lohi;
+  w.top = e.top;
   w.w1 = m->w1.w; w.w1s = m->w1.s; w.w1b = m->w1.b;
   w.w2 = m->w2.w; w.w2s = m->w2.s; w.w2b = m->w2.b;
   w.tokens = tokens_dev;

@@ -30,6 +30,40 @@ __device__ __forceinline__ uint16_t f2bf(float f) {
 __device__ __forceinline__ float ld_act(const void* p, int64_t i, bool bf16) {
   return bf16 ? bf2f(((const uint16_t*)p)[i]) : ((const float*)p)[i];
 }
+// The same with one 4-byte load whatever the dtype (for vectors of even
+// length), so that the conversion happens after the load is issued and a
+// run of such loads stays in flight together.
+__device__ __forceinline__ float ld_act_v(const void* p, int64_t i, bool bf16) {
+  const uint32_t w = *(const uint32_t*)((const char*)p + (bf16 ? (i >> 1) * 4 : i * 4));
+  return __uint_as_float(bf16 ? ((i & 1) ? (w & 0xFFFF0000u) : (w << 16)) : w);
+}
+// eight consecutive act-dtype values from index k (k % 8 == 0), raw words
+struct Raw8 {
+  u32x4 a, b;
+};
+__device__ __forceinline__ Raw8 ld_act8(const void* p, int64_t k, bool bf16) {
+  Raw8 r;
+  if (bf16) {
+    r.a = *(const u32x4*)((const uint16_t*)p + k);
+    r.b = r.a;
+  } else {
+    r.a = *(const u32x4*)((const float*)p + k);
+    r.b = *(const u32x4*)((const float*)p + k + 4);
+  }
+  return r;
+}
+__device__ __forceinline__ void cvt_act8(const Raw8& r, bool bf16, float* v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (bf16) {
+      v[2 * q] = __uint_as_float(r.a[q] << 16);
+      v[2 * q + 1] = __uint_as_float(r.a[q] & 0xFFFF0000u);
+    } else {
+      v[q] = __uint_as_float(r.a[q]);
+      v[4 + q] = __uint_as_float(r.b[q]);
+    }
+  }
+}
 __device__ __forceinline__ void st_act(void* p, int64_t i, float v, bool bf16) {
   if (bf16) ((uint16_t*)p)[i] = f2bf(v);
   else ((float*)p)[i] = v;
@@ -112,15 +146,19 @@ __device__ __forceinline__ void block_argmax(float& u, int& i, float* redu, int*
     if (better(redu[k], redi[k], u, i)) { u = redu[k]; i = redi[k]; }
 }
 
-// RoPE angle for pair k at integer position pos, in double: pos divided by the
-// wavelength theta^(2k/hd) for the first nrot pairs, 0 (identity) beyond
-__device__ __forceinline__ void rope_cs(int64_t pos, int k, int hd, double theta, int nrot, float& c, float& s) {
-  if (k >= nrot) { c = 1.f; s = 0.f; return; }
-  double ang = (double)pos / pow(theta, (2.0 * k) / (double)hd);
-  double sd, cd;
-  sincos(ang, &sd, &cd);
-  c = (float)cd;
-  s = (float)sd;
+// RoPE for pair k: angle = pos / theta^(2k/hd) for the first nrot pairs, 0
+// (identity) beyond.  rope_inv gives 1 / wavelength in double (once per pair);
+// rope_cs forms the angle in double, reduces it to [-pi, pi] in double
+// (positions reach 32k+, where an fp32 angle would be off by ~1e-3 rad) and
+// takes sin / cos of the reduced angle in fp32.
+__device__ __forceinline__ double rope_inv(int k, int hd, double theta, int nrot) {
+  return k < nrot ? 1.0 / pow(theta, (2.0 * k) / (double)hd) : 0.0;
+}
+__device__ __forceinline__ void rope_cs(int64_t pos, double inv, float& c, float& s) {
+  const double two_pi = 6.283185307179586;
+  const double ang = (double)pos * inv;
+  const double red = ang - rint(ang * (1.0 / two_pi)) * two_pi;
+  sincosf((float)red, &s, &c);
 }
 
 // gelu_pytorch_tanh in fp32

@@ -1,19 +1,27 @@
-// Weight-streaming GEMM y = x . W^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16).
+// Weight-streaming GEMM y = x . W^T on bf16 MFMA (v_mfma_f32_16x16x32_bf16)
+// with the split-K reduction and the consumer's epilogue fused in.
 //
 // Used for every linear layer of the drafter (deepspec.ts, matmulW: x @ W^T
 // with W kept in its [out, in] storage): q|k, o, gate|up, down, lm_head, fc
 // and the per-layer k_proj of the context projection.
 //
 // Work split: a 256-thread workgroup = 4 wave64s; wave w owns one 16-column
-// output tile (blockIdx.x*4 + w) and the workgroup owns one K slice
-// (blockIdx.y) and one block of MT*16 rows (blockIdx.z).  Each wave issues all
-// weight loads of a K sub-slice straight from HBM into registers first (16 B
-// per lane per 32-wide k step, the B operand layout needs no shuffling), then
-// the workgroup stages the activation sub-slice into LDS already split into
-// bf16 hi + lo halves in A-operand order, and the MFMAs run hi and lo against
-// the same weight registers.  Activations are fp32 in HBM; hi + lo carries
-// ~16 mantissa bits, which the draft round needs (scale-1 attention amplifies
-// input rounding).  bf16 inputs (the X-is-bf16 variant) are exact in hi.
+// output tile of the workgroup's 64-column block (blockIdx.x), the workgroup
+// owns one K slice (blockIdx.y) and one block of MT*16 rows (blockIdx.z).
+// Each wave issues all weight loads of a K sub-slice straight from HBM into
+// registers (16 B per lane per 32-wide k step: the B operand layout needs no
+// shuffling), then the workgroup stages the activation sub-slice into LDS
+// split into bf16 hi + lo halves in A-operand order, and the MFMAs run hi
+// and lo against the same weight registers.  Activations are fp32 in HBM;
+// hi + lo carries ~16 mantissa bits, which the draft round needs (scale-1
+// attention amplifies input rounding).  bf16 inputs are exact in hi alone.
+//
+// Input rows (XM_NORM): the sandwich norms of the backbone are applied while
+// staging, from the producer's per-64-column row statistics (NormIn), so no
+// kernel ever walks a whole row alone:
+//   hn = (h + rms(y) * w1) * sc,   x = rms(hn) * w2,
+// with sum hn^2 = sc^2 (sum h^2 + 2 r1 sum h w1 y + r1^2 sum (w1 y)^2).
+// Column block 0 also writes hn, the next residual.
 //
 // Weight kinds:
 //   bf16: used as is.
@@ -21,9 +29,14 @@
 //   q4  : affine 4-bit, groups of 64 along K.  Codes become the exact bf16
 //         values 1 + q/16 with two bit operations per pair, and
 //         sum_k x (s q + b) = 16 s * sum x (1 + q/16) + (b - 16 s) * sum x
-//         is applied per group after the group's MFMAs (sum x per row and
-//         group comes from the staging pass), so no dequantised weight is
-//         ever rounded.
+//         is applied per group after the group's MFMAs.
+//
+// Reduction (no extra launch, deterministic): with S > 1 K slices every
+// workgroup writes its partial tile, and the last one to arrive at its
+// column block (counter) sums the S partials in slice order and runs the
+// epilogue on its 64 columns.  Only the context K/V epilogue (a head's
+// RMSNorm, which must be final in the cache) needs a second arrival per
+// head.  Counters are zero on entry and are left zero.
 #include "dspark_kernels.hpp"
 #include "dspark_common.hpp"
 
@@ -40,11 +53,460 @@ __device__ __forceinline__ bf16x8 q4_decode(uint32_t w) {
   return __builtin_bit_cast(bf16x8, r);
 }
 
-template <int WK, bool XBF, int MT>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
+// Split-K partials (and the reduced tile a head epilogue reads) may be
+// written and read on different XCDs, whose L2 caches are not coherent with
+// each other.  They are stored and loaded with agent-scope atomic accesses
+// (per-access coherence bits, write-through / re-fetch at the device
+// coherence point) instead of cache-wide L2 write-back and invalidate.
+__device__ __forceinline__ void st_coh(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_coh(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// true in the workgroup that is the `total`-th to arrive at *ctr (which it
+// resets).  Every wave first drains its outstanding stores, so the
+// workgroup's coherent stores are complete before the counter moves.
+__device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned total, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == total - 1;
+    if (last) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = last;
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+// first output column of wave w in column block c.  gate|up: waves 0,1 take
+// gate columns 32c.., waves 2,3 the matching up columns.  q|k heads: waves
+// 0,1 take head dims [32c', 32c'+32), waves 2,3 their RoPE partners + hd/2
+// (c' = c mod hd/64), so a workgroup holds whole rotation pairs.
+template <int EPI>
+__device__ __forceinline__ int wave_col(int c, int w, int N, int hd) {
+  if constexpr (EPI == EPI_GELU) return (w >> 1) * (N >> 1) + 32 * c + 16 * (w & 1);
+  if constexpr (EPI == EPI_QK) {
+    const int hj = hd >> 6, head = c / hj, cp = c - head * hj;
+    return head * hd + (w >> 1) * (hd >> 1) + 32 * cp + 16 * (w & 1);
+  }
+  return 64 * c + 16 * w;
+}
+
+// ---------------------------------------------------------------------------
+// input rows (XM_NORM): per-row factors (r1, r2) and sc from the statistics
+// ---------------------------------------------------------------------------
+template <int MT>
+__device__ void norm_rows(const GemmArgs& g, int mbase, float2* rs) {
+  const NormIn& n = g.nin;
+  const float sc = n.sc ? ld_act(n.sc, 0, n.act_bf16) : 1.f;
+  const int tid = threadIdx.x, sub = tid & 15;
+  const float inv_k = 1.f / (float)g.K;
+#pragma unroll
+  for (int r0 = 0; r0 < MT * 16; r0 += 16) {
+    const int ml = r0 + (tid >> 4);
+    const int m = min(mbase + ml, g.M - 1);
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p0 = 0; p0 < n.nparts; p0 += 128) {
+      float4 v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = n.sums[(int64_t)min(p0 + sub + 16 * i, n.nparts - 1) * g.M + m];
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (p0 + sub + 16 * i < n.nparts) {
+          s.x += v[i].x;
+          s.y += v[i].y;
+          s.z += v[i].z;
+          s.w += v[i].w;
+        }
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      s.x += __shfl_xor(s.x, o);
+      s.y += __shfl_xor(s.y, o);
+      s.z += __shfl_xor(s.z, o);
+      s.w += __shfl_xor(s.w, o);
+    }
+    if (sub == 0) {
+      const float r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
+      const float t = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
+      const float r2 = 1.f / sqrtf(t * inv_k + n.eps);
+      rs[ml] = make_float2(r1, r2);
+    }
+  }
+  if (tid == 0) rs[MT * 16] = make_float2(sc, 0.f);
+}
+
+// ---------------------------------------------------------------------------
+// epilogues on the workgroup's reduced tile (acc: wave's 16 columns, rows
+// 16t + 4g + i of the row block)
+// ---------------------------------------------------------------------------
+
+// deepspec.ts, #forwardBackbone, q / block-k path of one head part:
+//   q = RoPE(q_norm(q_proj x)), v_b = rms(k_proj x), k_b = RoPE(k_norm(k_proj x))
+// The RMS factor of a head needs all hd columns; it is a per-row scalar that
+// commutes with RoPE, so this stores RoPE(w * y) and y unscaled plus the
+// part's sum y^2, and the attention kernel applies the factor.
+template <int MT>
+__device__ void epi_qk(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, float* tile) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tile[(wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
+  __syncthreads();
+  const int hd = e.hd, half = hd >> 1, hj = hd >> 6, head = cb / hj, cp = cb - head * hj;
+  const bool isq = head < e.nH;
+  const void* nw = isq ? e.qn : e.kn;
+  const int rep = e.nH / e.nKv, nq = rep * e.gamma;
+  constexpr int IT = MT * 16 * 32 / 256;
+  float ya[IT], yb[IT], wa[IT], wb[IT];
+  float2 cs[IT];
+#pragma unroll
+  for (int u = 0; u < IT; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 5, j = idx & 31, d = 32 * cp + j;
+    const int m = min(mbase + r, g.M - 1);
+    wa[u] = ld_act_v(nw, d, e.act_bf16);
+    wb[u] = ld_act_v(nw, d + half, e.act_bf16);
+    cs[u] = e.rt[(int64_t)m * half + d];
+    ya[u] = tile[((j >> 4) * MT * 16 + r) * 16 + (j & 15)];
+    yb[u] = tile[((2 + (j >> 4)) * MT * 16 + r) * 16 + (j & 15)];
+  }
+#pragma unroll
+  for (int u = 0; u < IT; ++u) {
+    const int idx = tid + 256 * u, r = idx >> 5, j = idx & 31, d = 32 * cp + j;
+    const int m = mbase + r;
+    const float ta = ya[u] * wa[u], tb = yb[u] * wb[u];
+    const float oa = ta * cs[u].x - tb * cs[u].y, ob = tb * cs[u].x + ta * cs[u].y;
+    float ss = ya[u] * ya[u] + yb[u] * yb[u];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    if (m < g.M) {
+      const int arow = m / e.gamma, gs = m - arow * e.gamma;
+      if (isq) {
+        const int kvh = head / rep, hl = head - kvh * rep;
+        float* dst = e.q + (((int64_t)arow * e.nKv + kvh) * nq + hl * e.gamma + gs) * hd;
+        dst[d] = oa;
+        dst[d + half] = ob;
+      } else {
+        const int kvh = head - e.nH;
+        const int64_t off = (((int64_t)arow * e.nKv + kvh) * e.gamma + gs) * hd;
+        e.kb[off + d] = oa;
+        e.kb[off + d + half] = ob;
+        e.vb[off + d] = ya[u];
+        e.vb[off + d + half] = yb[u];
+      }
+      if (j == 0) e.ssq[(int64_t)(head * hj + cp) * g.M + m] = ss;
+    }
+  }
+}
+
+// sublayer output y of 64 columns: store it and the row statistics the next
+// GEMM's input norms are formed from (see NormIn)
+template <int MT>
+__device__ void epi_sums(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
+                         float* red) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+  const float w1 = ld_act_v(e.w1, n, e.act_bf16);
+  float hv[MT][4];
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = min(mbase + t * 16 + 4 * gq + i, g.M - 1);
+      hv[t][i] = e.h ? e.h[(int64_t)m * g.N + n] : 0.f;
+    }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int m = mbase + t * 16 + 4 * gq + i;
+      if (m < g.M) e.Y[(int64_t)m * g.N + n] = acc[t][i];
+    }
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float y = acc[t][i], wy = w1 * y, h = hv[t][i];
+      float s0 = y * y, s1 = h * wy, s2 = wy * wy, s3 = h * h;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        s0 += __shfl_xor(s0, o);
+        s1 += __shfl_xor(s1, o);
+        s2 += __shfl_xor(s2, o);
+        s3 += __shfl_xor(s3, o);
+      }
+      if ((lane & 15) == 0) {
+        float* p = red + ((wave * MT * 16) + t * 16 + 4 * gq + i) * 4;
+        p[0] = s0;
+        p[1] = s1;
+        p[2] = s2;
+        p[3] = s3;
+      }
+    }
+  __syncthreads();
+  for (int r = tid; r < MT * 16; r += 256) {
+    const int m = mbase + r;
+    if (m >= g.M) continue;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* p = red + ((w * MT * 16) + r) * 4;
+      s.x += p[0];
+      s.y += p[1];
+      s.z += p[2];
+      s.w += p[3];
+    }
+    e.sums[(int64_t)cb * g.M + m] = s;
+  }
+}
+
+// deepspec.ts, #computeLogits for one 64-entry vocabulary chunk:
+// z = cap * tanh(y / cap), plus the chunk statistics the walk prunes with.
+// For any previous token |markov_w2[v] . markov_w1[prev]| <= B_v :=
+// ||w2_v|| * max ||w1||, so an entry with z_v + B_v below max_u (z_u - B_u)
+// can never win a step.  Per (row, chunk): lo = max (z - B), hi = max (z + B)
+// and the WALK_TOP best z + B with their indices.
+template <int MT>
+__device__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
+                       float* tile) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+  const int V = g.N;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = t * 16 + 4 * gq + i, m = mbase + r;
+      float z = acc[t][i];
+      if (e.cap > 0.f) z = e.cap * tanhf(z / e.cap);
+      if (m < g.M) e.Y[(int64_t)m * V + n] = z;
+      tile[r * 64 + 16 * wave + (lane & 15)] = z;
+    }
+  __syncthreads();
+  const int v = 64 * cb + lane;
+  const float b = e.aux ? e.aux[v] * e.aux[V] * (1.f + 1e-5f) : 0.f;
+  for (int r = wave; r < MT * 16; r += 4) {
+    const int m = mbase + r;
+    if (m >= g.M) break;
+    const float z = tile[r * 64 + lane];
+    const float lo = wave_max(z - b);
+    float u = z + b;
+    float2* top = e.top + ((int64_t)m * e.NC + cb) * WALK_TOP;
+    float hi = 0.f;
+    for (int t = 0; t < WALK_TOP; ++t) {
+      float bu = u;
+      int bi = v;
+      wave_argmax(bu, bi);
+      if (t == 0) hi = bu;
+      if (lane == 0) top[t] = make_float2(bu, __int_as_float(bi));
+      if (v == bi) u = -INFINITY;
+    }
+    if (lane == 0) e.lohi[(int64_t)m * e.NC + cb] = make_float2(lo, hi);
+  }
+}
+
+// deepspec.ts, #projectContextKVRows for one (layer, kv head) and the rows
+// [m0, m1) of the row block: V = rms(k) (no weight, no RoPE);
+// K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
+// rows is issued before the first use.
+template <int MT>
+__device__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int hd = e.hd, HJ = hd >> 6, half = hd >> 1;
+  const int layer = grp / e.nKv, kvh = grp - layer * e.nKv;
+  float kw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) kw[j] = j < HJ ? ld_act_v(e.kn_l[layer], lane + 64 * j, e.act_bf16) : 0.f;
+  constexpr int RB = MT == 1 ? 4 : 8;  // rows per wave per batch
+  for (int mb = m0 + wave * RB; mb < m1; mb += 4 * RB) {
+    float y[RB][4];
+    float2 cs[RB][4];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int m = min(mb + rr, m1 - 1);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = lane + 64 * j;
+        y[rr][j] = j < HJ ? ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d) : 0.f;
+        cs[rr][j] = j < HJ ? e.rt[(int64_t)m * half + (d < half ? d : d - half)] : make_float2(1.f, 0.f);
+      }
+    }
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int m = mb + rr;
+      if (m >= m1) break;
+      const int b = m / e.L, i = m - b * e.L;
+      float ss = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) ss += y[rr][j] * y[rr][j];
+      const float r = 1.f / sqrtf(wave_sum(ss) / hd + e.eps);
+      float t[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) t[j] = y[rr][j] * r * kw[j];
+      const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < HJ) {
+          const int d = lane + 64 * j;
+          float partner;
+          if (HJ >= 2) partner = t[(j + HJ / 2) % HJ];
+          else partner = __shfl_xor(t[0], 32);
+          const float c = cs[rr][j].x, s = cs[rr][j].y;
+          st_act(e.vout[layer], off + d, y[rr][j] * r, e.act_bf16);
+          st_act(e.kout[layer], off + d, d < half ? t[j] * c - partner * s : t[j] * c + partner * s, e.act_bf16);
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// activation staging: items (row ml, 8 consecutive k) -> LDS hi / lo planes
+// ---------------------------------------------------------------------------
+template <int WK, int XM, int MT>
+__device__ __forceinline__ void stage_x(const GemmArgs& g, int mbase, int kc, int klen, u32x4* xhi, u32x4* xlo,
+                                        float* xsum, int nfull, int ngmax, const float2* rs, bool write_h) {
+  const int tid = threadIdx.x;
+  const int kq = klen >> 3;
+  const int nitems = MT * 16 * kq;
+  constexpr int XB = XM == XM_NORM ? 2 : 4;  // items per thread per batch, all loads in flight together
+  for (int base = 0; base < nitems; base += 256 * XB) {
+    float v[XB][8];
+    if constexpr (XM == XM_NORM) {
+      const NormIn& n = g.nin;
+      const bool bf = n.act_bf16 != 0;
+      f32x4 hv[XB][2], yv[XB][2];
+      Raw8 w1r[XB], w2r[XB];
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
+        const int64_t m = min(mbase + ml, g.M - 1);
+        const int64_t k = kc + 8 * k8;
+        if (n.h) {
+          hv[b][0] = *(const f32x4*)(n.h + m * g.K + k);
+          hv[b][1] = *(const f32x4*)(n.h + m * g.K + k + 4);
+        }
+        if (n.y) {
+          yv[b][0] = *(const f32x4*)(n.y + m * g.K + k);
+          yv[b][1] = *(const f32x4*)(n.y + m * g.K + k + 4);
+          w1r[b] = ld_act8(n.w1, k, bf);
+        }
+        if (n.w2) w2r[b] = ld_act8(n.w2, k, bf);
+      }
+      const float sc = rs[MT * 16].x;
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq, k8 = it - ml * kq;
+        const int m = mbase + ml;
+        const bool ok = it < nitems && m < g.M;
+        const float2 r = rs[ok ? ml : 0];
+        float w1[8], w2[8], hn[8];
+        if (n.y) cvt_act8(w1r[b], bf, w1);
+        if (n.w2) cvt_act8(w2r[b], bf, w2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float h = n.h ? hv[b][q >> 2][q & 3] : 0.f;
+          const float y = n.y ? yv[b][q >> 2][q & 3] * r.x * w1[q] : 0.f;
+          hn[q] = (h + y) * sc;
+          v[b][q] = ok ? (n.w2 ? hn[q] * r.y * w2[q] : hn[q]) : 0.f;
+        }
+        if (write_h && ok) {
+          float* dst = n.hout + (int64_t)m * g.K + kc + 8 * k8;
+          *(f32x4*)dst = f32x4{hn[0], hn[1], hn[2], hn[3]};
+          *(f32x4*)(dst + 4) = f32x4{hn[4], hn[5], hn[6], hn[7]};
+        }
+      }
+    } else if constexpr (XM == XM_BF16) {
+      u32x4 r[XB];
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
+        const int64_t m = min(mbase + ml, g.M - 1);
+        r[b] = *(const u32x4*)((const uint16_t*)g.X + m * g.ldx + kc + 8 * k8);
+      }
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq;
+        const bool ok = it < nitems && mbase + ml < g.M;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[b][2 * q] = ok ? __uint_as_float(r[b][q] << 16) : 0.f;
+          v[b][2 * q + 1] = ok ? __uint_as_float(r[b][q] & 0xFFFF0000u) : 0.f;
+        }
+      }
+    } else {
+      f32x4 r[XB][2];
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
+        const int64_t m = min(mbase + ml, g.M - 1);
+        const float* px = (const float*)g.X + m * g.ldx + kc + 8 * k8;
+        r[b][0] = *(const f32x4*)px;
+        r[b][1] = *(const f32x4*)(px + 4);
+      }
+#pragma unroll
+      for (int b = 0; b < XB; ++b) {
+        const int it = base + tid + 256 * b;
+        const int ml = it / kq;
+        const bool ok = it < nitems && mbase + ml < g.M;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[b][q] = ok ? r[b][q >> 2][q & 3] : 0.f;
+      }
+    }
+    // LDS writes in A-operand order
+#pragma unroll
+    for (int b = 0; b < XB; ++b) {
+      const int it = base + tid + 256 * b;
+      if (it >= nitems) break;
+      const int ml = it / kq, k8 = it - ml * kq;
+      int s, qg;
+      float e8[8];
+      if constexpr (WK == WK_Q4) {
+        const int grp = k8 >> 3, rr = k8 & 7;
+        qg = rr >> 1;
+        s = 2 * grp + (rr & 1);
+        const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+        float sum = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          e8[q] = v[b][perm[q]];
+          sum += v[b][q];
+        }
+        atomicAdd(&xsum[ml * ngmax + grp], sum);
+      } else {
+        s = k8 >> 2;
+        qg = k8 & 3;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) e8[q] = v[b][q];
+      }
+      const int slot = ((ml >> 4) * nfull + s) * 64 + qg * 16 + (ml & 15);
+      if constexpr (XM == XM_BF16) {
+        xhi[slot] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
+      } else {
+        bf16x8 h, l;
+        split8(e8, h, l);
+        xhi[slot] = __builtin_bit_cast(u32x4, h);
+        xlo[slot] = __builtin_bit_cast(u32x4, l);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+template <int WK, int XM, int MT, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e) {
   extern __shared__ __align__(16) unsigned char smem[];
+  __shared__ int last_flag;
+  __shared__ float2 rs[MT * 16 + 1];
   constexpr int KCMAX = (WK == WK_F32) ? 256 : 512;
   constexpr int SMAX = KCMAX / 32;
+  constexpr bool XBF = XM == XM_BF16;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const int KC = g.kc;
   const int nfull = KC >> 5;
@@ -53,15 +515,16 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
   u32x4* xlo = xhi + MT * nfull * 64;
   float* xsum = (float*)(xhi + (XBF ? 1 : 2) * MT * nfull * 64);
 
-  const int nt = blockIdx.x * 4 + wave;
-  const bool active = nt * 16 < g.N;
+  const int cb = blockIdx.x;
+  const int n0w = wave_col<EPI>(cb, wave, g.N, e.hd);
   int si = 0;
   for (int i = 1; i < g.nseg; ++i)
-    if (nt * 16 >= g.seg[i].n0) si = i;
-  const int64_t wrow = (int64_t)(nt * 16 - g.seg[si].n0 + (lane & 15));
+    if (n0w >= g.seg[i].n0) si = i;
+  const int64_t wrow = (int64_t)(n0w - g.seg[si].n0 + (lane & 15));
   const int mbase = blockIdx.z * (MT * 16);
   const int kbeg = blockIdx.y * g.kslice;
   const int kend = min(g.K, kbeg + g.kslice);
+  const bool write_h = XM == XM_NORM && g.nin.hout != nullptr && blockIdx.x == 0;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -75,193 +538,255 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g) {
     u32x4 wv[WK == WK_F32 ? 2 * SMAX : (WK == WK_BF16 ? SMAX : 1)];
     u32x2 wq[WK == WK_Q4 ? SMAX / 2 : 1];
     float qs[WK == WK_Q4 ? SMAX / 2 : 1], qb[WK == WK_Q4 ? SMAX / 2 : 1];
-    if (active) {
-      if constexpr (WK == WK_BF16) {
-        const uint16_t* p = (const uint16_t*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
+    if constexpr (WK == WK_BF16) {
+      const uint16_t* p = (const uint16_t*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < nsteps) wv[s] = *(const u32x4*)(p + 32 * s);
-      } else if constexpr (WK == WK_F32) {
-        const float* p = (const float*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
+      for (int s = 0; s < SMAX; ++s)
+        if (s < nsteps) wv[s] = __builtin_nontemporal_load((const u32x4*)(p + 32 * s));
+    } else if constexpr (WK == WK_F32) {
+      const float* p = (const float*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < nsteps) {
-            wv[2 * s] = *(const u32x4*)(p + 32 * s);
-            wv[2 * s + 1] = *(const u32x4*)(p + 32 * s + 4);
-          }
-      } else {
-        const uint32_t* p = (const uint32_t*)g.seg[si].w + wrow * (g.K >> 3) + (kc >> 3) + 2 * gq;
-        const uint16_t* ps = (const uint16_t*)g.seg[si].s + wrow * (g.K >> 6) + (kc >> 6);
-        const uint16_t* pb = (const uint16_t*)g.seg[si].b + wrow * (g.K >> 6) + (kc >> 6);
+      for (int s = 0; s < SMAX; ++s)
+        if (s < nsteps) {
+          wv[2 * s] = *(const u32x4*)(p + 32 * s);
+          wv[2 * s + 1] = *(const u32x4*)(p + 32 * s + 4);
+        }
+    } else {
+      const uint32_t* p = (const uint32_t*)g.seg[si].w + wrow * (g.K >> 3) + (kc >> 3) + 2 * gq;
+      const uint16_t* ps = (const uint16_t*)g.seg[si].s + wrow * (g.K >> 6) + (kc >> 6);
+      const uint16_t* pb = (const uint16_t*)g.seg[si].b + wrow * (g.K >> 6) + (kc >> 6);
 #pragma unroll
-        for (int j = 0; j < SMAX / 2; ++j)
-          if (2 * j < nsteps) {
-            wq[j] = *(const u32x2*)(p + 8 * j);
-            qs[j] = bf2f(ps[j]);
-            qb[j] = bf2f(pb[j]);
-          }
-      }
+      for (int j = 0; j < SMAX / 2; ++j)
+        if (2 * j < nsteps) {
+          wq[j] = *(const u32x2*)(p + 8 * j);
+          qs[j] = bf2f(ps[j]);
+          qb[j] = bf2f(pb[j]);
+        }
     }
 
     // 2. activation sub-slice -> LDS (hi / lo planes, A-operand order)
+    if constexpr (XM == XM_NORM) {
+      if (kc == kbeg) {
+        norm_rows<MT>(g, mbase, rs);
+        __syncthreads();
+      }
+    }
     if constexpr (WK == WK_Q4) {
       for (int i = tid; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
       __syncthreads();
     }
-    const int kq = klen >> 3;
-    for (int it = tid; it < MT * 16 * kq; it += 256) {
-      const int ml = it / kq, k8 = it - ml * kq;
-      const int m = mbase + ml;
-      float v[8];
-      if (m < g.M) {
-        if constexpr (XBF) {
-          u32x4 r = *(const u32x4*)((const uint16_t*)g.X + (int64_t)m * g.ldx + kc + 8 * k8);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            v[2 * e] = __uint_as_float(r[e] << 16);
-            v[2 * e + 1] = __uint_as_float(r[e] & 0xFFFF0000u);
-          }
-        } else {
-          const float* px = (const float*)g.X + (int64_t)m * g.ldx + kc + 8 * k8;
-          f32x4 a = *(const f32x4*)px, b = *(const f32x4*)(px + 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { v[e] = a[e]; v[4 + e] = b[e]; }
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = 0.f;
-      }
-      int s, qg;
-      float e8[8];
-      if constexpr (WK == WK_Q4) {
-        const int grp = k8 >> 3, r = k8 & 7;
-        qg = r >> 1;
-        s = 2 * grp + (r & 1);
-        const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { e8[e] = v[perm[e]]; sum += v[e]; }
-        atomicAdd(&xsum[ml * ngmax + grp], sum);
-      } else {
-        s = k8 >> 2;
-        qg = k8 & 3;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) e8[e] = v[e];
-      }
-      const int slot = ((ml >> 4) * nfull + s) * 64 + qg * 16 + (ml & 15);
-      if constexpr (XBF) {
-        xhi[slot] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
-      } else {
-        bf16x8 h, l;
-        split8(e8, h, l);
-        xhi[slot] = __builtin_bit_cast(u32x4, h);
-        xlo[slot] = __builtin_bit_cast(u32x4, l);
-      }
-    }
+    stage_x<WK, XM, MT>(g, mbase, kc, klen, xhi, xlo, xsum, nfull, ngmax, rs, write_h);
     __syncthreads();
 
     // 3. MFMAs
-    if (active) {
-      if constexpr (WK == WK_BF16) {
+    if constexpr (WK == WK_BF16) {
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < nsteps) {
-            const bf16x8 w = __builtin_bit_cast(bf16x8, wv[s]);
+      for (int s = 0; s < SMAX; ++s)
+        if (s < nsteps) {
+          const bf16x8 w = __builtin_bit_cast(bf16x8, wv[s]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const int o = (t * nfull + s) * 64 + lane;
+            acc[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, acc[t]);
+            if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, acc[t]);
+          }
+        }
+    } else if constexpr (WK == WK_F32) {
+#pragma unroll
+      for (int s = 0; s < SMAX; ++s)
+        if (s < nsteps) {
+          float w8[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            w8[q] = __uint_as_float(wv[2 * s][q]);
+            w8[4 + q] = __uint_as_float(wv[2 * s + 1][q]);
+          }
+          bf16x8 wh, wl;
+          split8(w8, wh, wl);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const int o = (t * nfull + s) * 64 + lane;
+            const bf16x8 xh = __builtin_bit_cast(bf16x8, xhi[o]);
+            acc[t] = mfma16(xh, wh, acc[t]);
+            acc[t] = mfma16(xh, wl, acc[t]);
+            if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wh, acc[t]);
+          }
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < SMAX / 2; ++j)
+        if (2 * j < nsteps) {
+          f32x4 tmp[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) tmp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int sub = 0; sub < 2; ++sub) {
+            const bf16x8 w = q4_decode(wq[j][sub]);
 #pragma unroll
             for (int t = 0; t < MT; ++t) {
-              const int o = (t * nfull + s) * 64 + lane;
-              acc[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, acc[t]);
-              if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, acc[t]);
+              const int o = (t * nfull + 2 * j + sub) * 64 + lane;
+              tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, tmp[t]);
+              if constexpr (!XBF) tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, tmp[t]);
             }
           }
-      } else if constexpr (WK == WK_F32) {
+          const float sc = 16.f * qs[j], bc = qb[j] - sc;
 #pragma unroll
-        for (int s = 0; s < SMAX; ++s)
-          if (s < nsteps) {
-            float w8[8];
+          for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              w8[e] = __uint_as_float(wv[2 * s][e]);
-              w8[4 + e] = __uint_as_float(wv[2 * s + 1][e]);
-            }
-            bf16x8 wh, wl;
-            split8(w8, wh, wl);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              const int o = (t * nfull + s) * 64 + lane;
-              const bf16x8 xh = __builtin_bit_cast(bf16x8, xhi[o]);
-              acc[t] = mfma16(xh, wh, acc[t]);
-              acc[t] = mfma16(xh, wl, acc[t]);
-              if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wh, acc[t]);
-            }
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < SMAX / 2; ++j)
-          if (2 * j < nsteps) {
-            f32x4 tmp[MT];
-#pragma unroll
-            for (int t = 0; t < MT; ++t) tmp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int sub = 0; sub < 2; ++sub) {
-              const bf16x8 w = q4_decode(wq[j][sub]);
-#pragma unroll
-              for (int t = 0; t < MT; ++t) {
-                const int o = (t * nfull + 2 * j + sub) * 64 + lane;
-                tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, tmp[t]);
-                if constexpr (!XBF) tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, tmp[t]);
-              }
-            }
-            const float sc = 16.f * qs[j], bc = qb[j] - sc;
-#pragma unroll
-            for (int t = 0; t < MT; ++t)
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-                acc[t][i] += sc * tmp[t][i] + bc * xsum[(t * 16 + 4 * gq + i) * ngmax + j];
-          }
-      }
+            for (int i = 0; i < 4; ++i)
+              acc[t][i] += sc * tmp[t][i] + bc * xsum[(t * 16 + 4 * gq + i) * ngmax + j];
+        }
     }
     __syncthreads();
   }
 
-  // 4. partial tile -> P[blockIdx.y]
-  if (active) {
+  // 4. split-K reduction in the last workgroup of this column block
+  const int S = gridDim.y;
+  const int ncb = gridDim.x;
+  const int n = n0w + (lane & 15);
+  if (S > 1) {
     float* out = g.P + (int64_t)blockIdx.y * g.M * g.N;
-    const int n = nt * 16 + (lane & 15);
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = mbase + t * 16 + 4 * gq + i;
-        if (m < g.M) out[(int64_t)m * g.N + n] = acc[t][i];
+        if (m < g.M) st_coh(out + (int64_t)m * g.N + n, acc[t][i]);
       }
+    if (!arrive_last(e.cnt + blockIdx.z * ncb + cb, S, &last_flag)) return;
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    constexpr int PB = MT == 1 ? 16 : 4;  // partial slices loaded per batch
+    for (int s0 = 0; s0 < S; s0 += PB) {
+      float part[PB][MT][4];
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = min(mbase + t * 16 + 4 * gq + i, g.M - 1);
+            part[q][t][i] = ld_coh(g.P + ((int64_t)min(s0 + q, S - 1) * g.M + m) * g.N + n);
+          }
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+        if (s0 + q < S)
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] += part[q][t][i];
+    }
+  }
+
+  // 5. epilogue
+  float* ep = (float*)smem;
+  if constexpr (EPI == EPI_GELU) {
+    // deepspec.ts, #geluTanhMlp: act = gelu_tanh(gate x) * up x; waves 0,1
+    // hold gate columns 32cb.., waves 2,3 the matching up columns
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ep[(wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
+    __syncthreads();
+    const int I = g.N >> 1;
+    for (int idx = tid; idx < MT * 16 * 32; idx += 256) {
+      const int r = idx >> 5, col = idx & 31;
+      const int m = mbase + r;
+      if (m >= g.M) continue;
+      const float gt = ep[((col >> 4) * MT * 16 + r) * 16 + (col & 15)];
+      const float up = ep[((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15)];
+      e.act[(int64_t)m * I + 32 * cb + col] = gelu_tanh(gt) * up;
+    }
+  } else if constexpr (EPI == EPI_QK) {
+    epi_qk<MT>(g, e, acc, mbase, cb, ep);
+  } else if constexpr (EPI == EPI_SUMS) {
+    epi_sums<MT>(g, e, acc, mbase, cb, n, ep);
+  } else if constexpr (EPI == EPI_LM) {
+    epi_lm<MT>(g, e, acc, mbase, cb, n, ep);
+  } else if constexpr (EPI == EPI_KV) {
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mbase + t * 16 + 4 * gq + i;
+        if (m < g.M) st_coh(e.Y + (int64_t)m * g.N + n, acc[t][i]);
+      }
+    const int gcols = e.group_cols;
+    const int grp = (64 * cb) / gcols;
+    const int ngroups = (g.N + gcols - 1) / gcols;
+    const int members = (min(gcols, g.N - grp * gcols) + 63) / 64;
+    if (!arrive_last(e.cnt + gridDim.z * ncb + blockIdx.z * ngroups + grp, members, &last_flag)) return;
+    epi_kv<MT>(g, e, mbase, min(g.M, mbase + MT * 16), grp);
   }
 }
 
-size_t gemm_lds_bytes(int wkind, bool x_bf16, int mt, int kc) {
-  size_t b = (size_t)mt * (kc / 32) * 64 * 16 * (x_bf16 ? 1 : 2);
+size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc) {
+  size_t b = (size_t)mt * (kc / 32) * 64 * 16 * (xmode == XM_BF16 ? 1 : 2);
   if (wkind == WK_Q4) b += (size_t)mt * 16 * (kc / 64) * 4;
-  return b;
+  const size_t tile = (size_t)mt * 16 * 64 * 4;  // epilogue tiles
+  return b > tile ? b : tile;
 }
 
-template <int WK, bool XBF>
-static hipError_t launch_mt(const GemmArgs& a, int mt, int S, hipStream_t st) {
-  const int mblocks = (a.M + mt * 16 - 1) / (mt * 16);
-  dim3 grid((a.N / 16 + 3) / 4, S, mblocks);
-  const size_t lds = gemm_lds_bytes(WK, XBF, mt, a.kc);
-  switch (mt) {
-    case 1: hipLaunchKernelGGL((k_gemm<WK, XBF, 1>), grid, dim3(256), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((k_gemm<WK, XBF, 2>), grid, dim3(256), lds, st, a); break;
-    case 3: hipLaunchKernelGGL((k_gemm<WK, XBF, 3>), grid, dim3(256), lds, st, a); break;
-    default: hipLaunchKernelGGL((k_gemm<WK, XBF, 4>), grid, dim3(256), lds, st, a); break;
+size_t gemm_counter_words(int M, int N, int mt, int group_cols) {
+  const size_t mblocks = (M + mt * 16 - 1) / (mt * 16);
+  const size_t ncb = N / 64;
+  const size_t ngroups = group_cols > 0 ? (N + group_cols - 1) / group_cols : 0;
+  return mblocks * (ncb + ngroups);
+}
+
+// input modes each epilogue is built for: the backbone GEMMs whose input is
+// a normed residual (q|k, gate|up, lm_head) read XM_NORM; o and down read
+// plain f32 rows; fc reads the target features (act dtype); k_proj reads the
+// context rows (act dtype) or fc's output through hidden_norm.
+template <int XM, int EPI>
+constexpr bool built() {
+  if constexpr (EPI == EPI_QK || EPI == EPI_GELU || EPI == EPI_LM) return XM == XM_NORM;
+  if constexpr (EPI == EPI_SUMS) return XM != XM_NORM;
+  return EPI == EPI_KV;
+}
+
+template <int WK, int XM, int MT, int EPI>
+static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStream_t st) {
+  if constexpr (built<XM, EPI>()) {
+    const int mblocks = (a.M + MT * 16 - 1) / (MT * 16);
+    const dim3 grid(a.N / 64, S, mblocks);
+    hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI>), grid, dim3(256), gemm_lds_bytes(WK, XM, MT, a.kc), st, a, e);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_gemm(const GemmArgs& a, int wkind, bool x_bf16, int mt, int S, hipStream_t st) {
-  if (wkind == WK_BF16) return x_bf16 ? launch_mt<WK_BF16, true>(a, mt, S, st) : launch_mt<WK_BF16, false>(a, mt, S, st);
-  if (wkind == WK_F32) return x_bf16 ? launch_mt<WK_F32, true>(a, mt, S, st) : launch_mt<WK_F32, false>(a, mt, S, st);
-  return x_bf16 ? launch_mt<WK_Q4, true>(a, mt, S, st) : launch_mt<WK_Q4, false>(a, mt, S, st);
+template <int WK, int XM, int MT>
+static hipError_t launch_epi(const GemmArgs& a, const EpiArgs& e, int epi, int S, hipStream_t st) {
+  switch (epi) {
+    case EPI_QK: return launch_one<WK, XM, MT, EPI_QK>(a, e, S, st);
+    case EPI_GELU: return launch_one<WK, XM, MT, EPI_GELU>(a, e, S, st);
+    case EPI_SUMS: return launch_one<WK, XM, MT, EPI_SUMS>(a, e, S, st);
+    case EPI_LM: return launch_one<WK, XM, MT, EPI_LM>(a, e, S, st);
+    case EPI_KV: return launch_one<WK, XM, MT, EPI_KV>(a, e, S, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int WK, int XM>
+static hipError_t launch_mt(const GemmArgs& a, const EpiArgs& e, int epi, int mt, int S, hipStream_t st) {
+  return mt == 1 ? launch_epi<WK, XM, 1>(a, e, epi, S, st) : launch_epi<WK, XM, 4>(a, e, epi, S, st);
+}
+
+template <int WK>
+static hipError_t launch_xm(const GemmArgs& a, const EpiArgs& e, int epi, int xmode, int mt, int S,
+                            hipStream_t st) {
+  if (xmode == XM_BF16) return launch_mt<WK, XM_BF16>(a, e, epi, mt, S, st);
+  if (xmode == XM_NORM) return launch_mt<WK, XM_NORM>(a, e, epi, mt, S, st);
+  return launch_mt<WK, XM_F32>(a, e, epi, mt, S, st);
+}
+
+hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, int xmode, int mt, int S,
+                       hipStream_t st) {
+  if (wkind == WK_BF16) return launch_xm<WK_BF16>(a, e, epi, xmode, mt, S, st);
+  if (wkind == WK_F32) return launch_xm<WK_F32>(a, e, epi, xmode, mt, S, st);
+  return launch_xm<WK_Q4>(a, e, epi, xmode, mt, S, st);
 }
 
 }  // namespace dsp

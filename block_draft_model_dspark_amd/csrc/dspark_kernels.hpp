@@ -7,12 +7,32 @@
 
 namespace dsp {
 
-enum { WK_F32 = 0, WK_BF16 = 1, WK_Q4 = 2 };  // weight storage kinds
+enum { WK_F32 = 0, WK_BF16 = 1, WK_Q4 = 2 };   // weight storage kinds
+enum { XM_F32 = 0, XM_BF16 = 1, XM_NORM = 2 };  // how a GEMM reads its input rows
 
 constexpr int MAX_ROWS = 64;
 constexpr int MAX_SEG = 8;
-constexpr int WALK_CHUNK = 256;  // vocabulary entries per walk-statistics chunk
-constexpr int WALK_TOP = 4;      // best candidates kept per chunk
+constexpr int WALK_CHUNK = 64;  // vocabulary entries per walk-statistics chunk (one GEMM column block)
+constexpr int WALK_TOP = 4;     // best candidates kept per chunk
+constexpr int ATT_KEYS = 32;    // keys staged per attention pass
+
+// Row statistics of one 64-column block of a sublayer output y with the
+// residual h it is added to and the norm weight w1 of that sum:
+// (sum y^2, sum h*w1*y, sum (w1*y)^2, sum h^2).  Enough to form both RMSNorm
+// factors of the sandwich  hn = (h + rms(y)*w1) * sc,  x = rms(hn) * w2
+// without another pass over the row.
+struct NormIn {
+  const float* h;      // [M, K] residual, or null (zero)
+  const float* y;      // [M, K] sublayer output, or null (zero)
+  const float4* sums;  // [nparts, M] statistics of 64-column blocks
+  int nparts;          // K / 64
+  const void* w1;      // [K] act dtype (unused when y is null)
+  const void* w2;      // [K] act dtype, or null: x = hn
+  const void* sc;      // [1] act dtype, or null: sc = 1
+  float* hout;         // [M, K]: hn is written here by column block 0, or null
+  float eps;
+  int act_bf16;
+};
 
 // y[m, n] partials of a GEMM x[M, K] . W[N, K]^T over K slices:
 // P[s][m][n], s = blockIdx.y.  Output columns [seg[i].n0, seg[i+1].n0) read
@@ -25,14 +45,54 @@ struct GemmSeg {
   int pad_;
 };
 struct GemmArgs {
-  const void* X;      // [M, ldx] f32, or bf16 when the X-is-bf16 variant runs
+  const void* X;      // XM_F32: [M, ldx] f32; XM_BF16: [M, ldx] bf16; XM_NORM: see nin
   int64_t ldx;
-  int M, N, K;
+  int M, N, K;        // N a multiple of 64
   int kslice;         // K range per blockIdx.y
   int kc;             // K sub-slice staged per iteration
   int nseg;
   GemmSeg seg[MAX_SEG];
-  float* P;           // [S, M, N]
+  float* P;           // [S, M, N] split-K partials (S > 1)
+  NormIn nin;
+};
+
+// what the GEMM does with its result (see dspark_gemm.hip)
+enum { EPI_Y = 0, EPI_QK = 1, EPI_GELU = 2, EPI_SUMS = 3, EPI_LM = 4, EPI_KV = 5 };
+
+struct RopeCfg {
+  double theta;
+  int hd, nrot;       // rotated pairs: k < nrot turn, the rest pass through
+};
+
+struct EpiArgs {
+  float* Y;           // [M, N] fp32 result (EPI_Y, EPI_SUMS, EPI_LM, EPI_KV)
+  unsigned* cnt;      // reduction counters, zero on entry, left zero
+  int group_cols;     // EPI_KV: columns per head group
+  float eps;
+  int act_bf16;
+  // EPI_QK / EPI_KV
+  int nH, nKv, hd, gamma;
+  const float2* rt;   // [rows, hd/2] (cos, sin) of each row's position and pair
+  const void* qn; const void* kn;
+  float* q;           // [A, nKv, nq, hd] RoPE(q_norm_w * y), nq = (nH/nKv)*gamma, row hl*gamma + g
+  float* kb;          // [A, nKv, gamma, hd] RoPE(k_norm_w * y)
+  float* vb;          // [A, nKv, gamma, hd] y
+  float* ssq;         // [(nH+nKv) * hd/64, M] sum y^2 per head and 64-column part
+  int L;              // EPI_KV: context rows per batch row
+  const void* kn_l[MAX_SEG];
+  void* kout[MAX_SEG]; void* vout[MAX_SEG];  // [B, nKv, L, hd] act dtype
+  // EPI_GELU
+  float* act;         // [M, N/2]
+  // EPI_SUMS
+  const float* h;     // residual [M, N] or null
+  const void* w1;     // norm weight [N]
+  float4* sums;       // [N/64, M]
+  // EPI_LM
+  float cap;          // <= 0: none
+  const float* aux;   // [V] markov_w2 row norms, aux[V] = max markov_w1 row norm; null when rank 0
+  float2* lohi;       // [M, NC] (max z - B, max z + B) per chunk
+  float2* top;        // [M, NC, WALK_TOP] (z + B, index as float bits), best first
+  int NC;
 };
 
 // per-row data of a draft round
@@ -43,28 +103,24 @@ struct RowTab {
   int len[MAX_ROWS];  // context rows of each row
 };
 
-struct RopeCfg {
-  double theta;
-  int hd, nrot;       // rotated pairs: k < nrot turn, the rest pass through
-};
-
 struct EmbedArgs {
   const void* E; const void* Es; const void* Eb; int ekind; int group;
-  const void* w_in; int act_bf16;
-  int H; float eps; float scale; int mask_id;
-  float* h; float* x;
+  int H; float scale; int mask_id;
+  float* h;           // [M, H] scaled embedding rows
+  float4* sums;       // [H/64, M] (0, 0, 0, sum h^2)
+  float2* rt;         // [M, hd/2] RoPE table of the block positions
+  RopeCfg rope;
+  unsigned* cnt; int ncnt;  // GEMM counters zeroed here
   RowTab rows;
 };
 
-struct QkEpiArgs {
-  const float* P; int S, M, N;
-  const void* qn; const void* kn; int act_bf16;
-  int nH, nKv, hd; float eps;
+// counters + RoPE table of the context projection
+struct PrepArgs {
+  unsigned* cnt; int ncnt;
+  float2* rt;         // [B*L, hd/2]
+  int B, L;
   RopeCfg rope;
-  float* q;           // [A, nKv, nq, hd], nq = (nH/nKv)*gamma, row hl*gamma + g
-  float* kb;          // [A, nKv, gamma, hd]
-  float* vb;
-  RowTab rows;
+  int pos0[MAX_ROWS];
 };
 
 struct AttnRow {
@@ -74,11 +130,12 @@ struct AttnRow {
 struct AttnArgs {
   AttnRow row[MAX_ROWS];
   int len[MAX_ROWS];
-  int split_off[MAX_ROWS + 1];  // prefix sum of key splits per row
-  int A, gamma, nKv, nq, split;
-  const float* q; const float* kb; const float* vb;
+  int split_off[MAX_ROWS + 1];  // prefix sum of key splits per row (context splits, then one block split)
+  int A, gamma, nKv, nH, nq, split, M, hd;
+  float eps;
+  const float* q; const float* kb; const float* vb; const float* ssq;
   float* opart;       // [nsplit, nKv, nq, hd] unnormalised
-  float* ml;          // [nsplit, nKv, nq, 2] (running max, sum)
+  float* ml;          // [nsplit, nKv, nq, 2] (max, sum)
 };
 
 struct MergeArgs {
@@ -88,37 +145,10 @@ struct MergeArgs {
   float* O;           // [A*gamma, nH*hd]
 };
 
-// row-wise epilogues over GEMM partials
-struct RowEpiArgs {
-  const float* P; int S, M, N;
-  const void* w1; const void* w2; const void* scalar; int act_bf16;
-  float eps;
-  float* h;           // residual [M, N]
-  float* x;           // next GEMM input [M, N]
-  int mode;           // 0: o_proj (h += rms(o;w1); x = rms(h;w2))
-                      // 1: down   (h = (h + rms(d;w1))*scalar; x = rms(h;w2))
-                      // 2: plain  (x = rms(y;w1))
-};
-
-struct GateUpArgs {
-  const float* P; int S, M, I;
-  float* x;           // [M, I]
-};
-
-struct LmEpiArgs {
-  const float* P; int S, M, V;
-  float cap;          // <= 0: none
-  const float* aux;   // [V] markov_w2 row norms, aux[V] = max markov_w1 row norm; null when rank 0
-  float* z;           // [M, V]
-  float* lo;          // [M, NC]
-  float2* top;        // [M, NC, WALK_TOP] (value, index as float bits)
-  int NC;
-};
-
 struct WalkArgs {
   RowTab rows;
   int V, NC, rank, wkind, group;
-  const float* z; const float* lo; const float2* top;
+  const float* z; const float2* lohi; const float2* top;
   const void* w1; const void* w1s; const void* w1b;
   const void* w2; const void* w2s; const void* w2b;
   int32_t* tokens;
@@ -131,27 +161,16 @@ struct AuxArgs {
   float* aux;
 };
 
-struct KvEpiArgs {
-  const float* P; int S, M, N;
-  int B, L, layers, nKv, hd; float eps;
-  const void* kn[16]; int act_bf16;
-  RopeCfg rope;
-  int pos0[MAX_ROWS];
-  void* kout[16]; void* vout[16];
-};
-
 // launchers (return hipGetLastError())
-hipError_t launch_gemm(const GemmArgs& a, int wkind, bool x_bf16, int mt, int S, hipStream_t st);
-size_t gemm_lds_bytes(int wkind, bool x_bf16, int mt, int kc);
+hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, int xmode, int mt, int S,
+                       hipStream_t st);
+size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
+size_t gemm_counter_words(int M, int N, int mt, int group_cols);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
-hipError_t launch_qk_epi(const QkEpiArgs& a, hipStream_t st);
-hipError_t launch_attn(const AttnArgs& a, int hd, bool kv_bf16, int nsplit, hipStream_t st);
+hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
-hipError_t launch_row_epi(const RowEpiArgs& a, hipStream_t st);
-hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st);
-hipError_t launch_lm_epi(const LmEpiArgs& a, hipStream_t st);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 hipError_t launch_aux(const AuxArgs& a, hipStream_t st);
-hipError_t launch_kv_epi(const KvEpiArgs& a, hipStream_t st);
 
 }  // namespace dsp

@@ -1,19 +1,11 @@
-// Row-wise kernels of the draft round: scaled embedding, the GEMM epilogues
-// (RMSNorm, RoPE, residual, GELU-gate, softcap), and the context K/V epilogue.
-//
-// Each epilogue first sums the split-K partials P[s][m][n] of its GEMM.  All
-// arithmetic is fp32; RoPE angles are formed in double (positions reach
-// 32k+, where an fp32 angle would be off by ~1e-3 rad).
+// Row-wise kernels of the draft round: scaled embedding (with the RoPE table
+// of the block positions), the split-softmax merge of the attention, the
+// Markov walk and its per-model bound data, and the set-up kernel of the
+// context projection.  All arithmetic is fp32 (RoPE angles in fp64).
 #include "dspark_kernels.hpp"
 #include "dspark_common.hpp"
 
 namespace dsp {
-
-__device__ __forceinline__ float sum_parts(const float* P, int S, int M, int N, int m, int n) {
-  float v = 0.f;
-  for (int s = 0; s < S; ++s) v += P[((int64_t)s * M + m) * N + n];
-  return v;
-}
 
 // embedding row of a table in f32 / bf16 / q4 storage, element k
 __device__ __forceinline__ float table_elem(const void* E, const void* Es, const void* Eb, int kind, int group,
@@ -27,188 +19,106 @@ __device__ __forceinline__ float table_elem(const void* E, const void* Es, const
 }
 
 // ---------------------------------------------------------------------------
-// deepspec.ts, #forwardBackbone: h = embed([anchor, MASK...]) * sqrt(H);
-// x = input_layernorm(h) of layer 0.  grid M, block 256.
+// deepspec.ts, #forwardBackbone: h = embed([anchor, MASK...]) * sqrt(H).
+// Writes h, the row statistics (0, 0, 0, sum h^2) of every 64-column block
+// that the first q|k GEMM forms layer 0's input norm from, and the
+// (cos, sin) table of the row's position for every RoPE pair.
+// grid M, block 256.
 // ---------------------------------------------------------------------------
-constexpr int EPT = 32;  // elements per thread of a 256-thread row kernel (H <= 8192)
-
 __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
-  __shared__ float red[8];
-  const int m = blockIdx.x;
+  const int m = blockIdx.x, tid = threadIdx.x, M = gridDim.x;
+  // the GEMM reduction counters of this round start at zero
+  for (int i = m * 256 + tid; i < a.ncnt; i += gridDim.x * 256) a.cnt[i] = 0u;
   const int row = m / a.rows.gamma, g = m - row * a.rows.gamma;
   const int64_t id = g == 0 ? a.rows.anchor[row] : a.mask_id;
-  float v[EPT];
-  float ss = 0.f;
+  for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
+    float v[8];
+    float ss = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int k = threadIdx.x + 256 * e;
-    v[e] = 0.f;
-    if (k < a.H) {
-      v[e] = table_elem(a.E, a.Es, a.Eb, a.ekind, a.group, id, a.H, k) * a.scale;
-      a.h[(int64_t)m * a.H + k] = v[e];
-      ss += v[e] * v[e];
+    for (int q = 0; q < 8; ++q) {
+      v[q] = table_elem(a.E, a.Es, a.Eb, a.ekind, a.group, id, a.H, k0 + q) * a.scale;
+      ss += v[q] * v[q];
     }
+    float* dst = a.h + (int64_t)m * a.H + k0;
+    *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    // eight threads per 64-column block
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    if ((tid & 7) == 0) a.sums[(int64_t)(k0 >> 6) * M + m] = make_float4(0.f, 0.f, 0.f, ss);
   }
-  const float r = 1.f / sqrtf(block_sum(ss, red) / a.H + a.eps);
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int k = threadIdx.x + 256 * e;
-    if (k < a.H) a.x[(int64_t)m * a.H + k] = v[e] * r * ld_act(a.w_in, k, a.act_bf16);
+  const int half = a.rope.hd >> 1;
+  const int64_t pos = (int64_t)a.rows.pos[row] + g;
+  for (int d = tid; d < half; d += 256) {
+    float c, s;
+    rope_cs(pos, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
+    a.rt[(int64_t)m * half + d] = make_float2(c, s);
   }
 }
 
-// ---------------------------------------------------------------------------
-// deepspec.ts, #forwardBackbone q / block-k path:
-//   q = RoPE(q_norm(q_proj x), p+g); v_b = rms(k_proj x); k_b = RoPE(k_norm(k_proj x), p+g)
-// grid (M, nH + nKv), block hd
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_qk_epi(const QkEpiArgs a) {
-  __shared__ float red[8];
-  __shared__ float buf[256];
-  const int m = blockIdx.x, head = blockIdx.y, d = threadIdx.x, hd = a.hd, half = hd >> 1;
-  const int row = m / a.rows.gamma, g = m - row * a.rows.gamma;
-  const int col = head * hd + d;  // q heads first, then the kv heads
-  const float y = sum_parts(a.P, a.S, a.M, a.N, m, col);
-  const float r = 1.f / sqrtf(block_sum(y * y, red) / hd + a.eps);
-  const int64_t pos = (int64_t)a.rows.pos[row] + g;
-  float c, s;
-  rope_cs(pos, d < half ? d : d - half, hd, a.rope.theta, a.rope.nrot, c, s);
-  const int rep = a.nH / a.nKv;
-  const int nq = rep * a.rows.gamma;
-  if (head < a.nH) {
-    const float yn = y * r * ld_act(a.qn, d, a.act_bf16);
-    buf[d] = yn;
-    __syncthreads();
-    const float o = d < half ? yn * c - buf[d + half] * s : yn * c + buf[d - half] * s;
-    const int kvh = head / rep, hl = head - kvh * rep;
-    a.q[(((int64_t)row * a.nKv + kvh) * nq + hl * a.rows.gamma + g) * hd + d] = o;
-  } else {
-    const int kvh = head - a.nH;
-    const float vn = y * r;
-    const int64_t off = (((int64_t)row * a.nKv + kvh) * a.rows.gamma + g) * hd + d;
-    a.vb[off] = vn;
-    const float kn = vn * ld_act(a.kn, d, a.act_bf16);
-    buf[d] = kn;
-    __syncthreads();
-    a.kb[off] = d < half ? kn * c - buf[d + half] * s : kn * c + buf[d - half] * s;
+// context projection set-up: zero the GEMM counters and fill the RoPE table
+// of positions pos0[b] + i.  grid any, block 256.
+__global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x, nth = (int64_t)gridDim.x * 256;
+  for (int64_t i = gid; i < a.ncnt; i += nth) a.cnt[i] = 0u;
+  const int half = a.rope.hd >> 1;
+  const int64_t total = (int64_t)a.B * a.L * half;
+  for (int64_t i = gid; i < total; i += nth) {
+    const int64_t m = i / half;
+    const int d = (int)(i - m * half);
+    const int b = (int)(m / a.L), r = (int)(m - (int64_t)b * a.L);
+    float c, s;
+    rope_cs((int64_t)a.pos0[b] + r, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
+    a.rt[i] = make_float2(c, s);
   }
 }
 
 // ---------------------------------------------------------------------------
 // split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
-// grid A*nKv*nq, block hd
+// grid A*nKv*nq, block hd (>= 64)
 // ---------------------------------------------------------------------------
+constexpr int MERGE_SB = 64;  // splits weighted per pass
+
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  const int idx = blockIdx.x;
+  __shared__ float wsh[MERGE_SB], lsh[MERGE_SB];
+  __shared__ float red[8];
+  const int idx = blockIdx.x, tid = threadIdx.x;
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
-  const int s0 = a.split_off[row], s1 = a.split_off[row + 1];
+  const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
+  const float2* ml = (const float2*)a.ml;
   float mx = -INFINITY;
-  for (int s = s0; s < s1; ++s) mx = fmaxf(mx, a.ml[(((int64_t)s * a.nKv + kvh) * a.nq + j) * 2]);
-  float den = 0.f, num = 0.f;
-  for (int s = s0; s < s1; ++s) {
-    const int64_t b = ((int64_t)s * a.nKv + kvh) * a.nq + j;
-    const float w = expf(a.ml[b * 2] - mx);
-    den += w * a.ml[b * 2 + 1];
-    num += w * a.opart[b * a.hd + threadIdx.x];
+  for (int s = tid; s < ns; s += blockDim.x) mx = fmaxf(mx, ml[((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + j].x);
+  mx = block_max(mx, red);
+  float num = 0.f, den = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += MERGE_SB) {
+    const int cn = min(MERGE_SB, ns - c0);
+    __syncthreads();
+    if (tid < cn) {
+      const float2 v = ml[((int64_t)(s0 + c0 + tid) * a.nKv + kvh) * a.nq + j];
+      const float w = expf(v.x - mx);
+      wsh[tid] = w;
+      lsh[tid] = w * v.y;
+    }
+    __syncthreads();
+    for (int b0 = 0; b0 < cn; b0 += 16) {
+      float o[16];
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int s = s0 + c0 + min(b0 + q, cn - 1);
+        o[q] = a.opart[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
+      }
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        if (b0 + q < cn) {
+          num += wsh[b0 + q] * o[q];
+          den += lsh[b0 + q];
+        }
+    }
   }
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
-  a.O[((int64_t)row * a.gamma + g) * (a.nH * a.hd) + h * a.hd + threadIdx.x] = num / den;
-}
-
-// ---------------------------------------------------------------------------
-// row epilogues (grid M, block 256):
-//  mode 0, deepspec.ts #forwardBackbone after attention:
-//     h += post_attention_layernorm(o); x = pre_feedforward_layernorm(h)
-//  mode 1, after the MLP:
-//     h = (h + post_feedforward_layernorm(d)) * layer_scalar; x = next norm(h)
-//  mode 2, deepspec.ts #projectContext: x = hidden_norm(fc out)
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_row_epi(const RowEpiArgs a) {
-  __shared__ float red[8];
-  const int m = blockIdx.x, N = a.N;
-  float y[EPT];
-  float ss = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int k = threadIdx.x + 256 * e;
-    y[e] = k < N ? sum_parts(a.P, a.S, a.M, N, m, k) : 0.f;
-    ss += y[e] * y[e];
-  }
-  float r = 1.f / sqrtf(block_sum(ss, red) / N + a.eps);
-  if (a.mode == 2) {
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      const int k = threadIdx.x + 256 * e;
-      if (k < N) a.x[(int64_t)m * N + k] = y[e] * r * ld_act(a.w1, k, a.act_bf16);
-    }
-    return;
-  }
-  const float scal = a.mode == 1 ? ld_act(a.scalar, 0, a.act_bf16) : 1.f;
-  float ss2 = 0.f;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int k = threadIdx.x + 256 * e;
-    if (k < N) {
-      const int64_t o = (int64_t)m * N + k;
-      const float hn = (a.h[o] + y[e] * r * ld_act(a.w1, k, a.act_bf16)) * scal;
-      a.h[o] = hn;
-      y[e] = hn;
-      ss2 += hn * hn;
-    }
-  }
-  r = 1.f / sqrtf(block_sum(ss2, red) / N + a.eps);
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int k = threadIdx.x + 256 * e;
-    if (k < N) a.x[(int64_t)m * N + k] = y[e] * r * ld_act(a.w2, k, a.act_bf16);
-  }
-}
-
-// deepspec.ts, #geluTanhMlp: act = gelu_tanh(gate x) * up x.  P columns are
-// [gate | up], N = 2I.  grid ceil(M*I/256), block 256
-__global__ __launch_bounds__(256) void k_gateup(const GateUpArgs a) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= (int64_t)a.M * a.I) return;
-  const int m = (int)(idx / a.I), i = (int)(idx - (int64_t)m * a.I);
-  const float gt = sum_parts(a.P, a.S, a.M, 2 * a.I, m, i);
-  const float up = sum_parts(a.P, a.S, a.M, 2 * a.I, m, a.I + i);
-  a.x[idx] = gelu_tanh(gt) * up;
-}
-
-// ---------------------------------------------------------------------------
-// deepspec.ts, #computeLogits: z = cap * tanh(lm_head(h) / cap), plus the
-// per-chunk statistics the walk prunes with.  For a step, any prev token
-// gives |markov_w2[v] . markov_w1[prev]| <= ||w2_v|| * max ||w1|| =: B_v, so
-// a vocabulary entry with z_v + B_v below max_u (z_u - B_u) can never win.
-// Per (row, 256-entry chunk): lo = max (z - B) and the WALK_TOP best z + B.
-// grid (NC, M), block 256
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_lm_epi(const LmEpiArgs a) {
-  __shared__ float redu[4];
-  __shared__ int redi[4];
-  const int c = blockIdx.x, m = blockIdx.y;
-  const int v = c * WALK_CHUNK + threadIdx.x;
-  float z = -INFINITY, bnd = 0.f;
-  if (v < a.V) {
-    z = sum_parts(a.P, a.S, a.M, a.V, m, v);
-    if (a.cap > 0.f) z = a.cap * tanhf(z / a.cap);
-    a.z[(int64_t)m * a.V + v] = z;
-    if (a.aux) bnd = a.aux[v] * a.aux[a.V] * (1.f + 1e-5f);
-  }
-  const float lov = z - bnd;
-  const float lom = block_max(lov, redu);
-  float hv = z + bnd;
-  float2* top = a.top + ((int64_t)m * a.NC + c) * WALK_TOP;
-  for (int t = 0; t < WALK_TOP; ++t) {
-    float u = hv;
-    int i = v < a.V ? v : 0x7fffffff;
-    block_argmax(u, i, redu, redi);
-    if (threadIdx.x == 0) top[t] = make_float2(u, __int_as_float(i));
-    if (v == i) hv = -INFINITY;
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) a.lo[(int64_t)m * a.NC + c] = lom;
+  a.O[((int64_t)row * a.gamma + g) * (a.nH * a.hd) + h * a.hd + tid] = num / den;
 }
 
 // markov_w1 / markov_w2 element (table_elem with the head's own storage)
@@ -220,63 +130,118 @@ __device__ __forceinline__ float head_elem(const void* w, const void* s, const v
 // ---------------------------------------------------------------------------
 // deepspec.ts, draftRows sequential walk at temperature 0:
 //   prev = anchor; for k < gamma: tok = argmax(z[k] + markov_w2 markov_w1[prev]); prev = tok
-// One workgroup per draft row.  Only entries that survive the bound test
-// (k_lm_epi) are scored; a chunk whose WALK_TOP-th best still passes is
-// scored in full.  Ties go to the lower index.
+// One workgroup per draft row; ties go to the lower vocabulary index.
+//
+// Only entries that survive the bound test of the logits epilogue can win a
+// step (the winner w has z_w + B_w >= u_w >= max_v (z_v - B_v)), and that set
+// C_k does not depend on the previous token.  The previous token of step k
+// is the winner of step k-1, so it lies in C_{k-1} (the anchor for k = 0).
+// The fast path therefore builds every C_k from the per-chunk statistics and
+// top lists, scores the table z_k[c] + w2[c] . w1[p] for p in C_{k-1},
+// c in C_k in parallel, then walks the table in LDS.  If some step keeps more
+// than WALK_CMAX entries, a chunk's WALK_TOP-th best still passes, or too
+// many chunks pass, the row takes the per-step path that scores every
+// surviving entry against the actual previous token.
 // grid A, block 256
 // ---------------------------------------------------------------------------
-constexpr int WALK_CAP = 3 * 1024;  // NC <= 1024 chunks, < WALK_TOP candidates each otherwise
+constexpr int WALK_CMAX = 16;   // fast-path candidates per step
+constexpr int WALK_GMAX = 32;   // block size bound
+constexpr int WALK_FMAX = 512;  // fast-path flagged (step, chunk) pairs per row
+constexpr int WALK_TPT = 8;     // threads per scored (prev, candidate) pair
 
-__global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
-  __shared__ float redu[4];
-  __shared__ int redi[4];
-  __shared__ int cand[WALK_CAP];
-  __shared__ int ovf[1024];
-  __shared__ float e[256];
-  __shared__ int ncand, novf, prev_s;
-  const int row = blockIdx.x, tid = threadIdx.x, G = a.rows.gamma;
-  if (tid == 0) prev_s = a.rows.anchor[row];
-  for (int k = 0; k < G; ++k) {
-    const int64_t m = (int64_t)row * G + k;
-    float lm = -INFINITY;
-    for (int c = tid; c < a.NC; c += 256) lm = fmaxf(lm, a.lo[m * a.NC + c]);
-    lm = block_max(lm, redu);
-    const float thr = lm - 1e-4f * (1.f + fabsf(lm));
-    if (tid == 0) { ncand = 0; novf = 0; }
-    __syncthreads();
-    const int prev = prev_s;
-    for (int c = tid; c < a.NC; c += 256) {
-      const float2* tp = a.top + (m * a.NC + c) * WALK_TOP;
-      if (tp[WALK_TOP - 1].x >= thr) {
-        ovf[atomicAdd(&novf, 1)] = c;
-      } else {
-        for (int t = 0; t < WALK_TOP - 1; ++t)
-          if (tp[t].x >= thr) cand[atomicAdd(&ncand, 1)] = __float_as_int(tp[t].y);
+// dot(markov_w2[v], e) for a row of `rank` entries
+__device__ __forceinline__ float w2_dot(const WalkArgs& a, int64_t v, const float* e) {
+  float dot = 0.f;
+  if (a.wkind == WK_BF16) {
+    const u32x4* p = (const u32x4*)((const uint16_t*)a.w2 + v * a.rank);
+    for (int j8 = 0; j8 < (a.rank >> 3); ++j8) {
+      const u32x4 w = p[j8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        dot += __uint_as_float(w[q] << 16) * e[8 * j8 + 2 * q];
+        dot += __uint_as_float(w[q] & 0xFFFF0000u) * e[8 * j8 + 2 * q + 1];
       }
     }
+  } else {
+    for (int j = 0; j < a.rank; ++j) dot += head_elem(a.w2, a.w2s, a.w2b, a.wkind, a.group, v, a.rank, j) * e[j];
+  }
+  return dot;
+}
+
+// part `sub` of markov_w2[v] . markov_w1[prev]: 8-entry groups sub, sub + TPT, ...
+__device__ __forceinline__ float w1w2_dot_part(const WalkArgs& a, int64_t prev, int64_t v, int sub) {
+  const int n8 = a.rank >> 3;
+  float dot = 0.f;
+  if (a.wkind == WK_BF16) {
+    const u32x4* p1 = (const u32x4*)((const uint16_t*)a.w1 + prev * a.rank);
+    const u32x4* p2 = (const u32x4*)((const uint16_t*)a.w2 + v * a.rank);
+    for (int j0 = sub; j0 < n8; j0 += 4 * WALK_TPT) {
+      u32x4 x1[4], x2[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int j = min(j0 + q * WALK_TPT, n8 - 1);
+        x1[q] = p1[j];
+        x2[q] = p2[j];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (j0 + q * WALK_TPT < n8)
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            dot += __uint_as_float(x1[q][h] << 16) * __uint_as_float(x2[q][h] << 16);
+            dot += __uint_as_float(x1[q][h] & 0xFFFF0000u) * __uint_as_float(x2[q][h] & 0xFFFF0000u);
+          }
+    }
+  } else {
+    for (int j8 = sub; j8 < n8; j8 += WALK_TPT)
+      for (int j = 8 * j8; j < 8 * j8 + 8; ++j)
+        dot += head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j) *
+               head_elem(a.w2, a.w2s, a.w2b, a.wkind, a.group, v, a.rank, j);
+  }
+  return dot;
+}
+
+// the per-step path: every entry of a passing chunk is scored against the
+// actual previous token
+__device__ void walk_per_step(const WalkArgs& a, int row) {
+  __shared__ float redu[4];
+  __shared__ int redi[4];
+  __shared__ float e[256];
+  __shared__ int prev_s;
+  const int tid = threadIdx.x, G = a.rows.gamma;
+  if (tid == 0) prev_s = a.rows.anchor[row];
+  __syncthreads();
+  for (int k = 0; k < G; ++k) {
+    const int64_t m = (int64_t)row * G + k;
+    const float2* lh = a.lohi + m * a.NC;
+    float lm = -INFINITY;
+    for (int c = tid; c < a.NC; c += 256) lm = fmaxf(lm, lh[c].x);
+    lm = block_max(lm, redu);
+    const float thr = lm - 1e-4f * (1.f + fabsf(lm));
+    const int prev = prev_s;
     if (a.rank > 0)
-      for (int j = tid; j < a.rank; j += 256)
-        e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+      for (int j = tid; j < a.rank; j += 256) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
     __syncthreads();
     float bu = -INFINITY;
     int bi = 0x7fffffff;
-    const int nc = ncand, no = novf;
-    const int tot = nc + no * WALK_CHUNK;
-    for (int i = tid; i < tot; i += 256) {
-      int v;
-      if (i < nc) v = cand[i];
-      else {
-        const int q = i - nc;
-        v = ovf[q / WALK_CHUNK] * WALK_CHUNK + (q % WALK_CHUNK);
-        if (v >= a.V) continue;
+    for (int c = tid; c < a.NC; c += 256) {
+      if (!(lh[c].y >= thr)) continue;
+      const float2* tp = a.top + (m * a.NC + c) * WALK_TOP;
+      if (tp[WALK_TOP - 1].x < thr) {
+        for (int t = 0; t < WALK_TOP - 1; ++t)
+          if (tp[t].x >= thr) {
+            const int v = __float_as_int(tp[t].y);
+            float u = a.z[m * a.V + v];
+            if (a.rank > 0) u += w2_dot(a, v, e);
+            if (better(u, v, bu, bi)) { bu = u; bi = v; }
+          }
+      } else {
+        for (int v = c * WALK_CHUNK; v < min(c * WALK_CHUNK + WALK_CHUNK, a.V); ++v) {
+          float u = a.z[m * a.V + v];
+          if (a.rank > 0) u += w2_dot(a, v, e);
+          if (better(u, v, bu, bi)) { bu = u; bi = v; }
+        }
       }
-      float u = a.z[m * a.V + v];
-      if (a.rank > 0) {
-        float dot = 0.f;
-        for (int j = 0; j < a.rank; ++j) dot += head_elem(a.w2, a.w2s, a.w2b, a.wkind, a.group, v, a.rank, j) * e[j];
-        u += dot;
-      }
-      if (better(u, v, bu, bi)) { bu = u; bi = v; }
     }
     block_argmax(bu, bi, redu, redi);
     if (tid == 0) {
@@ -286,6 +251,136 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
       prev_s = ok ? bi : 0;
     }
     __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
+  __shared__ int cand[WALK_GMAX][WALK_CMAX];
+  __shared__ int ncand[WALK_GMAX];
+  __shared__ float thr[WALK_GMAX];
+  __shared__ float tab[WALK_GMAX][WALK_CMAX][WALK_CMAX];  // [k][prev index][candidate index]
+  __shared__ int flag_kc[WALK_FMAX];                      // k << 24 | chunk
+  __shared__ int toff[WALK_GMAX + 1];
+  __shared__ int nflag, slow;
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma;
+  const int NC = a.NC;
+  if (tid < WALK_GMAX) ncand[tid] = 0;
+  if (tid == 0) {
+    nflag = 0;
+    slow = 0;
+  }
+  // 1. per-step threshold max_c lo_c: TPS threads per step, 16 chunk loads in flight each
+  int TPS = 64;  // a power of two within one wave
+  while (TPS * G > 256) TPS >>= 1;
+  const int k = tid / TPS, sub = tid - k * TPS;
+  const bool kok = k < G;
+  const float2* lh = a.lohi + ((int64_t)row * G + min(k, G - 1)) * NC;
+  float lm = -INFINITY;
+  for (int c0 = 0; c0 < NC; c0 += TPS * 16) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = lh[min(c0 + sub + TPS * i, NC - 1)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c0 + sub + TPS * i < NC) lm = fmaxf(lm, v[i].x);
+  }
+  for (int o = TPS >> 1; o > 0; o >>= 1) lm = fmaxf(lm, __shfl_xor(lm, o));
+  const float th = lm - 1e-4f * (1.f + fabsf(lm));
+  if (kok && sub == 0) thr[k] = th;
+  __syncthreads();
+  // 2. chunks whose best z + B reaches the threshold
+  for (int c0 = 0; c0 < NC; c0 += TPS * 16) {
+    float2 v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = lh[min(c0 + sub + TPS * i, NC - 1)];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = c0 + sub + TPS * i;
+      if (kok && c < NC && v[i].y >= th) {
+        const int f = atomicAdd(&nflag, 1);
+        if (f < WALK_FMAX) flag_kc[f] = (k << 24) | c;
+      }
+    }
+  }
+  __syncthreads();
+  const int nf = nflag;
+  if (nf > WALK_FMAX) slow = 1;
+  // 3. candidates from the passing chunks' top lists
+  for (int f = tid; f < min(nf, WALK_FMAX); f += 256) {
+    const int kk = flag_kc[f] >> 24, c = flag_kc[f] & 0xFFFFFF;
+    const float2* tp = a.top + (((int64_t)row * G + kk) * NC + c) * WALK_TOP;
+    float2 t[WALK_TOP];
+#pragma unroll
+    for (int i = 0; i < WALK_TOP; ++i) t[i] = tp[i];
+    const float th2 = thr[kk];
+    if (!(t[WALK_TOP - 1].x < th2)) {
+      slow = 1;
+    } else {
+#pragma unroll
+      for (int i = 0; i < WALK_TOP - 1; ++i)
+        if (t[i].x >= th2) {
+          const int o = atomicAdd(&ncand[kk], 1);
+          if (o < WALK_CMAX) cand[kk][o] = __float_as_int(t[i].y);
+          else slow = 1;
+        }
+    }
+  }
+  __syncthreads();
+  if (slow) {
+    walk_per_step(a, row);
+    return;
+  }
+  // 4. score table: pairs (p, c) of every step, WALK_TPT threads per pair
+  if (tid == 0) {
+    int o = 0;
+    for (int kk = 0; kk < G; ++kk) {
+      toff[kk] = o;
+      o += (kk == 0 ? 1 : ncand[kk - 1]) * ncand[kk];
+    }
+    toff[G] = o;
+  }
+  __syncthreads();
+  const int ntri = toff[G];
+  for (int t0 = 0; t0 < ntri; t0 += 256 / WALK_TPT) {
+    const int t = t0 + tid / WALK_TPT, ts = tid % WALK_TPT;
+    const bool ok = t < ntri;
+    int kk = 0, pi = 0, ci = 0, prev = 0, v = 0;
+    if (ok) {
+      while (toff[kk + 1] <= t) ++kk;
+      const int r = t - toff[kk], nc = ncand[kk];
+      pi = r / nc;
+      ci = r - pi * nc;
+      prev = kk == 0 ? a.rows.anchor[row] : cand[kk - 1][pi];
+      v = cand[kk][ci];
+    }
+    float dot = (ok && a.rank > 0) ? w1w2_dot_part(a, prev, v, ts) : 0.f;
+#pragma unroll
+    for (int o = WALK_TPT >> 1; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
+    if (ok && ts == 0) tab[kk][pi][ci] = a.z[((int64_t)row * G + kk) * a.V + v] + dot;
+  }
+  __syncthreads();
+  // 5. the walk itself, from LDS
+  if (wave == 0) {
+    int pi = 0;
+    for (int kk = 0; kk < G; ++kk) {
+      const int nc = ncand[kk];
+      float u = -INFINITY;
+      int v = 0x7fffffff;
+      if (lane < nc) {
+        u = tab[kk][pi][lane];
+        v = cand[kk][lane];
+      }
+      int li = lane;
+      // argmax over (u, v) carrying the lane index of the winner
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ou = __shfl_xor(u, o);
+        const int ov = __shfl_xor(v, o), ol = __shfl_xor(li, o);
+        if (better(ou, ov, u, v)) { u = ou; v = ov; li = ol; }
+      }
+      const bool okv = v >= 0 && v < a.V;
+      if (lane == 0) a.tokens[(int64_t)row * G + kk] = okv ? v : -1;
+      pi = okv ? li : 0;
+    }
   }
 }
 
@@ -310,52 +405,19 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// deepspec.ts, #projectContextKVRows epilogue: per (context row, layer, kv head)
-//   V = rms(k) (no weight, no RoPE); K = RoPE(rms(k) * k_norm, pos0 + i)
-// grid (M = B*L, layers*nKv), block hd
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_kv_epi(const KvEpiArgs a) {
-  __shared__ float red[8];
-  __shared__ float buf[256];
-  const int m = blockIdx.x, lh = blockIdx.y, d = threadIdx.x, hd = a.hd, half = hd >> 1;
-  const int layer = lh / a.nKv, kvh = lh - layer * a.nKv;
-  const int b = m / a.L, i = m - b * a.L;
-  const float y = sum_parts(a.P, a.S, a.M, a.N, m, lh * hd + d);
-  const float vn = y / sqrtf(block_sum(y * y, red) / hd + a.eps);
-  const int64_t off = (((int64_t)b * a.nKv + kvh) * a.L + i) * hd + d;
-  st_act(a.vout[layer], off, vn, a.act_bf16);
-  const float kn = vn * ld_act(a.kn[layer], d, a.act_bf16);
-  buf[d] = kn;
-  __syncthreads();
-  float c, s;
-  rope_cs((int64_t)a.pos0[b] + i, d < half ? d : d - half, hd, a.rope.theta, a.rope.nrot, c, s);
-  st_act(a.kout[layer], off, d < half ? kn * c - buf[d + half] * s : kn * c + buf[d - half] * s, a.act_bf16);
-}
-
-// ---------------------------------------------------------------------------
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st) {
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
-hipError_t launch_qk_epi(const QkEpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_qk_epi, dim3(a.M, a.nH + a.nKv), dim3(a.hd), 0, st, a);
+hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
+  const int64_t rope_work = (int64_t)a.B * a.L * (a.rope.hd >> 1);
+  const int64_t work = rope_work > a.ncnt ? rope_work : a.ncnt;
+  const int64_t blocks = (work + 255) / 256;
+  hipLaunchKernelGGL(k_prep, dim3(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : (int)blocks)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_merge, dim3(a.A * a.nKv * a.nq), dim3(a.hd), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_row_epi(const RowEpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_row_epi, dim3(a.M), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_gateup(const GateUpArgs& a, hipStream_t st) {
-  const int64_t n = (int64_t)a.M * a.I;
-  hipLaunchKernelGGL(k_gateup, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_lm_epi(const LmEpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_lm_epi, dim3(a.NC, a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
@@ -364,10 +426,6 @@ hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
 }
 hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_aux, dim3((a.V + 3) / 4), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_kv_epi(const KvEpiArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_kv_epi, dim3(a.M, a.layers * a.nKv), dim3(a.hd), 0, st, a);
   return hipGetLastError();
 }
 
