@@ -126,6 +126,7 @@ def main():
     value = A * args.steps / (ms / 1e3)
 
     # per-kernel durations: HIP events around each library launch on its stream
+    args.profile_steps = max(1, args.profile_steps)
     dsp.profile_enable(True)
     for _ in range(args.profile_steps):
         step()
