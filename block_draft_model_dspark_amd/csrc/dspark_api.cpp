@@ -121,20 +121,21 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   GemmPlan p;
   // row tiles per workgroup: 1 for M <= 16, else 4 (2 and 3 are not enabled)
   p.mt = M <= 16 ? 1 : 4;
-  int kc = wk == WK_F32 ? 256 : 512;
+  // sub-slice width: 256 for one 16-row tile (two sub-slices in flight) and
+  // for fp32 weights, else 512, halved while the staged tile exceeds 64 KB
+  int kc = (p.mt == 1 || wk == WK_F32) ? 256 : 512;
   while (kc > 128 && gemm_lds_bytes(wk, xmode, p.mt, kc) > 65536) kc /= 2;
   const int mblocks = ceil_div(M, 16 * p.mt);
   const int wgs = (N / 64) * mblocks;
-  // split K only when the grid is too small to keep HBM busy (a weight
-  // stream needs many workgroups in flight); slices are multiples of 64 and
-  // at most 16 per column block (one batch of partial loads in the reduction)
-  const int target = 512;
-  int kslice = ceil_div(K, 64) * 64;
-  if (wgs < target) {
-    const int st = std::min(16, ceil_div(target, wgs));
-    kslice = std::max(128, ceil_div(ceil_div(K, st), 64) * 64);
-    kslice = std::min(kslice, ceil_div(K, 64) * 64);
-  }
+  // Split K only while the grid is too small to give every CU a weight
+  // stream; slices are multiples of 64, and normed inputs keep their norm
+  // weights for the whole slice in LDS (at most 2048 wide).
+  const int target = 256;
+  int S = 1;
+  if (wgs < target) S = std::min(16, ceil_div(target, wgs));
+  if (xmode == XM_NORM) S = std::max(S, ceil_div(K, 2048));
+  S = std::min(S, ceil_div(K, 64));
+  const int kslice = ceil_div(ceil_div(K, S), 64) * 64;
   p.S = ceil_div(K, kslice);
   p.kslice = kslice;
   p.kc = std::min(kc, kslice);
@@ -162,7 +163,7 @@ GemmSeg seg_of(const Mat& w, int n0) {
 
 // ---- draft workspace layout ---------------------------------------------
 struct DraftLayout {
-  size_t hA, hB, Y, sums, rt, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, top, total;
+  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, total;
   GemmPlan qk, o, gu, dn, lm;
   size_t cwords;
   int nsplit_max;
@@ -202,6 +203,7 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.Y = take((size_t)M * H * 4);
   d.sums = take((size_t)(H / 64) * M * 16);
   d.rt = take((size_t)M * (hd / 2) * 8);
+  d.scal = take((size_t)(c.num_hidden_layers + 1) * 4);
   d.O = take((size_t)M * nH * hd * 4);
   d.act = take((size_t)M * I * 4);
   d.P = take(pmax);
@@ -214,14 +216,13 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.ml = take((size_t)d.nsplit_max * nKv * m->nq * 2 * 4);
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
   d.lohi = take((size_t)M * NC * 8);
-  d.top = take((size_t)M * NC * WALK_TOP * 8);
   d.total = off;
   return d;
 }
 
 // ---- projection workspace layout -----------------------------------------
 struct ProjLayout {
-  size_t P, Y, C, sums, rt, cnt, total;
+  size_t P, Y, C, sums, rt, one, cnt, total;
   GemmPlan fc, kp;
   size_t cwords;
   int lay_per_gemm;
@@ -256,6 +257,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.C = feats ? take((size_t)M * H * 4) : 0;
   p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
   p.rt = take((size_t)M * (hd / 2) * 8);
+  p.one = take(4);
   p.cnt = take(p.cwords * 4);
   p.total = off;
   return p;
@@ -281,6 +283,7 @@ dspark_status check_config(const dspark_config& c) {
     return fail(DSPARK_ERR_UNSUPPORTED, "hidden, intermediate and fc input sizes must be multiples of 64");
   if (c.hidden_size > 8192 || c.intermediate_size > (1 << 20))
     return fail(DSPARK_ERR_UNSUPPORTED, "hidden_size > 8192 not built");
+  if (c.num_hidden_layers > MAX_LAYERS) return fail(DSPARK_ERR_UNSUPPORTED, "more than %d layers not built", MAX_LAYERS);
   if (c.vocab_size % 64 || c.vocab_size > 1024 * WALK_CHUNK)
     return fail(DSPARK_ERR_UNSUPPORTED, "vocab_size must be a multiple of 64 and at most %d", 1024 * WALK_CHUNK);
   if (c.block_size > 32) return fail(DSPARK_ERR_UNSUPPORTED, "block_size > 32 not built");
@@ -484,6 +487,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   pr.cnt = cnt;
   pr.ncnt = (int)p.cwords;
   pr.rt = rt;
+  pr.one = (float*)(ws + p.one);
   pr.B = B;
   pr.L = L;
   pr.rope = rope_of(m);
@@ -514,6 +518,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     nin.sums = e.sums;
     nin.nparts = H / 64;
     nin.w1 = m->hidden_norm;
+    nin.sc = pr.one;
     nin.eps = (float)c.rms_norm_eps;
     nin.act_bf16 = act_bf16(m);
   }
@@ -659,6 +664,11 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   em.scale = (float)std::sqrt((double)H);
   em.mask_id = c.mask_token_id;
   em.h = hA;
+  em.act_bf16 = abf;
+  em.nL = nL;
+  for (int l = 0; l < nL; ++l) em.scal_src[l] = m->L[l].scalar;
+  float* scal = (float*)(ws + d.scal);  // scal[0] = 1, scal[1 + l] = layer l's scalar
+  em.scal = scal;
   em.sums = sums;
   em.rt = rt;
   em.rope = rope_of(m);
@@ -668,7 +678,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   HIPCHECK(timed("embed", stream, [&] { return launch_embed(em, M, stream); }));
 
   // input rows of a GEMM: x = rms((h + rms(y) w1) sc) w2 from the statistics
-  auto norm_in = [&](const float* h, const float* y, const void* w1, const void* sc, const void* w2, float* hout) {
+  auto norm_in = [&](const float* h, const float* y, const void* w1, const float* sc, const void* w2, float* hout) {
     NormIn n{};
     n.h = h;
     n.y = y;
@@ -704,7 +714,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   // residual it read and writes the sum (q|k writes hB, gate|up writes hA).
   const float* y_prev = nullptr;  // pending sublayer output folded into the next input norm
   const void* w1_prev = nullptr;
-  const void* sc_prev = nullptr;
+  const float* sc_prev = scal;
   for (int l = 0; l < nL; ++l) {
     const LayerW& W = m->L[l];
     GemmArgs g{};
@@ -751,7 +761,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.seg[0] = seg_of(W.g, 0);
     g.seg[1] = seg_of(W.u, I);
     g.P = P;
-    g.nin = norm_in(hB, Y, W.pa, nullptr, W.pf, hA);
+    g.nin = norm_in(hB, Y, W.pa, scal, W.pf, hA);
     HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream); }));
 
     g = GemmArgs{};
@@ -769,7 +779,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream); }));
     y_prev = Y;
     w1_prev = W.pff;
-    sc_prev = W.scalar;
+    sc_prev = scal + 1 + l;
   }
 
   GemmArgs g{};
@@ -786,7 +796,6 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   e.cap = c.final_logit_softcapping > 0 ? (float)c.final_logit_softcapping : 0.f;
   e.aux = c.markov_rank > 0 ? (const float*)aux_dev : nullptr;
   e.lohi = (float2*)(ws + d.lohi);
-  e.top = (float2*)(ws + d.top);
   e.NC = NC;
   HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream); }));
 
@@ -799,7 +808,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   w.group = c.group_size;
   w.z = z;
   w.lohi = e.lohi;
-  w.top = e.top;
+  w.aux = e.aux;
   w.w1 = m->w1.w; w.w1s = m->w1.s; w.w1b = m->w1.b;
   w.w2 = m->w2.w; w.w2s = m->w2.s; w.w2b = m->w2.b;
   w.tokens = tokens_dev;

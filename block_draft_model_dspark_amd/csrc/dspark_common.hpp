@@ -42,16 +42,19 @@ struct Raw8 {
   u32x4 a, b;
 };
 __device__ __forceinline__ Raw8 ld_act8(const void* p, int64_t k, bool bf16) {
+  // two 16-byte loads either way (the second repeats the first for bf16), so
+  // no branch holds a load whose result must be waited for
+  const char* pa = (const char*)p + k * (bf16 ? 2 : 4);
   Raw8 r;
-  if (bf16) {
-    r.a = *(const u32x4*)((const uint16_t*)p + k);
-    r.b = r.a;
-  } else {
-    r.a = *(const u32x4*)((const float*)p + k);
-    r.b = *(const u32x4*)((const float*)p + k + 4);
-  }
+  r.a = *(const u32x4*)pa;
+  r.b = *(const u32x4*)(pa + (bf16 ? 0 : 16));
   return r;
 }
+// one act-dtype element as raw bits (converted later by cvt_act_raw)
+__device__ __forceinline__ uint32_t ld_act_raw(const void* p, int64_t i, bool bf16) {
+  return bf16 ? (uint32_t)((const uint16_t*)p)[i] : ((const uint32_t*)p)[i];
+}
+__device__ __forceinline__ float cvt_act_raw(uint32_t r, bool bf16) { return __uint_as_float(bf16 ? r << 16 : r); }
 __device__ __forceinline__ void cvt_act8(const Raw8& r, bool bf16, float* v) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -159,6 +162,13 @@ __device__ __forceinline__ void rope_cs(int64_t pos, double inv, float& c, float
   const double ang = (double)pos * inv;
   const double red = ang - rint(ang * (1.0 / two_pi)) * two_pi;
   sincosf((float)red, &s, &c);
+}
+
+// Markov walk pruning bound of vocabulary entry v: ||markov_w2[v]|| times
+// max_u ||markov_w1[u]|| (aux[v], aux[V]), with a relative margin for the
+// fp32 rounding of the dot products it bounds
+__device__ __forceinline__ float walk_bound(const float* aux, int64_t v, int V) {
+  return aux[v] * aux[V] * (1.f + 1e-5f);
 }
 
 // gelu_pytorch_tanh in fp32

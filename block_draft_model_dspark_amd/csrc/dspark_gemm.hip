@@ -98,23 +98,41 @@ __device__ __forceinline__ int wave_col(int c, int w, int N, int hd) {
 // ---------------------------------------------------------------------------
 // input rows (XM_NORM): per-row factors (r1, r2) and sc from the statistics
 // ---------------------------------------------------------------------------
-template <int MT>
-__device__ void norm_rows(const GemmArgs& g, int mbase, float2* rs) {
+// The first 16 rows' statistics (up to 128 parts) are loaded by
+// norm_issue before the weight loads are issued, so that they do not wait
+// behind the weights (a wave's loads complete in order); norm_finish reduces
+// them and handles any further rows or parts.
+constexpr int NV = 4;  // statistics parts per thread loaded ahead (16 threads per row)
+
+__device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4* v, float& sc) {
   const NormIn& n = g.nin;
-  const float sc = n.sc ? ld_act(n.sc, 0, n.act_bf16) : 1.f;
+  const int tid = threadIdx.x, sub = tid & 15;
+  const int m = min(mbase + (tid >> 4), g.M - 1);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = n.sums[(int64_t)min(sub + 16 * i, n.nparts - 1) * g.M + m];
+  sc = *n.sc;
+}
+
+template <int MT>
+__device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const float4* v0, float sc, float2* rs) {
+  const NormIn& n = g.nin;
   const int tid = threadIdx.x, sub = tid & 15;
   const float inv_k = 1.f / (float)g.K;
-#pragma unroll
   for (int r0 = 0; r0 < MT * 16; r0 += 16) {
     const int ml = r0 + (tid >> 4);
     const int m = min(mbase + ml, g.M - 1);
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < n.nparts; p0 += 128) {
-      float4 v[8];
+    for (int p0 = 0; p0 < n.nparts; p0 += 16 * NV) {
+      float4 v[NV];
+      if (r0 == 0 && p0 == 0) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = n.sums[(int64_t)min(p0 + sub + 16 * i, n.nparts - 1) * g.M + m];
+        for (int i = 0; i < NV; ++i) v[i] = v0[i];
+      } else {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+        for (int i = 0; i < NV; ++i) v[i] = n.sums[(int64_t)min(p0 + sub + 16 * i, n.nparts - 1) * g.M + m];
+      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
         if (p0 + sub + 16 * i < n.nparts) {
           s.x += v[i].x;
           s.y += v[i].y;
@@ -150,7 +168,7 @@ __device__ void norm_rows(const GemmArgs& g, int mbase, float2* rs) {
 // commutes with RoPE, so this stores RoPE(w * y) and y unscaled plus the
 // part's sum y^2, and the attention kernel applies the factor.
 template <int MT>
-__device__ void epi_qk(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, float* tile) {
+__device__ __forceinline__ void epi_qk(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, float* tile) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
@@ -206,7 +224,7 @@ __device__ void epi_qk(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, in
 // sublayer output y of 64 columns: store it and the row statistics the next
 // GEMM's input norms are formed from (see NormIn)
 template <int MT>
-__device__ void epi_sums(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
+__device__ __forceinline__ void epi_sums(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
                          float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const float w1 = ld_act_v(e.w1, n, e.act_bf16);
@@ -267,13 +285,13 @@ __device__ void epi_sums(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, 
 // z = cap * tanh(y / cap), plus the chunk statistics the walk prunes with.
 // For any previous token |markov_w2[v] . markov_w1[prev]| <= B_v :=
 // ||w2_v|| * max ||w1||, so an entry with z_v + B_v below max_u (z_u - B_u)
-// can never win a step.  Per (row, chunk): lo = max (z - B), hi = max (z + B)
-// and the WALK_TOP best z + B with their indices.
+// can never win a step.  Per (row, chunk): lo = max (z - B), hi = max (z + B).
 template <int MT>
-__device__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
+__device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
                        float* tile) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const int V = g.N;
+  const float b = e.aux ? walk_bound(e.aux, n, V) : 0.f;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -282,28 +300,29 @@ __device__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, in
       float z = acc[t][i];
       if (e.cap > 0.f) z = e.cap * tanhf(z / e.cap);
       if (m < g.M) e.Y[(int64_t)m * V + n] = z;
-      tile[r * 64 + 16 * wave + (lane & 15)] = z;
+      // per 16-column tile: max over the tile's columns of z - b and z + b
+      float lo = z - b, hi = z + b;
+#pragma unroll
+      for (int o = 8; o > 0; o >>= 1) {
+        lo = fmaxf(lo, __shfl_xor(lo, o));
+        hi = fmaxf(hi, __shfl_xor(hi, o));
+      }
+      if ((lane & 15) == 0) {
+        tile[(r * 4 + wave) * 2] = lo;
+        tile[(r * 4 + wave) * 2 + 1] = hi;
+      }
     }
   __syncthreads();
-  const int v = 64 * cb + lane;
-  const float b = e.aux ? e.aux[v] * e.aux[V] * (1.f + 1e-5f) : 0.f;
-  for (int r = wave; r < MT * 16; r += 4) {
+  for (int r = tid; r < MT * 16; r += 256) {
     const int m = mbase + r;
-    if (m >= g.M) break;
-    const float z = tile[r * 64 + lane];
-    const float lo = wave_max(z - b);
-    float u = z + b;
-    float2* top = e.top + ((int64_t)m * e.NC + cb) * WALK_TOP;
-    float hi = 0.f;
-    for (int t = 0; t < WALK_TOP; ++t) {
-      float bu = u;
-      int bi = v;
-      wave_argmax(bu, bi);
-      if (t == 0) hi = bu;
-      if (lane == 0) top[t] = make_float2(bu, __int_as_float(bi));
-      if (v == bi) u = -INFINITY;
+    if (m >= g.M) continue;
+    float lo = tile[r * 8], hi = tile[r * 8 + 1];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      lo = fmaxf(lo, tile[(r * 4 + w) * 2]);
+      hi = fmaxf(hi, tile[(r * 4 + w) * 2 + 1]);
     }
-    if (lane == 0) e.lohi[(int64_t)m * e.NC + cb] = make_float2(lo, hi);
+    e.lohi[(int64_t)m * e.NC + cb] = make_float2(lo, hi);
   }
 }
 
@@ -312,7 +331,7 @@ __device__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, in
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
 // rows is issued before the first use.
 template <int MT>
-__device__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp) {
+__device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hd = e.hd, HJ = hd >> 6, half = hd >> 1;
   const int layer = grp / e.nKv, kvh = grp - layer * e.nKv;
@@ -362,283 +381,418 @@ __device__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int 
 }
 
 // ---------------------------------------------------------------------------
-// activation staging: items (row ml, 8 consecutive k) -> LDS hi / lo planes
+// activation staging: items (row ml, 8 consecutive k) -> LDS hi / lo planes.
+// stage_load issues the loads of one batch of XB items per thread into
+// registers; stage_store converts them (norms for XM_NORM) and writes LDS.
 // ---------------------------------------------------------------------------
-template <int WK, int XM, int MT>
-__device__ __forceinline__ void stage_x(const GemmArgs& g, int mbase, int kc, int klen, u32x4* xhi, u32x4* xlo,
-                                        float* xsum, int nfull, int ngmax, const float2* rs, bool write_h) {
+// items per thread per batch: a 16-row tile with a 256-wide sub-slice stages
+// 2 items per thread, all in one batch
+template <int XM>
+constexpr int xbatch() { return 2; }
+
+template <int XB>
+struct XRegs {
+  f32x4 a[XB][2];  // XM_F32: x; XM_NORM: h
+  f32x4 y[XB][2];  // XM_NORM: y
+  u32x4 r16[XB];   // XM_BF16
+};
+
+// XM_NORM: the norm weights of the workgroup's K slice (at most KSMAX
+// wide), eight per thread (threads below klen/8), go through LDS
+// (wn[0..] = w1, wn[KSMAX..] = w2) instead of being loaded per item.
+// Raw words: w[0], w[1] = w1, w[2], w[3] = w2.
+constexpr int KSMAX = 2048;
+__device__ __forceinline__ void normw_load(const GemmArgs& g, int kc, int klen, u32x4* w) {
+  const NormIn& n = g.nin;
+  const int k8 = min((int)threadIdx.x, (klen >> 3) - 1);
+  const bool bf = n.act_bf16 != 0;
+  // unconditional loads from whichever vectors exist (at least one does)
+  const void* p1 = n.y ? n.w1 : n.w2;
+  const void* p2 = n.w2 ? n.w2 : p1;
+  const Raw8 a = ld_act8(p1, kc + 8 * k8, bf), b = ld_act8(p2, kc + 8 * k8, bf);
+  w[0] = a.a;
+  w[1] = a.b;
+  w[2] = b.a;
+  w[3] = b.b;
+}
+__device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u32x4* w, float* wn, int kcmax) {
+  const NormIn& n = g.nin;
+  const int k8 = threadIdx.x;
+  const bool bf = n.act_bf16 != 0;
+  if (k8 < (klen >> 3)) {
+    float v[8];
+    Raw8 r;
+    r.a = w[0];
+    r.b = w[1];
+    cvt_act8(r, bf, v);
+    *(f32x4*)&wn[8 * k8] = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)&wn[8 * k8 + 4] = f32x4{v[4], v[5], v[6], v[7]};
+    r.a = w[2];
+    r.b = w[3];
+    cvt_act8(r, bf, v);
+    *(f32x4*)&wn[kcmax + 8 * k8] = f32x4{v[0], v[1], v[2], v[3]};
+    *(f32x4*)&wn[kcmax + 8 * k8 + 4] = f32x4{v[4], v[5], v[6], v[7]};
+  }
+}
+
+template <int XM, int MT>
+__device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc, int klen, int base,
+                                           XRegs<xbatch<XM>()>& r) {
+  constexpr int XB = xbatch<XM>();
   const int tid = threadIdx.x;
   const int kq = klen >> 3;
   const int nitems = MT * 16 * kq;
-  constexpr int XB = XM == XM_NORM ? 2 : 4;  // items per thread per batch, all loads in flight together
-  for (int base = 0; base < nitems; base += 256 * XB) {
-    float v[XB][8];
+#pragma unroll
+  for (int b = 0; b < XB; ++b) {
+    const int it = base + tid + 256 * b;
+    const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
+    const int64_t m = min(mbase + ml, g.M - 1);
+    const int64_t k = kc + 8 * k8;
+    if constexpr (XM == XM_NORM) {
+      // both loads always issued (from whichever of h, y exists) so the
+      // number of loads in flight is fixed; stage_store ignores a missing one
+      const NormIn& n = g.nin;
+      const float* ph = n.h ? n.h : n.y;
+      const float* py = n.y ? n.y : n.h;
+      r.a[b][0] = *(const f32x4*)(ph + m * g.K + k);
+      r.a[b][1] = *(const f32x4*)(ph + m * g.K + k + 4);
+      r.y[b][0] = *(const f32x4*)(py + m * g.K + k);
+      r.y[b][1] = *(const f32x4*)(py + m * g.K + k + 4);
+    } else if constexpr (XM == XM_BF16) {
+      r.r16[b] = *(const u32x4*)((const uint16_t*)g.X + m * g.ldx + k);
+    } else {
+      const float* px = (const float*)g.X + m * g.ldx + k;
+      r.a[b][0] = *(const f32x4*)px;
+      r.a[b][1] = *(const f32x4*)(px + 4);
+    }
+  }
+}
+
+template <int WK, int XM, int MT>
+__device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc, int klen, int base,
+                                            const XRegs<xbatch<XM>()>& r,
+                                            u32x4* xhi, u32x4* xlo, float* xsum, int nfull, int ngmax,
+                                            const float2* rs, const float* wn, int kcmax, bool write_h) {
+  constexpr int XB = xbatch<XM>();
+  const int tid = threadIdx.x;
+  const int kq = klen >> 3;
+  const int nitems = MT * 16 * kq;
+#pragma unroll
+  for (int b = 0; b < XB; ++b) {
+    const int it = base + tid + 256 * b;
+    if (it >= nitems) break;
+    const int ml = it / kq, k8 = it - ml * kq;
+    const int m = mbase + ml;
+    const bool ok = m < g.M;
+    float v[8];
     if constexpr (XM == XM_NORM) {
       const NormIn& n = g.nin;
-      const bool bf = n.act_bf16 != 0;
-      f32x4 hv[XB][2], yv[XB][2];
-      Raw8 w1r[XB], w2r[XB];
-#pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
-        const int64_t m = min(mbase + ml, g.M - 1);
-        const int64_t k = kc + 8 * k8;
-        if (n.h) {
-          hv[b][0] = *(const f32x4*)(n.h + m * g.K + k);
-          hv[b][1] = *(const f32x4*)(n.h + m * g.K + k + 4);
-        }
-        if (n.y) {
-          yv[b][0] = *(const f32x4*)(n.y + m * g.K + k);
-          yv[b][1] = *(const f32x4*)(n.y + m * g.K + k + 4);
-          w1r[b] = ld_act8(n.w1, k, bf);
-        }
-        if (n.w2) w2r[b] = ld_act8(n.w2, k, bf);
-      }
       const float sc = rs[MT * 16].x;
+      const float2 rr = rs[ml];
+      const f32x4 w1a = *(const f32x4*)&wn[8 * k8], w1b = *(const f32x4*)&wn[8 * k8 + 4];
+      const f32x4 w2a = *(const f32x4*)&wn[kcmax + 8 * k8], w2b = *(const f32x4*)&wn[kcmax + 8 * k8 + 4];
+      float hn[8];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq, k8 = it - ml * kq;
-        const int m = mbase + ml;
-        const bool ok = it < nitems && m < g.M;
-        const float2 r = rs[ok ? ml : 0];
-        float w1[8], w2[8], hn[8];
-        if (n.y) cvt_act8(w1r[b], bf, w1);
-        if (n.w2) cvt_act8(w2r[b], bf, w2);
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const float h = n.h ? hv[b][q >> 2][q & 3] : 0.f;
-          const float y = n.y ? yv[b][q >> 2][q & 3] * r.x * w1[q] : 0.f;
-          hn[q] = (h + y) * sc;
-          v[b][q] = ok ? (n.w2 ? hn[q] * r.y * w2[q] : hn[q]) : 0.f;
-        }
-        if (write_h && ok) {
-          float* dst = n.hout + (int64_t)m * g.K + kc + 8 * k8;
-          *(f32x4*)dst = f32x4{hn[0], hn[1], hn[2], hn[3]};
-          *(f32x4*)(dst + 4) = f32x4{hn[4], hn[5], hn[6], hn[7]};
-        }
+      for (int q = 0; q < 8; ++q) {
+        const float w1 = q < 4 ? w1a[q & 3] : w1b[q & 3], w2 = q < 4 ? w2a[q & 3] : w2b[q & 3];
+        const float h = n.h ? r.a[b][q >> 2][q & 3] : 0.f;
+        const float y = n.y ? r.y[b][q >> 2][q & 3] * rr.x * w1 : 0.f;
+        hn[q] = (h + y) * sc;
+        v[q] = ok ? (n.w2 ? hn[q] * rr.y * w2 : hn[q]) : 0.f;
+      }
+      if (write_h && ok) {
+        float* dst = n.hout + (int64_t)m * g.K + kc + 8 * k8;
+        *(f32x4*)dst = f32x4{hn[0], hn[1], hn[2], hn[3]};
+        *(f32x4*)(dst + 4) = f32x4{hn[4], hn[5], hn[6], hn[7]};
       }
     } else if constexpr (XM == XM_BF16) {
-      u32x4 r[XB];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
-        const int64_t m = min(mbase + ml, g.M - 1);
-        r[b] = *(const u32x4*)((const uint16_t*)g.X + m * g.ldx + kc + 8 * k8);
-      }
-#pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq;
-        const bool ok = it < nitems && mbase + ml < g.M;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[b][2 * q] = ok ? __uint_as_float(r[b][q] << 16) : 0.f;
-          v[b][2 * q + 1] = ok ? __uint_as_float(r[b][q] & 0xFFFF0000u) : 0.f;
-        }
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = ok ? __uint_as_float(r.r16[b][q] << 16) : 0.f;
+        v[2 * q + 1] = ok ? __uint_as_float(r.r16[b][q] & 0xFFFF0000u) : 0.f;
       }
     } else {
-      f32x4 r[XB][2];
 #pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
-        const int64_t m = min(mbase + ml, g.M - 1);
-        const float* px = (const float*)g.X + m * g.ldx + kc + 8 * k8;
-        r[b][0] = *(const f32x4*)px;
-        r[b][1] = *(const f32x4*)(px + 4);
-      }
-#pragma unroll
-      for (int b = 0; b < XB; ++b) {
-        const int it = base + tid + 256 * b;
-        const int ml = it / kq;
-        const bool ok = it < nitems && mbase + ml < g.M;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[b][q] = ok ? r[b][q >> 2][q & 3] : 0.f;
-      }
+      for (int q = 0; q < 8; ++q) v[q] = ok ? r.a[b][q >> 2][q & 3] : 0.f;
     }
-    // LDS writes in A-operand order
+    int s, qg;
+    float e8[8];
+    if constexpr (WK == WK_Q4) {
+      const int grp = k8 >> 3, rr = k8 & 7;
+      qg = rr >> 1;
+      s = 2 * grp + (rr & 1);
+      const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+      float sum = 0.f;
 #pragma unroll
-    for (int b = 0; b < XB; ++b) {
-      const int it = base + tid + 256 * b;
-      if (it >= nitems) break;
-      const int ml = it / kq, k8 = it - ml * kq;
-      int s, qg;
-      float e8[8];
-      if constexpr (WK == WK_Q4) {
-        const int grp = k8 >> 3, rr = k8 & 7;
-        qg = rr >> 1;
-        s = 2 * grp + (rr & 1);
-        const int perm[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-        float sum = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          e8[q] = v[b][perm[q]];
-          sum += v[b][q];
-        }
-        atomicAdd(&xsum[ml * ngmax + grp], sum);
-      } else {
-        s = k8 >> 2;
-        qg = k8 & 3;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) e8[q] = v[b][q];
+      for (int q = 0; q < 8; ++q) {
+        e8[q] = v[perm[q]];
+        sum += v[q];
       }
-      const int slot = ((ml >> 4) * nfull + s) * 64 + qg * 16 + (ml & 15);
-      if constexpr (XM == XM_BF16) {
-        xhi[slot] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
-      } else {
-        bf16x8 h, l;
-        split8(e8, h, l);
-        xhi[slot] = __builtin_bit_cast(u32x4, h);
-        xlo[slot] = __builtin_bit_cast(u32x4, l);
-      }
+      atomicAdd(&xsum[ml * ngmax + grp], sum);
+    } else {
+      s = k8 >> 2;
+      qg = k8 & 3;
+#pragma unroll
+      for (int q = 0; q < 8; ++q) e8[q] = v[q];
+    }
+    const int slot = ((ml >> 4) * nfull + s) * 64 + qg * 16 + (ml & 15);
+    if constexpr (XM == XM_BF16) {
+      xhi[slot] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
+    } else {
+      bf16x8 h, l;
+      split8(e8, h, l);
+      xhi[slot] = __builtin_bit_cast(u32x4, h);
+      xlo[slot] = __builtin_bit_cast(u32x4, l);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-template <int WK, int XM, int MT, int EPI>
+// weights of one sub-slice in registers, and the MFMAs that consume them
+// ---------------------------------------------------------------------------
+template <int WK, int SMAX>
+struct WRegs {
+  u32x4 v[WK == WK_F32 ? 2 * SMAX : (WK == WK_BF16 ? SMAX : 1)];
+  u32x2 q[WK == WK_Q4 ? SMAX / 2 : 1];
+  float qs[WK == WK_Q4 ? SMAX / 2 : 1], qb[WK == WK_Q4 ? SMAX / 2 : 1];
+};
+
+template <int WK, int SMAX>
+__device__ __forceinline__ void load_w(const GemmArgs& g, int si, int64_t wrow, int kc, int nsteps,
+                                       WRegs<WK, SMAX>& w) {
+  const int gq = (threadIdx.x & 63) >> 4;
+  // every step is loaded (steps past nsteps repeat the last one and are not
+  // used), so the number of loads in flight is fixed and the compiler's wait
+  // counts stay exact
+  if constexpr (WK == WK_BF16) {
+    const uint16_t* p = (const uint16_t*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) w.v[s] = *(const u32x4*)(p + 32 * min(s, nsteps - 1));
+  } else if constexpr (WK == WK_F32) {
+    const float* p = (const float*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s) {
+      w.v[2 * s] = *(const u32x4*)(p + 32 * min(s, nsteps - 1));
+      w.v[2 * s + 1] = *(const u32x4*)(p + 32 * min(s, nsteps - 1) + 4);
+    }
+  } else {
+    const uint32_t* p = (const uint32_t*)g.seg[si].w + wrow * (g.K >> 3) + (kc >> 3) + 2 * gq;
+    const uint16_t* ps = (const uint16_t*)g.seg[si].s + wrow * (g.K >> 6) + (kc >> 6);
+    const uint16_t* pb = (const uint16_t*)g.seg[si].b + wrow * (g.K >> 6) + (kc >> 6);
+#pragma unroll
+    for (int j = 0; j < SMAX / 2; ++j)
+      if (2 * j < nsteps) {
+        w.q[j] = *(const u32x2*)(p + 8 * j);
+        w.qs[j] = bf2f(ps[j]);
+        w.qb[j] = bf2f(pb[j]);
+      }
+  }
+}
+
+template <int WK, int XM, int MT, int SMAX>
+__device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, const u32x4* xhi, const u32x4* xlo,
+                                      const float* xsum, int nfull, int ngmax, int nsteps) {
+  constexpr bool XBF = XM == XM_BF16;
+  const int lane = threadIdx.x & 63, gq = lane >> 4;
+  if constexpr (WK == WK_BF16) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < nsteps) {
+        const bf16x8 wb = __builtin_bit_cast(bf16x8, w.v[s]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int o = (t * nfull + s) * 64 + lane;
+          acc[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), wb, acc[t]);
+          if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wb, acc[t]);
+        }
+      }
+  } else if constexpr (WK == WK_F32) {
+#pragma unroll
+    for (int s = 0; s < SMAX; ++s)
+      if (s < nsteps) {
+        float w8[8];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          w8[q] = __uint_as_float(w.v[2 * s][q]);
+          w8[4 + q] = __uint_as_float(w.v[2 * s + 1][q]);
+        }
+        bf16x8 wh, wl;
+        split8(w8, wh, wl);
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+          const int o = (t * nfull + s) * 64 + lane;
+          const bf16x8 xh = __builtin_bit_cast(bf16x8, xhi[o]);
+          acc[t] = mfma16(xh, wh, acc[t]);
+          acc[t] = mfma16(xh, wl, acc[t]);
+          if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wh, acc[t]);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int j = 0; j < SMAX / 2; ++j)
+      if (2 * j < nsteps) {
+        f32x4 tmp[MT];
+#pragma unroll
+        for (int t = 0; t < MT; ++t) tmp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const bf16x8 wb = q4_decode(w.q[j][sub]);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            const int o = (t * nfull + 2 * j + sub) * 64 + lane;
+            tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), wb, tmp[t]);
+            if constexpr (!XBF) tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wb, tmp[t]);
+          }
+        }
+        const float sc = 16.f * w.qs[j], bc = w.qb[j] - sc;
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][i] += sc * tmp[t][i] + bc * xsum[(t * 16 + 4 * gq + i) * ngmax + j];
+      }
+  }
+}
+
+// LDS bytes of one staged activation sub-slice (hi / lo planes + q4 row sums)
+__host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, int kc) {
+  return (size_t)mt * (kc / 32) * 64 * 16 * (xmode == XM_BF16 ? 1 : 2) +
+         (wkind == WK_Q4 ? (size_t)mt * 16 * (kc / 64) * 4 : 0);
+}
+
+// ---------------------------------------------------------------------------
+template <int WK, int XM, int MT, int EPI, int NCH>
 __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e) {
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
   __shared__ float2 rs[MT * 16 + 1];
-  constexpr int KCMAX = (WK == WK_F32) ? 256 : 512;
+  __shared__ __align__(16) float wn[XM == XM_NORM ? 2 * KSMAX : 1];
+  // sub-slice width bound (the host plans kc <= KCMAX): 256 for one 16-row
+  // tile (double-buffered) and for fp32 weights, else 512
+  constexpr int KCMAX = (MT == 1 || WK == WK_F32) ? 256 : 512;
   constexpr int SMAX = KCMAX / 32;
-  constexpr bool XBF = XM == XM_BF16;
+  constexpr int XB = xbatch<XM>();
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
-  const int KC = g.kc;
+  const int KC = NCH > 0 ? KCMAX : g.kc;  // unrolled variants run at KCMAX (the launcher checks)
   const int nfull = KC >> 5;
   const int ngmax = KC >> 6;
-  u32x4* xhi = (u32x4*)smem;
-  u32x4* xlo = xhi + MT * nfull * 64;
-  float* xsum = (float*)(xhi + (XBF ? 1 : 2) * MT * nfull * 64);
+  const size_t xbuf = xbuf_bytes(WK, XM, MT, KC);
 
   const int cb = blockIdx.x;
-  const int n0w = wave_col<EPI>(cb, wave, g.N, e.hd);
+  // wave-uniform values in scalar registers, so that the weight segment is
+  // read from the kernel arguments with scalar loads (a vector load of the
+  // pointer would make the first weight load wait for every earlier load)
+  const int n0w = __builtin_amdgcn_readfirstlane(wave_col<EPI>(cb, wave, g.N, e.hd));
   int si = 0;
   for (int i = 1; i < g.nseg; ++i)
     if (n0w >= g.seg[i].n0) si = i;
+  si = __builtin_amdgcn_readfirstlane(si);
   const int64_t wrow = (int64_t)(n0w - g.seg[si].n0 + (lane & 15));
   const int mbase = blockIdx.z * (MT * 16);
   const int kbeg = blockIdx.y * g.kslice;
   const int kend = min(g.K, kbeg + g.kslice);
   const bool write_h = XM == XM_NORM && g.nin.hout != nullptr && blockIdx.x == 0;
+  // NCH > 0: every slice is exactly NCH sub-slices of KC (fully unrolled,
+  // so the loads of the next two sub-slices stay in flight with exact waits)
+  const int nch = NCH > 0 ? NCH : (kend - kbeg + KC - 1) / KC;
 
   f32x4 acc[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int kc = kbeg; kc < kend; kc += KC) {
-    const int klen = min(KC, kend - kc);
-    const int nsteps = klen >> 5;
+  // 1. the small loads first (a wave's loads complete in order): row
+  //    statistics and norm weights of the slice, then chunk 0's activations
+  //    and weights (and chunk 1's, double-buffered, for a 16-row tile)
+  float4 nv[NV];
+  float sc_in = 1.f;
+  u32x4 wr[4];
+  if constexpr (XM == XM_NORM) {
+    norm_issue(g, mbase, nv, sc_in);
+    normw_load(g, kbeg, kend - kbeg, wr);
+  }
+  XRegs<XB> xa, xb;
+  WRegs<WK, SMAX> wa, wb;
+  auto chunk_k = [&](int c) { return kbeg + c * KC; };
+  auto chunk_len = [&](int c) { return NCH > 0 ? KC : min(KC, kend - chunk_k(c)); };
+  stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa);
+  load_w<WK, SMAX>(g, si, wrow, chunk_k(0), chunk_len(0) >> 5, wa);
+  if (MT == 1 && (NCH > 1 || (NCH == 0 && nch > 1))) {
+    stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb);
+    load_w<WK, SMAX>(g, si, wrow, chunk_k(1), chunk_len(1) >> 5, wb);
+  }
+  if constexpr (XM == XM_NORM) {
+    norm_finish<MT>(g, mbase, nv, sc_in, rs);
+    normw_store(g, kend - kbeg, wr, wn, KSMAX);
+    __syncthreads();
+  }
 
-    // 1. weights of this sub-slice -> registers
-    u32x4 wv[WK == WK_F32 ? 2 * SMAX : (WK == WK_BF16 ? SMAX : 1)];
-    u32x2 wq[WK == WK_Q4 ? SMAX / 2 : 1];
-    float qs[WK == WK_Q4 ? SMAX / 2 : 1], qb[WK == WK_Q4 ? SMAX / 2 : 1];
-    if constexpr (WK == WK_BF16) {
-      const uint16_t* p = (const uint16_t*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < nsteps) wv[s] = __builtin_nontemporal_load((const u32x4*)(p + 32 * s));
-    } else if constexpr (WK == WK_F32) {
-      const float* p = (const float*)g.seg[si].w + wrow * g.K + kc + 8 * gq;
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < nsteps) {
-          wv[2 * s] = *(const u32x4*)(p + 32 * s);
-          wv[2 * s + 1] = *(const u32x4*)(p + 32 * s + 4);
-        }
-    } else {
-      const uint32_t* p = (const uint32_t*)g.seg[si].w + wrow * (g.K >> 3) + (kc >> 3) + 2 * gq;
-      const uint16_t* ps = (const uint16_t*)g.seg[si].s + wrow * (g.K >> 6) + (kc >> 6);
-      const uint16_t* pb = (const uint16_t*)g.seg[si].b + wrow * (g.K >> 6) + (kc >> 6);
-#pragma unroll
-      for (int j = 0; j < SMAX / 2; ++j)
-        if (2 * j < nsteps) {
-          wq[j] = *(const u32x2*)(p + 8 * j);
-          qs[j] = bf2f(ps[j]);
-          qb[j] = bf2f(pb[j]);
-        }
-    }
-
-    // 2. activation sub-slice -> LDS (hi / lo planes, A-operand order)
-    if constexpr (XM == XM_NORM) {
-      if (kc == kbeg) {
-        norm_rows<MT>(g, mbase, rs);
-        __syncthreads();
-      }
-    }
+  // 2. per chunk: activations -> LDS buffer (hi / lo planes, A-operand
+  //    order), then the MFMAs against the weight registers
+  auto run_chunk = [&](int c, const XRegs<XB>& xr, const WRegs<WK, SMAX>& w, int buf) {
+    const int kc = chunk_k(c), klen = chunk_len(c);
+    u32x4* xhi = (u32x4*)(smem + buf * xbuf);
+    u32x4* xlo = xhi + MT * nfull * 64;
+    float* xsum = (float*)(xhi + (XM == XM_BF16 ? 1 : 2) * MT * nfull * 64);
     if constexpr (WK == WK_Q4) {
       for (int i = tid; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
       __syncthreads();
     }
-    stage_x<WK, XM, MT>(g, mbase, kc, klen, xhi, xlo, xsum, nfull, ngmax, rs, write_h);
-    __syncthreads();
-
-    // 3. MFMAs
-    if constexpr (WK == WK_BF16) {
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < nsteps) {
-          const bf16x8 w = __builtin_bit_cast(bf16x8, wv[s]);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const int o = (t * nfull + s) * 64 + lane;
-            acc[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, acc[t]);
-            if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, acc[t]);
-          }
-        }
-    } else if constexpr (WK == WK_F32) {
-#pragma unroll
-      for (int s = 0; s < SMAX; ++s)
-        if (s < nsteps) {
-          float w8[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            w8[q] = __uint_as_float(wv[2 * s][q]);
-            w8[4 + q] = __uint_as_float(wv[2 * s + 1][q]);
-          }
-          bf16x8 wh, wl;
-          split8(w8, wh, wl);
-#pragma unroll
-          for (int t = 0; t < MT; ++t) {
-            const int o = (t * nfull + s) * 64 + lane;
-            const bf16x8 xh = __builtin_bit_cast(bf16x8, xhi[o]);
-            acc[t] = mfma16(xh, wh, acc[t]);
-            acc[t] = mfma16(xh, wl, acc[t]);
-            if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wh, acc[t]);
-          }
-        }
-    } else {
-#pragma unroll
-      for (int j = 0; j < SMAX / 2; ++j)
-        if (2 * j < nsteps) {
-          f32x4 tmp[MT];
-#pragma unroll
-          for (int t = 0; t < MT; ++t) tmp[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int sub = 0; sub < 2; ++sub) {
-            const bf16x8 w = q4_decode(wq[j][sub]);
-#pragma unroll
-            for (int t = 0; t < MT; ++t) {
-              const int o = (t * nfull + 2 * j + sub) * 64 + lane;
-              tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), w, tmp[t]);
-              if constexpr (!XBF) tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), w, tmp[t]);
-            }
-          }
-          const float sc = 16.f * qs[j], bc = qb[j] - sc;
-#pragma unroll
-          for (int t = 0; t < MT; ++t)
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-              acc[t][i] += sc * tmp[t][i] + bc * xsum[(t * 16 + 4 * gq + i) * ngmax + j];
-        }
+    stage_store<WK, XM, MT>(g, mbase, kc, klen, 0, xr, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg), KSMAX,
+                            write_h);
+    const int nitems = MT * 16 * (klen >> 3);
+    for (int base = 256 * XB; base < nitems; base += 256 * XB) {
+      XRegs<XB> xt;
+      stage_load<XM, MT>(g, mbase, kc, klen, base, xt);
+      stage_store<WK, XM, MT>(g, mbase, kc, klen, base, xt, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg),
+                              KSMAX, write_h);
     }
     __syncthreads();
+    mma_w<WK, XM, MT, SMAX>(acc, w, xhi, xlo, xsum, nfull, ngmax, klen >> 5);
+  };
+  if constexpr (MT == 1 && NCH > 0) {
+#pragma unroll
+    for (int c = 0; c < NCH; c += 2) {
+      run_chunk(c, xa, wa, 0);
+      if (c + 2 < NCH) {
+        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), KC, 0, xa);
+        load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 2), KC >> 5, wa);
+      }
+      if (c + 1 < NCH) {
+        run_chunk(c + 1, xb, wb, 1);
+        if (c + 3 < NCH) {
+          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), KC, 0, xb);
+          load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 3), KC >> 5, wb);
+        }
+      }
+    }
+  } else if constexpr (MT == 1) {
+    // 16-row tile: two chunks in flight, two LDS buffers (a buffer is only
+    // rewritten after the barrier that follows the other buffer's staging)
+    for (int c = 0; c < nch; c += 2) {
+      run_chunk(c, xa, wa, 0);
+      if (c + 2 < nch) {
+        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), chunk_len(c + 2), 0, xa);
+        load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 2), chunk_len(c + 2) >> 5, wa);
+      }
+      if (c + 1 < nch) {
+        run_chunk(c + 1, xb, wb, 1);
+        if (c + 3 < nch) {
+          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), chunk_len(c + 3), 0, xb);
+          load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 3), chunk_len(c + 3) >> 5, wb);
+        }
+      }
+    }
+  } else {
+    // 64-row tiles: one chunk at a time in one LDS buffer
+    for (int c = 0; c < nch; ++c) {
+      if (c > 0) {
+        __syncthreads();
+        stage_load<XM, MT>(g, mbase, chunk_k(c), chunk_len(c), 0, xa);
+        load_w<WK, SMAX>(g, si, wrow, chunk_k(c), chunk_len(c) >> 5, wa);
+      }
+      run_chunk(c, xa, wa, 0);
+    }
   }
+  __syncthreads();
 
   // 4. split-K reduction in the last workgroup of this column block
   const int S = gridDim.y;
@@ -721,9 +875,8 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
 }
 
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc) {
-  size_t b = (size_t)mt * (kc / 32) * 64 * 16 * (xmode == XM_BF16 ? 1 : 2);
-  if (wkind == WK_Q4) b += (size_t)mt * 16 * (kc / 64) * 4;
-  const size_t tile = (size_t)mt * 16 * 64 * 4;  // epilogue tiles
+  const size_t b = xbuf_bytes(wkind, xmode, mt, kc) * (mt == 1 ? 2 : 1);  // a 16-row tile double-buffers
+  const size_t tile = (size_t)mt * 16 * 64 * 4;                          // epilogue tiles
   return b > tile ? b : tile;
 }
 
@@ -750,7 +903,22 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
   if constexpr (built<XM, EPI>()) {
     const int mblocks = (a.M + MT * 16 - 1) / (MT * 16);
     const dim3 grid(a.N / 64, S, mblocks);
-    hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI>), grid, dim3(256), gemm_lds_bytes(WK, XM, MT, a.kc), st, a, e);
+    const size_t lds = gemm_lds_bytes(WK, XM, MT, a.kc);
+    // unrolled variants for bf16 weights and one 16-row tile when every
+    // slice is a whole number (1, 2, 4 or 8) of sub-slices
+    int nch = 0;
+    if (WK == WK_BF16 && MT == 1 && a.kc == 256 && a.K % a.kslice == 0 && a.kslice % a.kc == 0)
+      nch = a.kslice / a.kc;
+    if constexpr (WK == WK_BF16 && MT == 1) {
+      switch (nch) {
+        case 1: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 1>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 2: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 2>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 4: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 8: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        default: break;
+      }
+    }
+    hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 0>), grid, dim3(256), lds, st, a, e);
     return hipGetLastError();
   } else {
     return hipErrorInvalidValue;

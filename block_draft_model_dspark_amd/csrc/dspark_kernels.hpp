@@ -12,8 +12,8 @@ enum { XM_F32 = 0, XM_BF16 = 1, XM_NORM = 2 };  // how a GEMM reads its input ro
 
 constexpr int MAX_ROWS = 64;
 constexpr int MAX_SEG = 8;
+constexpr int MAX_LAYERS = 64;
 constexpr int WALK_CHUNK = 64;  // vocabulary entries per walk-statistics chunk (one GEMM column block)
-constexpr int WALK_TOP = 4;     // best candidates kept per chunk
 constexpr int ATT_KEYS = 32;    // keys staged per attention pass
 
 // Row statistics of one 64-column block of a sublayer output y with the
@@ -28,7 +28,7 @@ struct NormIn {
   int nparts;          // K / 64
   const void* w1;      // [K] act dtype (unused when y is null)
   const void* w2;      // [K] act dtype, or null: x = hn
-  const void* sc;      // [1] act dtype, or null: sc = 1
+  const float* sc;     // [1] fp32 residual scale (a layer_scalar copy, or 1)
   float* hout;         // [M, K]: hn is written here by column block 0, or null
   float eps;
   int act_bf16;
@@ -91,7 +91,6 @@ struct EpiArgs {
   float cap;          // <= 0: none
   const float* aux;   // [V] markov_w2 row norms, aux[V] = max markov_w1 row norm; null when rank 0
   float2* lohi;       // [M, NC] (max z - B, max z + B) per chunk
-  float2* top;        // [M, NC, WALK_TOP] (z + B, index as float bits), best first
   int NC;
 };
 
@@ -106,6 +105,9 @@ struct RowTab {
 struct EmbedArgs {
   const void* E; const void* Es; const void* Eb; int ekind; int group;
   int H; float scale; int mask_id;
+  int act_bf16, nL;
+  const void* scal_src[MAX_LAYERS];  // per layer layer_scalar [1] act dtype
+  float* scal;        // [nL + 1]: 1, then the layer scalars as fp32
   float* h;           // [M, H] scaled embedding rows
   float4* sums;       // [H/64, M] (0, 0, 0, sum h^2)
   float2* rt;         // [M, hd/2] RoPE table of the block positions
@@ -117,6 +119,7 @@ struct EmbedArgs {
 // counters + RoPE table of the context projection
 struct PrepArgs {
   unsigned* cnt; int ncnt;
+  float* one;         // [1] set to 1 (residual scale of the projection's input norm)
   float2* rt;         // [B*L, hd/2]
   int B, L;
   RopeCfg rope;
@@ -148,7 +151,7 @@ struct MergeArgs {
 struct WalkArgs {
   RowTab rows;
   int V, NC, rank, wkind, group;
-  const float* z; const float2* lohi; const float2* top;
+  const float* z; const float2* lohi; const float* aux;
   const void* w1; const void* w1s; const void* w1b;
   const void* w2; const void* w2s; const void* w2b;
   int32_t* tokens;

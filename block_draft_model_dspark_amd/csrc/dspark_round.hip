@@ -21,14 +21,16 @@ __device__ __forceinline__ float table_elem(const void* E, const void* Es, const
 // ---------------------------------------------------------------------------
 // deepspec.ts, #forwardBackbone: h = embed([anchor, MASK...]) * sqrt(H).
 // Writes h, the row statistics (0, 0, 0, sum h^2) of every 64-column block
-// that the first q|k GEMM forms layer 0's input norm from, and the
-// (cos, sin) table of the row's position for every RoPE pair.
+// that the first q|k GEMM forms layer 0's input norm from, the (cos, sin)
+// table of the row's position for every RoPE pair, and the layer scalars.
 // grid M, block 256.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   const int m = blockIdx.x, tid = threadIdx.x, M = gridDim.x;
   // the GEMM reduction counters of this round start at zero
   for (int i = m * 256 + tid; i < a.ncnt; i += gridDim.x * 256) a.cnt[i] = 0u;
+  // residual scales as fp32 for the GEMMs' input norms
+  if (m == 0 && tid <= a.nL) a.scal[tid] = tid == 0 ? 1.f : ld_act(a.scal_src[tid - 1], 0, a.act_bf16);
   const int row = m / a.rows.gamma, g = m - row * a.rows.gamma;
   const int64_t id = g == 0 ? a.rows.anchor[row] : a.mask_id;
   for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
@@ -62,6 +64,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
 __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x, nth = (int64_t)gridDim.x * 256;
   for (int64_t i = gid; i < a.ncnt; i += nth) a.cnt[i] = 0u;
+  if (gid == 0) a.one[0] = 1.f;
   const int half = a.rope.hd >> 1;
   const int64_t total = (int64_t)a.B * a.L * half;
   for (int64_t i = gid; i < total; i += nth) {
@@ -136,10 +139,10 @@ __device__ __forceinline__ float head_elem(const void* w, const void* s, const v
 // step (the winner w has z_w + B_w >= u_w >= max_v (z_v - B_v)), and that set
 // C_k does not depend on the previous token.  The previous token of step k
 // is the winner of step k-1, so it lies in C_{k-1} (the anchor for k = 0).
-// The fast path therefore builds every C_k from the per-chunk statistics and
-// top lists, scores the table z_k[c] + w2[c] . w1[p] for p in C_{k-1},
-// c in C_k in parallel, then walks the table in LDS.  If some step keeps more
-// than WALK_CMAX entries, a chunk's WALK_TOP-th best still passes, or too
+// The fast path therefore builds every C_k from the per-chunk bounds and the
+// logits of the chunks that can hold a member, scores the table
+// z_k[c] + w2[c] . w1[p] for p in C_{k-1}, c in C_k in parallel, then walks
+// the table in LDS.  If some step keeps more than WALK_CMAX entries or too
 // many chunks pass, the row takes the per-step path that scores every
 // surviving entry against the actual previous token.
 // grid A, block 256
@@ -226,21 +229,12 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
     int bi = 0x7fffffff;
     for (int c = tid; c < a.NC; c += 256) {
       if (!(lh[c].y >= thr)) continue;
-      const float2* tp = a.top + (m * a.NC + c) * WALK_TOP;
-      if (tp[WALK_TOP - 1].x < thr) {
-        for (int t = 0; t < WALK_TOP - 1; ++t)
-          if (tp[t].x >= thr) {
-            const int v = __float_as_int(tp[t].y);
-            float u = a.z[m * a.V + v];
-            if (a.rank > 0) u += w2_dot(a, v, e);
-            if (better(u, v, bu, bi)) { bu = u; bi = v; }
-          }
-      } else {
-        for (int v = c * WALK_CHUNK; v < min(c * WALK_CHUNK + WALK_CHUNK, a.V); ++v) {
-          float u = a.z[m * a.V + v];
-          if (a.rank > 0) u += w2_dot(a, v, e);
-          if (better(u, v, bu, bi)) { bu = u; bi = v; }
-        }
+      for (int v = c * WALK_CHUNK; v < min(c * WALK_CHUNK + WALK_CHUNK, a.V); ++v) {
+        const float zv = a.z[m * a.V + v];
+        if (!(zv + (a.aux ? walk_bound(a.aux, v, a.V) : 0.f) >= thr)) continue;
+        float u = zv;
+        if (a.rank > 0) u += w2_dot(a, v, e);
+        if (better(u, v, bu, bi)) { bu = u; bi = v; }
       }
     }
     block_argmax(bu, bi, redu, redi);
@@ -305,24 +299,35 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
   __syncthreads();
   const int nf = nflag;
   if (nf > WALK_FMAX) slow = 1;
-  // 3. candidates from the passing chunks' top lists
-  for (int f = tid; f < min(nf, WALK_FMAX); f += 256) {
-    const int kk = flag_kc[f] >> 24, c = flag_kc[f] & 0xFFFFFF;
-    const float2* tp = a.top + (((int64_t)row * G + kk) * NC + c) * WALK_TOP;
-    float2 t[WALK_TOP];
+  // 3. candidates: the entries of the passing chunks that reach the
+  //    threshold; one wave per chunk, four chunks in flight per wave
+  const int nfm = min(nf, WALK_FMAX);
+  for (int f0 = wave * 4; f0 < nfm; f0 += 16) {
+    float zz[4], bb[4];
+    int kq[4], vq[4];
 #pragma unroll
-    for (int i = 0; i < WALK_TOP; ++i) t[i] = tp[i];
-    const float th2 = thr[kk];
-    if (!(t[WALK_TOP - 1].x < th2)) {
-      slow = 1;
-    } else {
+    for (int q = 0; q < 4; ++q) {
+      const int f = flag_kc[min(f0 + q, nfm - 1)];
+      kq[q] = f >> 24;
+      vq[q] = (f & 0xFFFFFF) * WALK_CHUNK + lane;
+      zz[q] = a.z[((int64_t)row * G + kq[q]) * a.V + vq[q]];
+      bb[q] = a.aux ? walk_bound(a.aux, vq[q], a.V) : 0.f;
+    }
 #pragma unroll
-      for (int i = 0; i < WALK_TOP - 1; ++i)
-        if (t[i].x >= th2) {
-          const int o = atomicAdd(&ncand[kk], 1);
-          if (o < WALK_CMAX) cand[kk][o] = __float_as_int(t[i].y);
-          else slow = 1;
-        }
+    for (int q = 0; q < 4; ++q) {
+      if (f0 + q >= nfm) break;
+      const bool pass = zz[q] + bb[q] >= thr[kq[q]];
+      const uint64_t bal = __ballot(pass);
+      const int cnt = __popcll(bal);
+      if (cnt == 0) continue;
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&ncand[kq[q]], cnt);
+      base = __shfl(base, 0);
+      if (base + cnt > WALK_CMAX) {
+        if (lane == 0) slow = 1;
+      } else if (pass) {
+        cand[kq[q]][base + __popcll(bal & ((1ull << lane) - 1ull))] = vq[q];
+      }
     }
   }
   __syncthreads();
