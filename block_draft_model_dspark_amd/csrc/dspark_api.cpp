@@ -162,8 +162,13 @@ GemmSeg seg_of(const Mat& w, int n0) {
 }
 
 // ---- draft workspace layout ---------------------------------------------
+// Row pitches of the fp32 activation buffers are padded by 64 floats so that
+// the rows of one column range fall on different L2 / HBM channels.
+constexpr int ROW_PAD = 64;
+
 struct DraftLayout {
   size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, total;
+  int64_t ldh, ldo, ldact;
   GemmPlan qk, o, gu, dn, lm;
   size_t cwords;
   int nsplit_max;
@@ -198,14 +203,17 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
     off = align256(off + bytes);
     return o;
   };
-  d.hA = take((size_t)M * H * 4);
-  d.hB = take((size_t)M * H * 4);
-  d.Y = take((size_t)M * H * 4);
+  d.ldh = H + ROW_PAD;
+  d.ldo = (int64_t)nH * hd + ROW_PAD;
+  d.ldact = I + ROW_PAD;
+  d.hA = take((size_t)M * d.ldh * 4);
+  d.hB = take((size_t)M * d.ldh * 4);
+  d.Y = take((size_t)M * d.ldh * 4);
   d.sums = take((size_t)(H / 64) * M * 16);
   d.rt = take((size_t)M * (hd / 2) * 8);
   d.scal = take((size_t)(c.num_hidden_layers + 1) * 4);
-  d.O = take((size_t)M * nH * hd * 4);
-  d.act = take((size_t)M * I * 4);
+  d.O = take((size_t)M * d.ldo * 4);
+  d.act = take((size_t)M * d.ldact * 4);
   d.P = take(pmax);
   d.cnt = take(d.cwords * 4);
   d.q = take((size_t)A * nKv * m->nq * hd * 4);
@@ -511,11 +519,13 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     e.cnt = cnt;
     e.act_bf16 = act_bf16(m);
     e.h = nullptr;
+    e.ldy = H;
     e.w1 = m->hidden_norm;
     e.sums = (float4*)(ws + p.sums);
     HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream); }));
     nin.y = e.Y;
     nin.sums = e.sums;
+    nin.ld = H;
     nin.nparts = H / 64;
     nin.w1 = m->hidden_norm;
     nin.sc = pr.one;
@@ -653,6 +663,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   mg.opart = at.opart;
   mg.ml = at.ml;
   mg.O = O;
+  mg.ldo = d.ldo;
 
   EmbedArgs em{};
   em.E = m->embed.w;
@@ -664,6 +675,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   em.scale = (float)std::sqrt((double)H);
   em.mask_id = c.mask_token_id;
   em.h = hA;
+  em.ldh = d.ldh;
   em.act_bf16 = abf;
   em.nL = nL;
   for (int l = 0; l < nL; ++l) em.scal_src[l] = m->L[l].scalar;
@@ -688,6 +700,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     n.w2 = w2;
     n.sc = sc;
     n.hout = hout;
+    n.ld = d.ldh;
     n.eps = eps;
     n.act_bf16 = abf;
     return n;
@@ -707,6 +720,8 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   e.vb = (float*)(ws + d.vb);
   e.ssq = (float*)(ws + d.ssq);
   e.act = act;
+  e.ld_act = d.ldact;
+  e.ldy = d.ldh;
   e.sums = sums;
 
   // The residual stream is formed lazily: a sublayer output y stays in Y
@@ -740,7 +755,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
 
     g = GemmArgs{};
     g.X = O;
-    g.ldx = nH * hd;
+    g.ldx = d.ldo;
     g.M = M;
     g.N = H;
     g.K = nH * hd;
@@ -766,7 +781,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
 
     g = GemmArgs{};
     g.X = act;
-    g.ldx = I;
+    g.ldx = d.ldact;
     g.M = M;
     g.N = H;
     g.K = I;

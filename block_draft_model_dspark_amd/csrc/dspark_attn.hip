@@ -101,15 +101,119 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
 
 __device__ __forceinline__ uint16_t half_of(const u32x4& w, int e) { return (uint16_t)(w[e >> 1] >> (16 * (e & 1))); }
 
-template <int HD, bool KVB>
-__global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
-  constexpr int NS = HD / 32, NT = HD / 16, KSTR = HD + 8, VSTR = 40, HJ = HD / 64;
+// The keys of one split: every load of chunk c + 1 is issued before chunk c's
+// MFMAs, and chunk 0's before the query rows are converted (a wave's loads
+// complete in order, so the query loads go first).  ONE: bf16 context keys,
+// 32 per pass in one plane; else fp32 keys (the block's own, scaled by their
+// RMS factor: rkey for this thread's key, or an fp32 cache: 1) in two 16-key
+// passes of hi / lo planes.
+template <int HD, bool ONE>
+__device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, int j0, int j1, float rkey,
+                                          const f32x4 (*x)[2], float r, bf16x8* qh, bf16x8* ql, f32x4* o,
+                                          float& m_run, float& l_part, uint16_t* Ks, uint16_t* Vt) {
+  constexpr int NS = HD / 32, KSTR = HD + 8, VSTR = 40;
   constexpr int NTH = 64 * ATT_QW;
   constexpr int IPT = ATT_KEYS * (HD / 8) / NTH;  // staging items (key, 8 dims) per thread
-  static_assert(IPT >= 1 && NTH % ATT_KEYS == 0, "staging layout");
-  __shared__ __align__(16) uint16_t Ks[32 * KSTR];
-  __shared__ __align__(16) uint16_t Vt[HD * VSTR];
-  __shared__ float rk[ATT_KEYS];
+  const int tid = threadIdx.x;
+  const int key = tid & (ATT_KEYS - 1);  // the key this thread stages (all its items)
+  u32x4 kk[ONE ? IPT : 1], vv[ONE ? IPT : 1];
+  f32x4 kf[ONE ? 1 : IPT][2], vf[ONE ? 1 : IPT][2];
+  auto load = [&](int jc) {
+    const int kc = jc + min(key, j1 - jc - 1);
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      const int c8 = (tid + NTH * i) / ATT_KEYS;
+      if constexpr (ONE) {
+        kk[i] = *(const u32x4*)((const uint16_t*)kbase + (int64_t)kc * HD + 8 * c8);
+        vv[i] = *(const u32x4*)((const uint16_t*)vbase + (int64_t)kc * HD + 8 * c8);
+      } else {
+        const float* kp = (const float*)kbase + (int64_t)kc * HD + 8 * c8;
+        const float* vp = (const float*)vbase + (int64_t)kc * HD + 8 * c8;
+        kf[i][0] = *(const f32x4*)kp;
+        kf[i][1] = *(const f32x4*)(kp + 4);
+        vf[i][0] = *(const f32x4*)vp;
+        vf[i][1] = *(const f32x4*)(vp + 4);
+      }
+    }
+  };
+  load(j0);
+  // the query operand, now that the first keys are in flight
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    float t[8];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      t[e] = x[s][0][e] * r;
+      t[4 + e] = x[s][1][e] * r;
+    }
+    split8(t, qh[s], ql[s]);
+  }
+  for (int jc = j0; jc < j1; jc += ATT_KEYS) {
+    const int nk = min(ATT_KEYS, j1 - jc);
+    const bool ok = key < nk;
+    if constexpr (ONE) {
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < IPT; ++i) {
+        const int c8 = (tid + NTH * i) / ATT_KEYS;
+        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
+        *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
+        const u32x4 vw = ok ? vv[i] : z;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) Vt[(8 * c8 + e) * VSTR + key] = half_of(vw, e);
+      }
+      __syncthreads();
+      if (jc + ATT_KEYS < j1) load(jc + ATT_KEYS);
+      attn_pass<HD, true>(Ks, Vt, qh, ql, o, m_run, l_part, nk);
+    } else {
+      float kv8[IPT][8], vv8[IPT][8];
+      const float sc = ok ? rkey : 0.f;
+#pragma unroll
+      for (int i = 0; i < IPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv8[i][e] = kf[i][0][e] * sc;
+          kv8[i][4 + e] = kf[i][1][e] * sc;
+          vv8[i][e] = vf[i][0][e] * sc;
+          vv8[i][4 + e] = vf[i][1][e] * sc;
+        }
+      if (jc + ATT_KEYS < j1) load(jc + ATT_KEYS);
+      for (int pass = 0; pass < 2 && 16 * pass < nk; ++pass) {
+        __syncthreads();
+        if ((key >> 4) == pass) {
+          const int rr = key & 15;
+#pragma unroll
+          for (int i = 0; i < IPT; ++i) {
+            const int c8 = (tid + NTH * i) / ATT_KEYS;
+            bf16x8 kh, kl, vh, vl;
+            split8(kv8[i], kh, kl);
+            split8(vv8[i], vh, vl);
+            *(u32x4*)&Ks[rr * KSTR + 8 * c8] = __builtin_bit_cast(u32x4, kh);
+            *(u32x4*)&Ks[(16 + rr) * KSTR + 8 * c8] = __builtin_bit_cast(u32x4, kl);
+            // halves are taken from the whole-vector bit pattern (bit-casting a
+            // single __bf16 vector element is lowered to element 0 by this compiler)
+            const u32x4 vhw = __builtin_bit_cast(u32x4, vh), vlw = __builtin_bit_cast(u32x4, vl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              Vt[(8 * c8 + e) * VSTR + rr] = half_of(vhw, e);
+              Vt[(8 * c8 + e) * VSTR + 16 + rr] = half_of(vlw, e);
+            }
+          }
+        }
+        __syncthreads();
+        attn_pass<HD, false>(Ks, Vt, qh, ql, o, m_run, l_part, min(16, nk - 16 * pass));
+      }
+    }
+  }
+}
+
+template <int HD, bool KVB>
+__global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
+  constexpr int NS = HD / 32, NT = HD / 16, HJ = HD / 64;
+  constexpr int NTH = 64 * ATT_QW;
+  static_assert(ATT_KEYS * (HD / 8) / NTH >= 1 && NTH % ATT_KEYS == 0, "staging layout");
+  __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
+  __shared__ __align__(16) uint16_t Vt[HD * 40];
 
   const int sg = blockIdx.x, kvh = blockIdx.y;
   int row = 0;
@@ -123,128 +227,49 @@ __global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
   const bool qok = qrow < a.nq;
   const int rep = a.nH / a.nKv;
 
-  // RMS factors of the block keys (k_norm / weightless v share the factor)
-  if (blk && tid < a.gamma) {
-    const int m = row * a.gamma + tid;
-    float ss = 0.f;
-#pragma unroll
-    for (int p = 0; p < HJ; ++p) ss += a.ssq[(int64_t)((a.nH + kvh) * HJ + p) * a.M + m];
-    rk[tid] = 1.f / sqrtf(ss / HD + a.eps);
-  }
-
-  // query operand (B of S^T = K q^T): col = query row, k = hd 32s + 8gq..
-  bf16x8 qh[NS], ql[NS];
+  // query rows (B of S^T = K q^T: col = query row, k = hd 32s + 8gq..) and
+  // their sums of squares: the first loads of the kernel
+  f32x4 x[NS][2];
+  float ss = 0.f;
   {
     const int qr = qok ? qrow : 0;
     const int hl = qr / a.gamma, g = qr - hl * a.gamma, head = kvh * rep + hl;
     const int m = row * a.gamma + g;
     const float* qp = a.q + (((int64_t)row * a.nKv + kvh) * a.nq + qr) * HD;
-    f32x4 x[NS][2];
 #pragma unroll
     for (int s = 0; s < NS; ++s) {
       x[s][0] = *(const f32x4*)(qp + 32 * s + 8 * gq);
       x[s][1] = *(const f32x4*)(qp + 32 * s + 8 * gq + 4);
     }
-    float ss = 0.f;
 #pragma unroll
     for (int p = 0; p < HJ; ++p) ss += a.ssq[(int64_t)(head * HJ + p) * a.M + m];
-    const float r = qok ? 1.f / sqrtf(ss / HD + a.eps) : 0.f;
+  }
+  // RMS factor of the block key this thread stages (k_norm / weightless v
+  // share it)
+  const int key = tid & (ATT_KEYS - 1);
+  float sk = 0.f;
+  if (blk) {
+    const int kq = min(key, a.gamma - 1);
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      float t[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        t[e] = x[s][0][e] * r;
-        t[4 + e] = x[s][1][e] * r;
-      }
-      split8(t, qh[s], ql[s]);
-    }
+    for (int p = 0; p < HJ; ++p) sk += a.ssq[(int64_t)((a.nH + kvh) * HJ + p) * a.M + row * a.gamma + kq];
   }
 
+  bf16x8 qh[NS], ql[NS];
   f32x4 o[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
+  const float r = qok ? 1.f / sqrtf(ss / HD + a.eps) : 0.f;
 
-  const int64_t kvoff = (int64_t)kvh * len * HD;
-  const float* kbp = a.kb + ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
-  const float* vbp = a.vb + ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
-  const int key = tid & (ATT_KEYS - 1);  // the key this thread stages (all its items)
-
-  for (int jc = j0; jc < j1; jc += ATT_KEYS) {
-    const int nk = min(ATT_KEYS, j1 - jc);
-    const int kc = jc + min(key, nk - 1);
-    if (KVB && !blk) {
-      const uint16_t* kp = (const uint16_t*)a.row[row].k + kvoff + (int64_t)kc * HD;
-      const uint16_t* vp = (const uint16_t*)a.row[row].v + kvoff + (int64_t)kc * HD;
-      u32x4 kk[IPT], vv[IPT];
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        const int c8 = (tid + NTH * i) / ATT_KEYS;
-        kk[i] = *(const u32x4*)(kp + 8 * c8);
-        vv[i] = *(const u32x4*)(vp + 8 * c8);
-      }
-      __syncthreads();
-      const bool ok = key < nk;
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        const int c8 = (tid + NTH * i) / ATT_KEYS;
-        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
-        const u32x4 vw = ok ? vv[i] : z;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(8 * c8 + e) * VSTR + key] = half_of(vw, e);
-      }
-      __syncthreads();
-      attn_pass<HD, true>(Ks, Vt, qh, ql, o, m_run, l_part, nk);
-    } else {
-      const float* kp = blk ? kbp + (int64_t)kc * HD : (const float*)a.row[row].k + kvoff + (int64_t)kc * HD;
-      const float* vp = blk ? vbp + (int64_t)kc * HD : (const float*)a.row[row].v + kvoff + (int64_t)kc * HD;
-      f32x4 kf[IPT][2], vf[IPT][2];
-#pragma unroll
-      for (int i = 0; i < IPT; ++i) {
-        const int c8 = (tid + NTH * i) / ATT_KEYS;
-        kf[i][0] = *(const f32x4*)(kp + 8 * c8);
-        kf[i][1] = *(const f32x4*)(kp + 8 * c8 + 4);
-        vf[i][0] = *(const f32x4*)(vp + 8 * c8);
-        vf[i][1] = *(const f32x4*)(vp + 8 * c8 + 4);
-      }
-      for (int pass = 0; pass < 2 && 16 * pass < nk; ++pass) {
-        __syncthreads();
-        if ((key >> 4) == pass) {
-          const int r = key & 15;
-          const bool ok = key < nk;
-          const float sc = ok ? (blk ? rk[key] : 1.f) : 0.f;
-#pragma unroll
-          for (int i = 0; i < IPT; ++i) {
-            const int c8 = (tid + NTH * i) / ATT_KEYS;
-            float kv8[8], vv8[8];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              kv8[e] = kf[i][0][e] * sc;
-              kv8[4 + e] = kf[i][1][e] * sc;
-              vv8[e] = vf[i][0][e] * sc;
-              vv8[4 + e] = vf[i][1][e] * sc;
-            }
-            bf16x8 kh, kl, vh, vl;
-            split8(kv8, kh, kl);
-            split8(vv8, vh, vl);
-            *(u32x4*)&Ks[r * KSTR + 8 * c8] = __builtin_bit_cast(u32x4, kh);
-            *(u32x4*)&Ks[(16 + r) * KSTR + 8 * c8] = __builtin_bit_cast(u32x4, kl);
-            // halves are taken from the whole-vector bit pattern (bit-casting a
-            // single __bf16 vector element is lowered to element 0 by this compiler)
-            const u32x4 vhw = __builtin_bit_cast(u32x4, vh), vlw = __builtin_bit_cast(u32x4, vl);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              Vt[(8 * c8 + e) * VSTR + r] = half_of(vhw, e);
-              Vt[(8 * c8 + e) * VSTR + 16 + r] = half_of(vlw, e);
-            }
-          }
-        }
-        __syncthreads();
-        attn_pass<HD, false>(Ks, Vt, qh, ql, o, m_run, l_part, min(16, nk - 16 * pass));
-      }
-    }
+  if (blk) {
+    const int64_t off = ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
+    attn_keys<HD, false>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), x, r, qh, ql, o, m_run,
+                         l_part, Ks, Vt);
+  } else {
+    const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
+    const char* kb = (const char*)a.row[row].k + kvoff;
+    const char* vb = (const char*)a.row[row].v + kvoff;
+    attn_keys<HD, KVB>(kb, vb, j0, j1, 1.f, x, r, qh, ql, o, m_run, l_part, Ks, Vt);
   }
 
   float l = l_part;

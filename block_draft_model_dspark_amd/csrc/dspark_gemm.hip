@@ -140,13 +140,10 @@ __device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const 
           s.w += v[i].w;
         }
     }
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-      s.x += __shfl_xor(s.x, o);
-      s.y += __shfl_xor(s.y, o);
-      s.z += __shfl_xor(s.z, o);
-      s.w += __shfl_xor(s.w, o);
-    }
+    s.x = row16_sum(s.x);
+    s.y = row16_sum(s.y);
+    s.z = row16_sum(s.z);
+    s.w = row16_sum(s.w);
     if (sub == 0) {
       const float r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
       const float t = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
@@ -198,9 +195,7 @@ __device__ __forceinline__ void epi_qk(const GemmArgs& g, const EpiArgs& e, cons
     const int m = mbase + r;
     const float ta = ya[u] * wa[u], tb = yb[u] * wb[u];
     const float oa = ta * cs[u].x - tb * cs[u].y, ob = tb * cs[u].x + ta * cs[u].y;
-    float ss = ya[u] * ya[u] + yb[u] * yb[u];
-#pragma unroll
-    for (int o = 16; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+    const float ss = half_sum(ya[u] * ya[u] + yb[u] * yb[u]);
     if (m < g.M) {
       const int arow = m / e.gamma, gs = m - arow * e.gamma;
       if (isq) {
@@ -234,28 +229,21 @@ __device__ __forceinline__ void epi_sums(const GemmArgs& g, const EpiArgs& e, co
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(mbase + t * 16 + 4 * gq + i, g.M - 1);
-      hv[t][i] = e.h ? e.h[(int64_t)m * g.N + n] : 0.f;
+      hv[t][i] = e.h ? e.h[(int64_t)m * e.ldy + n] : 0.f;
     }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mbase + t * 16 + 4 * gq + i;
-      if (m < g.M) e.Y[(int64_t)m * g.N + n] = acc[t][i];
+      if (m < g.M) e.Y[(int64_t)m * e.ldy + n] = acc[t][i];
     }
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float y = acc[t][i], wy = w1 * y, h = hv[t][i];
-      float s0 = y * y, s1 = h * wy, s2 = wy * wy, s3 = h * h;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        s0 += __shfl_xor(s0, o);
-        s1 += __shfl_xor(s1, o);
-        s2 += __shfl_xor(s2, o);
-        s3 += __shfl_xor(s3, o);
-      }
+      const float s0 = row16_sum(y * y), s1 = row16_sum(h * wy), s2 = row16_sum(wy * wy), s3 = row16_sum(h * h);
       if ((lane & 15) == 0) {
         float* p = red + ((wave * MT * 16) + t * 16 + 4 * gq + i) * 4;
         p[0] = s0;
@@ -301,12 +289,7 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
       if (e.cap > 0.f) z = e.cap * tanhf(z / e.cap);
       if (m < g.M) e.Y[(int64_t)m * V + n] = z;
       // per 16-column tile: max over the tile's columns of z - b and z + b
-      float lo = z - b, hi = z + b;
-#pragma unroll
-      for (int o = 8; o > 0; o >>= 1) {
-        lo = fmaxf(lo, __shfl_xor(lo, o));
-        hi = fmaxf(hi, __shfl_xor(hi, o));
-      }
+      const float lo = row16_max(z - b), hi = row16_max(z + b);
       if ((lane & 15) == 0) {
         tile[(r * 4 + wave) * 2] = lo;
         tile[(r * 4 + wave) * 2 + 1] = hi;
@@ -335,9 +318,17 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int hd = e.hd, HJ = hd >> 6, half = hd >> 1;
   const int layer = grp / e.nKv, kvh = grp - layer * e.nKv;
-  float kw[4];
+  // per-layer pointers read once (a kernel-argument array indexed at run time)
+  void* const kout = e.kout[layer];
+  void* const vout = e.vout[layer];
+  const void* const knw = e.kn_l[layer];
+  const bool bf = e.act_bf16 != 0;
+  uint32_t kraw[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) kw[j] = j < HJ ? ld_act_v(e.kn_l[layer], lane + 64 * j, e.act_bf16) : 0.f;
+  for (int j = 0; j < 4; ++j) {
+    const int d = min(lane + 64 * j, hd - 1);
+    kraw[j] = *(const uint32_t*)((const char*)knw + (bf ? (d >> 1) * 4 : d * 4));
+  }
   constexpr int RB = MT == 1 ? 4 : 8;  // rows per wave per batch
   for (int mb = m0 + wave * RB; mb < m1; mb += 4 * RB) {
     float y[RB][4];
@@ -347,10 +338,16 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
       const int m = min(mb + rr, m1 - 1);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int d = lane + 64 * j;
-        y[rr][j] = j < HJ ? ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d) : 0.f;
-        cs[rr][j] = j < HJ ? e.rt[(int64_t)m * half + (d < half ? d : d - half)] : make_float2(1.f, 0.f);
+        const int d = min(lane + 64 * j, hd - 1);
+        y[rr][j] = ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d);
+        cs[rr][j] = e.rt[(int64_t)m * half + (d < half ? d : d - half)];
       }
+    }
+    float kw[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int d = lane + 64 * j;
+      kw[j] = __uint_as_float(bf ? ((d & 1) ? (kraw[j] & 0xFFFF0000u) : (kraw[j] << 16)) : kraw[j]);
     }
 #pragma unroll
     for (int rr = 0; rr < RB; ++rr) {
@@ -359,23 +356,38 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
       const int b = m / e.L, i = m - b * e.L;
       float ss = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ss += y[rr][j] * y[rr][j];
+      for (int j = 0; j < 4; ++j)
+        if (j < HJ) ss += y[rr][j] * y[rr][j];
       const float r = 1.f / sqrtf(wave_sum(ss) / hd + e.eps);
-      float t[4];
+      float t[4], kv[4], vv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) t[j] = y[rr][j] * r * kw[j];
-      const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        if (j < HJ) {
-          const int d = lane + 64 * j;
-          float partner;
-          if (HJ >= 2) partner = t[(j + HJ / 2) % HJ];
-          else partner = __shfl_xor(t[0], 32);
-          const float c = cs[rr][j].x, s = cs[rr][j].y;
-          st_act(e.vout[layer], off + d, y[rr][j] * r, e.act_bf16);
-          st_act(e.kout[layer], off + d, d < half ? t[j] * c - partner * s : t[j] * c + partner * s, e.act_bf16);
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int d = lane + 64 * j;
+        float partner;
+        if (HJ >= 2) partner = t[(j + HJ / 2) % HJ];
+        else partner = __shfl_xor(t[0], 32);
+        const float c = cs[rr][j].x, sn = cs[rr][j].y;
+        vv[j] = y[rr][j] * r;
+        kv[j] = d < half ? t[j] * c - partner * sn : t[j] * c + partner * sn;
+      }
+      const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
+      if (bf) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < HJ) {
+            ((uint16_t*)vout)[off + lane + 64 * j] = f2bf(vv[j]);
+            ((uint16_t*)kout)[off + lane + 64 * j] = f2bf(kv[j]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (j < HJ) {
+            ((float*)vout)[off + lane + 64 * j] = vv[j];
+            ((float*)kout)[off + lane + 64 * j] = kv[j];
+          }
+      }
     }
   }
 }
@@ -385,10 +397,13 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
 // stage_load issues the loads of one batch of XB items per thread into
 // registers; stage_store converts them (norms for XM_NORM) and writes LDS.
 // ---------------------------------------------------------------------------
-// items per thread per batch: a 16-row tile with a 256-wide sub-slice stages
-// 2 items per thread, all in one batch
-template <int XM>
-constexpr int xbatch() { return 2; }
+// items per thread per batch, all of a sub-slice where the registers allow:
+// a 16-row tile (256 wide) has 2 per thread; a 64-row tile has 16 (bf16
+// rows, 512 wide) or 8 (f32 rows, 256 wide), normed rows take 2 batches of 4
+template <int XM, int MT>
+constexpr int xbatch() {
+  return MT == 1 ? 2 : (XM == XM_BF16 ? 16 : (XM == XM_F32 ? 8 : 4));
+}
 
 template <int XB>
 struct XRegs {
@@ -437,8 +452,8 @@ __device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u
 
 template <int XM, int MT>
 __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc, int klen, int base,
-                                           XRegs<xbatch<XM>()>& r) {
-  constexpr int XB = xbatch<XM>();
+                                           XRegs<xbatch<XM, MT>()>& r) {
+  constexpr int XB = xbatch<XM, MT>();
   const int tid = threadIdx.x;
   const int kq = klen >> 3;
   const int nitems = MT * 16 * kq;
@@ -454,10 +469,10 @@ __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc,
       const NormIn& n = g.nin;
       const float* ph = n.h ? n.h : n.y;
       const float* py = n.y ? n.y : n.h;
-      r.a[b][0] = *(const f32x4*)(ph + m * g.K + k);
-      r.a[b][1] = *(const f32x4*)(ph + m * g.K + k + 4);
-      r.y[b][0] = *(const f32x4*)(py + m * g.K + k);
-      r.y[b][1] = *(const f32x4*)(py + m * g.K + k + 4);
+      r.a[b][0] = *(const f32x4*)(ph + m * n.ld + k);
+      r.a[b][1] = *(const f32x4*)(ph + m * n.ld + k + 4);
+      r.y[b][0] = *(const f32x4*)(py + m * n.ld + k);
+      r.y[b][1] = *(const f32x4*)(py + m * n.ld + k + 4);
     } else if constexpr (XM == XM_BF16) {
       r.r16[b] = *(const u32x4*)((const uint16_t*)g.X + m * g.ldx + k);
     } else {
@@ -470,10 +485,10 @@ __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc,
 
 template <int WK, int XM, int MT>
 __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc, int klen, int base,
-                                            const XRegs<xbatch<XM>()>& r,
+                                            const XRegs<xbatch<XM, MT>()>& r,
                                             u32x4* xhi, u32x4* xlo, float* xsum, int nfull, int ngmax,
                                             const float2* rs, const float* wn, int kcmax, bool write_h) {
-  constexpr int XB = xbatch<XM>();
+  constexpr int XB = xbatch<XM, MT>();
   const int tid = threadIdx.x;
   const int kq = klen >> 3;
   const int nitems = MT * 16 * kq;
@@ -501,7 +516,7 @@ __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc
         v[q] = ok ? (n.w2 ? hn[q] * rr.y * w2 : hn[q]) : 0.f;
       }
       if (write_h && ok) {
-        float* dst = n.hout + (int64_t)m * g.K + kc + 8 * k8;
+        float* dst = n.hout + (int64_t)m * n.ld + kc + 8 * k8;
         *(f32x4*)dst = f32x4{hn[0], hn[1], hn[2], hn[3]};
         *(f32x4*)(dst + 4) = f32x4{hn[4], hn[5], hn[6], hn[7]};
       }
@@ -670,7 +685,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   // tile (double-buffered) and for fp32 weights, else 512
   constexpr int KCMAX = (MT == 1 || WK == WK_F32) ? 256 : 512;
   constexpr int SMAX = KCMAX / 32;
-  constexpr int XB = xbatch<XM>();
+  constexpr int XB = xbatch<XM, MT>();
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const int KC = NCH > 0 ? KCMAX : g.kc;  // unrolled variants run at KCMAX (the launcher checks)
   const int nfull = KC >> 5;
@@ -842,14 +857,13 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
 #pragma unroll
       for (int i = 0; i < 4; ++i) ep[(wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
     __syncthreads();
-    const int I = g.N >> 1;
     for (int idx = tid; idx < MT * 16 * 32; idx += 256) {
       const int r = idx >> 5, col = idx & 31;
       const int m = mbase + r;
       if (m >= g.M) continue;
       const float gt = ep[((col >> 4) * MT * 16 + r) * 16 + (col & 15)];
       const float up = ep[((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15)];
-      e.act[(int64_t)m * I + 32 * cb + col] = gelu_tanh(gt) * up;
+      e.act[(int64_t)m * e.ld_act + 32 * cb + col] = gelu_tanh(gt) * up;
     }
   } else if constexpr (EPI == EPI_QK) {
     epi_qk<MT>(g, e, acc, mbase, cb, ep);

@@ -30,6 +30,7 @@ struct NormIn {
   const void* w2;      // [K] act dtype, or null: x = hn
   const float* sc;     // [1] fp32 residual scale (a layer_scalar copy, or 1)
   float* hout;         // [M, K]: hn is written here by column block 0, or null
+  int64_t ld;          // row pitch (floats) of h, y and hout
   float eps;
   int act_bf16;
 };
@@ -82,8 +83,10 @@ struct EpiArgs {
   const void* kn_l[MAX_SEG];
   void* kout[MAX_SEG]; void* vout[MAX_SEG];  // [B, nKv, L, hd] act dtype
   // EPI_GELU
-  float* act;         // [M, N/2]
+  float* act;         // [M, N/2], row pitch ld_act
+  int64_t ld_act;
   // EPI_SUMS
+  int64_t ldy;        // row pitch (floats) of Y and h
   const float* h;     // residual [M, N] or null
   const void* w1;     // norm weight [N]
   float4* sums;       // [N/64, M]
@@ -108,7 +111,8 @@ struct EmbedArgs {
   int act_bf16, nL;
   const void* scal_src[MAX_LAYERS];  // per layer layer_scalar [1] act dtype
   float* scal;        // [nL + 1]: 1, then the layer scalars as fp32
-  float* h;           // [M, H] scaled embedding rows
+  float* h;           // [M, H] scaled embedding rows, row pitch ldh
+  int64_t ldh;
   float4* sums;       // [H/64, M] (0, 0, 0, sum h^2)
   float2* rt;         // [M, hd/2] RoPE table of the block positions
   RopeCfg rope;
@@ -145,7 +149,8 @@ struct MergeArgs {
   int split_off[MAX_ROWS + 1];
   int A, gamma, nKv, nq, nH, hd;
   const float* opart; const float* ml;
-  float* O;           // [A*gamma, nH*hd]
+  float* O;           // [A*gamma, nH*hd], row pitch ldo
+  int64_t ldo;
 };
 
 struct WalkArgs {

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
       v[q] = table_elem(a.E, a.Es, a.Eb, a.ekind, a.group, id, a.H, k0 + q) * a.scale;
       ss += v[q] * v[q];
     }
-    float* dst = a.h + (int64_t)m * a.H + k0;
+    float* dst = a.h + (int64_t)m * a.ldh + k0;
     *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
     *(f32x4*)(dst + 4) = f32x4{v[4], v[5], v[6], v[7]};
     // eight threads per 64-column block
@@ -79,49 +79,53 @@ __global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
 
 // ---------------------------------------------------------------------------
 // split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
-// grid A*nKv*nq, block hd (>= 64)
+// (running max over passes of MERGE_SB splits).  grid A*nKv*nq, block hd (>= 64)
 // ---------------------------------------------------------------------------
-constexpr int MERGE_SB = 64;  // splits weighted per pass
+constexpr int MERGE_SB = 32;  // splits per pass: their partial rows are loaded first, then (max, sum)
 
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  __shared__ float wsh[MERGE_SB], lsh[MERGE_SB];
-  __shared__ float red[8];
+  __shared__ float2 wl[MERGE_SB];
+  __shared__ float cmax;
   const int idx = blockIdx.x, tid = threadIdx.x;
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
   const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
-  float mx = -INFINITY;
-  for (int s = tid; s < ns; s += blockDim.x) mx = fmaxf(mx, ml[((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + j].x);
-  mx = block_max(mx, red);
-  float num = 0.f, den = 0.f;
+  float num = 0.f, den = 0.f, mrun = -INFINITY;
   for (int c0 = 0; c0 < ns; c0 += MERGE_SB) {
     const int cn = min(MERGE_SB, ns - c0);
+    float o[MERGE_SB];
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q) {
+      const int s = s0 + c0 + min(q, cn - 1);
+      o[q] = a.opart[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
+    }
+    const float2 v = ml[((int64_t)(s0 + c0 + min(tid, cn - 1)) * a.nKv + kvh) * a.nq + j];
+    if (tid < 64) {
+      const float mm = wave_max(tid < cn ? v.x : -INFINITY);
+      if (tid == 0) cmax = mm;
+    }
     __syncthreads();
+    const float mnew = fmaxf(mrun, cmax);
     if (tid < cn) {
-      const float2 v = ml[((int64_t)(s0 + c0 + tid) * a.nKv + kvh) * a.nq + j];
-      const float w = expf(v.x - mx);
-      wsh[tid] = w;
-      lsh[tid] = w * v.y;
+      const float w = expf(v.x - mnew);
+      wl[tid] = make_float2(w, w * v.y);
     }
+    const float rescale = expf(mrun - mnew);
+    num *= rescale;
+    den *= rescale;
+    mrun = mnew;
     __syncthreads();
-    for (int b0 = 0; b0 < cn; b0 += 16) {
-      float o[16];
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int s = s0 + c0 + min(b0 + q, cn - 1);
-        o[q] = a.opart[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
+    for (int q = 0; q < MERGE_SB; ++q)
+      if (q < cn) {
+        num += wl[q].x * o[q];
+        den += wl[q].y;
       }
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        if (b0 + q < cn) {
-          num += wsh[b0 + q] * o[q];
-          den += lsh[b0 + q];
-        }
-    }
+    __syncthreads();
   }
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
-  a.O[((int64_t)row * a.gamma + g) * (a.nH * a.hd) + h * a.hd + tid] = num / den;
+  a.O[((int64_t)row * a.gamma + g) * a.ldo + h * a.hd + tid] = num / den;
 }
 
 // markov_w1 / markov_w2 element (table_elem with the head's own storage)
@@ -145,12 +149,13 @@ __device__ __forceinline__ float head_elem(const void* w, const void* s, const v
 // the table in LDS.  If some step keeps more than WALK_CMAX entries or too
 // many chunks pass, the row takes the per-step path that scores every
 // surviving entry against the actual previous token.
-// grid A, block 256
+// grid A, block WALK_NT
 // ---------------------------------------------------------------------------
 constexpr int WALK_CMAX = 16;   // fast-path candidates per step
 constexpr int WALK_GMAX = 32;   // block size bound
 constexpr int WALK_FMAX = 512;  // fast-path flagged (step, chunk) pairs per row
 constexpr int WALK_TPT = 8;     // threads per scored (prev, candidate) pair
+constexpr int WALK_NT = 1024;   // threads per row
 
 // dot(markov_w2[v], e) for a row of `rank` entries
 __device__ __forceinline__ float w2_dot(const WalkArgs& a, int64_t v, const float* e) {
@@ -207,8 +212,8 @@ __device__ __forceinline__ float w1w2_dot_part(const WalkArgs& a, int64_t prev, 
 // the per-step path: every entry of a passing chunk is scored against the
 // actual previous token
 __device__ void walk_per_step(const WalkArgs& a, int row) {
-  __shared__ float redu[4];
-  __shared__ int redi[4];
+  __shared__ float redu[WALK_NT / 64];
+  __shared__ int redi[WALK_NT / 64];
   __shared__ float e[256];
   __shared__ int prev_s;
   const int tid = threadIdx.x, G = a.rows.gamma;
@@ -218,16 +223,16 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
     const int64_t m = (int64_t)row * G + k;
     const float2* lh = a.lohi + m * a.NC;
     float lm = -INFINITY;
-    for (int c = tid; c < a.NC; c += 256) lm = fmaxf(lm, lh[c].x);
+    for (int c = tid; c < a.NC; c += WALK_NT) lm = fmaxf(lm, lh[c].x);
     lm = block_max(lm, redu);
     const float thr = lm - 1e-4f * (1.f + fabsf(lm));
     const int prev = prev_s;
     if (a.rank > 0)
-      for (int j = tid; j < a.rank; j += 256) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+      for (int j = tid; j < a.rank; j += WALK_NT) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
     __syncthreads();
     float bu = -INFINITY;
     int bi = 0x7fffffff;
-    for (int c = tid; c < a.NC; c += 256) {
+    for (int c = tid; c < a.NC; c += WALK_NT) {
       if (!(lh[c].y >= thr)) continue;
       for (int v = c * WALK_CHUNK; v < min(c * WALK_CHUNK + WALK_CHUNK, a.V); ++v) {
         const float zv = a.z[m * a.V + v];
@@ -248,7 +253,7 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
+__global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
   __shared__ int cand[WALK_GMAX][WALK_CMAX];
   __shared__ int ncand[WALK_GMAX];
   __shared__ float thr[WALK_GMAX];
@@ -263,15 +268,16 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
     nflag = 0;
     slow = 0;
   }
-  // 1. per-step threshold max_c lo_c: TPS threads per step, 16 chunk loads in flight each
+  // 1. per-step threshold max_c lo_c: TPS threads per step, 16 chunk
+  //    statistics in flight each (kept for step 2 when one batch covers them)
   int TPS = 64;  // a power of two within one wave
-  while (TPS * G > 256) TPS >>= 1;
+  while (TPS * G > WALK_NT) TPS >>= 1;
   const int k = tid / TPS, sub = tid - k * TPS;
   const bool kok = k < G;
   const float2* lh = a.lohi + ((int64_t)row * G + min(k, G - 1)) * NC;
   float lm = -INFINITY;
+  float2 v[16];
   for (int c0 = 0; c0 < NC; c0 += TPS * 16) {
-    float2 v[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] = lh[min(c0 + sub + TPS * i, NC - 1)];
 #pragma unroll
@@ -284,9 +290,10 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
   __syncthreads();
   // 2. chunks whose best z + B reaches the threshold
   for (int c0 = 0; c0 < NC; c0 += TPS * 16) {
-    float2 v[16];
+    if (NC > TPS * 16) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = lh[min(c0 + sub + TPS * i, NC - 1)];
+      for (int i = 0; i < 16; ++i) v[i] = lh[min(c0 + sub + TPS * i, NC - 1)];
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int c = c0 + sub + TPS * i;
@@ -302,7 +309,7 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
   // 3. candidates: the entries of the passing chunks that reach the
   //    threshold; one wave per chunk, four chunks in flight per wave
   const int nfm = min(nf, WALK_FMAX);
-  for (int f0 = wave * 4; f0 < nfm; f0 += 16) {
+  for (int f0 = wave * 4; f0 < nfm; f0 += 4 * (WALK_NT / 64)) {
     float zz[4], bb[4];
     int kq[4], vq[4];
 #pragma unroll
@@ -346,7 +353,7 @@ __global__ __launch_bounds__(256) void k_walk(const WalkArgs a) {
   }
   __syncthreads();
   const int ntri = toff[G];
-  for (int t0 = 0; t0 < ntri; t0 += 256 / WALK_TPT) {
+  for (int t0 = 0; t0 < ntri; t0 += WALK_NT / WALK_TPT) {
     const int t = t0 + tid / WALK_TPT, ts = tid % WALK_TPT;
     const bool ok = t < ntri;
     int kk = 0, pi = 0, ci = 0, prev = 0, v = 0;
@@ -426,7 +433,7 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_walk, dim3(a.rows.A), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_walk, dim3(a.rows.A), dim3(WALK_NT), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_aux(const AuxArgs& a, hipStream_t st) {
