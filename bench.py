@@ -22,6 +22,35 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/sec (gamma=16) at 1 MI355X; % MFMA / HBM roofline per kernel"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+GEMM_SOURCES = ("block_draft_model_dspark_amd/csrc/dspark_gemm.hip",
+                "block_draft_model_dspark_amd/csrc/dspark_common.hpp",
+                "block_draft_model_dspark_amd/csrc/dspark_kernels.hpp")
+# HBM bytes the GEMM launches of one step move, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes over them, each scaled by what the same counter reads for a
+# plain copy of known size (--calibrate-copy-mib).  Valid only for the GEMM
+# sources it was taken on (their sha256): otherwise the traffic is unknown.
+GEMM_TRAFFIC = {"sources_sha256": None, "bytes_per_step": None}
+
+
+def sources_sha256():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def calibrate_copy(mib, reps):
+    """Plain device copies of a known size, for scaling byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "reps": reps}))
 
 
 def gemm_bytes(cfg, M_round, M_ctx):
@@ -79,6 +108,8 @@ def main():
     ap.add_argument("--profile-steps", type=int, default=50)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run plain copies of this many MiB (byte-counter calibration)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -91,6 +122,9 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        calibrate_copy(args.calibrate_copy_mib, 4)
+        return
     dsp.load_library()
     w = synth.WORKLOADS["full_bf16_a1"]
     cfg = w.model
@@ -102,7 +136,7 @@ def main():
     anchors = synth.anchors(w)
     k_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
     v_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
-    pws = torch.empty(dsp.project_workspace_bytes(model, dsp.INPUT_CONTEXT_HIDDEN, 1, L), dtype=torch.uint8,
+    pws = torch.zeros(dsp.project_workspace_bytes(model, dsp.INPUT_CONTEXT_HIDDEN, 1, L), dtype=torch.uint8,
                       device="cuda")
     call = dsp.DraftCall(model, [[k[0]] for k in k_out], [[v[0]] for v in v_out], [L], anchors, [L])
 
@@ -141,6 +175,12 @@ def main():
     kernels = {k: {"launches_per_step": v[0] / args.profile_steps, "us_per_step": 1e3 * v[1] / args.profile_steps}
                for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
     kern_sum_us = sum(v["us_per_step"] for v in kernels.values())
+    for k, v in kernels.items():
+        if k in roles:
+            v["algorithmic_GBs"] = round(roles[k][0] * roles[k][1] / (v["us_per_step"] * 1e3), 1)
+    traffic = None
+    if GEMM_TRAFFIC["sources_sha256"] == sources_sha256():
+        traffic = GEMM_TRAFFIC["bytes_per_step"]
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
@@ -153,7 +193,7 @@ def main():
                    "tokens_per_s": round(value * cfg.gamma, 1)},
         "roofline": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "bytes_per_step": g_bytes, "launches_per_step": g_launch,
                      "us_per_step": round(1e3 * g_ms, 2)},
         "kernels": kernels,

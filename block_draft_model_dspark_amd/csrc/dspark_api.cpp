@@ -119,11 +119,12 @@ struct GemmPlan {
 
 GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   GemmPlan p;
-  // row tiles per workgroup: 1 for M <= 16, else 4 (2 and 3 are not enabled)
-  p.mt = M <= 16 ? 1 : 4;
-  // sub-slice width: 256 for one 16-row tile (two sub-slices in flight) and
-  // for fp32 weights, else 512, halved while the staged tile exceeds 64 KB
-  int kc = (p.mt == 1 || wk == WK_F32) ? 256 : 512;
+  // one 16-row tile per workgroup whatever M: tall inputs (the context
+  // projection) get more workgroups, each on the pipelined 16-row main loop,
+  // which measured faster than 64-row tiles there
+  p.mt = 1;
+  // sub-slice width: 256 (two sub-slices in flight)
+  int kc = 256;
   while (kc > 128 && gemm_lds_bytes(wk, xmode, p.mt, kc) > 65536) kc /= 2;
   const int mblocks = ceil_div(M, 16 * p.mt);
   const int wgs = (N / 64) * mblocks;
@@ -230,7 +231,7 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
 
 // ---- projection workspace layout -----------------------------------------
 struct ProjLayout {
-  size_t P, Y, C, sums, rt, one, cnt, total;
+  size_t P, Y, C, sums, cnt, total;
   GemmPlan fc, kp;
   size_t cwords;
   int lay_per_gemm;
@@ -264,8 +265,6 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.Y = take((size_t)M * Nk * 4);
   p.C = feats ? take((size_t)M * H * 4) : 0;
   p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
-  p.rt = take((size_t)M * (hd / 2) * 8);
-  p.one = take(4);
   p.cnt = take(p.cwords * 4);
   p.total = off;
   return p;
@@ -489,18 +488,9 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
 
   char* ws = (char*)ws_dev;
   const int M = B * L, H = c.hidden_size, hd = c.global_head_dim, nKv = c.num_global_key_value_heads;
+  // reduction counters: zero before the first call on this workspace, left
+  // zero by every call
   unsigned* cnt = (unsigned*)(ws + p.cnt);
-  float2* rt = (float2*)(ws + p.rt);
-  PrepArgs pr{};
-  pr.cnt = cnt;
-  pr.ncnt = (int)p.cwords;
-  pr.rt = rt;
-  pr.one = (float*)(ws + p.one);
-  pr.B = B;
-  pr.L = L;
-  pr.rope = rope_of(m);
-  for (int b = 0; b < B; ++b) pr.pos0[b] = pos0_host[b];
-  HIPCHECK(timed("prep", stream, [&] { return launch_prep(pr, stream); }));
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
   NormIn nin{};
   if (feats) {
@@ -528,7 +518,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     nin.ld = H;
     nin.nparts = H / 64;
     nin.w1 = m->hidden_norm;
-    nin.sc = pr.one;
+    nin.sc = nullptr;  // residual scale 1
     nin.eps = (float)c.rms_norm_eps;
     nin.act_bf16 = act_bf16(m);
   }
@@ -555,8 +545,9 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     e.nH = c.num_attention_heads;
     e.nKv = nKv;
     e.hd = hd;
-    e.rt = rt;
     e.L = L;
+    e.rope = rope_of(m);
+    for (int b = 0; b < B; ++b) e.pos0[b] = pos0_host[b];
     for (int i = 0; i < nl; ++i) {
       e.kn_l[i] = m->L[l0 + i].kn;
       e.kout[i] = k_out_dev[l0 + i];

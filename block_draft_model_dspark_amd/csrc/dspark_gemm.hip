@@ -98,11 +98,13 @@ __device__ __forceinline__ int wave_col(int c, int w, int N, int hd) {
 // ---------------------------------------------------------------------------
 // input rows (XM_NORM): per-row factors (r1, r2) and sc from the statistics
 // ---------------------------------------------------------------------------
-// The first 16 rows' statistics (up to 128 parts) are loaded by
-// norm_issue before the weight loads are issued, so that they do not wait
-// behind the weights (a wave's loads complete in order); norm_finish reduces
-// them and handles any further rows or parts.
-constexpr int NV = 4;  // statistics parts per thread loaded ahead (16 threads per row)
+// The first 16 rows' statistics are loaded by norm_issue before the weight
+// loads are issued, so that they do not wait behind the weights (a wave's
+// loads complete in order).  Every thread issues the same fixed number of
+// loads (indices clamped, surplus parts masked when summing): a load under a
+// run-time condition would make the compiler wait for every load in flight.
+// norm_finish reduces them; further 16-row tiles (MT > 1) load theirs there.
+constexpr int NV = 8;  // parts per thread, 16 threads per row: K up to 16 * NV * 64 = 8192
 
 __device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4* v, float& sc) {
   const NormIn& n = g.nin;
@@ -110,7 +112,7 @@ __device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4*
   const int m = min(mbase + (tid >> 4), g.M - 1);
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = n.sums[(int64_t)min(sub + 16 * i, n.nparts - 1) * g.M + m];
-  sc = *n.sc;
+  sc = n.sc ? *n.sc : 1.f;
 }
 
 template <int MT>
@@ -118,36 +120,31 @@ __device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const 
   const NormIn& n = g.nin;
   const int tid = threadIdx.x, sub = tid & 15;
   const float inv_k = 1.f / (float)g.K;
-  for (int r0 = 0; r0 < MT * 16; r0 += 16) {
-    const int ml = r0 + (tid >> 4);
+#pragma unroll
+  for (int t = 0; t < MT; ++t) {
+    const int ml = 16 * t + (tid >> 4);
     const int m = min(mbase + ml, g.M - 1);
+    float4 v[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      v[i] = t == 0 ? v0[i] : n.sums[(int64_t)min(sub + 16 * i, n.nparts - 1) * g.M + m];
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int p0 = 0; p0 < n.nparts; p0 += 16 * NV) {
-      float4 v[NV];
-      if (r0 == 0 && p0 == 0) {
 #pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = v0[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < NV; ++i) v[i] = n.sums[(int64_t)min(p0 + sub + 16 * i, n.nparts - 1) * g.M + m];
+    for (int i = 0; i < NV; ++i)
+      if (sub + 16 * i < n.nparts) {
+        s.x += v[i].x;
+        s.y += v[i].y;
+        s.z += v[i].z;
+        s.w += v[i].w;
       }
-#pragma unroll
-      for (int i = 0; i < NV; ++i)
-        if (p0 + sub + 16 * i < n.nparts) {
-          s.x += v[i].x;
-          s.y += v[i].y;
-          s.z += v[i].z;
-          s.w += v[i].w;
-        }
-    }
     s.x = row16_sum(s.x);
     s.y = row16_sum(s.y);
     s.z = row16_sum(s.z);
     s.w = row16_sum(s.w);
     if (sub == 0) {
       const float r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
-      const float t = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
-      const float r2 = 1.f / sqrtf(t * inv_k + n.eps);
+      const float t2 = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
+      const float r2 = 1.f / sqrtf(t2 * inv_k + n.eps);
       rs[ml] = make_float2(r1, r2);
     }
   }
@@ -314,8 +311,11 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
 // rows is issued before the first use.
 template <int MT>
-__device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp,
+                                       const double* rinv, float2* rcs) {
+  static_assert(MT == 1, "the K/V epilogue is built for one 16-row tile");
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hd = e.hd, HJ = hd >> 6, half = hd >> 1;
   const int layer = grp / e.nKv, kvh = grp - layer * e.nKv;
   // per-layer pointers read once (a kernel-argument array indexed at run time)
@@ -323,71 +323,92 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
   void* const vout = e.vout[layer];
   const void* const knw = e.kn_l[layer];
   const bool bf = e.act_bf16 != 0;
+  // 1. loads: norm weights, then this wave's four rows of the group's y
   uint32_t kraw[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int d = min(lane + 64 * j, hd - 1);
     kraw[j] = *(const uint32_t*)((const char*)knw + (bf ? (d >> 1) * 4 : d * 4));
   }
-  constexpr int RB = MT == 1 ? 4 : 8;  // rows per wave per batch
-  for (int mb = m0 + wave * RB; mb < m1; mb += 4 * RB) {
-    float y[RB][4];
-    float2 cs[RB][4];
+  constexpr int RB = 4;
+  const int mb = m0 + wave * RB;
+  float y[RB][4];
 #pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int m = min(mb + rr, m1 - 1);
+  for (int rr = 0; rr < RB; ++rr) {
+    const int m = min(mb + rr, m1 - 1);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = min(lane + 64 * j, hd - 1);
-        y[rr][j] = ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d);
-        cs[rr][j] = e.rt[(int64_t)m * half + (d < half ? d : d - half)];
-      }
+    for (int j = 0; j < 4; ++j) {
+      const int d = min(lane + 64 * j, hd - 1);
+      y[rr][j] = ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d);
     }
-    float kw[4];
+  }
+  // 2. while they are in flight: (cos, sin) of the tile's row positions and
+  //    pairs.  The rows span batch rows b_first..b_last, whose starting
+  //    positions are read with uniform (scalar) loads.
+  const int b_first = m0 / e.L, b_last = (m1 - 1) / e.L;
+  for (int idx = tid; idx < 16 * half; idx += 256) {
+    const int r = idx / half, pr = idx - r * half;
+    const int m = min(m0 + r, m1 - 1);
+    const int b = m / e.L;
+    int p0 = 0;
+    for (int bb = b_first; bb <= b_last; ++bb) {
+      const int pv = e.pos0[bb];  // uniform index: a scalar load, taken unconditionally
+      p0 = b == bb ? pv : p0;
+    }
+    float c, sn;
+    rope_cs_hw((int64_t)p0 + (m - b * e.L), rinv[pr], c, sn);
+    rcs[idx] = make_float2(c, sn);
+  }
+  __syncthreads();
+  float kw[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int d = lane + 64 * j;
+    kw[j] = __uint_as_float(bf ? ((d & 1) ? (kraw[j] & 0xFFFF0000u) : (kraw[j] << 16)) : kraw[j]);
+  }
+  // 3. per row: RMS factor, V = y r, K = RoPE(y r k_norm)
+#pragma unroll
+  for (int rr = 0; rr < RB; ++rr) {
+    const int m = mb + rr;  // wave-uniform
+    if (m >= m1) break;
+    const int b = m / e.L, i = m - b * e.L;
+    float ss = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < HJ) ss += y[rr][j] * y[rr][j];
+    const float r = rsqrtf(wave_sum(ss) / hd + e.eps);
+    float t[4], kv[4], vv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = y[rr][j] * r * kw[j];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = lane + 64 * j;
-      kw[j] = __uint_as_float(bf ? ((d & 1) ? (kraw[j] & 0xFFFF0000u) : (kraw[j] << 16)) : kraw[j]);
+      float partner;
+      if (HJ >= 2) partner = t[(j + HJ / 2) % HJ];
+      else partner = __shfl_xor(t[0], 32);
+      const float2 cs = rcs[(m - m0) * half + (d < half ? d : d - half)];
+      vv[j] = y[rr][j] * r;
+      kv[j] = d < half ? t[j] * cs.x - partner * cs.y : t[j] * cs.x + partner * cs.y;
     }
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int m = mb + rr;
-      if (m >= m1) break;
-      const int b = m / e.L, i = m - b * e.L;
-      float ss = 0.f;
+    const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
+    if (bf) {
+      uint16_t* const vo = (uint16_t*)vout + off;
+      uint16_t* const ko = (uint16_t*)kout + off;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < HJ) ss += y[rr][j] * y[rr][j];
-      const float r = 1.f / sqrtf(wave_sum(ss) / hd + e.eps);
-      float t[4], kv[4], vv[4];
+        if (j < HJ) {
+          vo[lane + 64 * j] = f2bf(vv[j]);
+          ko[lane + 64 * j] = f2bf(kv[j]);
+        }
+    } else {
+      float* const vo = (float*)vout + off;
+      float* const ko = (float*)kout + off;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) t[j] = y[rr][j] * r * kw[j];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = lane + 64 * j;
-        float partner;
-        if (HJ >= 2) partner = t[(j + HJ / 2) % HJ];
-        else partner = __shfl_xor(t[0], 32);
-        const float c = cs[rr][j].x, sn = cs[rr][j].y;
-        vv[j] = y[rr][j] * r;
-        kv[j] = d < half ? t[j] * c - partner * sn : t[j] * c + partner * sn;
-      }
-      const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
-      if (bf) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (j < HJ) {
-            ((uint16_t*)vout)[off + lane + 64 * j] = f2bf(vv[j]);
-            ((uint16_t*)kout)[off + lane + 64 * j] = f2bf(kv[j]);
-          }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          if (j < HJ) {
-            ((float*)vout)[off + lane + 64 * j] = vv[j];
-            ((float*)kout)[off + lane + 64 * j] = kv[j];
-          }
-      }
+      for (int j = 0; j < 4; ++j)
+        if (j < HJ) {
+          vo[lane + 64 * j] = vv[j];
+          ko[lane + 64 * j] = kv[j];
+        }
     }
   }
 }
@@ -397,12 +418,12 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
 // stage_load issues the loads of one batch of XB items per thread into
 // registers; stage_store converts them (norms for XM_NORM) and writes LDS.
 // ---------------------------------------------------------------------------
-// items per thread per batch, all of a sub-slice where the registers allow:
-// a 16-row tile (256 wide) has 2 per thread; a 64-row tile has 16 (bf16
-// rows, 512 wide) or 8 (f32 rows, 256 wide), normed rows take 2 batches of 4
+// items per thread per batch, all of a 256-wide sub-slice where the
+// registers allow: a 16-row tile has 2 per thread, a 64-row tile 8 (bf16 or
+// f32 rows); normed 64-row tiles take batches of 4
 template <int XM, int MT>
 constexpr int xbatch() {
-  return MT == 1 ? 2 : (XM == XM_BF16 ? 16 : (XM == XM_F32 ? 8 : 4));
+  return MT == 1 ? 2 : (XM == XM_NORM ? 4 : 8);
 }
 
 template <int XB>
@@ -681,9 +702,15 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   __shared__ int last_flag;
   __shared__ float2 rs[MT * 16 + 1];
   __shared__ __align__(16) float wn[XM == XM_NORM ? 2 * KSMAX : 1];
+  // EPI_KV: 1 / wavelength of each RoPE pair (double), formed while the
+  // first loads are in flight, and the (cos, sin) table of the tile's rows
+  // built by whichever workgroup finishes a head group
+  __shared__ double rinv[EPI == EPI_KV ? 128 : 1];
+  __shared__ float2 rcs[EPI == EPI_KV ? MT * 16 * 128 : 1];
   // sub-slice width bound (the host plans kc <= KCMAX): 256 for one 16-row
-  // tile (double-buffered) and for fp32 weights, else 512
-  constexpr int KCMAX = (MT == 1 || WK == WK_F32) ? 256 : 512;
+  // tile, for the unrolled (double-buffered) variants and for fp32 weights,
+  // else 512
+  constexpr int KCMAX = (MT == 1 || NCH > 0 || WK == WK_F32) ? 256 : 512;
   constexpr int SMAX = KCMAX / 32;
   constexpr int XB = xbatch<XM, MT>();
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
@@ -730,9 +757,12 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   auto chunk_len = [&](int c) { return NCH > 0 ? KC : min(KC, kend - chunk_k(c)); };
   stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa);
   load_w<WK, SMAX>(g, si, wrow, chunk_k(0), chunk_len(0) >> 5, wa);
-  if (MT == 1 && (NCH > 1 || (NCH == 0 && nch > 1))) {
+  if (NCH > 1 || (MT == 1 && NCH == 0 && nch > 1)) {
     stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb);
     load_w<WK, SMAX>(g, si, wrow, chunk_k(1), chunk_len(1) >> 5, wb);
+  }
+  if constexpr (EPI == EPI_KV) {
+    if (tid < (e.hd >> 1)) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
   }
   if constexpr (XM == XM_NORM) {
     norm_finish<MT>(g, mbase, nv, sc_in, rs);
@@ -763,7 +793,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
     __syncthreads();
     mma_w<WK, XM, MT, SMAX>(acc, w, xhi, xlo, xsum, nfull, ngmax, klen >> 5);
   };
-  if constexpr (MT == 1 && NCH > 0) {
+  if constexpr (NCH > 0) {
 #pragma unroll
     for (int c = 0; c < NCH; c += 2) {
       run_chunk(c, xa, wa, 0);
@@ -884,7 +914,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
     const int ngroups = (g.N + gcols - 1) / gcols;
     const int members = (min(gcols, g.N - grp * gcols) + 63) / 64;
     if (!arrive_last(e.cnt + gridDim.z * ncb + blockIdx.z * ngroups + grp, members, &last_flag)) return;
-    epi_kv<MT>(g, e, mbase, min(g.M, mbase + MT * 16), grp);
+    epi_kv<MT>(g, e, mbase, min(g.M, mbase + MT * 16), grp, rinv, rcs);
   }
 }
 
@@ -917,13 +947,18 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
   if constexpr (built<XM, EPI>()) {
     const int mblocks = (a.M + MT * 16 - 1) / (MT * 16);
     const dim3 grid(a.N / 64, S, mblocks);
-    const size_t lds = gemm_lds_bytes(WK, XM, MT, a.kc);
-    // unrolled variants for bf16 weights and one 16-row tile when every
-    // slice is a whole number (1, 2, 4 or 8) of sub-slices
+    size_t lds = gemm_lds_bytes(WK, XM, MT, a.kc);
+    // unrolled variants (two sub-slices in flight, two LDS buffers) for bf16
+    // weights with one 16-row tile, or 64-row tiles of bf16 rows, when every
+    // slice is a whole number (1, 2, 4 or 8) of 256-wide sub-slices
+    constexpr bool unrolled = WK == WK_BF16 && (MT == 1 || XM == XM_BF16);
     int nch = 0;
-    if (WK == WK_BF16 && MT == 1 && a.kc == 256 && a.K % a.kslice == 0 && a.kslice % a.kc == 0)
-      nch = a.kslice / a.kc;
-    if constexpr (WK == WK_BF16 && MT == 1) {
+    if (unrolled && a.kc == 256 && a.K % a.kslice == 0 && a.kslice % a.kc == 0) nch = a.kslice / a.kc;
+    if (nch > 0) {
+      const size_t two = xbuf_bytes(WK, XM, MT, 256) * 2;
+      lds = two > lds ? two : lds;
+    }
+    if constexpr (unrolled) {
       switch (nch) {
         case 1: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 1>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
         case 2: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 2>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
@@ -953,7 +988,7 @@ static hipError_t launch_epi(const GemmArgs& a, const EpiArgs& e, int epi, int S
 
 template <int WK, int XM>
 static hipError_t launch_mt(const GemmArgs& a, const EpiArgs& e, int epi, int mt, int S, hipStream_t st) {
-  return mt == 1 ? launch_epi<WK, XM, 1>(a, e, epi, S, st) : launch_epi<WK, XM, 4>(a, e, epi, S, st);
+  return mt == 1 ? launch_epi<WK, XM, 1>(a, e, epi, S, st) : hipErrorInvalidValue;
 }
 
 template <int WK>

@@ -28,7 +28,7 @@ struct NormIn {
   int nparts;          // K / 64
   const void* w1;      // [K] act dtype (unused when y is null)
   const void* w2;      // [K] act dtype, or null: x = hn
-  const float* sc;     // [1] fp32 residual scale (a layer_scalar copy, or 1)
+  const float* sc;     // [1] fp32 residual scale (a layer_scalar copy), or null: 1
   float* hout;         // [M, K]: hn is written here by column block 0, or null
   int64_t ld;          // row pitch (floats) of h, y and hout
   float eps;
@@ -73,13 +73,15 @@ struct EpiArgs {
   int act_bf16;
   // EPI_QK / EPI_KV
   int nH, nKv, hd, gamma;
-  const float2* rt;   // [rows, hd/2] (cos, sin) of each row's position and pair
+  const float2* rt;   // EPI_QK: [rows, hd/2] (cos, sin) of each row's position and pair
   const void* qn; const void* kn;
   float* q;           // [A, nKv, nq, hd] RoPE(q_norm_w * y), nq = (nH/nKv)*gamma, row hl*gamma + g
   float* kb;          // [A, nKv, gamma, hd] RoPE(k_norm_w * y)
   float* vb;          // [A, nKv, gamma, hd] y
   float* ssq;         // [(nH+nKv) * hd/64, M] sum y^2 per head and 64-column part
   int L;              // EPI_KV: context rows per batch row
+  RopeCfg rope;       // EPI_KV: RoPE of position pos0[b] + i for row b * L + i
+  int pos0[MAX_ROWS];
   const void* kn_l[MAX_SEG];
   void* kout[MAX_SEG]; void* vout[MAX_SEG];  // [B, nKv, L, hd] act dtype
   // EPI_GELU
@@ -118,16 +120,6 @@ struct EmbedArgs {
   RopeCfg rope;
   unsigned* cnt; int ncnt;  // GEMM counters zeroed here
   RowTab rows;
-};
-
-// counters + RoPE table of the context projection
-struct PrepArgs {
-  unsigned* cnt; int ncnt;
-  float* one;         // [1] set to 1 (residual scale of the projection's input norm)
-  float2* rt;         // [B*L, hd/2]
-  int B, L;
-  RopeCfg rope;
-  int pos0[MAX_ROWS];
 };
 
 struct AttnRow {
@@ -174,7 +166,6 @@ hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, 
                        hipStream_t st);
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
 size_t gemm_counter_words(int M, int N, int mt, int group_cols);
-hipError_t launch_prep(const PrepArgs& a, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);

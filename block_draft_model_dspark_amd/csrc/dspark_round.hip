@@ -59,24 +59,6 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   }
 }
 
-// context projection set-up: zero the GEMM counters and fill the RoPE table
-// of positions pos0[b] + i.  grid any, block 256.
-__global__ __launch_bounds__(256) void k_prep(const PrepArgs a) {
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x, nth = (int64_t)gridDim.x * 256;
-  for (int64_t i = gid; i < a.ncnt; i += nth) a.cnt[i] = 0u;
-  if (gid == 0) a.one[0] = 1.f;
-  const int half = a.rope.hd >> 1;
-  const int64_t total = (int64_t)a.B * a.L * half;
-  for (int64_t i = gid; i < total; i += nth) {
-    const int64_t m = i / half;
-    const int d = (int)(i - m * half);
-    const int b = (int)(m / a.L), r = (int)(m - (int64_t)b * a.L);
-    float c, s;
-    rope_cs((int64_t)a.pos0[b] + r, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
-    a.rt[i] = make_float2(c, s);
-  }
-}
-
 // ---------------------------------------------------------------------------
 // split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
 // (running max over passes of MERGE_SB splits).  grid A*nKv*nq, block hd (>= 64)
@@ -419,13 +401,6 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st) {
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, a);
-  return hipGetLastError();
-}
-hipError_t launch_prep(const PrepArgs& a, hipStream_t st) {
-  const int64_t rope_work = (int64_t)a.B * a.L * (a.rope.hd >> 1);
-  const int64_t work = rope_work > a.ncnt ? rope_work : a.ncnt;
-  const int64_t blocks = (work + 255) / 256;
-  hipLaunchKernelGGL(k_prep, dim3(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : (int)blocks)), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
