@@ -1,7 +1,7 @@
 // Row-wise kernels of the draft round: scaled embedding (with the RoPE table
-// of the block positions), the split-softmax merge of the attention, the
-// Markov walk and its per-model bound data, and the set-up kernel of the
-// context projection.  All arithmetic is fp32 (RoPE angles in fp64).
+// of the block positions), the split-softmax merge of the attention, and the
+// Markov walk with its per-model bound data.  All arithmetic is fp32 (RoPE
+// angles in fp64).
 #include "dspark_kernels.hpp"
 #include "dspark_common.hpp"
 
