@@ -106,9 +106,9 @@ __device__ __forceinline__ int wave_col(int c, int w, int N, int hd) {
 // norm_finish reduces them; further 16-row tiles (MT > 1) load theirs there.
 constexpr int NV = 8;  // parts per thread, 16 threads per row: K up to 16 * NV * 64 = 8192
 
-__device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4* v, float& sc) {
+__device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4* v, float& sc, int vt) {
   const NormIn& n = g.nin;
-  const int tid = threadIdx.x, sub = tid & 15;
+  const int tid = vt, sub = tid & 15;
   const int m = min(mbase + (tid >> 4), g.M - 1);
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = n.sums[(int64_t)min(sub + 16 * i, n.nparts - 1) * g.M + m];
@@ -116,9 +116,10 @@ __device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4*
 }
 
 template <int MT>
-__device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const float4* v0, float sc, float2* rs) {
+__device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const float4* v0, float sc, float2* rs,
+                                            int vt) {
   const NormIn& n = g.nin;
-  const int tid = threadIdx.x, sub = tid & 15;
+  const int tid = vt, sub = tid & 15;
   const float inv_k = 1.f / (float)g.K;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -438,9 +439,9 @@ struct XRegs {
 // (wn[0..] = w1, wn[KSMAX..] = w2) instead of being loaded per item.
 // Raw words: w[0], w[1] = w1, w[2], w[3] = w2.
 constexpr int KSMAX = 2048;
-__device__ __forceinline__ void normw_load(const GemmArgs& g, int kc, int klen, u32x4* w) {
+__device__ __forceinline__ void normw_load(const GemmArgs& g, int kc, int klen, u32x4* w, int vt) {
   const NormIn& n = g.nin;
-  const int k8 = min((int)threadIdx.x, (klen >> 3) - 1);
+  const int k8 = min(vt, (klen >> 3) - 1);
   const bool bf = n.act_bf16 != 0;
   // unconditional loads from whichever vectors exist (at least one does)
   const void* p1 = n.y ? n.w1 : n.w2;
@@ -451,9 +452,10 @@ __device__ __forceinline__ void normw_load(const GemmArgs& g, int kc, int klen, 
   w[2] = b.a;
   w[3] = b.b;
 }
-__device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u32x4* w, float* wn, int kcmax) {
+__device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u32x4* w, float* wn, int kcmax,
+                                            int vt) {
   const NormIn& n = g.nin;
-  const int k8 = threadIdx.x;
+  const int k8 = vt;
   const bool bf = n.act_bf16 != 0;
   if (k8 < (klen >> 3)) {
     float v[8];
@@ -473,9 +475,9 @@ __device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u
 
 template <int XM, int MT>
 __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc, int klen, int base,
-                                           XRegs<xbatch<XM, MT>()>& r) {
+                                           XRegs<xbatch<XM, MT>()>& r, int vt) {
   constexpr int XB = xbatch<XM, MT>();
-  const int tid = threadIdx.x;
+  const int tid = vt;
   const int kq = klen >> 3;
   const int nitems = MT * 16 * kq;
 #pragma unroll
@@ -508,9 +510,9 @@ template <int WK, int XM, int MT>
 __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc, int klen, int base,
                                             const XRegs<xbatch<XM, MT>()>& r,
                                             u32x4* xhi, u32x4* xlo, float* xsum, int nfull, int ngmax,
-                                            const float2* rs, const float* wn, int kcmax, bool write_h) {
+                                            const float2* rs, const float* wn, int kcmax, bool write_h, int vt) {
   constexpr int XB = xbatch<XM, MT>();
-  const int tid = threadIdx.x;
+  const int tid = vt;
   const int kq = klen >> 3;
   const int nitems = MT * 16 * kq;
 #pragma unroll
@@ -696,11 +698,18 @@ __host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, in
 }
 
 // ---------------------------------------------------------------------------
-template <int WK, int XM, int MT, int EPI, int NCH>
-__global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e) {
+// NW = 8 (gate|up only, unrolled, no split-K): eight waves, two per SIMD.
+// Waves 4..7 run the same 64 columns over the second half of the K slice
+// as a second set of four (their own staging buffers and row factors, the
+// same barriers); the epilogue adds the two halves.  Two waves per SIMD hide
+// one another's staging and MFMA phases behind the weight stream without
+// the cross-workgroup reduction a split K would need.
+template <int WK, int XM, int MT, int EPI, int NCH, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArgs e) {
+  static_assert(NW == 4 || (NW == 8 && NCH > 0 && MT == 1 && EPI == EPI_GELU), "eight waves: gate|up, unrolled");
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
-  __shared__ float2 rs[MT * 16 + 1];
+  __shared__ float2 rs_all[NW / 4][MT * 16 + 1];
   __shared__ __align__(16) float wn[XM == XM_NORM ? 2 * KSMAX : 1];
   // EPI_KV: 1 / wavelength of each RoPE pair (double), formed while the
   // first loads are in flight, and the (cos, sin) table of the tile's rows
@@ -713,7 +722,10 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   constexpr int KCMAX = (MT == 1 || NCH > 0 || WK == WK_F32) ? 256 : 512;
   constexpr int SMAX = KCMAX / 32;
   constexpr int XB = xbatch<XM, MT>();
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
+  // position within the set of four waves, and which set (K half)
+  const int vt = tid & 255, wave = vt >> 6, half = NW == 8 ? tid >> 8 : 0;
+  float2* const rs = rs_all[half];
   const int KC = NCH > 0 ? KCMAX : g.kc;  // unrolled variants run at KCMAX (the launcher checks)
   const int nfull = KC >> 5;
   const int ngmax = KC >> 6;
@@ -736,6 +748,9 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   // NCH > 0: every slice is exactly NCH sub-slices of KC (fully unrolled,
   // so the loads of the next two sub-slices stay in flight with exact waits)
   const int nch = NCH > 0 ? NCH : (kend - kbeg + KC - 1) / KC;
+  // this set's part of the slice (NW = 8: NCH sub-slices of each half)
+  const int hbeg = kbeg + half * NCH * KC;
+  const int hlen = NW == 8 ? NCH * KC : kend - kbeg;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -748,25 +763,25 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   float sc_in = 1.f;
   u32x4 wr[4];
   if constexpr (XM == XM_NORM) {
-    norm_issue(g, mbase, nv, sc_in);
-    normw_load(g, kbeg, kend - kbeg, wr);
+    norm_issue(g, mbase, nv, sc_in, vt);
+    normw_load(g, hbeg, hlen, wr, vt);
   }
   XRegs<XB> xa, xb;
   WRegs<WK, SMAX> wa, wb;
-  auto chunk_k = [&](int c) { return kbeg + c * KC; };
+  auto chunk_k = [&](int c) { return hbeg + c * KC; };
   auto chunk_len = [&](int c) { return NCH > 0 ? KC : min(KC, kend - chunk_k(c)); };
-  stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa);
+  stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa, vt);
   load_w<WK, SMAX>(g, si, wrow, chunk_k(0), chunk_len(0) >> 5, wa);
   if (NCH > 1 || (MT == 1 && NCH == 0 && nch > 1)) {
-    stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb);
+    stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb, vt);
     load_w<WK, SMAX>(g, si, wrow, chunk_k(1), chunk_len(1) >> 5, wb);
   }
   if constexpr (EPI == EPI_KV) {
     if (tid < (e.hd >> 1)) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
   }
   if constexpr (XM == XM_NORM) {
-    norm_finish<MT>(g, mbase, nv, sc_in, rs);
-    normw_store(g, kend - kbeg, wr, wn, KSMAX);
+    norm_finish<MT>(g, mbase, nv, sc_in, rs, vt);
+    normw_store(g, hlen, wr, wn + (hbeg - kbeg), KSMAX, vt);
     __syncthreads();
   }
 
@@ -774,7 +789,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   //    order), then the MFMAs against the weight registers
   auto run_chunk = [&](int c, const XRegs<XB>& xr, const WRegs<WK, SMAX>& w, int buf) {
     const int kc = chunk_k(c), klen = chunk_len(c);
-    u32x4* xhi = (u32x4*)(smem + buf * xbuf);
+    u32x4* xhi = (u32x4*)(smem + (buf * (NW / 4) + half) * xbuf);
     u32x4* xlo = xhi + MT * nfull * 64;
     float* xsum = (float*)(xhi + (XM == XM_BF16 ? 1 : 2) * MT * nfull * 64);
     if constexpr (WK == WK_Q4) {
@@ -782,13 +797,13 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
       __syncthreads();
     }
     stage_store<WK, XM, MT>(g, mbase, kc, klen, 0, xr, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg), KSMAX,
-                            write_h);
+                            write_h, vt);
     const int nitems = MT * 16 * (klen >> 3);
     for (int base = 256 * XB; base < nitems; base += 256 * XB) {
       XRegs<XB> xt;
-      stage_load<XM, MT>(g, mbase, kc, klen, base, xt);
+      stage_load<XM, MT>(g, mbase, kc, klen, base, xt, vt);
       stage_store<WK, XM, MT>(g, mbase, kc, klen, base, xt, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg),
-                              KSMAX, write_h);
+                              KSMAX, write_h, vt);
     }
     __syncthreads();
     mma_w<WK, XM, MT, SMAX>(acc, w, xhi, xlo, xsum, nfull, ngmax, klen >> 5);
@@ -798,13 +813,13 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
     for (int c = 0; c < NCH; c += 2) {
       run_chunk(c, xa, wa, 0);
       if (c + 2 < NCH) {
-        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), KC, 0, xa);
+        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), KC, 0, xa, vt);
         load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 2), KC >> 5, wa);
       }
       if (c + 1 < NCH) {
         run_chunk(c + 1, xb, wb, 1);
         if (c + 3 < NCH) {
-          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), KC, 0, xb);
+          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), KC, 0, xb, vt);
           load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 3), KC >> 5, wb);
         }
       }
@@ -815,13 +830,13 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
     for (int c = 0; c < nch; c += 2) {
       run_chunk(c, xa, wa, 0);
       if (c + 2 < nch) {
-        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), chunk_len(c + 2), 0, xa);
+        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), chunk_len(c + 2), 0, xa, vt);
         load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 2), chunk_len(c + 2) >> 5, wa);
       }
       if (c + 1 < nch) {
         run_chunk(c + 1, xb, wb, 1);
         if (c + 3 < nch) {
-          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), chunk_len(c + 3), 0, xb);
+          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), chunk_len(c + 3), 0, xb, vt);
           load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 3), chunk_len(c + 3) >> 5, wb);
         }
       }
@@ -831,7 +846,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
     for (int c = 0; c < nch; ++c) {
       if (c > 0) {
         __syncthreads();
-        stage_load<XM, MT>(g, mbase, chunk_k(c), chunk_len(c), 0, xa);
+        stage_load<XM, MT>(g, mbase, chunk_k(c), chunk_len(c), 0, xa, vt);
         load_w<WK, SMAX>(g, si, wrow, chunk_k(c), chunk_len(c) >> 5, wa);
       }
       run_chunk(c, xa, wa, 0);
@@ -843,7 +858,7 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   const int S = gridDim.y;
   const int ncb = gridDim.x;
   const int n = n0w + (lane & 15);
-  if (S > 1) {
+  if (NW == 4 && S > 1) {
     float* out = g.P + (int64_t)blockIdx.y * g.M * g.N;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -882,17 +897,25 @@ __global__ __launch_bounds__(256) void k_gemm(const GemmArgs g, const EpiArgs e)
   if constexpr (EPI == EPI_GELU) {
     // deepspec.ts, #geluTanhMlp: act = gelu_tanh(gate x) * up x; waves 0,1
     // hold gate columns 32cb.., waves 2,3 the matching up columns
+    // (eight waves: one tile per K half, added here)
+    constexpr int TILE = 4 * MT * 16 * 16;
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ep[(wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
+      for (int i = 0; i < 4; ++i)
+        ep[half * TILE + (wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
     __syncthreads();
-    for (int idx = tid; idx < MT * 16 * 32; idx += 256) {
+    for (int idx = tid; idx < MT * 16 * 32; idx += 64 * NW) {
       const int r = idx >> 5, col = idx & 31;
       const int m = mbase + r;
       if (m >= g.M) continue;
-      const float gt = ep[((col >> 4) * MT * 16 + r) * 16 + (col & 15)];
-      const float up = ep[((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15)];
+      const int og = ((col >> 4) * MT * 16 + r) * 16 + (col & 15);
+      const int ou = ((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15);
+      float gt = ep[og], up = ep[ou];
+      if (NW == 8) {
+        gt += ep[TILE + og];
+        up += ep[TILE + ou];
+      }
       e.act[(int64_t)m * e.ld_act + 32 * cb + col] = gelu_tanh(gt) * up;
     }
   } else if constexpr (EPI == EPI_QK) {
@@ -957,6 +980,15 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
     if (nch > 0) {
       const size_t two = xbuf_bytes(WK, XM, MT, 256) * 2;
       lds = two > lds ? two : lds;
+    }
+    if constexpr (unrolled && EPI == EPI_GELU && MT == 1) {
+      // gate|up over a whole row (no split-K): eight waves, four sub-slices
+      // per K half, each half with its own two staging buffers
+      if (nch == 8 && S == 1) {
+        const size_t lds8 = xbuf_bytes(WK, XM, MT, 256) * 4;
+        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4, 8>), grid, dim3(512), lds8, st, a, e);
+        return hipGetLastError();
+      }
     }
     if constexpr (unrolled) {
       switch (nch) {
