@@ -5,19 +5,20 @@
 // mask, over [row a's context K/V ++ its own gamma block keys]; all query
 // heads of a KV group read that group's single K/V head.
 //
-// Layout: one workgroup per (row, key split, kv head, group of 4 x 16 query
-// rows); wave w owns 16 query rows of the group (row index hl*gamma + g).
-// A row's context keys are cut into splits of a.split keys and its block
-// keys form one more split.  Keys go through LDS in chunks of 32, all loads
-// of a chunk issued before the first LDS write: K rows as is, V transposed
-// (Vt[d][key]).  Scores are computed as S^T = K q^T so that each lane holds
-// one query column and the softmax max is a 2-step lane exchange; the output
-// is O^T = V^T P^T.  Query rows and probabilities are fp32 split into bf16
-// hi + lo (two MFMAs); the bf16 context cache is exact in one plane.  fp32
-// keys (the block's own keys, or an fp32 cache) go in 16-key passes as hi
-// and lo planes: the score adds K_lo q_hi, and V hi/lo planes sit in the two
-// k-halves of one MFMA against duplicated probabilities, so one MFMA sums
-// both.
+// Layout: one workgroup per (row, key split, kv head, 16 query rows) (query
+// row index hl*gamma + g).  A row's context keys are cut into splits of
+// a.split keys and its block keys form one more split.  The workgroup loads
+// its 16 query rows once (RMS factor applied, split into bf16 hi + lo) into
+// LDS; keys go through LDS in chunks of 32, all loads of a chunk issued
+// before the first LDS write: K rows as is, V transposed (Vt[d][key]).  Every
+// wave forms the scores S^T = K q^T of the chunk (each lane holds one query
+// column; the softmax max is a 2-step lane exchange) and the output for its
+// quarter of the head dimension, O^T = V^T P^T.  Probabilities are fp32
+// split into hi + lo (two MFMAs); the bf16 context cache is exact in one
+// plane.  fp32 keys (the block's own keys, or an fp32 cache) go in 16-key
+// passes as hi and lo planes: the score adds K_lo q_hi, and V hi/lo planes
+// sit in the two k-halves of one MFMA against duplicated probabilities, so
+// one MFMA sums both.
 //
 // The q|k GEMM leaves q and the block's k, v without their per-head RMS
 // factor (a per-row scalar); it is formed here from the stored sums of
@@ -29,14 +30,15 @@
 
 namespace dsp {
 
-constexpr int ATT_QW = 4;  // waves (16 query rows each) per workgroup
+constexpr int ATT_NTH = 256;  // threads per workgroup (4 waves, one quarter of hd each)
 
 // one pass over the keys staged in LDS: ONE = 32 one-plane keys, else 16
-// keys as hi (rows 0..15) and lo (rows 16..31) planes
+// keys as hi (rows 0..15) and lo (rows 16..31) planes.  o: this wave's
+// HD/64 output tiles (head dims 16 t0 + 16 t ..).
 template <int HD, bool ONE>
 __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt, const bf16x8* qh, const bf16x8* ql,
-                                          f32x4* o, float& m_run, float& l_part, int nvalid) {
-  constexpr int NS = HD / 32, NT = HD / 16, KSTR = HD + 8, VSTR = 40;
+                                          f32x4* o, int t0, float& m_run, float& l_part, int nvalid) {
+  constexpr int NS = HD / 32, NTW = HD / 64, KSTR = HD + 8, VSTR = 40;
   const int lane = threadIdx.x & 63, gq = lane >> 4, ln = lane & 15;
   float sv[8];
   {
@@ -70,7 +72,7 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
   if (mnew > m_run) {
     const float sc = expf(m_run - mnew);
 #pragma unroll
-    for (int t = 0; t < NT; ++t) o[t] *= sc;
+    for (int t = 0; t < NTW; ++t) o[t] *= sc;
     l_part *= sc;
     m_run = mnew;
   }
@@ -87,10 +89,10 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
   }
   bf16x8 ph, pl;
   split8(pe, ph, pl);
-  // O^T += V^T P^T
+  // O^T += V^T P^T over this wave's head dims
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    const int hr = 16 * t + ln;
+  for (int t = 0; t < NTW; ++t) {
+    const int hr = 16 * (t0 + t) + ln;
     const u32x2 va = *(const u32x2*)&Vt[hr * VSTR + 4 * gq];
     const u32x2 vb = *(const u32x2*)&Vt[hr * VSTR + 16 + 4 * gq];
     const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{va[0], va[1], vb[0], vb[1]});
@@ -102,18 +104,17 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
 __device__ __forceinline__ uint16_t half_of(const u32x4& w, int e) { return (uint16_t)(w[e >> 1] >> (16 * (e & 1))); }
 
 // The keys of one split: every load of chunk c + 1 is issued before chunk c's
-// MFMAs, and chunk 0's before the query rows are converted (a wave's loads
-// complete in order, so the query loads go first).  ONE: bf16 context keys,
-// 32 per pass in one plane; else fp32 keys (the block's own, scaled by their
-// RMS factor: rkey for this thread's key, or an fp32 cache: 1) in two 16-key
-// passes of hi / lo planes.
-template <int HD, bool ONE>
+// MFMAs, and chunk 0's before the query operand is formed (prep fills qh,
+// ql; a wave's loads complete in order, so the query loads went first).
+// ONE: bf16 context keys, 32 per pass in one plane; else fp32 keys (the
+// block's own, scaled by their RMS factor: rkey for this thread's key, or an
+// fp32 cache: 1) in two 16-key passes of hi / lo planes.
+template <int HD, bool ONE, class Prep>
 __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, int j0, int j1, float rkey,
-                                          const f32x4 (*x)[2], float r, bf16x8* qh, bf16x8* ql, f32x4* o,
+                                          Prep&& prep, const bf16x8* qh, const bf16x8* ql, f32x4* o, int t0,
                                           float& m_run, float& l_part, uint16_t* Ks, uint16_t* Vt) {
-  constexpr int NS = HD / 32, KSTR = HD + 8, VSTR = 40;
-  constexpr int NTH = 64 * ATT_QW;
-  constexpr int IPT = ATT_KEYS * (HD / 8) / NTH;  // staging items (key, 8 dims) per thread
+  constexpr int KSTR = HD + 8, VSTR = 40;
+  constexpr int IPT = ATT_KEYS * (HD / 8) / ATT_NTH;  // staging items (key, 8 dims) per thread
   const int tid = threadIdx.x;
   const int key = tid & (ATT_KEYS - 1);  // the key this thread stages (all its items)
   u32x4 kk[ONE ? IPT : 1], vv[ONE ? IPT : 1];
@@ -122,7 +123,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
     const int kc = jc + min(key, j1 - jc - 1);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int c8 = (tid + NTH * i) / ATT_KEYS;
+      const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
       if constexpr (ONE) {
         kk[i] = *(const u32x4*)((const uint16_t*)kbase + (int64_t)kc * HD + 8 * c8);
         vv[i] = *(const u32x4*)((const uint16_t*)vbase + (int64_t)kc * HD + 8 * c8);
@@ -137,17 +138,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
     }
   };
   load(j0);
-  // the query operand, now that the first keys are in flight
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    float t[8];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      t[e] = x[s][0][e] * r;
-      t[4 + e] = x[s][1][e] * r;
-    }
-    split8(t, qh[s], ql[s]);
-  }
+  prep();
   for (int jc = j0; jc < j1; jc += ATT_KEYS) {
     const int nk = min(ATT_KEYS, j1 - jc);
     const bool ok = key < nk;
@@ -155,7 +146,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
-        const int c8 = (tid + NTH * i) / ATT_KEYS;
+        const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
         const u32x4 vw = ok ? vv[i] : z;
@@ -164,7 +155,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
       }
       __syncthreads();
       if (jc + ATT_KEYS < j1) load(jc + ATT_KEYS);
-      attn_pass<HD, true>(Ks, Vt, qh, ql, o, m_run, l_part, nk);
+      attn_pass<HD, true>(Ks, Vt, qh, ql, o, t0, m_run, l_part, nk);
     } else {
       float kv8[IPT][8], vv8[IPT][8];
       const float sc = ok ? rkey : 0.f;
@@ -184,7 +175,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
           const int rr = key & 15;
 #pragma unroll
           for (int i = 0; i < IPT; ++i) {
-            const int c8 = (tid + NTH * i) / ATT_KEYS;
+            const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
             bf16x8 kh, kl, vh, vl;
             split8(kv8[i], kh, kl);
             split8(vv8[i], vh, vl);
@@ -201,19 +192,19 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
           }
         }
         __syncthreads();
-        attn_pass<HD, false>(Ks, Vt, qh, ql, o, m_run, l_part, min(16, nk - 16 * pass));
+        attn_pass<HD, false>(Ks, Vt, qh, ql, o, t0, m_run, l_part, min(16, nk - 16 * pass));
       }
     }
   }
 }
 
 template <int HD, bool KVB>
-__global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
-  constexpr int NS = HD / 32, NT = HD / 16, HJ = HD / 64;
-  constexpr int NTH = 64 * ATT_QW;
-  static_assert(ATT_KEYS * (HD / 8) / NTH >= 1 && NTH % ATT_KEYS == 0, "staging layout");
+__global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
+  constexpr int NS = HD / 32, NTW = HD / 64, HJ = HD / 64;
+  static_assert(ATT_KEYS * (HD / 8) / ATT_NTH >= 1 && ATT_NTH % ATT_KEYS == 0, "staging layout");
   __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
   __shared__ __align__(16) uint16_t Vt[HD * 40];
+  __shared__ __align__(16) u32x4 qop[2][NS][64];  // q hi / lo in B-operand order
 
   const int sg = blockIdx.x, kvh = blockIdx.y;
   int row = 0;
@@ -223,26 +214,27 @@ __global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
   const int len = a.len[row];
   const int j0 = blk ? 0 : sp * a.split, j1 = blk ? a.gamma : min(len, j0 + a.split);
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
-  const int qrow = (blockIdx.z * ATT_QW + wave) * 16 + ln;
-  const bool qok = qrow < a.nq;
   const int rep = a.nH / a.nKv;
+  const int q0 = blockIdx.z * 16;  // first query row of the workgroup
 
-  // query rows (B of S^T = K q^T: col = query row, k = hd 32s + 8gq..) and
-  // their sums of squares: the first loads of the kernel
-  f32x4 x[NS][2];
-  float ss = 0.f;
-  {
-    const int qr = qok ? qrow : 0;
+  // 1. the workgroup's 16 query rows, as items (query, 8 dims): their loads
+  //    and the rows' sums of squares first, then the first keys' loads
+  constexpr int QC8 = HD / 8, QIT = (16 * QC8 + ATT_NTH - 1) / ATT_NTH;  // items per thread
+  f32x4 qv[QIT][2];
+  float qss[QIT];
+#pragma unroll
+  for (int k = 0; k < QIT; ++k) {
+    const int it = min(tid + ATT_NTH * k, 16 * QC8 - 1);
+    const int qi = it / QC8, c8 = it - qi * QC8;
+    const int qr = min(q0 + qi, a.nq - 1);
     const int hl = qr / a.gamma, g = qr - hl * a.gamma, head = kvh * rep + hl;
-    const int m = row * a.gamma + g;
-    const float* qp = a.q + (((int64_t)row * a.nKv + kvh) * a.nq + qr) * HD;
+    const float* qp = a.q + (((int64_t)row * a.nKv + kvh) * a.nq + qr) * HD + 8 * c8;
+    qv[k][0] = *(const f32x4*)qp;
+    qv[k][1] = *(const f32x4*)(qp + 4);
+    float ss = 0.f;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      x[s][0] = *(const f32x4*)(qp + 32 * s + 8 * gq);
-      x[s][1] = *(const f32x4*)(qp + 32 * s + 8 * gq + 4);
-    }
-#pragma unroll
-    for (int p = 0; p < HJ; ++p) ss += a.ssq[(int64_t)(head * HJ + p) * a.M + m];
+    for (int p = 0; p < HJ; ++p) ss += a.ssq[(int64_t)(head * HJ + p) * a.M + row * a.gamma + g];
+    qss[k] = ss;
   }
   // RMS factor of the block key this thread stages (k_norm / weightless v
   // share it)
@@ -253,33 +245,63 @@ __global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
 #pragma unroll
     for (int p = 0; p < HJ; ++p) sk += a.ssq[(int64_t)((a.nH + kvh) * HJ + p) * a.M + row * a.gamma + kq];
   }
-
+  // q hi / lo into LDS: element (query qi, dim d) is B-operand lane
+  // qi + 16 ((d mod 32) / 8), word d mod 8, of k-step d / 32; then every
+  // wave takes the whole operand
   bf16x8 qh[NS], ql[NS];
-  f32x4 o[NT];
+  auto prep = [&]() {
 #pragma unroll
-  for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < QIT; ++k) {
+      const int it = tid + ATT_NTH * k;
+      if (it < 16 * QC8) {
+        const int qi = it / QC8, c8 = it - qi * QC8, d = 8 * c8;
+        const float r = q0 + qi < a.nq ? 1.f / sqrtf(qss[k] / HD + a.eps) : 0.f;
+        float t[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t[e] = qv[k][0][e] * r;
+          t[4 + e] = qv[k][1][e] * r;
+        }
+        bf16x8 h, l;
+        split8(t, h, l);
+        qop[0][d >> 5][qi + 16 * ((d & 31) >> 3)] = __builtin_bit_cast(u32x4, h);
+        qop[1][d >> 5][qi + 16 * ((d & 31) >> 3)] = __builtin_bit_cast(u32x4, l);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      qh[s] = __builtin_bit_cast(bf16x8, qop[0][s][lane]);
+      ql[s] = __builtin_bit_cast(bf16x8, qop[1][s][lane]);
+    }
+  };
+
+  f32x4 o[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_part = 0.f;
-  const float r = qok ? 1.f / sqrtf(ss / HD + a.eps) : 0.f;
+  const int t0 = wave * NTW;  // this wave's first 16-dim output tile
 
   if (blk) {
     const int64_t off = ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
-    attn_keys<HD, false>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), x, r, qh, ql, o, m_run,
-                         l_part, Ks, Vt);
+    attn_keys<HD, false>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), prep, qh, ql, o, t0,
+                         m_run, l_part, Ks, Vt);
   } else {
     const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
     const char* kb = (const char*)a.row[row].k + kvoff;
     const char* vb = (const char*)a.row[row].v + kvoff;
-    attn_keys<HD, KVB>(kb, vb, j0, j1, 1.f, x, r, qh, ql, o, m_run, l_part, Ks, Vt);
+    attn_keys<HD, KVB>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt);
   }
 
   float l = l_part;
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
-  if (qok) {
+  const int qrow = q0 + ln;
+  if (qrow < a.nq) {
     const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qrow;
 #pragma unroll
-    for (int t = 0; t < NT; ++t) *(f32x4*)&a.opart[base * HD + 16 * t + 4 * gq] = o[t];
-    if (gq == 0) {
+    for (int t = 0; t < NTW; ++t) *(f32x4*)&a.opart[base * HD + 16 * (t0 + t) + 4 * gq] = o[t];
+    if (wave == 0 && gq == 0) {
       a.ml[base * 2] = m_run;
       a.ml[base * 2 + 1] = l;
     }
@@ -287,8 +309,7 @@ __global__ __launch_bounds__(64 * ATT_QW) void k_attn(const AttnArgs a) {
 }
 
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st) {
-  const int groups = (a.nq + 16 * ATT_QW - 1) / (16 * ATT_QW);
-  dim3 grid(nsplit, a.nKv, groups), block(64 * ATT_QW);
+  dim3 grid(nsplit, a.nKv, (a.nq + 15) / 16), block(ATT_NTH);
 #define DSP_ATTN(H)                                                                            \
   if (kv_bf16) hipLaunchKernelGGL((k_attn<H, true>), grid, block, 0, st, a);                   \
   else hipLaunchKernelGGL((k_attn<H, false>), grid, block, 0, st, a);
