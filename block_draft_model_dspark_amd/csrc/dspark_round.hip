@@ -237,7 +237,9 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
 
 __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
   __shared__ int cand[WALK_GMAX][WALK_CMAX];
+  __shared__ float candz[WALK_GMAX][WALK_CMAX];  // the candidates' logits
   __shared__ int ncand[WALK_GMAX];
+  __shared__ int best[WALK_GMAX][WALK_CMAX];     // [k][prev index]: index of the step-k winner
   __shared__ float thr[WALK_GMAX];
   __shared__ float tab[WALK_GMAX][WALK_CMAX][WALK_CMAX];  // [k][prev index][candidate index]
   __shared__ int flag_kc[WALK_FMAX];                      // k << 24 | chunk
@@ -315,7 +317,9 @@ __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
       if (base + cnt > WALK_CMAX) {
         if (lane == 0) slow = 1;
       } else if (pass) {
-        cand[kq[q]][base + __popcll(bal & ((1ull << lane) - 1ull))] = vq[q];
+        const int ci = base + __popcll(bal & ((1ull << lane) - 1ull));
+        cand[kq[q]][ci] = vq[q];
+        candz[kq[q]][ci] = zz[q];
       }
     }
   }
@@ -350,30 +354,38 @@ __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
     float dot = (ok && a.rank > 0) ? w1w2_dot_part(a, prev, v, ts) : 0.f;
 #pragma unroll
     for (int o = WALK_TPT >> 1; o > 0; o >>= 1) dot += __shfl_xor(dot, o);
-    if (ok && ts == 0) tab[kk][pi][ci] = a.z[((int64_t)row * G + kk) * a.V + v] + dot;
+    if (ok && ts == 0) tab[kk][pi][ci] = candz[kk][ci] + dot;
   }
   __syncthreads();
-  // 5. the walk itself, from LDS
-  if (wave == 0) {
+  // 5. for every step and previous candidate, the winning candidate (all in
+  //    parallel: one thread per (k, prev index), ties to the lower id)
+  for (int t = tid; t < G * WALK_CMAX; t += WALK_NT) {
+    const int kk = t / WALK_CMAX, pi = t - kk * WALK_CMAX;
+    const int np = kk == 0 ? 1 : ncand[kk - 1], nc = ncand[kk];
+    int bi = 0;
+    if (pi < np && nc > 0) {
+      float bu = tab[kk][pi][0];
+      int bv = cand[kk][0];
+      for (int ci = 1; ci < nc; ++ci) {
+        const float u = tab[kk][pi][ci];
+        const int v = cand[kk][ci];
+        if (better(u, v, bu, bv)) {
+          bu = u;
+          bv = v;
+          bi = ci;
+        }
+      }
+    }
+    best[kk][pi] = nc > 0 ? bi : -1;
+  }
+  __syncthreads();
+  // 6. the walk itself: a chain of lookups best[k][prev index]
+  if (tid == 0) {
     int pi = 0;
     for (int kk = 0; kk < G; ++kk) {
-      const int nc = ncand[kk];
-      float u = -INFINITY;
-      int v = 0x7fffffff;
-      if (lane < nc) {
-        u = tab[kk][pi][lane];
-        v = cand[kk][lane];
-      }
-      int li = lane;
-      // argmax over (u, v) carrying the lane index of the winner
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ou = __shfl_xor(u, o);
-        const int ov = __shfl_xor(v, o), ol = __shfl_xor(li, o);
-        if (better(ou, ov, u, v)) { u = ou; v = ov; li = ol; }
-      }
-      const bool okv = v >= 0 && v < a.V;
-      if (lane == 0) a.tokens[(int64_t)row * G + kk] = okv ? v : -1;
-      pi = okv ? li : 0;
+      const int bi = best[kk][pi];
+      a.tokens[(int64_t)row * G + kk] = bi >= 0 ? cand[kk][bi] : -1;
+      pi = bi >= 0 ? bi : 0;
     }
   }
 }
