@@ -141,7 +141,7 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   p.kslice = kslice;
   p.kc = std::min(kc, kslice);
   p.xmode = xmode;
-  p.pbytes = p.S > 1 ? (size_t)p.S * M * N * 4 : 0;
+  p.pbytes = p.S > 1 ? (size_t)p.S * mblocks * 16 * p.mt * N * 4 : 0;  // whole 16-row tiles
   p.cwords = gemm_counter_words(M, N, p.mt, group_cols);
   return p;
 }
@@ -255,6 +255,13 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.kp = plan_gemm(c.weight_dtype, feats ? XM_NORM : xmode_in(m), M, Nk, H, hd);
   pbytes = std::max(pbytes, p.kp.pbytes);
   p.cwords = std::max(p.cwords, p.kp.cwords);
+  // a last, smaller group of layers is planned on its own (it may split K)
+  const int rem = c.num_hidden_layers % p.lay_per_gemm;
+  if (rem) {
+    const GemmPlan r = plan_gemm(c.weight_dtype, p.kp.xmode, M, rem * nKv * hd, H, hd);
+    pbytes = std::max(pbytes, r.pbytes);
+    p.cwords = std::max(p.cwords, r.cwords);
+  }
   size_t off = 0;
   auto take = [&](size_t bytes) {
     size_t o = off;

@@ -859,18 +859,20 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   const int ncb = gridDim.x;
   const int n = n0w + (lane & 15);
   if (NW == 4 && S > 1) {
-    float* out = g.P + (int64_t)blockIdx.y * g.M * g.N;
+    // partials in accumulator order, P[s][tile][t][i][thread] with tile =
+    // (row block, column block): every store and load instruction of a wave
+    // covers 256 contiguous bytes
+    const int64_t tiles = (int64_t)gridDim.z * ncb;
+    const int64_t tile = (int64_t)blockIdx.z * ncb + cb;
+    auto pidx = [&](int sl, int t, int i) { return (((sl * tiles + tile) * MT + t) * 4 + i) * 256 + tid; };
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mbase + t * 16 + 4 * gq + i;
-        if (m < g.M) st_coh(out + (int64_t)m * g.N + n, acc[t][i]);
-      }
+      for (int i = 0; i < 4; ++i) st_coh(g.P + pidx(blockIdx.y, t, i), acc[t][i]);
     if (!arrive_last(e.cnt + blockIdx.z * ncb + cb, S, &last_flag)) return;
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    constexpr int PB = MT == 1 ? 16 : 4;  // partial slices loaded per batch
+    constexpr int PB = MT == 1 ? 8 : 4;  // partial slices loaded per batch
     for (int s0 = 0; s0 < S; s0 += PB) {
       float part[PB][MT][4];
 #pragma unroll
@@ -878,10 +880,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
 #pragma unroll
         for (int t = 0; t < MT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = min(mbase + t * 16 + 4 * gq + i, g.M - 1);
-            part[q][t][i] = ld_coh(g.P + ((int64_t)min(s0 + q, S - 1) * g.M + m) * g.N + n);
-          }
+          for (int i = 0; i < 4; ++i) part[q][t][i] = ld_coh(g.P + pidx(min(s0 + q, S - 1), t, i));
 #pragma unroll
       for (int q = 0; q < PB; ++q)
         if (s0 + q < S)

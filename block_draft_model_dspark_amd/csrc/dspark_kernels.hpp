@@ -53,7 +53,7 @@ struct GemmArgs {
   int kc;             // K sub-slice staged per iteration
   int nseg;
   GemmSeg seg[MAX_SEG];
-  float* P;           // [S, M, N] split-K partials (S > 1)
+  float* P;           // split-K partials (S > 1): S x ceil(M/16) x (N/64) tiles of 16 x 64 fp32
   NormIn nin;
 };
 
