@@ -275,7 +275,9 @@ __device__ __forceinline__ void epi_sums(const GemmArgs& g, const EpiArgs& e, co
 template <int MT>
 __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb, int n,
                        float* tile) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+  // (position within a set of four waves: an eight-wave workgroup runs two
+  // column blocks, each set with its own tile)
+  const int tid = threadIdx.x & 255, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const int V = g.N;
   const float b = e.aux ? walk_bound(e.aux, n, V) : 0.f;
 #pragma unroll
@@ -475,7 +477,7 @@ __device__ __forceinline__ void normw_store(const GemmArgs& g, int klen, const u
 
 template <int XM, int MT>
 __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc, int klen, int base,
-                                           XRegs<xbatch<XM, MT>()>& r, int vt) {
+                                           XRegs<xbatch<XM, MT>()>& r, int vt, bool live = true) {
   constexpr int XB = xbatch<XM, MT>();
   const int tid = vt;
   const int kq = klen >> 3;
@@ -484,8 +486,10 @@ __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc,
   for (int b = 0; b < XB; ++b) {
     const int it = base + tid + 256 * b;
     const int ml = it / kq, k8 = it < nitems ? it - ml * kq : 0;
-    const int64_t m = min(mbase + ml, g.M - 1);
-    const int64_t k = kc + 8 * k8;
+    // !live: the same number of loads, all of one row piece (a set of waves
+    // that does not stage keeps its load count, so every wait stays exact)
+    const int64_t m = live ? min(mbase + ml, g.M - 1) : 0;
+    const int64_t k = live ? kc + 8 * k8 : 0;
     if constexpr (XM == XM_NORM) {
       // both loads always issued (from whichever of h, y exists) so the
       // number of loads in flight is fixed; stage_store ignores a missing one
@@ -698,15 +702,20 @@ __host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, in
 }
 
 // ---------------------------------------------------------------------------
-// NW = 8 (gate|up only, unrolled, no split-K): eight waves, two per SIMD.
-// Waves 4..7 run the same 64 columns over the second half of the K slice
-// as a second set of four (their own staging buffers and row factors, the
-// same barriers); the epilogue adds the two halves.  Two waves per SIMD hide
-// one another's staging and MFMA phases behind the weight stream without
-// the cross-workgroup reduction a split K would need.
+// NW = 8 (unrolled, no split-K): eight waves, two per SIMD, as two sets of
+// four with the same barriers.  gate|up: waves 4..7 run the same 64 columns
+// over the second half of the K slice (their own staging buffers and row
+// factors); the epilogue adds the two halves.  lm_head: waves 4..7 run the
+// next 64 columns over the same K slice and multiply the activations the
+// first set stages, so they are read once for 128 columns.  Two waves per
+// SIMD hide one another's staging and MFMA phases behind the weight stream
+// without the cross-workgroup reduction a split K would need.
 template <int WK, int XM, int MT, int EPI, int NCH, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArgs e) {
-  static_assert(NW == 4 || (NW == 8 && NCH > 0 && MT == 1 && EPI == EPI_GELU), "eight waves: gate|up, unrolled");
+  static_assert(NW == 4 || (NW == 8 && NCH > 0 && MT == 1 && (EPI == EPI_GELU || EPI == EPI_LM)),
+                "eight waves: gate|up or lm_head, unrolled");
+  constexpr bool KH = NW == 8 && EPI == EPI_GELU;   // sets split K
+  constexpr bool COL2 = NW == 8 && EPI == EPI_LM;   // sets split columns
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
   __shared__ float2 rs_all[NW / 4][MT * 16 + 1];
@@ -723,15 +732,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   constexpr int SMAX = KCMAX / 32;
   constexpr int XB = xbatch<XM, MT>();
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4;
-  // position within the set of four waves, and which set (K half)
+  // position within the set of four waves, and which set
   const int vt = tid & 255, wave = vt >> 6, half = NW == 8 ? tid >> 8 : 0;
+  const bool stager = !COL2 || half == 0;  // stages activations into LDS
   float2* const rs = rs_all[half];
   const int KC = NCH > 0 ? KCMAX : g.kc;  // unrolled variants run at KCMAX (the launcher checks)
   const int nfull = KC >> 5;
   const int ngmax = KC >> 6;
   const size_t xbuf = xbuf_bytes(WK, XM, MT, KC);
 
-  const int cb = blockIdx.x;
+  const int cb = COL2 ? 2 * blockIdx.x + half : blockIdx.x;
   // wave-uniform values in scalar registers, so that the weight segment is
   // read from the kernel arguments with scalar loads (a vector load of the
   // pointer would make the first weight load wait for every earlier load)
@@ -749,8 +759,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   // so the loads of the next two sub-slices stay in flight with exact waits)
   const int nch = NCH > 0 ? NCH : (kend - kbeg + KC - 1) / KC;
   // this set's part of the slice (NW = 8: NCH sub-slices of each half)
-  const int hbeg = kbeg + half * NCH * KC;
-  const int hlen = NW == 8 ? NCH * KC : kend - kbeg;
+  const int hbeg = KH ? kbeg + half * NCH * KC : kbeg;
+  const int hlen = KH ? NCH * KC : kend - kbeg;
 
   f32x4 acc[MT];
 #pragma unroll
@@ -770,10 +780,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   WRegs<WK, SMAX> wa, wb;
   auto chunk_k = [&](int c) { return hbeg + c * KC; };
   auto chunk_len = [&](int c) { return NCH > 0 ? KC : min(KC, kend - chunk_k(c)); };
-  stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa, vt);
+  stage_load<XM, MT>(g, mbase, chunk_k(0), chunk_len(0), 0, xa, vt, stager);
   load_w<WK, SMAX>(g, si, wrow, chunk_k(0), chunk_len(0) >> 5, wa);
   if (NCH > 1 || (MT == 1 && NCH == 0 && nch > 1)) {
-    stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb, vt);
+    stage_load<XM, MT>(g, mbase, chunk_k(1), chunk_len(1), 0, xb, vt, stager);
     load_w<WK, SMAX>(g, si, wrow, chunk_k(1), chunk_len(1) >> 5, wb);
   }
   if constexpr (EPI == EPI_KV) {
@@ -781,7 +791,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   }
   if constexpr (XM == XM_NORM) {
     norm_finish<MT>(g, mbase, nv, sc_in, rs, vt);
-    normw_store(g, hlen, wr, wn + (hbeg - kbeg), KSMAX, vt);
+    if (stager) normw_store(g, hlen, wr, wn + (hbeg - kbeg), KSMAX, vt);
     __syncthreads();
   }
 
@@ -789,21 +799,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   //    order), then the MFMAs against the weight registers
   auto run_chunk = [&](int c, const XRegs<XB>& xr, const WRegs<WK, SMAX>& w, int buf) {
     const int kc = chunk_k(c), klen = chunk_len(c);
-    u32x4* xhi = (u32x4*)(smem + (buf * (NW / 4) + half) * xbuf);
+    u32x4* xhi = (u32x4*)(smem + (KH ? buf * 2 + half : buf) * xbuf);
     u32x4* xlo = xhi + MT * nfull * 64;
     float* xsum = (float*)(xhi + (XM == XM_BF16 ? 1 : 2) * MT * nfull * 64);
     if constexpr (WK == WK_Q4) {
       for (int i = tid; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
       __syncthreads();
     }
-    stage_store<WK, XM, MT>(g, mbase, kc, klen, 0, xr, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg), KSMAX,
-                            write_h, vt);
+    if (stager)
+      stage_store<WK, XM, MT>(g, mbase, kc, klen, 0, xr, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg), KSMAX,
+                              write_h, vt);
     const int nitems = MT * 16 * (klen >> 3);
     for (int base = 256 * XB; base < nitems; base += 256 * XB) {
       XRegs<XB> xt;
-      stage_load<XM, MT>(g, mbase, kc, klen, base, xt, vt);
-      stage_store<WK, XM, MT>(g, mbase, kc, klen, base, xt, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg),
-                              KSMAX, write_h, vt);
+      stage_load<XM, MT>(g, mbase, kc, klen, base, xt, vt, stager);
+      if (stager)
+        stage_store<WK, XM, MT>(g, mbase, kc, klen, base, xt, xhi, xlo, xsum, nfull, ngmax, rs, wn + (kc - kbeg),
+                                KSMAX, write_h, vt);
     }
     __syncthreads();
     mma_w<WK, XM, MT, SMAX>(acc, w, xhi, xlo, xsum, nfull, ngmax, klen >> 5);
@@ -813,13 +825,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     for (int c = 0; c < NCH; c += 2) {
       run_chunk(c, xa, wa, 0);
       if (c + 2 < NCH) {
-        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), KC, 0, xa, vt);
+        stage_load<XM, MT>(g, mbase, chunk_k(c + 2), KC, 0, xa, vt, stager);
         load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 2), KC >> 5, wa);
       }
       if (c + 1 < NCH) {
         run_chunk(c + 1, xb, wb, 1);
         if (c + 3 < NCH) {
-          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), KC, 0, xb, vt);
+          stage_load<XM, MT>(g, mbase, chunk_k(c + 3), KC, 0, xb, vt, stager);
           load_w<WK, SMAX>(g, si, wrow, chunk_k(c + 3), KC >> 5, wb);
         }
       }
@@ -922,7 +934,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   } else if constexpr (EPI == EPI_SUMS) {
     epi_sums<MT>(g, e, acc, mbase, cb, n, ep);
   } else if constexpr (EPI == EPI_LM) {
-    epi_lm<MT>(g, e, acc, mbase, cb, n, ep);
+    epi_lm<MT>(g, e, acc, mbase, cb, n, ep + half * 2 * 64 * MT);
   } else if constexpr (EPI == EPI_KV) {
 #pragma unroll
     for (int t = 0; t < MT; ++t)
@@ -979,6 +991,14 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
     if (nch > 0) {
       const size_t two = xbuf_bytes(WK, XM, MT, 256) * 2;
       lds = two > lds ? two : lds;
+    }
+    if constexpr (unrolled && EPI == EPI_LM && MT == 1) {
+      // lm_head over a whole row (no split-K): eight waves on two column
+      // blocks that share one staging of the activations
+      if (nch == 8 && S == 1 && (a.N / 64) % 2 == 0) {
+        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8, 8>), dim3(a.N / 128, S, grid.z), dim3(512), lds, st, a, e);
+        return hipGetLastError();
+      }
     }
     if constexpr (unrolled && EPI == EPI_GELU && MT == 1) {
       // gate|up over a whole row (no split-K): eight waves, four sub-slices
