@@ -36,9 +36,21 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
     float v[8];
     float ss = 0.f;
+    if (a.ekind == WK_BF16) {
+      // one 16-byte load of the eight bf16 values
+      const u32x4 w = *(const u32x4*)((const uint16_t*)a.E + id * a.H + k0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[2 * q] = __uint_as_float(w[q] << 16);
+        v[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = table_elem(a.E, a.Es, a.Eb, a.ekind, a.group, id, a.H, k0 + q);
+    }
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
-      v[q] = table_elem(a.E, a.Es, a.Eb, a.ekind, a.group, id, a.H, k0 + q) * a.scale;
+      v[q] *= a.scale;
       ss += v[q] * v[q];
     }
     float* dst = a.h + (int64_t)m * a.ldh + k0;
