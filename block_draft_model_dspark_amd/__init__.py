@@ -234,8 +234,7 @@ def project_context_kv(model: Model, x, pos0: Sequence[int], input_kind: int = I
                        k_out=None, v_out=None, workspace=None, stream=None):
     """deepspec.ts, #projectContextKVRows.  x [B, L, H] (or [B, L, fc_in] for
     target features), act dtype, on the GPU.  Returns per-layer (K, V) lists,
-    each [B, nKv, L, hd].  A caller-supplied workspace must be zero-filled
-    before its first use (the library leaves it reusable)."""
+    each [B, nKv, L, hd]."""
     import torch
     cfg = model.cfg
     B, L = int(x.shape[0]), int(x.shape[1])
@@ -245,7 +244,7 @@ def project_context_kv(model: Model, x, pos0: Sequence[int], input_kind: int = I
         v_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
     n = project_workspace_bytes(model, input_kind, B, L)
     if workspace is None or workspace.numel() < n:
-        workspace = torch.zeros(n, dtype=torch.uint8, device=x.device)
+        workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
     pos = (ctypes.c_int32 * B)(*[int(p) for p in pos0])
     kp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in k_out])
     vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_out])

@@ -495,9 +495,10 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
 
   char* ws = (char*)ws_dev;
   const int M = B * L, H = c.hidden_size, hd = c.global_head_dim, nKv = c.num_global_key_value_heads;
-  // reduction counters: zero before the first call on this workspace, left
-  // zero by every call
+  // reduction counters, zeroed here: the workspace may hold other data (a
+  // call of another input kind or shape lays it out differently)
   unsigned* cnt = (unsigned*)(ws + p.cnt);
+  HIPCHECK(timed("zero_counters", stream, [&] { return launch_zero(cnt, (int64_t)p.cwords, stream); }));
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
   NormIn nin{};
   if (feats) {

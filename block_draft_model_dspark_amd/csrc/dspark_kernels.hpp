@@ -168,6 +168,7 @@ size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
 size_t gemm_counter_words(int M, int N, int mt, int group_cols);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
+hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 hipError_t launch_aux(const AuxArgs& a, hipStream_t st);

@@ -71,6 +71,13 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   }
 }
 
+// zero n words (the reduction counters of a context projection: its
+// workspace may have held other data, e.g. a call of another shape).
+// grid any, block 256.
+__global__ __launch_bounds__(256) void k_zero(unsigned* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
 // ---------------------------------------------------------------------------
 // split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
 // (running max over passes of MERGE_SB splits).  grid A*nKv*nq, block hd (>= 64)
@@ -425,6 +432,11 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
 // ---------------------------------------------------------------------------
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st) {
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st) {
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(k_zero, dim3(blocks < 1 ? 1 : (blocks > 1024 ? 1024 : (unsigned)blocks)), dim3(256), 0, st, p, n);
   return hipGetLastError();
 }
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {

@@ -124,9 +124,7 @@ size_t dspark_project_workspace_bytes(const dspark_model* m, int input_kind, int
  *   pos0_host[B] first absolute position of each batch row (>= 0)
  *   k_out_dev[l], v_out_dev[l]  per layer, [B, nKv, L, hd] act dtype
  * Workspace: dspark_project_workspace_bytes(m, input_kind, B, L) bytes,
- * 256-byte aligned, zero-filled before its first use (it holds the GEMM
- * reduction counters, which every call leaves zero again, so a workspace
- * reused for later calls needs no clearing). */
+ * 256-byte aligned, any contents (the call clears what it needs). */
 dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, const void* x_dev, int B, int L,
                                         const int32_t* pos0_host, void* const* k_out_dev, void* const* v_out_dev,
                                         void* ws_dev, size_t ws_bytes, hipStream_t stream);

@@ -106,6 +106,31 @@ def test_context_kv_chunked_equals_single_pass(gpu_lib):
         assert torch.allclose(vc, v1[li].float(), rtol=1e-2, atol=1e-2)
 
 
+def test_projection_workspace_reused_across_calls(gpu_lib):
+    """One projection workspace reused across calls of both input kinds and
+    different shapes (whose layouts overlap each other's counters) gives the
+    bits of calls on fresh workspaces."""
+    import torch
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=1024, mask_token_id=1023)
+    w = synth.Workload("pf_reuse", cfg, rows=0, prefill_rows=100, prefill_batch=2)
+    case = Case(cfg)
+    xf = gpu_lib.act_tensor(synth.target_features(w))
+    xh = gpu_lib.act_tensor(synth.ctx_hidden(w, 0, 300))[None]
+    n = max(gpu_lib.project_workspace_bytes(case.gm, gpu_lib.INPUT_TARGET_FEATURES, 2, 100),
+            gpu_lib.project_workspace_bytes(case.gm, gpu_lib.INPUT_CONTEXT_HIDDEN, 1, 300))
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")  # not zero: the call clears what it needs
+    kf0, vf0 = gpu_lib.project_context_kv(case.gm, xf, [3, 500], input_kind=gpu_lib.INPUT_TARGET_FEATURES)
+    kh0, vh0 = gpu_lib.project_context_kv(case.gm, xh, [7])
+    for _ in range(3):
+        kf, vf = gpu_lib.project_context_kv(case.gm, xf, [3, 500], input_kind=gpu_lib.INPUT_TARGET_FEATURES,
+                                            workspace=ws)
+        kh, vh = gpu_lib.project_context_kv(case.gm, xh, [7], workspace=ws)
+        torch.cuda.synchronize()
+        for li in range(cfg.num_hidden_layers):
+            assert torch.equal(kf[li], kf0[li]) and torch.equal(vf[li], vf0[li]), li
+            assert torch.equal(kh[li], kh0[li]) and torch.equal(vh[li], vh0[li]), li
+
+
 # ------------------------------------------------------------------ draft rounds
 
 
