@@ -117,12 +117,9 @@ struct GemmPlan {
   size_t cwords;   // reduction counters
 };
 
-GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
+GemmPlan plan_gemm_mt(int wk, int xmode, int M, int N, int K, int group_cols, int mt) {
   GemmPlan p;
-  // one 16-row tile per workgroup whatever M: tall inputs (the context
-  // projection) get more workgroups, each on the pipelined 16-row main loop,
-  // which measured faster than 64-row tiles there
-  p.mt = 1;
+  p.mt = mt;
   // sub-slice width: 256 (two sub-slices in flight)
   int kc = 256;
   while (kc > 128 && gemm_lds_bytes(wk, xmode, p.mt, kc) > 65536) kc /= 2;
@@ -144,6 +141,20 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   p.pbytes = p.S > 1 ? (size_t)p.S * mblocks * 16 * p.mt * N * 4 : 0;  // whole 16-row tiles
   p.cwords = gemm_counter_words(M, N, p.mt, group_cols);
   return p;
+}
+
+// One 16-row tile per workgroup, except the context projection over tall
+// bf16 rows: 32-row tiles on eight-wave workgroups (two K halves) when the
+// slice is a whole even number (2, 4 or 8) of 256-wide sub-slices, which
+// reads each weight tile half as often as 16-row tiles.
+GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
+  if (group_cols > 0 && wk == WK_BF16 && xmode == XM_BF16 && M >= 32) {
+    const GemmPlan p2 = plan_gemm_mt(wk, xmode, M, N, K, group_cols, 2);
+    const int nch = p2.kslice / 256;
+    if (p2.kc == 256 && K % p2.kslice == 0 && p2.kslice % 256 == 0 && p2.S == 1 && (nch == 2 || nch == 4 || nch == 8))
+      return p2;
+  }
+  return plan_gemm_mt(wk, xmode, M, N, K, group_cols, 1);
 }
 
 hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st) {

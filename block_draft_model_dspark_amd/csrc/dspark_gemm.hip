@@ -313,10 +313,11 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
 // [m0, m1) of the row block: V = rms(k) (no weight, no RoPE);
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
 // rows is issued before the first use.
-template <int MT>
+template <int MT, int NT>
 __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp,
                                        const double* rinv, float2* rcs) {
-  static_assert(MT == 1, "the K/V epilogue is built for one 16-row tile");
+  // one wave per four rows of the tile
+  static_assert(MT * 16 == 4 * (NT / 64), "the K/V epilogue gives each wave four rows");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hd = e.hd, HJ = hd >> 6, half = hd >> 1;
@@ -349,7 +350,7 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
   //    pairs.  The rows span batch rows b_first..b_last, whose starting
   //    positions are read with uniform (scalar) loads.
   const int b_first = m0 / e.L, b_last = (m1 - 1) / e.L;
-  for (int idx = tid; idx < 16 * half; idx += 256) {
+  for (int idx = tid; idx < MT * 16 * half; idx += NT) {
     const int r = idx / half, pr = idx - r * half;
     const int m = min(m0 + r, m1 - 1);
     const int b = m / e.L;
@@ -422,11 +423,11 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
 // registers; stage_store converts them (norms for XM_NORM) and writes LDS.
 // ---------------------------------------------------------------------------
 // items per thread per batch, all of a 256-wide sub-slice where the
-// registers allow: a 16-row tile has 2 per thread, a 64-row tile 8 (bf16 or
-// f32 rows); normed 64-row tiles take batches of 4
+// registers allow: a 16-row tile has 2 per thread, a 32-row tile 4, a 64-row
+// tile 8 (bf16 or f32 rows); normed 64-row tiles take batches of 4
 template <int XM, int MT>
 constexpr int xbatch() {
-  return MT == 1 ? 2 : (XM == XM_NORM ? 4 : 8);
+  return MT == 1 ? 2 : (MT == 2 || XM == XM_NORM ? 4 : 8);
 }
 
 template <int XB>
@@ -712,9 +713,10 @@ __host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, in
 // without the cross-workgroup reduction a split K would need.
 template <int WK, int XM, int MT, int EPI, int NCH, int NW = 4>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArgs e) {
-  static_assert(NW == 4 || (NW == 8 && NCH > 0 && MT == 1 && (EPI == EPI_GELU || EPI == EPI_LM)),
-                "eight waves: gate|up or lm_head, unrolled");
-  constexpr bool KH = NW == 8 && EPI == EPI_GELU;   // sets split K
+  static_assert(NW == 4 || (NW == 8 && NCH > 0 &&
+                              ((MT == 1 && (EPI == EPI_GELU || EPI == EPI_LM)) || (MT == 2 && EPI == EPI_KV))),
+                "eight waves: gate|up, lm_head or the 32-row context projection, unrolled");
+  constexpr bool KH = NW == 8 && EPI != EPI_LM;     // sets split K
   constexpr bool COL2 = NW == 8 && EPI == EPI_LM;   // sets split columns
   extern __shared__ __align__(16) unsigned char smem[];
   __shared__ int last_flag;
@@ -936,19 +938,30 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   } else if constexpr (EPI == EPI_LM) {
     epi_lm<MT>(g, e, acc, mbase, cb, n, ep + half * 2 * 64 * MT);
   } else if constexpr (EPI == EPI_KV) {
+    if constexpr (KH) {
+      // add the second K half (waves 4..7) into the first through LDS
+      if (half == 1)
 #pragma unroll
-    for (int t = 0; t < MT; ++t)
+        for (int t = 0; t < MT; ++t) *(f32x4*)&ep[(t * 256 + vt) * 4] = acc[t];
+      __syncthreads();
+      if (half == 0)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mbase + t * 16 + 4 * gq + i;
-        if (m < g.M) st_coh(e.Y + (int64_t)m * g.N + n, acc[t][i]);
-      }
+        for (int t = 0; t < MT; ++t) acc[t] += *(const f32x4*)&ep[(t * 256 + vt) * 4];
+    }
+    if (half == 0)
+#pragma unroll
+      for (int t = 0; t < MT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mbase + t * 16 + 4 * gq + i;
+          if (m < g.M) st_coh(e.Y + (int64_t)m * g.N + n, acc[t][i]);
+        }
     const int gcols = e.group_cols;
     const int grp = (64 * cb) / gcols;
     const int ngroups = (g.N + gcols - 1) / gcols;
     const int members = (min(gcols, g.N - grp * gcols) + 63) / 64;
     if (!arrive_last(e.cnt + gridDim.z * ncb + blockIdx.z * ngroups + grp, members, &last_flag)) return;
-    epi_kv<MT>(g, e, mbase, min(g.M, mbase + MT * 16), grp, rinv, rcs);
+    epi_kv<MT, 64 * NW>(g, e, mbase, min(g.M, mbase + MT * 16), grp, rinv, rcs);
   }
 }
 
@@ -985,13 +998,27 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
     // unrolled variants (two sub-slices in flight, two LDS buffers) for bf16
     // weights with one 16-row tile, or 64-row tiles of bf16 rows, when every
     // slice is a whole number (1, 2, 4 or 8) of 256-wide sub-slices
-    constexpr bool unrolled = WK == WK_BF16 && (MT == 1 || XM == XM_BF16);
+    constexpr bool unrolled = WK == WK_BF16 && (MT <= 2 || XM == XM_BF16);
     int nch = 0;
     if (unrolled && a.kc == 256 && a.K % a.kslice == 0 && a.kslice % a.kc == 0) nch = a.kslice / a.kc;
     if (nch > 0) {
       const size_t two = xbuf_bytes(WK, XM, MT, 256) * 2;
       lds = two > lds ? two : lds;
     }
+    if constexpr (MT == 2) {
+      // 32-row tiles (context projection, bf16 rows): eight waves, the K
+      // slice in two halves of 1, 2 or 4 sub-slices
+      static_assert(WK == WK_BF16 && XM == XM_BF16 && EPI == EPI_KV, "32-row tiles: bf16 context projection");
+      const int n2 = nch / 2;
+      const size_t lds8 = xbuf_bytes(WK, XM, MT, 256) * 4;
+      if (nch % 2 == 0) switch (n2) {
+          case 1: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 1, 8>), grid, dim3(512), lds8, st, a, e); return hipGetLastError();
+          case 2: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 2, 8>), grid, dim3(512), lds8, st, a, e); return hipGetLastError();
+          case 4: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4, 8>), grid, dim3(512), lds8, st, a, e); return hipGetLastError();
+          default: break;
+        }
+      return hipErrorInvalidValue;
+    } else {
     if constexpr (unrolled && EPI == EPI_LM && MT == 1) {
       // lm_head over a whole row (no split-K): eight waves on two column
       // blocks that share one staging of the activations
@@ -1020,6 +1047,7 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
     }
     hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 0>), grid, dim3(256), lds, st, a, e);
     return hipGetLastError();
+    }
   } else {
     return hipErrorInvalidValue;
   }
@@ -1039,7 +1067,11 @@ static hipError_t launch_epi(const GemmArgs& a, const EpiArgs& e, int epi, int S
 
 template <int WK, int XM>
 static hipError_t launch_mt(const GemmArgs& a, const EpiArgs& e, int epi, int mt, int S, hipStream_t st) {
-  return mt == 1 ? launch_epi<WK, XM, 1>(a, e, epi, S, st) : hipErrorInvalidValue;
+  if (mt == 1) return launch_epi<WK, XM, 1>(a, e, epi, S, st);
+  if constexpr (WK == WK_BF16 && XM == XM_BF16) {
+    if (mt == 2 && epi == EPI_KV) return launch_one<WK, XM, 2, EPI_KV>(a, e, S, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int WK>
