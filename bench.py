@@ -29,8 +29,8 @@ GEMM_SOURCES = ("block_draft_model_dspark_amd/csrc/dspark_gemm.hip",
 # WRITE_SIZE passes over them, each scaled by what the same counter reads for a
 # plain copy of known size (--calibrate-copy-mib).  Valid only for the GEMM
 # sources it was taken on (their sha256): otherwise the traffic is unknown.
-GEMM_TRAFFIC = {"sources_sha256": "125ac0bab40480139bbb925c5a6e8f5ac679a10dec96549e136764a2d67c6bec",
-                "bytes_per_step": 715690256}
+GEMM_TRAFFIC = {"sources_sha256": "2a1ae6133c3326c40b121a987d93ed02936adaad14cc593b4a8c0cd56acd20ef",
+                "bytes_per_step": 713389523}
 
 
 def sources_sha256():
