@@ -1,15 +1,19 @@
 #!/usr/bin/env python3
 """Throughput of the DSpark draft round on one MI355X.
 
-One step = the whole hot path for one batch of the full-size workload:
-context K/V projection of the 512 context rows (4 layers of k_proj, k/v
-norms, RoPE) followed by one draft round (embedding, 4 backbone layers,
-lm_head with softcap, Markov walk) for A = 1 block of gamma = 16 tokens.
-Inputs and weights are seeded synthetic data resident in HBM before timing.
+Default step (--workload full_bf16_a1) = the whole hot path for one batch of
+the full-size workload: context K/V projection of the 512 context rows
+(4 layers of k_proj, k/v norms, RoPE) followed by one draft round (embedding,
+4 backbone layers, lm_head with softcap, Markov walk) for A = 1 block of
+gamma = 16 tokens.  --workload prefill_8192 times the K/V projection of 8192
+target-feature rows (fc, hidden_norm, 4-layer k_proj) in context rows/s;
+--workload rows_a32 times one round over 32 ragged rows with per-row context
+K/V.  Inputs and weights are seeded synthetic data resident in HBM before
+timing.
 
-Prints one JSON line: draft blocks/s, the roofline of the dominant kernel
-(the weight-streaming GEMM) measured with HIP events on the launch stream, and
-the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line: the throughput, the roofline of the dominant kernel
+measured with HIP events on the launch stream, and the CPU oracle timed on a
+bounded sample of the same workload.
 """
 import argparse
 import json
@@ -22,6 +26,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "draft blocks/sec (gamma=16) at 1 MI355X; % MFMA / HBM roofline per kernel"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 GEMM_SOURCES = ("block_draft_model_dspark_amd/csrc/dspark_gemm.hip",
                 "block_draft_model_dspark_amd/csrc/dspark_common.hpp",
                 "block_draft_model_dspark_amd/csrc/dspark_kernels.hpp")
@@ -70,9 +75,32 @@ def gemm_bytes(cfg, M_round, M_ctx):
     return roles  # role -> (bytes per launch, launches per step)
 
 
+def attn_bytes(cfg, lens):
+    """Algorithmic bytes of the attention launches of one round: every row's
+    context K and V once in the act dtype (bf16), per layer."""
+    return sum(lens) * cfg.nKv * cfg.hd * 2 * 2
+
+
+def gemm_flops_round(cfg, M_round):
+    """MFMA flops of the GEMMs of one draft round over M_round block rows."""
+    H, I, V, hd, nH, nKv, L = cfg.H, cfg.I, cfg.V, cfg.hd, cfg.nH, cfg.nKv, cfg.L
+    per_layer = (nH + nKv) * hd * H + H * nH * hd + 2 * I * H + H * I
+    return 2 * M_round * (L * per_layer + V * H)
+
+
+def oracle_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        t = max((p.get("num_threads", 0) for p in threadpool_info()), default=0)
+        if t:
+            return t
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, seconds):
     """The CPU oracle (as it stands) on the same step, bounded in time."""
-    import numpy as np
     import synth
     from oracle import dspark_oracle as O
     cfg = w.model
@@ -80,12 +108,6 @@ def cpu_baseline(w, seconds):
     L = w.fixed_ctx_len
     ctx = O.decode(synth.ctx_hidden(w, 0, L))[None]
     anchors = synth.anchors(w)
-    threads = None
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((p.get("num_threads", 0) for p in threadpool_info()), default=None)
-    except Exception:
-        pass
     n = 0
     t0 = time.perf_counter()
     while True:
@@ -95,10 +117,251 @@ def cpu_baseline(w, seconds):
         el = time.perf_counter() - t0
         if (el >= seconds and n >= 3) or n >= 1000:
             break
-    return {"value": n * w.rows / el, "unit": "blocks/s", "cores": threads or len(os.sched_getaffinity(0)),
+    return {"value": n * w.rows / el, "unit": "blocks/s", "cores": oracle_threads(),
             "kind": "oracle",
             "sample": f"{n} steps of the full-size workload (512-row context K/V projection + 1 draft round), "
                       f"{el:.1f} s, float64 NumPy"}
+
+
+def cpu_baseline_prefill(w, seconds):
+    """The oracle's fc + hidden_norm + 4-layer K/V projection on a bounded
+    sample of the 8192 rows (the step is row-wise), scaled to rows/s."""
+    import synth
+    from oracle import dspark_oracle as O
+    cfg = w.model
+    om = O.OracleModel(cfg, synth.make_model(cfg, with_fc=True))
+    x = O.decode(synth.target_features(w))
+    rows = 256
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        r0 = (n * rows) % w.prefill_rows
+        c = O.project_context(om, x[:, r0:r0 + rows])
+        O.project_context_kv(om, c, r0)
+        n += 1
+        el = time.perf_counter() - t0
+        if (el >= seconds and n >= 2) or n >= 1000:
+            break
+    return {"value": n * rows / el, "unit": "context rows/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"{n} chunks of {rows} of the 8192 target-feature rows through fc, hidden_norm and "
+                      f"the 4-layer K/V projection, {el:.1f} s, float64 NumPy"}
+
+
+def cpu_baseline_rows(w, lens, seconds):
+    """The oracle's draft round on the first rows of the batch (their own
+    direct K/V and lengths), one row at a time until the time bound."""
+    import synth
+    from oracle import dspark_oracle as O
+    cfg = w.model
+    om = O.OracleModel(cfg, synth.make_model(cfg, with_fc=False))
+    anchors = synth.anchors(w)
+    n = 0
+    el = 0.0
+    while n < w.rows:
+        kv = [(O.decode(d["k"]), O.decode(d["v"]))
+              for d in (synth.direct_kv(w, n, li, lens[n]) for li in range(cfg.L))]
+        t0 = time.perf_counter()
+        O.draft_rows(om, [kv], [anchors[n]], [lens[n]])
+        el += time.perf_counter() - t0
+        n += 1
+        if el >= seconds:
+            break
+    return {"value": n / el, "unit": "blocks/s", "cores": oracle_threads(), "kind": "oracle",
+            "sample": f"the first {n} of the 32 ragged rows (context lengths {lens[:n]}), one round each, "
+                      f"{el:.1f} s, float64 NumPy (K/V decoding excluded)"}
+
+
+def kernel_table(prof, nsteps):
+    return {k: {"launches_per_step": v[0] / nsteps, "us_per_step": 1e3 * v[1] / nsteps}
+            for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
+
+
+def run_timed(step, args):
+    import torch
+    import block_draft_model_dspark_amd as dsp
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    # per-kernel durations: HIP events around each library launch on its stream
+    nprof = max(1, args.profile_steps)
+    dsp.profile_enable(True)
+    for _ in range(nprof):
+        step()
+    torch.cuda.synchronize()
+    prof = dsp.profile_read()
+    dsp.profile_enable(False)
+    return ms, prof, nprof
+
+
+def bench_full(args, dsp, synth, torch):
+    """Context K/V projection of 512 rows + one draft round of one block."""
+    w = synth.WORKLOADS["full_bf16_a1"]
+    cfg = w.model
+    stored = synth.make_model(cfg, with_fc=False)
+    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
+    del stored
+    L, A = w.fixed_ctx_len, w.rows
+    x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
+    anchors = synth.anchors(w)
+    k_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
+    v_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
+    pws = torch.empty(dsp.project_workspace_bytes(model, dsp.INPUT_CONTEXT_HIDDEN, 1, L), dtype=torch.uint8,
+                      device="cuda")
+    call = dsp.DraftCall(model, [[k[0]] for k in k_out], [[v[0]] for v in v_out], [L], anchors, [L])
+
+    def step():
+        dsp.project_context_kv(model, x, [0], k_out=k_out, v_out=v_out, workspace=pws)
+        call()
+
+    ms, prof, nprof = run_timed(step, args)
+    ms_step = ms / args.steps
+    value = A * args.steps / (ms / 1e3)
+    roles = gemm_bytes(cfg, A * cfg.gamma, L)
+    g_bytes = sum(b * n for b, n in roles.values())  # per step
+    g_ms = sum(v[1] for k, v in prof.items() if k.startswith("gemm.")) / nprof
+    g_launch = sum(v[0] for k, v in prof.items() if k.startswith("gemm.")) / nprof
+    achieved = g_bytes / (g_ms / 1e3) / 1e9
+    kernels = kernel_table(prof, nprof)
+    kern_sum_us = sum(v["us_per_step"] for v in kernels.values())
+    for k, v in kernels.items():
+        if k in roles:
+            v["algorithmic_GBs"] = round(roles[k][0] * roles[k][1] / (v["us_per_step"] * 1e3), 1)
+    traffic = None
+    if GEMM_TRAFFIC["sources_sha256"] == sources_sha256():
+        traffic = GEMM_TRAFFIC["bytes_per_step"]
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "full_bf16_a1: 4 layers, H 2048, 8x256 q heads, 1 kv head, I 8192, V 32768, "
+                               "softcap 30, Markov rank 64; A=1 block, gamma 16, Lctx 512",
+                   "rows": A, "gamma": cfg.gamma, "ctx_len": L,
+                   "step": "context K/V projection of 512 rows + one draft round",
+                   "tokens_per_s": round(value * cfg.gamma, 1)},
+        "roofline": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_step": g_bytes, "launches_per_step": g_launch,
+                     "us_per_step": round(1e3 * g_ms, 2)},
+        "kernels": kernels,
+        "kernel_sum_us_per_step": round(kern_sum_us, 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    return out
+
+
+def bench_prefill(args, dsp, synth, torch):
+    """fc + hidden_norm + 4-layer K/V projection of 8192 target-feature rows."""
+    w = synth.WORKLOADS["prefill_8192"]
+    cfg = w.model
+    stored = synth.make_model(cfg, with_fc=True)
+    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
+    del stored
+    B, L = w.prefill_batch, w.prefill_rows
+    x = dsp.act_tensor(synth.target_features(w))
+    k_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
+    v_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
+    kind = dsp.INPUT_TARGET_FEATURES
+    pws = torch.empty(dsp.project_workspace_bytes(model, kind, B, L), dtype=torch.uint8, device="cuda")
+
+    def step():
+        dsp.project_context_kv(model, x, [0] * B, input_kind=kind, k_out=k_out, v_out=v_out, workspace=pws)
+
+    ms, prof, nprof = run_timed(step, args)
+    M = B * L
+    flops = {"gemm.fc": 2 * M * cfg.fc_in * cfg.H, "gemm.k_proj": 2 * M * cfg.H * cfg.L * cfg.nKv * cfg.hd}
+    kernels = kernel_table(prof, nprof)
+    for k, v in kernels.items():
+        if k in flops:
+            v["TFLOPs"] = round(flops[k] / (v["us_per_step"] * 1e-6) / 1e12, 1)
+    fc_us = kernels["gemm.fc"]["us_per_step"] / kernels["gemm.fc"]["launches_per_step"]
+    achieved = flops["gemm.fc"] / (fc_us * 1e-6) / 1e12
+    value = M * args.steps / (ms / 1e3)
+    out = {
+        "metric": "context rows/s (K/V projection prefill); % MFMA roofline", "value": round(value, 1),
+        "unit": "context rows/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "prefill_8192: B=1, L=8192 rows of 3x2560 target features, fc 7680->2048, "
+                               "hidden_norm, k_proj + k/v norms + RoPE for 4 layers (1 kv head x 256), offset 0",
+                   "rows": M, "step": "one dspark_project_context_kv call over all 8192 rows"},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm fc role (7680->2048 over 8192 rows)",
+                     "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops["gemm.fc"], "us_per_launch": round(fc_us, 2)},
+        "kernels": kernels,
+        "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+    return out
+
+
+def bench_rows(args, dsp, synth, torch):
+    """One draft round over 32 ragged rows whose context K/V is stored per row."""
+    w = synth.WORKLOADS["rows_a32"]
+    cfg = w.model
+    stored = synth.make_model(cfg, with_fc=False)
+    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
+    del stored
+    lens = synth.ctx_lens(w)
+    A = w.rows
+    k_rows = [[None] * A for _ in range(cfg.L)]
+    v_rows = [[None] * A for _ in range(cfg.L)]
+    for a in range(A):
+        for li in range(cfg.L):
+            kv = synth.direct_kv(w, a, li, lens[a])
+            k_rows[li][a] = dsp.act_tensor(kv["k"])
+            v_rows[li][a] = dsp.act_tensor(kv["v"])
+    anchors = synth.anchors(w)
+    call = dsp.DraftCall(model, k_rows, v_rows, lens, anchors, lens)
+
+    ms, prof, nprof = run_timed(call, args)
+    kernels = kernel_table(prof, nprof)
+    M = A * cfg.gamma
+    fl = gemm_flops_round(cfg, M)
+    g_ms = sum(v[1] for k, v in prof.items() if k.startswith("gemm.")) / nprof
+    g_tflops = fl / (g_ms * 1e-3) / 1e12
+    ab = attn_bytes(cfg, lens)
+    at_us = kernels["attn"]["us_per_step"]
+    kernels["attn"]["algorithmic_GBs"] = round(ab / (at_us * 1e3), 1)
+    value = A * args.steps / (ms / 1e3)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rows_a32: full_bf16 model, A=32 blocks of gamma 16, per-row context "
+                               "lengths uniform in [1024, 4096] stored per row",
+                   "rows": A, "gamma": cfg.gamma, "ctx_lens_sum": sum(lens),
+                   "step": "one dspark_draft_rows call",
+                   "tokens_per_s": round(value * cfg.gamma, 1)},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm (bf16 MFMA GEMM, all roles over 512 block rows)",
+                     "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_step": fl, "us_per_step": round(1e3 * g_ms, 2)},
+        "roofline_attn": {"bound": "hbm", "kernel": "ctx++block attention (context K/V streaming)",
+                          "achieved": round(ab / (at_us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(ab / (at_us * 1e3) / HBM_PEAK_GBS, 4), "traffic": None,
+                          "bytes_per_step": ab, "us_per_step": round(at_us, 2)},
+        "kernels": kernels,
+        "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_rows(w, lens, args.cpu_seconds)
+    return out
+
+
+BENCHES = {"full_bf16_a1": bench_full, "prefill_8192": bench_prefill, "rows_a32": bench_rows}
 
 
 def main():
@@ -107,6 +370,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--profile-steps", type=int, default=50)
+    ap.add_argument("--workload", choices=sorted(BENCHES), default="full_bf16_a1",
+                    help="full_bf16_a1 (default) is the headline line; the others are per-workload measurements")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -127,82 +392,7 @@ def main():
         calibrate_copy(args.calibrate_copy_mib, 4)
         return
     dsp.load_library()
-    w = synth.WORKLOADS["full_bf16_a1"]
-    cfg = w.model
-    stored = synth.make_model(cfg, with_fc=False)
-    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
-    del stored
-    L, A = w.fixed_ctx_len, w.rows
-    x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
-    anchors = synth.anchors(w)
-    k_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
-    v_out = [torch.empty(1, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
-    pws = torch.empty(dsp.project_workspace_bytes(model, dsp.INPUT_CONTEXT_HIDDEN, 1, L), dtype=torch.uint8,
-                      device="cuda")
-    call = dsp.DraftCall(model, [[k[0]] for k in k_out], [[v[0]] for v in v_out], [L], anchors, [L])
-
-    def step():
-        dsp.project_context_kv(model, x, [0], k_out=k_out, v_out=v_out, workspace=pws)
-        call()
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    ms_step = ms / args.steps
-    value = A * args.steps / (ms / 1e3)
-
-    # per-kernel durations: HIP events around each library launch on its stream
-    args.profile_steps = max(1, args.profile_steps)
-    dsp.profile_enable(True)
-    for _ in range(args.profile_steps):
-        step()
-    torch.cuda.synchronize()
-    prof = dsp.profile_read()
-    dsp.profile_enable(False)
-    roles = gemm_bytes(cfg, A * cfg.gamma, L)
-    g_bytes = sum(b * n for b, n in roles.values())  # per step
-    g_ms = sum(v[1] for k, v in prof.items() if k.startswith("gemm.")) / args.profile_steps
-    g_launch = sum(v[0] for k, v in prof.items() if k.startswith("gemm.")) / args.profile_steps
-    achieved = g_bytes / (g_ms / 1e3) / 1e9
-    kernels = {k: {"launches_per_step": v[0] / args.profile_steps, "us_per_step": 1e3 * v[1] / args.profile_steps}
-               for k, v in sorted(prof.items(), key=lambda kv: -kv[1][1])}
-    kern_sum_us = sum(v["us_per_step"] for v in kernels.values())
-    for k, v in kernels.items():
-        if k in roles:
-            v["algorithmic_GBs"] = round(roles[k][0] * roles[k][1] / (v["us_per_step"] * 1e3), 1)
-    traffic = None
-    if GEMM_TRAFFIC["sources_sha256"] == sources_sha256():
-        traffic = GEMM_TRAFFIC["bytes_per_step"]
-
-    out = {
-        "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "full_bf16_a1: 4 layers, H 2048, 8x256 q heads, 1 kv head, I 8192, V 32768, "
-                               "softcap 30, Markov rank 64; A=1 block, gamma 16, Lctx 512",
-                   "rows": A, "gamma": cfg.gamma, "ctx_len": L,
-                   "step": "context K/V projection of 512 rows + one draft round",
-                   "tokens_per_s": round(value * cfg.gamma, 1)},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "bytes_per_step": g_bytes, "launches_per_step": g_launch,
-                     "us_per_step": round(1e3 * g_ms, 2)},
-        "kernels": kernels,
-        "kernel_sum_us_per_step": round(kern_sum_us, 2),
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
-    print(json.dumps(out))
+    print(json.dumps(BENCHES[args.workload](args, dsp, synth, torch)))
 
 
 if __name__ == "__main__":
