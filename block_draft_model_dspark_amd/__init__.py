@@ -21,7 +21,8 @@ F32, BF16, Q4 = 0, 1, 2
 INPUT_CONTEXT_HIDDEN, INPUT_TARGET_FEATURES = 0, 1
 _KIND = {"f32": F32, "bf16": BF16, "q4": Q4}
 
-EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_aux_bytes", "dspark_model_prepare",
+EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tall_rows", "dspark_model_aux_bytes",
+            "dspark_model_prepare",
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
             "dspark_last_error")
@@ -73,6 +74,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                         ctypes.POINTER(P)]
     lib.dspark_model_destroy.argtypes = [P]
     lib.dspark_model_destroy.restype = None
+    lib.dspark_model_set_tall_rows.argtypes = [P, ctypes.c_int]
     lib.dspark_model_aux_bytes.argtypes = [P]
     lib.dspark_model_aux_bytes.restype = SZ
     lib.dspark_model_prepare.argtypes = [P, P, SZ, P]
@@ -91,8 +93,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_profile_read.restype = ctypes.c_int
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
-    for fn in ("dspark_model_create", "dspark_model_prepare", "dspark_project_context_kv", "dspark_draft_rows",
-               "dspark_draft_block"):
+    for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
+               "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -203,6 +205,11 @@ class Model:
         n = _lib.dspark_model_aux_bytes(self.handle)
         self.aux = torch.empty(n, dtype=torch.uint8, device="cuda")
         _check(_lib.dspark_model_prepare(self.handle, self.aux.data_ptr(), n, _stream_handle(stream)))
+        return self
+
+    def set_tall_rows(self, rows: int):
+        """GEMMs over >= rows activation rows take the tiled MFMA path (0: never)."""
+        _check(_lib.dspark_model_set_tall_rows(self.handle, int(rows)))
         return self
 
     @property

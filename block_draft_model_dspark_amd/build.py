@@ -11,7 +11,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libdspark.so")
-SOURCES = ["dspark_gemm.hip", "dspark_round.hip", "dspark_attn.hip", "dspark_api.cpp"]
+SOURCES = ["dspark_gemm.hip", "dspark_tall.hip", "dspark_round.hip", "dspark_attn.hip", "dspark_api.cpp"]
 ARCH = os.environ.get("DSPARK_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.join(ROOT, "include"),

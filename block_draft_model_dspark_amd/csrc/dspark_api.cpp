@@ -95,6 +95,7 @@ struct dspark_model {
   std::vector<LayerW> L;
   int nrot = 0;
   int nq = 0;
+  int tall_rows = 256;  // GEMMs over at least this many rows take the tiled path (0: never)
 };
 
 namespace {
@@ -115,6 +116,9 @@ struct GemmPlan {
   int mt, kc, S, kslice, xmode;
   size_t pbytes;   // split-K partials
   size_t cwords;   // reduction counters
+  int tall = TALL_NONE;  // tiled path over many rows: output tile
+  int np = 0;            // tiled path: bf16 input planes (1: bf16 rows as they are; 2: hi + lo)
+  size_t xbytes = 0;     // tiled path: the input planes (np == 2)
 };
 
 GemmPlan plan_gemm_mt(int wk, int xmode, int M, int N, int K, int group_cols, int mt) {
@@ -147,7 +151,30 @@ GemmPlan plan_gemm_mt(int wk, int xmode, int M, int N, int K, int group_cols, in
 // bf16 rows: 32-row tiles on eight-wave workgroups (two K halves) when the
 // slice is a whole even number (2, 4 or 8) of 256-wide sub-slices, which
 // reads each weight tile half as often as 16-row tiles.
-GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
+GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols, int tall_rows) {
+  // many rows: the tiled path (bf16 weights; its epilogues need whole
+  // 64-column blocks, head groups of at most 256 columns for the context
+  // projection, and at most 256 statistics parts for normed inputs)
+  // (the context projection of bf16 rows has a 32-row-tile streaming
+  // variant that stays ahead up to about four times the threshold)
+  const int64_t min_rows = group_cols > 0 && xmode == XM_BF16 ? 4 * (int64_t)tall_rows : tall_rows;
+  if (wk == WK_BF16 && tall_rows > 0 && M >= min_rows && K % 64 == 0 && N % 64 == 0 &&
+      (xmode != XM_NORM || K <= 256 * 64) && (group_cols == 0 || (group_cols <= 256 && N % group_cols == 0))) {
+    GemmPlan p{};
+    p.mt = 1;
+    p.S = 1;
+    p.kc = 0;
+    p.kslice = K;
+    p.xmode = xmode;
+    p.pbytes = 0;
+    p.cwords = 0;
+    // 128 x 128 tiles when they still give most CUs a tile, else 64 x 64
+    const int64_t tiles128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
+    p.tall = tiles128 >= 200 ? TALL_128 : TALL_64;
+    p.np = xmode == XM_BF16 ? 1 : 2;
+    p.xbytes = p.np == 2 ? (size_t)2 * M * K * 2 : 0;
+    return p;
+  }
   if (group_cols > 0 && wk == WK_BF16 && xmode == XM_BF16 && M >= 32) {
     const GemmPlan p2 = plan_gemm_mt(wk, xmode, M, N, K, group_cols, 2);
     const int nch = p2.kslice / 256;
@@ -157,10 +184,53 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols) {
   return plan_gemm_mt(wk, xmode, M, N, K, group_cols, 1);
 }
 
-hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st) {
+// workspace of the tiled path: bf16 input planes, and the product of the
+// GEMMs whose epilogue output is not the product itself (q|k, gate|up)
+struct TallBufs {
+  uint16_t* xop = nullptr;
+  float* T = nullptr;
+};
+
+hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st,
+                    const TallBufs& tb = TallBufs{}) {
   a.kslice = p.kslice;
   a.kc = p.kc;
-  return launch_gemm(a, e, epi, wk, p.xmode, p.mt, p.S, st);
+  if (p.tall == TALL_NONE) return launch_gemm(a, e, epi, wk, p.xmode, p.mt, p.S, st);
+  TallArgs t{};
+  if (p.xmode == XM_BF16) {
+    t.X = (const uint16_t*)a.X;
+    t.ldx = a.ldx;
+    t.plane = 0;
+  } else {
+    if (!tb.xop) return hipErrorInvalidValue;
+    const hipError_t r = launch_xprep(a, p.xmode, tb.xop, (int64_t)a.M * a.K, st);
+    if (r != hipSuccess) return r;
+    t.X = tb.xop;
+    t.ldx = a.K;
+    t.plane = (int64_t)a.M * a.K;
+  }
+  t.M = a.M;
+  t.N = a.N;
+  t.K = a.K;
+  t.nseg = a.nseg;
+  for (int i = 0; i < MAX_SEG; ++i) t.seg[i] = a.seg[i];
+  // the product goes where the epilogue's own output goes when the epilogue
+  // only reads it back in place (row statistics, softcap) or reads it from
+  // there (context K/V); q|k and gate|up take the separate buffer
+  if (epi == EPI_SUMS) {
+    t.T = e.Y;
+    t.ldt = e.ldy;
+  } else if (epi == EPI_KV || epi == EPI_LM) {
+    t.T = e.Y;
+    t.ldt = a.N;
+  } else {
+    if (!tb.T) return hipErrorInvalidValue;
+    t.T = tb.T;
+    t.ldt = a.N;
+  }
+  hipError_t r = launch_tall(t, p.tall, p.np, st);
+  if (r != hipSuccess) return r;
+  return launch_gemm_epi(a, e, epi, t.T, t.ldt, st);
 }
 
 GemmSeg seg_of(const Mat& w, int n0) {
@@ -179,7 +249,7 @@ GemmSeg seg_of(const Mat& w, int n0) {
 constexpr int ROW_PAD = 64;
 
 struct DraftLayout {
-  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, total;
+  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, xop, T, total;
   int64_t ldh, ldo, ldact;
   GemmPlan qk, o, gu, dn, lm;
   size_t cwords;
@@ -200,11 +270,12 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   const int nH = c.num_attention_heads, nKv = c.num_global_key_value_heads;
   const int wk = c.weight_dtype;
   DraftLayout d;
-  d.qk = plan_gemm(wk, XM_NORM, M, (nH + nKv) * hd, H, 0);
-  d.o = plan_gemm(wk, XM_F32, M, H, nH * hd, 0);
-  d.gu = plan_gemm(wk, XM_NORM, M, 2 * I, H, 0);
-  d.dn = plan_gemm(wk, XM_F32, M, H, I, 0);
-  d.lm = plan_gemm(wk, XM_NORM, M, c.vocab_size, H, 0);
+  const int tr = m->tall_rows;
+  d.qk = plan_gemm(wk, XM_NORM, M, (nH + nKv) * hd, H, 0, tr);
+  d.o = plan_gemm(wk, XM_F32, M, H, nH * hd, 0, tr);
+  d.gu = plan_gemm(wk, XM_NORM, M, 2 * I, H, 0, tr);
+  d.dn = plan_gemm(wk, XM_F32, M, H, I, 0, tr);
+  d.lm = plan_gemm(wk, XM_NORM, M, c.vocab_size, H, 0, tr);
   const size_t pmax = std::max({d.qk.pbytes, d.o.pbytes, d.gu.pbytes, d.dn.pbytes, d.lm.pbytes, (size_t)4});
   d.cwords = std::max({d.qk.cwords, d.o.cwords, d.gu.cwords, d.dn.cwords, d.lm.cwords});
   d.nsplit_max = 512 + 2 * A;
@@ -236,13 +307,16 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.ml = take((size_t)d.nsplit_max * nKv * m->nq * 2 * 4);
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
   d.lohi = take((size_t)M * NC * 8);
+  d.xop = take(std::max({d.qk.xbytes, d.o.xbytes, d.gu.xbytes, d.dn.xbytes, d.lm.xbytes, (size_t)4}));
+  d.T = take(std::max({d.qk.tall ? (size_t)M * (nH + nKv) * hd * 4 : 0, d.gu.tall ? (size_t)M * 2 * I * 4 : 0,
+                       (size_t)4}));
   d.total = off;
   return d;
 }
 
 // ---- projection workspace layout -----------------------------------------
 struct ProjLayout {
-  size_t P, Y, C, sums, cnt, total;
+  size_t P, Y, C, sums, cnt, xop, total;
   GemmPlan fc, kp;
   size_t cwords;
   int lay_per_gemm;
@@ -259,18 +333,20 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
   size_t pbytes = 4;
   if (feats) {
-    p.fc = plan_gemm(c.weight_dtype, xmode_in(m), M, H, c.fc_in, 0);
+    p.fc = plan_gemm(c.weight_dtype, xmode_in(m), M, H, c.fc_in, 0, m->tall_rows);
     pbytes = std::max(pbytes, p.fc.pbytes);
     p.cwords = p.fc.cwords;
   }
-  p.kp = plan_gemm(c.weight_dtype, feats ? XM_NORM : xmode_in(m), M, Nk, H, hd);
+  p.kp = plan_gemm(c.weight_dtype, feats ? XM_NORM : xmode_in(m), M, Nk, H, hd, m->tall_rows);
+  size_t xbytes = std::max(p.fc.xbytes, p.kp.xbytes);
   pbytes = std::max(pbytes, p.kp.pbytes);
   p.cwords = std::max(p.cwords, p.kp.cwords);
   // a last, smaller group of layers is planned on its own (it may split K)
   const int rem = c.num_hidden_layers % p.lay_per_gemm;
   if (rem) {
-    const GemmPlan r = plan_gemm(c.weight_dtype, p.kp.xmode, M, rem * nKv * hd, H, hd);
+    const GemmPlan r = plan_gemm(c.weight_dtype, p.kp.xmode, M, rem * nKv * hd, H, hd, m->tall_rows);
     pbytes = std::max(pbytes, r.pbytes);
+    xbytes = std::max(xbytes, r.xbytes);
     p.cwords = std::max(p.cwords, r.cwords);
   }
   size_t off = 0;
@@ -284,6 +360,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.C = feats ? take((size_t)M * H * 4) : 0;
   p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
   p.cnt = take(p.cwords * 4);
+  p.xop = take(std::max(xbytes, (size_t)4));
   p.total = off;
   return p;
 }
@@ -454,6 +531,13 @@ dspark_status dspark_model_create(const dspark_config* cfg, const dspark_weight*
 
 void dspark_model_destroy(dspark_model* m) { delete m; }
 
+dspark_status dspark_model_set_tall_rows(dspark_model* m, int rows) {
+  g_err.clear();
+  if (!m) return fail(DSPARK_ERR_INVALID_ARG, "null model");
+  m->tall_rows = rows > 0 ? rows : 0;
+  return DSPARK_OK;
+}
+
 size_t dspark_model_aux_bytes(const dspark_model* m) {
   if (!m) return 0;
   return align256(((size_t)m->c.vocab_size + 1) * 4);
@@ -511,6 +595,8 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   unsigned* cnt = (unsigned*)(ws + p.cnt);
   HIPCHECK(timed("zero_counters", stream, [&] { return launch_zero(cnt, (int64_t)p.cwords, stream); }));
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
+  TallBufs tb;
+  tb.xop = (uint16_t*)(ws + p.xop);
   NormIn nin{};
   if (feats) {
     // fc rows and their statistics; k_proj reads hidden_norm(fc x)
@@ -531,7 +617,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     e.ldy = H;
     e.w1 = m->hidden_norm;
     e.sums = (float4*)(ws + p.sums);
-    HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream); }));
+    HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream, tb); }));
     nin.y = e.Y;
     nin.sums = e.sums;
     nin.ld = H;
@@ -554,7 +640,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     g.P = (float*)(ws + p.P);
     g.nin = nin;
     GemmPlan gp = p.kp;
-    if (nl != p.lay_per_gemm) gp = plan_gemm(c.weight_dtype, p.kp.xmode, M, g.N, H, hd);
+    if (nl != p.lay_per_gemm) gp = plan_gemm(c.weight_dtype, p.kp.xmode, M, g.N, H, hd, m->tall_rows);
     EpiArgs e{};
     e.Y = (float*)(ws + p.Y);
     e.cnt = cnt;
@@ -572,7 +658,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
       e.kout[i] = k_out_dev[l0 + i];
       e.vout[i] = v_out_dev[l0 + i];
     }
-    HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream); }));
+    HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream, tb); }));
   }
   return DSPARK_OK;
 }
@@ -635,6 +721,9 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   unsigned* cnt = (unsigned*)(ws + d.cnt);
   const int wk = m->lm.kind;
   const int NC = nc_of(m);
+  TallBufs tb;
+  tb.xop = (uint16_t*)(ws + d.xop);
+  tb.T = (float*)(ws + d.T);
 
   // attention split plan: context splits of `split` keys, then the block split
   const int split = attn_split(total_keys - (int64_t)A * G);
@@ -754,7 +843,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, W.in, hB);
     e.qn = W.qn;
     e.kn = W.kn;
-    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream); }));
+    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream, tb); }));
 
     for (int a = 0; a < A; ++a) {
       at.row[a].k = k_ctx_dev[l * A + a];
@@ -775,7 +864,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     e.Y = Y;
     e.h = hB;
     e.w1 = W.pa;
-    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream); }));
+    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream, tb); }));
 
     g = GemmArgs{};
     g.ldx = H;
@@ -787,7 +876,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.seg[1] = seg_of(W.u, I);
     g.P = P;
     g.nin = norm_in(hB, Y, W.pa, scal, W.pf, hA);
-    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream); }));
+    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream, tb); }));
 
     g = GemmArgs{};
     g.X = act;
@@ -801,7 +890,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     e.Y = Y;
     e.h = hA;
     e.w1 = W.pff;
-    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream); }));
+    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream, tb); }));
     y_prev = Y;
     w1_prev = W.pff;
     sc_prev = scal + 1 + l;
@@ -822,7 +911,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   e.aux = c.markov_rank > 0 ? (const float*)aux_dev : nullptr;
   e.lohi = (float2*)(ws + d.lohi);
   e.NC = NC;
-  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream); }));
+  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream, tb); }));
 
   WalkArgs w{};
   w.rows = rows;

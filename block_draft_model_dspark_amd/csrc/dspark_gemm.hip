@@ -309,6 +309,35 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
   }
 }
 
+// deepspec.ts, #geluTanhMlp: act = gelu_tanh(gate x) * up x.  Waves 0,1 (of
+// each set of four) hold gate columns 32cb.., waves 2,3 the matching up
+// columns; an eight-wave workgroup holds one tile per K half, added here.
+template <int MT, int NW>
+__device__ __forceinline__ void epi_gelu(const GemmArgs& g, const EpiArgs& e, const f32x4* acc, int mbase, int cb,
+                                         float* ep, int half) {
+  const int tid = threadIdx.x, wave = (tid & 255) >> 6, lane = tid & 63, gq = lane >> 4;
+  constexpr int TILE = 4 * MT * 16 * 16;
+#pragma unroll
+  for (int t = 0; t < MT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      ep[half * TILE + (wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
+  __syncthreads();
+  for (int idx = tid; idx < MT * 16 * 32; idx += 64 * NW) {
+    const int r = idx >> 5, col = idx & 31;
+    const int m = mbase + r;
+    if (m >= g.M) continue;
+    const int og = ((col >> 4) * MT * 16 + r) * 16 + (col & 15);
+    const int ou = ((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15);
+    float gt = ep[og], up = ep[ou];
+    if (NW == 8) {
+      gt += ep[TILE + og];
+      up += ep[TILE + ou];
+    }
+    e.act[(int64_t)m * e.ld_act + 32 * cb + col] = gelu_tanh(gt) * up;
+  }
+}
+
 // deepspec.ts, #projectContextKVRows for one (layer, kv head) and the rows
 // [m0, m1) of the row block: V = rms(k) (no weight, no RoPE);
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
@@ -908,29 +937,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   // 5. epilogue
   float* ep = (float*)smem;
   if constexpr (EPI == EPI_GELU) {
-    // deepspec.ts, #geluTanhMlp: act = gelu_tanh(gate x) * up x; waves 0,1
-    // hold gate columns 32cb.., waves 2,3 the matching up columns
-    // (eight waves: one tile per K half, added here)
-    constexpr int TILE = 4 * MT * 16 * 16;
-#pragma unroll
-    for (int t = 0; t < MT; ++t)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ep[half * TILE + (wave * MT * 16 + t * 16 + 4 * gq + i) * 16 + (lane & 15)] = acc[t][i];
-    __syncthreads();
-    for (int idx = tid; idx < MT * 16 * 32; idx += 64 * NW) {
-      const int r = idx >> 5, col = idx & 31;
-      const int m = mbase + r;
-      if (m >= g.M) continue;
-      const int og = ((col >> 4) * MT * 16 + r) * 16 + (col & 15);
-      const int ou = ((2 + (col >> 4)) * MT * 16 + r) * 16 + (col & 15);
-      float gt = ep[og], up = ep[ou];
-      if (NW == 8) {
-        gt += ep[TILE + og];
-        up += ep[TILE + ou];
-      }
-      e.act[(int64_t)m * e.ld_act + 32 * cb + col] = gelu_tanh(gt) * up;
-    }
+    epi_gelu<MT, NW>(g, e, acc, mbase, cb, ep, half);
   } else if constexpr (EPI == EPI_QK) {
     epi_qk<MT>(g, e, acc, mbase, cb, ep);
   } else if constexpr (EPI == EPI_SUMS) {
@@ -963,6 +970,56 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     if (!arrive_last(e.cnt + gridDim.z * ncb + blockIdx.z * ngroups + grp, members, &last_flag)) return;
     epi_kv<MT, 64 * NW>(g, e, mbase, min(g.M, mbase + MT * 16), grp, rinv, rcs);
   }
+}
+
+// The epilogue of a GEMM whose product the tiled kernel (dspark_tall.hip)
+// already wrote to T (row pitch ldt): one 16 x 64 tile per workgroup, the
+// product read into the accumulator layout of the weight-streaming kernel
+// (wave w: columns wave_col(cb, w) + lane mod 16, rows 4 (lane / 16) + i).
+template <int EPI>
+__global__ __launch_bounds__(256) void k_gemm_epi(const GemmArgs g, const EpiArgs e, const float* T, int64_t ldt) {
+  __shared__ __align__(16) float ep[4 * 16 * 16];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
+  const int cb = blockIdx.x, mbase = blockIdx.y * 16;
+  const int n = wave_col<EPI>(cb, wave, g.N, e.hd) + (lane & 15);
+  f32x4 acc[1];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[0][i] = T[(int64_t)min(mbase + 4 * gq + i, g.M - 1) * ldt + n];
+  if constexpr (EPI == EPI_GELU) epi_gelu<1, 4>(g, e, acc, mbase, cb, ep, 0);
+  else if constexpr (EPI == EPI_QK) epi_qk<1>(g, e, acc, mbase, cb, ep);
+  else if constexpr (EPI == EPI_SUMS) epi_sums<1>(g, e, acc, mbase, cb, n, ep);
+  else if constexpr (EPI == EPI_LM) epi_lm<1>(g, e, acc, mbase, cb, n, ep);
+}
+
+// context K/V epilogue over a product already in e.Y (pitch N): one
+// workgroup per (layer and kv-head group, 16 rows)
+__global__ __launch_bounds__(256) void k_kv_epi(const GemmArgs g, const EpiArgs e) {
+  __shared__ double rinv[128];
+  __shared__ float2 rcs[16 * 128];
+  if ((int)threadIdx.x < (e.hd >> 1)) rinv[threadIdx.x] = rope_inv(threadIdx.x, e.rope.hd, e.rope.theta, e.rope.nrot);
+  __syncthreads();
+  const int mbase = blockIdx.y * 16;
+  epi_kv<1, 256>(g, e, mbase, min(g.M, mbase + 16), blockIdx.x, rinv, rcs);
+}
+
+hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt,
+                           hipStream_t st) {
+  const int mblocks = (a.M + 15) / 16;
+  if (a.N % 64 != 0) return hipErrorInvalidValue;
+  const dim3 grid(a.N / 64, mblocks);
+  switch (epi) {
+    case EPI_GELU: hipLaunchKernelGGL(k_gemm_epi<EPI_GELU>, grid, dim3(256), 0, st, a, e, T, ldt); break;
+    case EPI_QK: hipLaunchKernelGGL(k_gemm_epi<EPI_QK>, grid, dim3(256), 0, st, a, e, T, ldt); break;
+    case EPI_SUMS: hipLaunchKernelGGL(k_gemm_epi<EPI_SUMS>, grid, dim3(256), 0, st, a, e, T, ldt); break;
+    case EPI_LM: hipLaunchKernelGGL(k_gemm_epi<EPI_LM>, grid, dim3(256), 0, st, a, e, T, ldt); break;
+    case EPI_KV: {
+      if (e.group_cols != e.hd || e.hd > 256 || a.N % e.hd != 0) return hipErrorInvalidValue;
+      hipLaunchKernelGGL(k_kv_epi, dim3(a.N / e.hd, mblocks), dim3(256), 0, st, a, e);
+      break;
+    }
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc) {

@@ -99,6 +99,19 @@ struct EpiArgs {
   int NC;
 };
 
+// tiled GEMM over many rows (dspark_tall.hip): T[m, n] = sum over the np
+// bf16 input planes X_p[m, :] . W[n, :], fp32, row pitch ldt
+enum { TALL_NONE = 0, TALL_64 = 1, TALL_128 = 2 };  // output tile (square)
+struct TallArgs {
+  const uint16_t* X;  // plane 0 [M, ldx] bf16; plane p at X + p * plane
+  int64_t ldx, plane;
+  int M, N, K;        // K a multiple of 64
+  int nseg;
+  GemmSeg seg[MAX_SEG];  // bf16 weights [rows, K] per column segment
+  float* T;
+  int64_t ldt;
+};
+
 // per-row data of a draft round
 struct RowTab {
   int A, gamma;
@@ -166,6 +179,12 @@ hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, 
                        hipStream_t st);
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
 size_t gemm_counter_words(int M, int N, int mt, int group_cols);
+hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t plane, hipStream_t st);
+hipError_t launch_tall(const TallArgs& t, int tile, int np, hipStream_t st);
+// the epilogue of a GEMM whose product is in T (row pitch ldt); EPI_KV reads
+// it from e.Y (pitch N)
+hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt,
+                           hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st);

@@ -1,0 +1,255 @@
+// Tiled bf16 MFMA GEMM for many activation rows.
+//
+// The weight-streaming GEMM (dspark_gemm.hip) gives each workgroup one or
+// two 16-row tiles and streams the weights once per row block: right for the
+// 16-row draft block, wasteful once there are hundreds of rows (a batch of
+// draft rows, or a long context to project), where the same weight tile is
+// fetched again for every row block and the work is bound by MFMA rate, not
+// by HBM.  For those shapes the product is formed here in three steps:
+//   1. k_xprep: the input rows as bf16 planes.  fp32 rows (and normed
+//      residual rows, formed from the stored row statistics exactly as the
+//      weight-streaming kernel forms them) become a hi and a lo plane whose
+//      sum carries the fp32 value; bf16 input rows are used as they are.
+//   2. k_tall: T[m, n] = sum over planes of X_p[m, :] . W[n, :] in fp32,
+//      BM x BN output tiles, both operands staged through LDS in 64-wide K
+//      steps (the next step's global loads in flight during this step's
+//      MFMAs), four waves of (BM/2) x (BN/2).
+//   3. the GEMM's own epilogue (norm statistics, q|k RoPE, GELU gate, logit
+//      softcap, context K/V) reads T: k_gemm_epi / k_kv_epi.
+#include "dspark_kernels.hpp"
+#include "dspark_common.hpp"
+
+namespace dsp {
+
+// ---------------------------------------------------------------------------
+// 1. input rows -> bf16 hi / lo planes [2][M][K] (plane stride t.plane)
+// ---------------------------------------------------------------------------
+// One workgroup per row.  XM_NORM: deepspec.ts, #forwardBackbone sandwich
+// norms; hn = (h + rms(y) * w1 * y) * sc, x = rms(hn) * w2 (x = hn without
+// w2), the RMS factors taken from the 64-column statistics (see NormIn), and
+// hn written to hout when it is given.
+template <int XM>
+__global__ __launch_bounds__(256) void k_xprep(const GemmArgs g, uint16_t* xop, int64_t plane) {
+  __shared__ float4 red[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int K = g.K;
+  float r1 = 1.f, r2 = 1.f, sc = 1.f;
+  if constexpr (XM == XM_NORM) {
+    const NormIn& n = g.nin;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int p = tid; p < n.nparts; p += 256) {
+      const float4 v = n.sums[(int64_t)p * g.M + m];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    s.x = wave_sum(s.x);
+    s.y = wave_sum(s.y);
+    s.z = wave_sum(s.z);
+    s.w = wave_sum(s.w);
+    if (lane == 0) red[wave] = s;
+    __syncthreads();
+    s = red[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) {
+      s.x += red[w].x;
+      s.y += red[w].y;
+      s.z += red[w].z;
+      s.w += red[w].w;
+    }
+    sc = n.sc ? *n.sc : 1.f;
+    const float inv_k = 1.f / (float)K;
+    r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
+    const float t2 = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
+    r2 = 1.f / sqrtf(t2 * inv_k + n.eps);
+  }
+  for (int k8 = tid; k8 < (K >> 3); k8 += 256) {
+    const int k = 8 * k8;
+    float v[8];
+    if constexpr (XM == XM_NORM) {
+      const NormIn& n = g.nin;
+      const bool bf = n.act_bf16 != 0;
+      float h[8], y[8], w1[8], w2[8];
+      const float* ph = n.h ? n.h : n.y;
+      const float* py = n.y ? n.y : n.h;
+      const f32x4 h0 = *(const f32x4*)(ph + (int64_t)m * n.ld + k), h1 = *(const f32x4*)(ph + (int64_t)m * n.ld + k + 4);
+      const f32x4 y0 = *(const f32x4*)(py + (int64_t)m * n.ld + k), y1 = *(const f32x4*)(py + (int64_t)m * n.ld + k + 4);
+      const void* p1 = n.y ? n.w1 : n.w2;
+      const void* p2 = n.w2 ? n.w2 : p1;
+      cvt_act8(ld_act8(p1, k, bf), bf, w1);
+      cvt_act8(ld_act8(p2, k, bf), bf, w2);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        h[q] = h0[q];
+        h[4 + q] = h1[q];
+        y[q] = y0[q];
+        y[4 + q] = y1[q];
+      }
+      float hn[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float hv = n.h ? h[q] : 0.f;
+        const float yv = n.y ? y[q] * r1 * w1[q] : 0.f;
+        hn[q] = (hv + yv) * sc;
+        v[q] = n.w2 ? hn[q] * r2 * w2[q] : hn[q];
+      }
+      if (n.hout) {
+        float* dst = n.hout + (int64_t)m * n.ld + k;
+        *(f32x4*)dst = f32x4{hn[0], hn[1], hn[2], hn[3]};
+        *(f32x4*)(dst + 4) = f32x4{hn[4], hn[5], hn[6], hn[7]};
+      }
+    } else {
+      const float* px = (const float*)g.X + (int64_t)m * g.ldx + k;
+      const f32x4 a = *(const f32x4*)px, b = *(const f32x4*)(px + 4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = a[q];
+        v[4 + q] = b[q];
+      }
+    }
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
+    *(u32x4*)(xop + (int64_t)m * K + k) = __builtin_bit_cast(u32x4, hi);
+    *(u32x4*)(xop + plane + (int64_t)m * K + k) = __builtin_bit_cast(u32x4, lo);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. T = sum_p X_p W^T, BM x BN tiles, K steps of 64
+// ---------------------------------------------------------------------------
+constexpr int TBK = 64;        // K step
+constexpr int TLD = TBK + 8;   // LDS row pitch (bf16): 16 consecutive rows of one
+                               // 16-byte column fall on distinct banks
+
+template <int BM, int BN, int NP>
+__global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
+  constexpr int AIT = BM * (TBK / 8) / 256, BIT = BN * (TBK / 8) / 256;  // 16-byte items per thread
+  static_assert(AIT >= 1 && BIT >= 1, "tile too small for 256 threads");
+  __shared__ __align__(16) uint16_t As[NP][BM * TLD];
+  __shared__ __align__(16) uint16_t Bs[BN * TLD];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+
+  // this thread's rows of the two tiles (clamped: rows past M or N repeat
+  // the last one and are never stored) and the weight segment of each
+  const uint16_t* ap[AIT];
+  const uint16_t* bp[BIT];
+#pragma unroll
+  for (int j = 0; j < AIT; ++j) {
+    const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
+    ap[j] = t.X + (int64_t)min(m0 + r, t.M - 1) * t.ldx + 8 * c8;
+  }
+#pragma unroll
+  for (int j = 0; j < BIT; ++j) {
+    const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
+    const int n = min(n0 + r, t.N - 1);
+    // segment lookup with uniform (scalar) reads of the argument array
+    const void* w = t.seg[0].w;
+    int nb = t.seg[0].n0;
+#pragma unroll
+    for (int i = 1; i < MAX_SEG; ++i) {
+      const void* wi = t.seg[i].w;
+      const int ni = t.seg[i].n0;
+      const bool in = i < t.nseg && n >= ni;
+      w = in ? wi : w;
+      nb = in ? ni : nb;
+    }
+    bp[j] = (const uint16_t*)w + (int64_t)(n - nb) * t.K + 8 * c8;
+  }
+  u32x4 ra[NP][AIT], rb[BIT];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int j = 0; j < AIT; ++j) ra[p][j] = *(const u32x4*)(ap[j] + p * t.plane + k0);
+#pragma unroll
+    for (int j = 0; j < BIT; ++j) rb[j] = *(const u32x4*)(bp[j] + k0);
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < AIT; ++j) {
+      const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
+#pragma unroll
+      for (int p = 0; p < NP; ++p) *(u32x4*)&As[p][r * TLD + 8 * c8] = ra[p][j];
+    }
+#pragma unroll
+    for (int j = 0; j < BIT; ++j) {
+      const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
+      *(u32x4*)&Bs[r * TLD + 8 * c8] = rb[j];
+    }
+  };
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  load(0);
+  for (int k0 = 0; k0 < t.K; k0 += TBK) {
+    __syncthreads();  // every wave is done reading the previous step
+    store();
+    __syncthreads();
+    // next step's loads (the last step reloads itself: a fixed load count)
+    load(k0 + TBK < t.K ? k0 + TBK : k0);
+#pragma unroll
+    for (int s = 0; s < TBK / 32; ++s) {
+      bf16x8 bfr[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+        bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&Bs[(WN * wn + 16 * j + ln) * TLD + 32 * s + 8 * gq]);
+#pragma unroll
+      for (int p = 0; p < NP; ++p)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+          const bf16x8 afr =
+              __builtin_bit_cast(bf16x8, *(const u32x4*)&As[p][(WM * wm + 16 * i + ln) * TLD + 32 * s + 8 * gq]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(afr, bfr[j], acc[i][j]);
+        }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = n0 + WN * wn + 16 * j + ln;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int m = m0 + WM * wm + 16 * i + 4 * gq + q;
+        if (m < t.M && n < t.N) t.T[(int64_t)m * t.ldt + n] = acc[i][j][q];
+      }
+    }
+}
+
+hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t plane, hipStream_t st) {
+  if (xmode == XM_NORM) {
+    if (g.nin.nparts * 64 != g.K) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_xprep<XM_NORM>, dim3(g.M), dim3(256), 0, st, g, xop, plane);
+  } else if (xmode == XM_F32) {
+    hipLaunchKernelGGL(k_xprep<XM_F32>, dim3(g.M), dim3(256), 0, st, g, xop, plane);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_tall(const TallArgs& t, int tile, int np, hipStream_t st) {
+  if (t.K % TBK != 0 || t.M <= 0 || t.N <= 0 || t.nseg < 1 || t.nseg > MAX_SEG) return hipErrorInvalidValue;
+  const int bm = tile == TALL_128 ? 128 : 64, bn = bm;
+  const dim3 grid((t.N + bn - 1) / bn, (t.M + bm - 1) / bm);
+  if (tile == TALL_128) {
+    if (np == 1) hipLaunchKernelGGL((k_tall<128, 128, 1>), grid, dim3(256), 0, st, t);
+    else hipLaunchKernelGGL((k_tall<128, 128, 2>), grid, dim3(256), 0, st, t);
+  } else {
+    if (np == 1) hipLaunchKernelGGL((k_tall<64, 64, 1>), grid, dim3(256), 0, st, t);
+    else hipLaunchKernelGGL((k_tall<64, 64, 2>), grid, dim3(256), 0, st, t);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace dsp

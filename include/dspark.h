@@ -100,6 +100,16 @@ dspark_status dspark_model_create(const dspark_config* cfg, const dspark_weight*
                                   dspark_model** out);
 void dspark_model_destroy(dspark_model* m);
 
+/* GEMMs over at least `rows` activation rows (a batch of draft rows, a long
+ * context to project) run as a tiled bf16 MFMA GEMM over a product buffer in
+ * the workspace, followed by the GEMM's epilogue; fewer rows stream the
+ * weights once per 16-row tile.  Both compute the same product (fp32
+ * activations as bf16 hi + lo planes); the context projection of bf16 rows
+ * switches at four times `rows`.  rows <= 0 keeps every GEMM on the
+ * weight-streaming kernel.  Default 256.  Workspace sizes depend on it: set it
+ * before sizing workspaces.  DSPARK_ERR_INVALID_ARG for a null model. */
+dspark_status dspark_model_set_tall_rows(dspark_model* m, int rows);
+
 /* Per-model derived data the Markov walk uses to skip vocabulary entries that
  * cannot win a step (row norms of markov_w2 and the largest markov_w1 row
  * norm).  The caller allocates `aux_bytes` of device memory, calls prepare
