@@ -264,6 +264,16 @@ int attn_split(int64_t total_ctx) {
   return (int)std::max<int64_t>(ATT_KEYS, s);
 }
 
+// the same for the wide kernel (every query row of a kv head per
+// workgroup): about 384 context splits, fewer partial outputs to merge
+int attn_split_wide(int64_t total_ctx) {
+  int64_t s = (total_ctx + 383) / 384;
+  s = (s + ATT_KEYS - 1) / ATT_KEYS * ATT_KEYS;
+  return (int)std::max<int64_t>(ATT_KEYS, s);
+}
+// contexts long enough in total for the wide attention kernel
+constexpr int64_t ATTN_WIDE_MIN_KEYS = 2048;
+
 DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   const dspark_config& c = m->c;
   const int M = A * c.block_size, H = c.hidden_size, I = c.intermediate_size, hd = c.global_head_dim;
@@ -726,7 +736,9 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   tb.T = (float*)(ws + d.T);
 
   // attention split plan: context splits of `split` keys, then the block split
-  const int split = attn_split(total_keys - (int64_t)A * G);
+  const int64_t total_ctx = total_keys - (int64_t)A * G;
+  const bool wide = total_ctx >= ATTN_WIDE_MIN_KEYS && attn_wide_ok(m->nq, hd);
+  const int split = wide ? attn_split_wide(total_ctx) : attn_split(total_ctx);
   AttnArgs at{};
   MergeArgs mg{};
   int nsplit = 0;
@@ -849,7 +861,10 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
       at.row[a].k = k_ctx_dev[l * A + a];
       at.row[a].v = v_ctx_dev[l * A + a];
     }
-    HIPCHECK(timed("attn", stream, [&] { return launch_attn(at, c.act_dtype == DSPARK_BF16, nsplit, stream); }));
+    HIPCHECK(timed("attn", stream, [&] {
+      return wide ? launch_attn_wide(at, c.act_dtype == DSPARK_BF16, nsplit, stream)
+                  : launch_attn(at, c.act_dtype == DSPARK_BF16, nsplit, stream);
+    }));
     HIPCHECK(timed("attn_merge", stream, [&] { return launch_merge(mg, stream); }));
 
     g = GemmArgs{};

@@ -33,12 +33,12 @@ namespace dsp {
 constexpr int ATT_NTH = 256;  // threads per workgroup (4 waves, one quarter of hd each)
 
 // one pass over the keys staged in LDS: ONE = 32 one-plane keys, else 16
-// keys as hi (rows 0..15) and lo (rows 16..31) planes.  o: this wave's
-// HD/64 output tiles (head dims 16 t0 + 16 t ..).
-template <int HD, bool ONE>
+// keys as hi (rows 0..15) and lo (rows 16..31) planes.  o: this wave's NTW
+// output tiles (head dims 16 t0 + 16 t ..).
+template <int HD, bool ONE, int NTW>
 __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt, const bf16x8* qh, const bf16x8* ql,
                                           f32x4* o, int t0, float& m_run, float& l_part, int nvalid) {
-  constexpr int NS = HD / 32, NTW = HD / 64, KSTR = HD + 8, VSTR = 40;
+  constexpr int NS = HD / 32, KSTR = HD + 8, VSTR = 40;
   const int lane = threadIdx.x & 63, gq = lane >> 4, ln = lane & 15;
   float sv[8];
   {
@@ -108,13 +108,15 @@ __device__ __forceinline__ uint16_t half_of(const u32x4& w, int e) { return (uin
 // ql; a wave's loads complete in order, so the query loads went first).
 // ONE: bf16 context keys, 32 per pass in one plane; else fp32 keys (the
 // block's own, scaled by their RMS factor: rkey for this thread's key, or an
-// fp32 cache: 1) in two 16-key passes of hi / lo planes.
-template <int HD, bool ONE, class Prep>
+// fp32 cache: 1) in two 16-key passes of hi / lo planes.  NTH threads stage;
+// each wave accumulates NTW output tiles from t0.
+template <int HD, bool ONE, int NTH, int NTW, class Prep>
 __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, int j0, int j1, float rkey,
                                           Prep&& prep, const bf16x8* qh, const bf16x8* ql, f32x4* o, int t0,
                                           float& m_run, float& l_part, uint16_t* Ks, uint16_t* Vt) {
   constexpr int KSTR = HD + 8, VSTR = 40;
-  constexpr int IPT = ATT_KEYS * (HD / 8) / ATT_NTH;  // staging items (key, 8 dims) per thread
+  constexpr int IPT = ATT_KEYS * (HD / 8) / NTH;  // staging items (key, 8 dims) per thread
+  static_assert(IPT >= 1 && ATT_KEYS * (HD / 8) % NTH == 0 && NTH % ATT_KEYS == 0, "staging layout");
   const int tid = threadIdx.x;
   const int key = tid & (ATT_KEYS - 1);  // the key this thread stages (all its items)
   u32x4 kk[ONE ? IPT : 1], vv[ONE ? IPT : 1];
@@ -123,7 +125,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
     const int kc = jc + min(key, j1 - jc - 1);
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
+      const int c8 = (tid + NTH * i) / ATT_KEYS;
       if constexpr (ONE) {
         kk[i] = *(const u32x4*)((const uint16_t*)kbase + (int64_t)kc * HD + 8 * c8);
         vv[i] = *(const u32x4*)((const uint16_t*)vbase + (int64_t)kc * HD + 8 * c8);
@@ -146,7 +148,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
-        const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
+        const int c8 = (tid + NTH * i) / ATT_KEYS;
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
         const u32x4 vw = ok ? vv[i] : z;
@@ -155,7 +157,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
       }
       __syncthreads();
       if (jc + ATT_KEYS < j1) load(jc + ATT_KEYS);
-      attn_pass<HD, true>(Ks, Vt, qh, ql, o, t0, m_run, l_part, nk);
+      attn_pass<HD, true, NTW>(Ks, Vt, qh, ql, o, t0, m_run, l_part, nk);
     } else {
       float kv8[IPT][8], vv8[IPT][8];
       const float sc = ok ? rkey : 0.f;
@@ -175,7 +177,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
           const int rr = key & 15;
 #pragma unroll
           for (int i = 0; i < IPT; ++i) {
-            const int c8 = (tid + ATT_NTH * i) / ATT_KEYS;
+            const int c8 = (tid + NTH * i) / ATT_KEYS;
             bf16x8 kh, kl, vh, vl;
             split8(kv8[i], kh, kl);
             split8(vv8[i], vh, vl);
@@ -192,7 +194,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
           }
         }
         __syncthreads();
-        attn_pass<HD, false>(Ks, Vt, qh, ql, o, t0, m_run, l_part, min(16, nk - 16 * pass));
+        attn_pass<HD, false, NTW>(Ks, Vt, qh, ql, o, t0, m_run, l_part, min(16, nk - 16 * pass));
       }
     }
   }
@@ -284,13 +286,13 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
 
   if (blk) {
     const int64_t off = ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
-    attn_keys<HD, false>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), prep, qh, ql, o, t0,
-                         m_run, l_part, Ks, Vt);
+    attn_keys<HD, false, ATT_NTH, NTW>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), prep, qh, ql,
+                                       o, t0, m_run, l_part, Ks, Vt);
   } else {
     const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
     const char* kb = (const char*)a.row[row].k + kvoff;
     const char* vb = (const char*)a.row[row].v + kvoff;
-    attn_keys<HD, KVB>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt);
+    attn_keys<HD, KVB, ATT_NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt);
   }
 
   float l = l_part;
@@ -306,6 +308,118 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
       a.ml[base * 2 + 1] = l;
     }
   }
+}
+
+// Many keys per row (a batch of long contexts): one workgroup per (row, key
+// split, kv head) holding every query row of the group, wave w the 16 rows
+// 16w.. over the whole head dimension.  Each staged key chunk then serves all
+// query rows, and no wave repeats another's scores.  The query operand is
+// loaded straight into B-operand order (lane: query l mod 16, dims
+// 32s + 8(l / 16) ..), scaled by its RMS factor and split into hi / lo.
+template <int HD, bool KVB, int NQT>
+__global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
+  constexpr int NTH = 64 * NQT, NS = HD / 32, NTW = HD / 16, HJ = HD / 64;
+  __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
+  __shared__ __align__(16) uint16_t Vt[HD * 40];
+
+  const int sg = blockIdx.x, kvh = blockIdx.y;
+  int row = 0;
+  while (a.split_off[row + 1] <= sg) ++row;
+  const int sp = sg - a.split_off[row];
+  const bool blk = sp == a.split_off[row + 1] - a.split_off[row] - 1;  // the row's block keys
+  const int len = a.len[row];
+  const int j0 = blk ? 0 : sp * a.split, j1 = blk ? a.gamma : min(len, j0 + a.split);
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, ln = lane & 15;
+  const int rep = a.nH / a.nKv;
+  const int qr = wave * 16 + ln;  // this lane's query row (nq == 16 NQT)
+  const int hl = qr / a.gamma, g = qr - hl * a.gamma, head = kvh * rep + hl;
+
+  // 1. this lane's query dims and the row's sums of squares, then (inside
+  //    attn_keys) the first keys' loads, then the operand is formed
+  const float* qp = a.q + (((int64_t)row * a.nKv + kvh) * a.nq + qr) * HD + 8 * gq;
+  f32x4 qv[NS][2];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    qv[s][0] = *(const f32x4*)(qp + 32 * s);
+    qv[s][1] = *(const f32x4*)(qp + 32 * s + 4);
+  }
+  float qss = 0.f;
+#pragma unroll
+  for (int p = 0; p < HJ; ++p) qss += a.ssq[(int64_t)(head * HJ + p) * a.M + row * a.gamma + g];
+  const int key = tid & (ATT_KEYS - 1);
+  float sk = 0.f;
+  if (blk) {
+    const int kq = min(key, a.gamma - 1);
+#pragma unroll
+    for (int p = 0; p < HJ; ++p) sk += a.ssq[(int64_t)((a.nH + kvh) * HJ + p) * a.M + row * a.gamma + kq];
+  }
+  bf16x8 qh[NS], ql[NS];
+  auto prep = [&]() {
+    const float r = 1.f / sqrtf(qss / HD + a.eps);
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      float t[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        t[e] = qv[s][0][e] * r;
+        t[4 + e] = qv[s][1][e] * r;
+      }
+      split8(t, qh[s], ql[s]);
+    }
+  };
+
+  f32x4 o[NTW];
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_part = 0.f;
+  if (blk) {
+    const int64_t off = ((int64_t)row * a.nKv + kvh) * a.gamma * HD;
+    attn_keys<HD, false, NTH, NTW>(a.kb + off, a.vb + off, j0, j1, 1.f / sqrtf(sk / HD + a.eps), prep, qh, ql, o, 0,
+                                   m_run, l_part, Ks, Vt);
+  } else {
+    const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
+    const char* kb = (const char*)a.row[row].k + kvoff;
+    const char* vb = (const char*)a.row[row].v + kvoff;
+    attn_keys<HD, KVB, NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, 0, m_run, l_part, Ks, Vt);
+  }
+
+  float l = l_part;
+  l += __shfl_xor(l, 16);
+  l += __shfl_xor(l, 32);
+  const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qr;
+#pragma unroll
+  for (int t = 0; t < NTW; ++t) *(f32x4*)&a.opart[base * HD + 16 * t + 4 * gq] = o[t];
+  if (gq == 0) {
+    a.ml[base * 2] = m_run;
+    a.ml[base * 2 + 1] = l;
+  }
+}
+
+bool attn_wide_ok(int nq, int hd) {
+  const int nqt = nq / 16;
+  if (nq % 16 != 0 || (nqt != 2 && nqt != 4 && nqt != 8)) return false;
+  if (hd != 64 && hd != 128 && hd != 256) return false;
+  // at most two staging items per thread (more spill registers)
+  const int items = ATT_KEYS * (hd / 8), nth = 64 * nqt;
+  return items % nth == 0 && items >= nth && items <= 2 * nth;
+}
+
+hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st) {
+  if (!attn_wide_ok(a.nq, a.hd)) return hipErrorInvalidValue;
+  const dim3 grid(nsplit, a.nKv);
+  const int nqt = a.nq / 16;
+#define DSP_WIDE(H, Q)                                                                                    \
+  if (kv_bf16) hipLaunchKernelGGL((k_attn_wide<H, true, Q>), grid, dim3(64 * Q), 0, st, a);              \
+  else hipLaunchKernelGGL((k_attn_wide<H, false, Q>), grid, dim3(64 * Q), 0, st, a);
+  if (a.hd == 64) {
+    if (nqt == 2) { DSP_WIDE(64, 2) }
+    else { DSP_WIDE(64, 4) }
+  } else if (a.hd == 128) {
+    if (nqt == 4) { DSP_WIDE(128, 4) }
+    else { DSP_WIDE(128, 8) }
+  } else { DSP_WIDE(256, 8) }
+#undef DSP_WIDE
+  return hipGetLastError();
 }
 
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st) {

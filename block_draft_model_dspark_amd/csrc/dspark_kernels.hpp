@@ -187,6 +187,10 @@ hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const f
                            hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
+// one workgroup per (row, split, kv head) with every query row (nq = 32, 64
+// or 128 rows, staging layout permitting)
+bool attn_wide_ok(int nq, int hd);
+hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);

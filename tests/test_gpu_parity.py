@@ -178,6 +178,23 @@ def test_ragged_rows_small(gpu_lib):
     assert checked >= 40
 
 
+def test_wide_attention_ragged_rows(gpu_lib):
+    """Contexts long enough in total (>= 2048 keys) for the attention kernel
+    that holds every query row of a kv head per workgroup: an empty context,
+    a single key, lengths off the 32-key chunk and the split boundaries."""
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=4096, mask_token_id=4095)
+    w = synth.Workload("wide_attn", cfg, rows=5, ctx_lens=(0, 1, 37, 1300, 2100))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(5):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 40
+
+
 def test_rows_a32_ragged_full_size(gpu_lib):
     """32 rows, context lengths uniform in [1024, 4096], stored per row."""
     w = synth.WORKLOADS["rows_a32"]
