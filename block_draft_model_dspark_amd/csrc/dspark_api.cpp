@@ -119,6 +119,7 @@ struct GemmPlan {
   int tall = TALL_NONE;  // tiled path over many rows: output tile
   int np = 0;            // tiled path: bf16 input planes (1: bf16 rows as they are; 2: hi + lo)
   size_t xbytes = 0;     // tiled path: the input planes (np == 2)
+  size_t tbytes = 0;     // tiled path: partial products of a split K (S > 1)
 };
 
 GemmPlan plan_gemm_mt(int wk, int xmode, int M, int N, int K, int group_cols, int mt) {
@@ -162,17 +163,28 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols, int t
       (xmode != XM_NORM || K <= 256 * 64) && (group_cols == 0 || (group_cols <= 256 && N % group_cols == 0))) {
     GemmPlan p{};
     p.mt = 1;
-    p.S = 1;
     p.kc = 0;
-    p.kslice = K;
     p.xmode = xmode;
     p.pbytes = 0;
     p.cwords = 0;
-    // 128 x 128 tiles when they still give most CUs a tile, else 64 x 64
+    // 128 x 128 tiles when they still give most CUs a tile, else 64 x 64;
+    // fewer than 512 tiles split K (not the context projection, whose
+    // epilogue reads the product in place) into slices of an even number of
+    // 64-wide steps, for several workgroups per CU
     const int64_t tiles128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
     p.tall = tiles128 >= 200 ? TALL_128 : TALL_64;
+    const int bt = p.tall == TALL_128 ? 128 : 64;
+    const int64_t tiles = (int64_t)ceil_div(M, bt) * ceil_div(N, bt);
+    const int steps = K / 64;
+    int S = 1;
+    if (tiles < 512 && group_cols == 0) S = (int)std::min<int64_t>(4, (768 + tiles - 1) / tiles);
+    S = std::max(1, std::min(S, steps / 2));
+    const int sl = 2 * ceil_div(ceil_div(steps, S), 2);  // steps per slice, even
+    p.kslice = std::min(K, 64 * sl);
+    p.S = ceil_div(K, p.kslice);
     p.np = xmode == XM_BF16 ? 1 : 2;
     p.xbytes = p.np == 2 ? (size_t)2 * M * K * 2 : 0;
+    p.tbytes = p.S > 1 ? (size_t)p.S * M * N * 4 : 0;
     return p;
   }
   if (group_cols > 0 && wk == WK_BF16 && xmode == XM_BF16 && M >= 32) {
@@ -212,12 +224,20 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
   t.M = a.M;
   t.N = a.N;
   t.K = a.K;
+  t.kslice = p.kslice;
   t.nseg = a.nseg;
   for (int i = 0; i < MAX_SEG; ++i) t.seg[i] = a.seg[i];
   // the product goes where the epilogue's own output goes when the epilogue
   // only reads it back in place (row statistics, softcap) or reads it from
-  // there (context K/V); q|k and gate|up take the separate buffer
-  if (epi == EPI_SUMS) {
+  // there (context K/V); q|k and gate|up, and the partial products of a
+  // split K, take the separate buffer
+  t.tstride = 0;
+  if (p.S > 1) {
+    if (!tb.T || epi == EPI_KV) return hipErrorInvalidValue;
+    t.T = tb.T;
+    t.ldt = a.N;
+    t.tstride = (int64_t)a.M * a.N;
+  } else if (epi == EPI_SUMS) {
     t.T = e.Y;
     t.ldt = e.ldy;
   } else if (epi == EPI_KV || epi == EPI_LM) {
@@ -228,9 +248,9 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.T = tb.T;
     t.ldt = a.N;
   }
-  hipError_t r = launch_tall(t, p.tall, p.np, st);
+  hipError_t r = launch_tall(t, p.tall, p.np, p.S, st);
   if (r != hipSuccess) return r;
-  return launch_gemm_epi(a, e, epi, t.T, t.ldt, st);
+  return launch_gemm_epi(a, e, epi, t.T, t.ldt, p.S, t.tstride, st);
 }
 
 GemmSeg seg_of(const Mat& w, int n0) {
@@ -319,14 +339,14 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.lohi = take((size_t)M * NC * 8);
   d.xop = take(std::max({d.qk.xbytes, d.o.xbytes, d.gu.xbytes, d.dn.xbytes, d.lm.xbytes, (size_t)4}));
   d.T = take(std::max({d.qk.tall ? (size_t)M * (nH + nKv) * hd * 4 : 0, d.gu.tall ? (size_t)M * 2 * I * 4 : 0,
-                       (size_t)4}));
+                       d.qk.tbytes, d.o.tbytes, d.gu.tbytes, d.dn.tbytes, d.lm.tbytes, (size_t)4}));
   d.total = off;
   return d;
 }
 
 // ---- projection workspace layout -----------------------------------------
 struct ProjLayout {
-  size_t P, Y, C, sums, cnt, xop, total;
+  size_t P, Y, C, sums, cnt, xop, T, total;
   GemmPlan fc, kp;
   size_t cwords;
   int lay_per_gemm;
@@ -349,6 +369,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   }
   p.kp = plan_gemm(c.weight_dtype, feats ? XM_NORM : xmode_in(m), M, Nk, H, hd, m->tall_rows);
   size_t xbytes = std::max(p.fc.xbytes, p.kp.xbytes);
+  const size_t tbytes = p.fc.tbytes;  // (the context projection never splits K on the tiled path)
   pbytes = std::max(pbytes, p.kp.pbytes);
   p.cwords = std::max(p.cwords, p.kp.cwords);
   // a last, smaller group of layers is planned on its own (it may split K)
@@ -371,6 +392,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
   p.cnt = take(p.cwords * 4);
   p.xop = take(std::max(xbytes, (size_t)4));
+  p.T = take(std::max(tbytes, (size_t)4));
   p.total = off;
   return p;
 }
@@ -607,6 +629,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
   TallBufs tb;
   tb.xop = (uint16_t*)(ws + p.xop);
+  tb.T = (float*)(ws + p.T);
   NormIn nin{};
   if (feats) {
     // fc rows and their statistics; k_proj reads hidden_norm(fc x)

@@ -973,11 +973,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
 }
 
 // The epilogue of a GEMM whose product the tiled kernel (dspark_tall.hip)
-// already wrote to T (row pitch ldt): one 16 x 64 tile per workgroup, the
-// product read into the accumulator layout of the weight-streaming kernel
-// (wave w: columns wave_col(cb, w) + lane mod 16, rows 4 (lane / 16) + i).
+// already wrote to T (row pitch ldt; S partial planes tstride apart, added
+// here in slice order): one 16 x 64 tile per workgroup, the product read into
+// the accumulator layout of the weight-streaming kernel (wave w: columns
+// wave_col(cb, w) + lane mod 16, rows 4 (lane / 16) + i).
 template <int EPI>
-__global__ __launch_bounds__(256) void k_gemm_epi(const GemmArgs g, const EpiArgs e, const float* T, int64_t ldt) {
+__global__ __launch_bounds__(256) void k_gemm_epi(const GemmArgs g, const EpiArgs e, const float* T, int64_t ldt,
+                                                  int S, int64_t tstride) {
   __shared__ __align__(16) float ep[4 * 16 * 16];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const int cb = blockIdx.x, mbase = blockIdx.y * 16;
@@ -985,6 +987,13 @@ __global__ __launch_bounds__(256) void k_gemm_epi(const GemmArgs g, const EpiArg
   f32x4 acc[1];
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[0][i] = T[(int64_t)min(mbase + 4 * gq + i, g.M - 1) * ldt + n];
+  for (int s = 1; s < S; ++s) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = T[s * tstride + (int64_t)min(mbase + 4 * gq + i, g.M - 1) * ldt + n];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[0][i] += v[i];
+  }
   if constexpr (EPI == EPI_GELU) epi_gelu<1, 4>(g, e, acc, mbase, cb, ep, 0);
   else if constexpr (EPI == EPI_QK) epi_qk<1>(g, e, acc, mbase, cb, ep);
   else if constexpr (EPI == EPI_SUMS) epi_sums<1>(g, e, acc, mbase, cb, n, ep);
@@ -1002,18 +1011,18 @@ __global__ __launch_bounds__(256) void k_kv_epi(const GemmArgs g, const EpiArgs 
   epi_kv<1, 256>(g, e, mbase, min(g.M, mbase + 16), blockIdx.x, rinv, rcs);
 }
 
-hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt,
-                           hipStream_t st) {
+hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt, int S,
+                           int64_t tstride, hipStream_t st) {
   const int mblocks = (a.M + 15) / 16;
-  if (a.N % 64 != 0) return hipErrorInvalidValue;
+  if (a.N % 64 != 0 || S < 1) return hipErrorInvalidValue;
   const dim3 grid(a.N / 64, mblocks);
   switch (epi) {
-    case EPI_GELU: hipLaunchKernelGGL(k_gemm_epi<EPI_GELU>, grid, dim3(256), 0, st, a, e, T, ldt); break;
-    case EPI_QK: hipLaunchKernelGGL(k_gemm_epi<EPI_QK>, grid, dim3(256), 0, st, a, e, T, ldt); break;
-    case EPI_SUMS: hipLaunchKernelGGL(k_gemm_epi<EPI_SUMS>, grid, dim3(256), 0, st, a, e, T, ldt); break;
-    case EPI_LM: hipLaunchKernelGGL(k_gemm_epi<EPI_LM>, grid, dim3(256), 0, st, a, e, T, ldt); break;
+    case EPI_GELU: hipLaunchKernelGGL(k_gemm_epi<EPI_GELU>, grid, dim3(256), 0, st, a, e, T, ldt, S, tstride); break;
+    case EPI_QK: hipLaunchKernelGGL(k_gemm_epi<EPI_QK>, grid, dim3(256), 0, st, a, e, T, ldt, S, tstride); break;
+    case EPI_SUMS: hipLaunchKernelGGL(k_gemm_epi<EPI_SUMS>, grid, dim3(256), 0, st, a, e, T, ldt, S, tstride); break;
+    case EPI_LM: hipLaunchKernelGGL(k_gemm_epi<EPI_LM>, grid, dim3(256), 0, st, a, e, T, ldt, S, tstride); break;
     case EPI_KV: {
-      if (e.group_cols != e.hd || e.hd > 256 || a.N % e.hd != 0) return hipErrorInvalidValue;
+      if (S != 1 || e.group_cols != e.hd || e.hd > 256 || a.N % e.hd != 0) return hipErrorInvalidValue;
       hipLaunchKernelGGL(k_kv_epi, dim3(a.N / e.hd, mblocks), dim3(256), 0, st, a, e);
       break;
     }

@@ -108,8 +108,9 @@ struct TallArgs {
   int M, N, K;        // K a multiple of 64
   int nseg;
   GemmSeg seg[MAX_SEG];  // bf16 weights [rows, K] per column segment
-  float* T;
-  int64_t ldt;
+  int kslice;         // K range per blockIdx.z (a multiple of 64)
+  float* T;           // partial product of slice z at T + z * tstride
+  int64_t ldt, tstride;
 };
 
 // per-row data of a draft round
@@ -180,11 +181,12 @@ hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, 
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
 size_t gemm_counter_words(int M, int N, int mt, int group_cols);
 hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t plane, hipStream_t st);
-hipError_t launch_tall(const TallArgs& t, int tile, int np, hipStream_t st);
-// the epilogue of a GEMM whose product is in T (row pitch ldt); EPI_KV reads
-// it from e.Y (pitch N)
-hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt,
-                           hipStream_t st);
+hipError_t launch_tall(const TallArgs& t, int tile, int np, int S, hipStream_t st);
+// the epilogue of a GEMM whose product is the sum of S partial planes in T
+// (row pitch ldt, plane stride tstride); EPI_KV reads it from e.Y (pitch N,
+// S == 1)
+hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt, int S,
+                           int64_t tstride, hipStream_t st);
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st);
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 // one workgroup per (row, split, kv head) with every query row (nq = 32, 64

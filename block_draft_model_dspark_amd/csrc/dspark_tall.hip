@@ -12,8 +12,9 @@
 //      sum carries the fp32 value; bf16 input rows are used as they are.
 //   2. k_tall: T[m, n] = sum over planes of X_p[m, :] . W[n, :] in fp32,
 //      BM x BN output tiles, both operands staged through LDS in 64-wide K
-//      steps (the next step's global loads in flight during this step's
-//      MFMAs), four waves of (BM/2) x (BN/2).
+//      steps (the global loads of the next two steps in flight during this
+//      step's MFMAs), four waves of (BM/2) x (BN/2).  Few output tiles split
+//      K over blockIdx.z into partial planes that the epilogue adds.
 //   3. the GEMM's own epilogue (norm statistics, q|k RoPE, GELU gate, logit
 //      softcap, context K/V) reads T: k_gemm_epi / k_kv_epi.
 #include "dspark_kernels.hpp"
@@ -123,7 +124,7 @@ constexpr int TLD = TBK + 8;   // LDS row pitch (bf16): 16 consecutive rows of o
                                // 16-byte column fall on distinct banks
 
 template <int BM, int BN, int NP>
-__global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
+__global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
   constexpr int AIT = BM * (TBK / 8) / 256, BIT = BN * (TBK / 8) / 256;  // 16-byte items per thread
   static_assert(AIT >= 1 && BIT >= 1, "tile too small for 256 threads");
@@ -132,6 +133,7 @@ __global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  const int kb = blockIdx.z * t.kslice, ke = min(t.K, kb + t.kslice);  // this slice of K (multiples of 64)
 
   // this thread's rows of the two tiles (clamped: rows past M or N repeat
   // the last one and are never stored) and the weight segment of each
@@ -159,26 +161,33 @@ __global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
     }
     bp[j] = (const uint16_t*)w + (int64_t)(n - nb) * t.K + 8 * c8;
   }
-  u32x4 ra[NP][AIT], rb[BIT];
-  auto load = [&](int k0) {
+  // two register sets: the steps k and k + 64 are loading while step k - 64
+  // is multiplied (a step past the slice reloads the slice's last one, so
+  // every thread always has the same loads in flight)
+  struct Stage {
+    u32x4 a[NP][AIT], b[BIT];
+  };
+  Stage st0, st1;
+  auto load = [&](Stage& r, int k0) {
+    k0 = min(k0, ke - TBK);
 #pragma unroll
     for (int p = 0; p < NP; ++p)
 #pragma unroll
-      for (int j = 0; j < AIT; ++j) ra[p][j] = *(const u32x4*)(ap[j] + p * t.plane + k0);
+      for (int j = 0; j < AIT; ++j) r.a[p][j] = *(const u32x4*)(ap[j] + p * t.plane + k0);
 #pragma unroll
-    for (int j = 0; j < BIT; ++j) rb[j] = *(const u32x4*)(bp[j] + k0);
+    for (int j = 0; j < BIT; ++j) r.b[j] = *(const u32x4*)(bp[j] + k0);
   };
-  auto store = [&]() {
+  auto store = [&](const Stage& r) {
 #pragma unroll
     for (int j = 0; j < AIT; ++j) {
-      const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
+      const int it = tid + 256 * j, rr = it >> 3, c8 = it & 7;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) *(u32x4*)&As[p][r * TLD + 8 * c8] = ra[p][j];
+      for (int p = 0; p < NP; ++p) *(u32x4*)&As[p][rr * TLD + 8 * c8] = r.a[p][j];
     }
 #pragma unroll
     for (int j = 0; j < BIT; ++j) {
-      const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
-      *(u32x4*)&Bs[r * TLD + 8 * c8] = rb[j];
+      const int it = tid + 256 * j, rr = it >> 3, c8 = it & 7;
+      *(u32x4*)&Bs[rr * TLD + 8 * c8] = r.b[j];
     }
   };
 
@@ -188,13 +197,7 @@ __global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  for (int k0 = 0; k0 < t.K; k0 += TBK) {
-    __syncthreads();  // every wave is done reading the previous step
-    store();
-    __syncthreads();
-    // next step's loads (the last step reloads itself: a fixed load count)
-    load(k0 + TBK < t.K ? k0 + TBK : k0);
+  auto step = [&]() {
 #pragma unroll
     for (int s = 0; s < TBK / 32; ++s) {
       bf16x8 bfr[FN];
@@ -211,7 +214,29 @@ __global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(afr, bfr[j], acc[i][j]);
         }
     }
+  };
+  load(st0, kb);
+  load(st1, kb + TBK);
+  int k0 = kb;
+  for (; k0 + 2 * TBK <= ke; k0 += 2 * TBK) {
+    __syncthreads();  // every wave is done reading the previous step
+    store(st0);
+    __syncthreads();
+    load(st0, k0 + 2 * TBK);
+    step();
+    __syncthreads();
+    store(st1);
+    __syncthreads();
+    load(st1, k0 + 3 * TBK);
+    step();
   }
+  if (k0 < ke) {  // an odd last step (uniform)
+    __syncthreads();
+    store(st0);
+    __syncthreads();
+    step();
+  }
+  float* const T = t.T + blockIdx.z * t.tstride;
 
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -221,7 +246,7 @@ __global__ __launch_bounds__(256) void k_tall(const TallArgs t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int m = m0 + WM * wm + 16 * i + 4 * gq + q;
-        if (m < t.M && n < t.N) t.T[(int64_t)m * t.ldt + n] = acc[i][j][q];
+        if (m < t.M && n < t.N) T[(int64_t)m * t.ldt + n] = acc[i][j][q];
       }
     }
 }
@@ -238,10 +263,12 @@ hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t pla
   return hipGetLastError();
 }
 
-hipError_t launch_tall(const TallArgs& t, int tile, int np, hipStream_t st) {
-  if (t.K % TBK != 0 || t.M <= 0 || t.N <= 0 || t.nseg < 1 || t.nseg > MAX_SEG) return hipErrorInvalidValue;
+hipError_t launch_tall(const TallArgs& t, int tile, int np, int S, hipStream_t st) {
+  if (t.K % TBK != 0 || t.kslice % TBK != 0 || t.kslice <= 0 || (int64_t)S * t.kslice < t.K ||
+      (int64_t)(S - 1) * t.kslice >= t.K || t.M <= 0 || t.N <= 0 || t.nseg < 1 || t.nseg > MAX_SEG)
+    return hipErrorInvalidValue;
   const int bm = tile == TALL_128 ? 128 : 64, bn = bm;
-  const dim3 grid((t.N + bn - 1) / bn, (t.M + bm - 1) / bm);
+  const dim3 grid((t.N + bn - 1) / bn, (t.M + bm - 1) / bm, S);
   if (tile == TALL_128) {
     if (np == 1) hipLaunchKernelGGL((k_tall<128, 128, 1>), grid, dim3(256), 0, st, t);
     else hipLaunchKernelGGL((k_tall<128, 128, 2>), grid, dim3(256), 0, st, t);
