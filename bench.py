@@ -77,8 +77,8 @@ def gemm_bytes(cfg, M_round, M_ctx):
 
 def attn_bytes(cfg, lens):
     """Algorithmic bytes of the attention launches of one round: every row's
-    context K and V once in the act dtype (bf16), per layer."""
-    return sum(lens) * cfg.nKv * cfg.hd * 2 * 2
+    context K and V once in the act dtype (bf16), in each of the layers."""
+    return cfg.L * sum(lens) * cfg.nKv * cfg.hd * 2 * 2
 
 
 def gemm_flops_round(cfg, M_round):

@@ -285,9 +285,14 @@ int attn_split(int64_t total_ctx) {
 }
 
 // the same for the wide kernel (every query row of a kv head per
-// workgroup): about 384 context splits, fewer partial outputs to merge
-int attn_split_wide(int64_t total_ctx) {
-  int64_t s = (total_ctx + 383) / 384;
+// workgroup, one workgroup per compute unit): the context splits and the A
+// block splits fit the 256 compute units of an MI355X in one round (each row
+// adds up to one short tail split), so no second round runs at part
+// occupancy, and fewer partial outputs are merged
+constexpr int ATTN_CUS = 256;
+int attn_split_wide(int64_t total_ctx, int A) {
+  const int64_t slots = std::max<int64_t>(ATTN_CUS - 2 * (int64_t)A, ATTN_CUS / 2);
+  int64_t s = (total_ctx + slots - 1) / slots;
   s = (s + ATT_KEYS - 1) / ATT_KEYS * ATT_KEYS;
   return (int)std::max<int64_t>(ATT_KEYS, s);
 }
@@ -761,7 +766,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   // attention split plan: context splits of `split` keys, then the block split
   const int64_t total_ctx = total_keys - (int64_t)A * G;
   const bool wide = total_ctx >= ATTN_WIDE_MIN_KEYS && attn_wide_ok(m->nq, hd);
-  const int split = wide ? attn_split_wide(total_ctx) : attn_split(total_ctx);
+  const int split = wide ? attn_split_wide(total_ctx, A) : attn_split(total_ctx);
   AttnArgs at{};
   MergeArgs mg{};
   int nsplit = 0;
@@ -786,7 +791,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   at.kb = (const float*)(ws + d.kb);
   at.vb = (const float*)(ws + d.vb);
   at.ssq = (const float*)(ws + d.ssq);
-  at.opart = (float*)(ws + d.opart);
+  at.opart = ws + d.opart;
   at.ml = (float*)(ws + d.ml);
   mg.A = A;
   mg.gamma = G;
@@ -795,6 +800,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   mg.nH = nH;
   mg.hd = hd;
   mg.opart = at.opart;
+  mg.part_f16 = c.act_dtype == DSPARK_BF16 ? 1 : 0;  // the attention kernels' KVB variant
   mg.ml = at.ml;
   mg.O = O;
   mg.ldo = d.ldo;

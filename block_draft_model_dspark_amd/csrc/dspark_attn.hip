@@ -200,6 +200,24 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
   }
 }
 
+// this lane's output tiles t0.. (dims 16 t + 4 (lane / 16) .. + 3 of its
+// query) at element offset off: a bf16 cache stores fp16 O / l (bounded by
+// the largest |v|, so in range, and half the bytes of fp32), an fp32 cache
+// the fp32 sums themselves
+template <bool F16, int NTW>
+__device__ __forceinline__ void store_part(void* opart, int64_t off, int t0, const f32x4 (&o)[NTW], float l) {
+  if constexpr (F16) {
+    const float rl = 1.f / l;
+#pragma unroll
+    for (int t = 0; t < NTW; ++t)
+      *(u32x2*)((uint16_t*)opart + off + 16 * (t0 + t)) =
+          u32x2{pack_f16x2(o[t][0] * rl, o[t][1] * rl), pack_f16x2(o[t][2] * rl, o[t][3] * rl)};
+  } else {
+#pragma unroll
+    for (int t = 0; t < NTW; ++t) *(f32x4*)((float*)opart + off + 16 * (t0 + t)) = o[t];
+  }
+}
+
 template <int HD, bool KVB>
 __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
   constexpr int NS = HD / 32, NTW = HD / 64, HJ = HD / 64;
@@ -301,8 +319,7 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
   const int qrow = q0 + ln;
   if (qrow < a.nq) {
     const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qrow;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) *(f32x4*)&a.opart[base * HD + 16 * (t0 + t) + 4 * gq] = o[t];
+    store_part<KVB>(a.opart, base * HD + 4 * gq, t0, o, l);
     if (wave == 0 && gq == 0) {
       a.ml[base * 2] = m_run;
       a.ml[base * 2 + 1] = l;
@@ -387,8 +404,7 @@ __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qr;
-#pragma unroll
-  for (int t = 0; t < NTW; ++t) *(f32x4*)&a.opart[base * HD + 16 * t + 4 * gq] = o[t];
+  store_part<KVB>(a.opart, base * HD + 4 * gq, 0, o, l);
   if (gq == 0) {
     a.ml[base * 2] = m_run;
     a.ml[base * 2 + 1] = l;

@@ -147,14 +147,17 @@ struct AttnArgs {
   int A, gamma, nKv, nH, nq, split, M, hd;
   float eps;
   const float* q; const float* kb; const float* vb; const float* ssq;
-  float* opart;       // [nsplit, nKv, nq, hd] unnormalised
+  // [nsplit, nKv, nq, hd]: fp32 unnormalised for an fp32 cache; for a bf16
+  // cache, fp16 of O / sum (|O / sum| <= max |v|, unit-RMS value rows)
+  void* opart;
   float* ml;          // [nsplit, nKv, nq, 2] (max, sum)
 };
 
 struct MergeArgs {
   int split_off[MAX_ROWS + 1];
   int A, gamma, nKv, nq, nH, hd;
-  const float* opart; const float* ml;
+  int part_f16;       // partials are fp16 O / sum (else fp32 unnormalised)
+  const void* opart; const float* ml;
   float* O;           // [A*gamma, nH*hd], row pitch ldo
   int64_t ldo;
 };

@@ -79,26 +79,98 @@ __global__ __launch_bounds__(256) void k_zero(unsigned* p, int64_t n) {
 }
 
 // ---------------------------------------------------------------------------
-// split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s
-// (running max over passes of MERGE_SB splits).  grid A*nKv*nq, block hd (>= 64)
+// split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s with
+// M = max_s m_s; F16: the partials hold O_s / l_s in fp16 (weight e^{m_s-M} l_s).
+// Each thread owns 8 head dims of one query row (hd / 8 threads per row), so
+// a split's partial row is one 16-byte (fp16) or 32-byte (fp32) load per
+// thread, eight splits in flight.  grid ceil(A*nKv*nq / (256 / (hd / 8))), block 256
 // ---------------------------------------------------------------------------
-constexpr int MERGE_SB = 32;  // splits per pass: their partial rows are loaded first, then (max, sum)
+constexpr int MERGE_SB = 8;          // splits loaded per batch
+constexpr int MERGE_FEW_ROWS = 512;  // up to this many query rows: k_merge_rows
 
+template <bool F16>
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  __shared__ float2 wl[MERGE_SB];
+  const int tid = threadIdx.x, lpq = a.hd >> 3;
+  const int nrows = a.A * a.nKv * a.nq;
+  const int qg = blockIdx.x * (256 / lpq) + tid / lpq;
+  if (qg >= nrows) return;
+  const int d0 = 8 * (tid - (tid / lpq) * lpq);
+  const int j = qg % a.nq, kvh = (qg / a.nq) % a.nKv, row = qg / (a.nq * a.nKv);
+  const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
+  const float2* ml = (const float2*)a.ml;
+  auto mli = [&](int s) { return ((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + j; };
+  float mx = -INFINITY;
+  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[mli(s)].x);
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, den = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += MERGE_SB) {
+    u32x4 raw[MERGE_SB][F16 ? 1 : 2];
+    float2 wv[MERGE_SB];
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q) {
+      const int s = c0 + min(q, ns - c0 - 1);
+      const int64_t i = mli(s) * a.hd + d0;
+      if constexpr (F16) {
+        raw[q][0] = *(const u32x4*)((const uint16_t*)a.opart + i);
+      } else {
+        raw[q][0] = *(const u32x4*)((const float*)a.opart + i);
+        raw[q][1] = *(const u32x4*)((const float*)a.opart + i + 4);
+      }
+      wv[q] = ml[mli(s)];
+    }
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q)
+      if (c0 + q < ns) {
+        const float w = expf(wv[q].x - mx), wl = w * wv[q].y;
+        den += wl;
+        float v[8];
+        if constexpr (F16) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[2 * e] = f16_to_f32((uint16_t)(raw[q][0][e] & 0xFFFFu));
+            v[2 * e + 1] = f16_to_f32((uint16_t)(raw[q][0][e] >> 16));
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            v[e] = __uint_as_float(raw[q][0][e]);
+            v[4 + e] = __uint_as_float(raw[q][1][e]);
+          }
+        }
+        const float ws = F16 ? wl : w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) num[e] += ws * v[e];
+      }
+  }
+  const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
+  const int h = kvh * rep + hl;
+  const float rd = 1.f / den;
+  float* dst = a.O + ((int64_t)row * a.gamma + g) * a.ldo + h * a.hd + d0;
+  *(f32x4*)dst = f32x4{num[0] * rd, num[1] * rd, num[2] * rd, num[3] * rd};
+  *(f32x4*)(dst + 4) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
+}
+
+// Few query rows (a single draft row): one workgroup per query row, one
+// thread per head dim, the splits in passes of MERGE_RB with every partial
+// load of a pass in flight.  grid A*nKv*nq, block hd (>= 64)
+constexpr int MERGE_RB = 32;
+
+template <bool F16>
+__global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
+  __shared__ float2 wl[MERGE_RB];
   __shared__ float cmax;
   const int idx = blockIdx.x, tid = threadIdx.x;
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
   const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
   float num = 0.f, den = 0.f, mrun = -INFINITY;
-  for (int c0 = 0; c0 < ns; c0 += MERGE_SB) {
-    const int cn = min(MERGE_SB, ns - c0);
-    float o[MERGE_SB];
+  for (int c0 = 0; c0 < ns; c0 += MERGE_RB) {
+    const int cn = min(MERGE_RB, ns - c0);
+    float o[MERGE_RB];
 #pragma unroll
-    for (int q = 0; q < MERGE_SB; ++q) {
+    for (int q = 0; q < MERGE_RB; ++q) {
       const int s = s0 + c0 + min(q, cn - 1);
-      o[q] = a.opart[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
+      const int64_t i = (((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid;
+      o[q] = F16 ? f16_to_f32(((const uint16_t*)a.opart)[i]) : ((const float*)a.opart)[i];
     }
     const float2 v = ml[((int64_t)(s0 + c0 + min(tid, cn - 1)) * a.nKv + kvh) * a.nq + j];
     if (tid < 64) {
@@ -117,9 +189,9 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
     mrun = mnew;
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < MERGE_SB; ++q)
+    for (int q = 0; q < MERGE_RB; ++q)
       if (q < cn) {
-        num += wl[q].x * o[q];
+        num += (F16 ? wl[q].y : wl[q].x) * o[q];
         den += wl[q].y;
       }
     __syncthreads();
@@ -440,7 +512,17 @@ hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st) {
   return hipGetLastError();
 }
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
-  hipLaunchKernelGGL(k_merge, dim3(a.A * a.nKv * a.nq), dim3(a.hd), 0, st, a);
+  const int nrows = a.A * a.nKv * a.nq;
+  if (nrows <= MERGE_FEW_ROWS) {
+    // few rows: a workgroup per row keeps enough of the chip busy
+    if (a.part_f16) hipLaunchKernelGGL(k_merge_rows<true>, dim3(nrows), dim3(a.hd), 0, st, a);
+    else hipLaunchKernelGGL(k_merge_rows<false>, dim3(nrows), dim3(a.hd), 0, st, a);
+    return hipGetLastError();
+  }
+  const int per = 256 / (a.hd / 8);  // query rows per workgroup
+  const dim3 grid((nrows + per - 1) / per);
+  if (a.part_f16) hipLaunchKernelGGL(k_merge<true>, grid, dim3(256), 0, st, a);
+  else hipLaunchKernelGGL(k_merge<false>, grid, dim3(256), 0, st, a);
   return hipGetLastError();
 }
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {

@@ -161,6 +161,24 @@ def test_full_bf16_round(gpu_lib, markov_active):
     assert checked >= 8
 
 
+def test_tiny_f32_many_ragged_rows(gpu_lib):
+    """fp32 model, 20 rows (640 query rows: the merge that gives each thread
+    eight head dims of a row, fp32 partials), ragged contexts from empty to
+    several 32-key chunks, 2079 context keys in total (the attention kernel
+    that holds every query row of a kv head); Markov head active; bar 1e-4."""
+    w0 = synth.WORKLOADS["tiny_f32"]
+    lens = [0, 1, 2, 7, 31, 32, 33, 40, 63, 64, 65, 96, 100, 127, 128, 129, 150, 200, 255, 556]
+    w = synth.Workload("tiny_many_rows", w0.model, rows=len(lens), ctx_lens=tuple(lens))
+    case = Case(w0.model, markov_active=True, with_fc=False)
+    o_rows, k_rows, v_rows = case.kv_rows_from_oracle([_ctx(w, a, L) for a, L in enumerate(lens)], [0] * len(lens))
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(len(lens)):
+        assert rel_err(logits[a], ref["logits"][a]) <= 1e-4, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 40
+
+
 def test_ragged_rows_small(gpu_lib):
     """Rows with different context lengths, including an empty context, a
     single row and lengths off every tile boundary; Markov head active."""
