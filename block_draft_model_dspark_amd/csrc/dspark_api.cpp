@@ -777,6 +777,18 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   }
   at.split_off[A] = nsplit;
   if (nsplit > d.nsplit_max) return fail(DSPARK_ERR_SHAPE, "attention splits %d exceed the plan", nsplit);
+  // wide kernel: the splits of row a on XCD a mod 8 when that keeps the
+  // eight XCDs' shares within a quarter of the even share
+  int attn_grid = nsplit;
+  if (wide && A >= 8) {
+    int load[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int a = 0; a < A; ++a) load[a & 7] += at.split_off[a + 1] - at.split_off[a];
+    const int mx = *std::max_element(load, load + 8);
+    if (4 * 8 * (int64_t)mx <= 5 * (int64_t)nsplit) {
+      at.xcd_rows = 1;
+      attn_grid = 8 * mx;
+    }
+  }
   std::memcpy(mg.split_off, at.split_off, sizeof at.split_off);
   at.A = A;
   at.gamma = G;
@@ -891,7 +903,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
       at.row[a].v = v_ctx_dev[l * A + a];
     }
     HIPCHECK(timed("attn", stream, [&] {
-      return wide ? launch_attn_wide(at, c.act_dtype == DSPARK_BF16, nsplit, stream)
+      return wide ? launch_attn_wide(at, c.act_dtype == DSPARK_BF16, attn_grid, stream)
                   : launch_attn(at, c.act_dtype == DSPARK_BF16, nsplit, stream);
     }));
     HIPCHECK(timed("attn_merge", stream, [&] { return launch_merge(mg, stream); }));

@@ -339,9 +339,25 @@ __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
   __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
   __shared__ __align__(16) uint16_t Vt[HD * 40];
 
-  const int sg = blockIdx.x, kvh = blockIdx.y;
-  int row = 0;
-  while (a.split_off[row + 1] <= sg) ++row;
+  const int kvh = blockIdx.y;
+  int sg = blockIdx.x, row = 0;
+  if (a.xcd_rows) {
+    // slot x / 8 among the splits of rows x mod 8, x mod 8 + 8, ...
+    int slot = (int)(blockIdx.x >> 3);
+    sg = -1;
+    for (int r = blockIdx.x & 7; r < a.A; r += 8) {
+      const int n = a.split_off[r + 1] - a.split_off[r];
+      if (slot < n) {
+        sg = a.split_off[r] + slot;
+        row = r;
+        break;
+      }
+      slot -= n;
+    }
+    if (sg < 0) return;  // an idle slot of a less loaded XCD (uniform: no barrier reached)
+  } else {
+    while (a.split_off[row + 1] <= sg) ++row;
+  }
   const int sp = sg - a.split_off[row];
   const bool blk = sp == a.split_off[row + 1] - a.split_off[row] - 1;  // the row's block keys
   const int len = a.len[row];
@@ -422,7 +438,7 @@ bool attn_wide_ok(int nq, int hd) {
 
 hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st) {
   if (!attn_wide_ok(a.nq, a.hd)) return hipErrorInvalidValue;
-  const dim3 grid(nsplit, a.nKv);
+  const dim3 grid(nsplit, a.nKv);  // nsplit: the split count, or 8 * slots per XCD (xcd_rows)
   const int nqt = a.nq / 16;
 #define DSP_WIDE(H, Q)                                                                                    \
   if (kv_bf16) hipLaunchKernelGGL((k_attn_wide<H, true, Q>), grid, dim3(64 * Q), 0, st, a);              \

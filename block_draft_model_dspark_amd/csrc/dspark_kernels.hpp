@@ -145,6 +145,11 @@ struct AttnArgs {
   int len[MAX_ROWS];
   int split_off[MAX_ROWS + 1];  // prefix sum of key splits per row (context splits, then one block split)
   int A, gamma, nKv, nH, nq, split, M, hd;
+  // wide kernel: 0 = workgroup x runs split x; else workgroup x runs slot
+  // x / 8 of the splits of rows x mod 8, x mod 8 + 8, ... (workgroups are
+  // dealt to the eight XCDs in turn, so all splits of a row share one L2 and
+  // its query rows are fetched once), grid 8 * wide_slots
+  int xcd_rows;
   float eps;
   const float* q; const float* kb; const float* vb; const float* ssq;
   // [nsplit, nKv, nq, hd]: fp32 unnormalised for an fp32 cache; for a bf16
