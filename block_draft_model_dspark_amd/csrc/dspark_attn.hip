@@ -152,8 +152,20 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
         const u32x4 z = u32x4{0u, 0u, 0u, 0u};
         *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
         const u32x4 vw = ok ? vv[i] : z;
+        // V^T in 32-bit words of two keys: the lanes of keys 2k and 2k + 1
+        // (adjacent lanes, same dims) swap half their dims, then the even
+        // lane writes dims 0..3 and the odd lane dims 4..7 of the pair
+        const bool odd = key & 1;
+        const uint32_t s0 = odd ? vw[0] : vw[2], s1 = odd ? vw[1] : vw[3];
+        const uint32_t r0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, false);  // lane ^ 1
+        const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
+        const uint32_t m0 = odd ? vw[2] : vw[0], m1 = odd ? vw[3] : vw[1];  // this lane's four dims
+        const int e0 = odd ? 4 : 0;
+        uint32_t* vrow = (uint32_t*)&Vt[(8 * c8 + e0) * VSTR + (key & ~1)];
+        const uint32_t mine[4] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16};
+        const uint32_t part[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) Vt[(8 * c8 + e) * VSTR + key] = half_of(vw, e);
+        for (int e = 0; e < 4; ++e) vrow[e * (VSTR / 2)] = odd ? (part[e] | (mine[e] << 16)) : (mine[e] | (part[e] << 16));
       }
       __syncthreads();
       if (jc + ATT_KEYS < j1) load(jc + ATT_KEYS);
