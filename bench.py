@@ -27,24 +27,38 @@ sys.path.insert(0, ROOT)
 METRIC = "draft blocks/sec (gamma=16) at 1 MI355X; % MFMA / HBM roofline per kernel"
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
-GEMM_SOURCES = ("block_draft_model_dspark_amd/csrc/dspark_gemm.hip",
-                "block_draft_model_dspark_amd/csrc/dspark_common.hpp",
-                "block_draft_model_dspark_amd/csrc/dspark_kernels.hpp")
-# HBM bytes the GEMM launches of one step move, from rocprofv3 FETCH_SIZE and
-# WRITE_SIZE passes over them, each scaled by what the same counter reads for a
-# plain copy of known size (--calibrate-copy-mib).  Valid only for the GEMM
-# sources it was taken on (their sha256): otherwise the traffic is unknown.
-GEMM_TRAFFIC = {"sources_sha256": "2a1ae6133c3326c40b121a987d93ed02936adaad14cc593b4a8c0cd56acd20ef",
-                "bytes_per_step": 713389523}
+CSRC = "block_draft_model_dspark_amd/csrc/"
+# HBM bytes per step of a kernel group, from rocprofv3 FETCH_SIZE and
+# WRITE_SIZE passes over a short run of the same workload, each scaled by what
+# the same counter reads for a plain copy of known size (--calibrate-copy-mib:
+# FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the sources the
+# counters were taken on (their sha256): otherwise the traffic is unknown.
+TRAFFIC = {
+    # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
+    "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
+                  "sha256": "8896025cae467c440c54539c92c416ac076b00b897b434a498adc0cf4e4f3a18",
+                  "bytes_per_step": 713367756},
+    # rows_a32: the 4 wide-attention launches of one round
+    "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
+                  "sha256": "aad7c175ce097a39d9fa6665ac74fb3068619a3874527eebde8a51b4476da755",
+                  "bytes_per_step": 387748326},
+    # rows_a32: the 17 tiled-GEMM launches of one round (their epilogues excluded)
+    "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
+                  "sha256": "64d1e9cab26eee92879a6fbee18c53871fccdfe9c644634353d5e860d2126537",
+                  "bytes_per_step": 2577942425},
+}
 
 
-def sources_sha256():
+def traffic(key):
+    """The recorded bytes per step of a kernel group while its sources are
+    unchanged, else None."""
     import hashlib
+    t = TRAFFIC[key]
     h = hashlib.sha256()
-    for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in t["sources"]:
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
-    return h.hexdigest()
+    return t["bytes_per_step"] if h.hexdigest() == t["sha256"] else None
 
 
 def calibrate_copy(mib, reps):
@@ -235,9 +249,7 @@ def bench_full(args, dsp, synth, torch):
     for k, v in kernels.items():
         if k in roles:
             v["algorithmic_GBs"] = round(roles[k][0] * roles[k][1] / (v["us_per_step"] * 1e3), 1)
-    traffic = None
-    if GEMM_TRAFFIC["sources_sha256"] == sources_sha256():
-        traffic = GEMM_TRAFFIC["bytes_per_step"]
+    traffic_b = traffic("gemm_full")
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -249,7 +261,7 @@ def bench_full(args, dsp, synth, torch):
                    "tokens_per_s": round(value * cfg.gamma, 1)},
         "roofline": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_b,
                      "bytes_per_step": g_bytes, "launches_per_step": g_launch,
                      "us_per_step": round(1e3 * g_ms, 2)},
         "kernels": kernels,
@@ -347,11 +359,11 @@ def bench_rows(args, dsp, synth, torch):
                    "tokens_per_s": round(value * cfg.gamma, 1)},
         "roofline": {"bound": "mfma", "kernel": "k_gemm (bf16 MFMA GEMM, all roles over 512 block rows)",
                      "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic("tall_rows"),
                      "flops_per_step": fl, "us_per_step": round(1e3 * g_ms, 2)},
         "roofline_attn": {"bound": "hbm", "kernel": "ctx++block attention (context K/V streaming)",
                           "achieved": round(ab / (at_us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(ab / (at_us * 1e3) / HBM_PEAK_GBS, 4), "traffic": None,
+                          "frac": round(ab / (at_us * 1e3) / HBM_PEAK_GBS, 4), "traffic": traffic("attn_rows"),
                           "bytes_per_step": ab, "us_per_step": round(at_us, 2)},
         "kernels": kernels,
         "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
