@@ -167,12 +167,14 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols, int t
     p.xmode = xmode;
     p.pbytes = 0;
     p.cwords = 0;
-    // 128 x 128 tiles when they still give most CUs a tile, else 64 x 64;
+    // 128 x 128 tiles when they still give most CUs a tile, or when K is long
+    // enough (>= 4096: the down projection) for split-K slices of >= 1024,
+    // else 64 x 64 (their LDS reads per MFMA are twice as many);
     // fewer than 512 tiles split K (not the context projection, whose
     // epilogue reads the product in place) into slices of an even number of
     // 64-wide steps, for several workgroups per CU
     const int64_t tiles128 = (int64_t)ceil_div(M, 128) * ceil_div(N, 128);
-    p.tall = tiles128 >= 200 ? TALL_128 : TALL_64;
+    p.tall = (tiles128 >= 200 || (tiles128 >= 48 && K >= 4096)) ? TALL_128 : TALL_64;
     const int bt = p.tall == TALL_128 ? 128 : 64;
     const int64_t tiles = (int64_t)ceil_div(M, bt) * ceil_div(N, bt);
     const int steps = K / 64;
