@@ -31,6 +31,8 @@
 namespace dsp {
 
 constexpr int ATT_NTH = 256;  // threads per workgroup (4 waves, one quarter of hd each)
+constexpr float ATT_LOG2E = 1.4426950408889634f;
+constexpr float ATT_RESCALE = 8.f;  // slack of the softmax reference max (natural-log units)
 
 // one pass over the keys staged in LDS: ONE = 32 one-plane keys, else 16
 // keys as hi (rows 0..15) and lo (rows 16..31) planes.  o: this wave's NTW
@@ -62,24 +64,29 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
       sv[4 + i] = (ONE && 16 + 4 * gq + i < nvalid) ? s1[i] : -INFINITY;
     }
   }
-  // online softmax for this lane's query column
+  // online softmax for this lane's query column.  The reference max m_run
+  // moves only when a chunk's max passes it by more than ATT_RESCALE, so the
+  // O rescale (a multiply per accumulator) runs after the first chunk only
+  // rarely; probabilities stay below e^ATT_RESCALE, and (m_run, l) stay
+  // consistent for the merge whatever reference was used.  exp(x) is the
+  // hardware 2^(x log2 e).
   float mx = sv[0];
 #pragma unroll
   for (int e = 1; e < 8; ++e) mx = fmaxf(mx, sv[e]);
   mx = fmaxf(mx, __shfl_xor(mx, 16));
   mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(m_run, mx);
-  if (mnew > m_run) {
-    const float sc = expf(m_run - mnew);
+  if (mx > m_run + ATT_RESCALE) {
+    const float sc = __builtin_amdgcn_exp2f((m_run - mx) * ATT_LOG2E);
 #pragma unroll
     for (int t = 0; t < NTW; ++t) o[t] *= sc;
     l_part *= sc;
-    m_run = mnew;
+    m_run = mx;
   }
+  const float mb = m_run * ATT_LOG2E;
   float pe[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float p = expf(sv[e] - m_run);
+    const float p = __builtin_amdgcn_exp2f(fmaf(sv[e], ATT_LOG2E, -mb));
     l_part += p;
     pe[e] = p;
   }
@@ -148,10 +155,11 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
+        // keys past the chunk hold a copy of its last key: their scores are
+        // masked to -inf, so their probabilities are exactly 0
         const int c8 = (tid + NTH * i) / ATT_KEYS;
-        const u32x4 z = u32x4{0u, 0u, 0u, 0u};
-        *(u32x4*)&Ks[key * KSTR + 8 * c8] = ok ? kk[i] : z;
-        const u32x4 vw = ok ? vv[i] : z;
+        *(u32x4*)&Ks[key * KSTR + 8 * c8] = kk[i];
+        const u32x4 vw = vv[i];
         // V^T in 32-bit words of two keys: the lanes of keys 2k and 2k + 1
         // (adjacent lanes, same dims) swap half their dims, then the even
         // lane writes dims 0..3 and the odd lane dims 4..7 of the pair

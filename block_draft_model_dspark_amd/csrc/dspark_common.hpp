@@ -72,7 +72,6 @@ __device__ __forceinline__ void st_act(void* p, int64_t i, float v, bool bf16) {
   else ((float*)p)[i] = v;
 }
 
-// x ~= hi + lo with both bf16: hi = rne(x), lo = rne(x - hi)
 // two floats -> packed fp16 pair (round to nearest even)
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
   const _Float16 ha = (_Float16)a, hb = (_Float16)b;
@@ -80,6 +79,7 @@ __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
 }
 __device__ __forceinline__ float f16_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// x ~= hi + lo with both bf16: hi = rne(x), lo = rne(x - hi)
 __device__ __forceinline__ void split8(const float* v, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
