@@ -250,6 +250,16 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.T = tb.T;
     t.ldt = a.N;
   }
+  // logits: softcap and the walk's chunk bounds in the tiled kernel itself
+  // when its 128 x 128 tiles hold the final product
+  if (epi == EPI_LM && p.tall == TALL_128 && p.S == 1 && a.N % 64 == 0) {
+    t.lm = 1;
+    t.cap = e.cap;
+    t.aux = e.aux;
+    t.lohi = e.lohi;
+    t.NC = e.NC;
+    return launch_tall(t, p.tall, p.np, p.S, st);
+  }
   hipError_t r = launch_tall(t, p.tall, p.np, p.S, st);
   if (r != hipSuccess) return r;
   return launch_gemm_epi(a, e, epi, t.T, t.ldt, p.S, t.tstride, st);

@@ -111,6 +111,15 @@ struct TallArgs {
   int kslice;         // K range per blockIdx.z (a multiple of 64)
   float* T;           // partial product of slice z at T + z * tstride
   int64_t ldt, tstride;
+  // logits in the tiled kernel itself (128 x 128 tiles, one K slice): T
+  // holds z = cap tanh(x / cap) (cap 0: x), and lohi[m, c] = (max z - B,
+  // max z + B) over the 64 vocabulary entries of chunk c, B the walk bound
+  // of each entry (aux null: 0)
+  int lm;
+  float cap;
+  const float* aux;
+  float2* lohi;       // [M, NC]
+  int NC;
 };
 
 // per-row data of a draft round

@@ -238,6 +238,39 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   }
   float* const T = t.T + blockIdx.z * t.tstride;
 
+  if constexpr (WN == 64) {
+    if (t.lm) {  // uniform: the wave's 64 columns are one walk chunk
+      const int nc0 = n0 + WN * wn;
+      float b[FN];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int n = min(nc0 + 16 * j + ln, t.N - 1);
+        b[j] = t.aux ? walk_bound(t.aux, n, t.N) : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int m = m0 + WM * wm + 16 * i + 4 * gq + q;
+          float lo = -INFINITY, hi = -INFINITY;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            const int n = nc0 + 16 * j + ln;
+            float z = acc[i][j][q];
+            if (t.cap > 0.f) z = t.cap * tanhf(z / t.cap);
+            if (n < t.N) {
+              if (m < t.M) T[(int64_t)m * t.ldt + n] = z;
+              lo = fmaxf(lo, z - b[j]);
+              hi = fmaxf(hi, z + b[j]);
+            }
+          }
+          lo = row16_max(lo);
+          hi = row16_max(hi);
+          if (ln == 0 && m < t.M && nc0 < t.N) t.lohi[(int64_t)m * t.NC + nc0 / 64] = make_float2(lo, hi);
+        }
+      return;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -267,6 +300,9 @@ hipError_t launch_tall(const TallArgs& t, int tile, int np, int S, hipStream_t s
   if (t.K % TBK != 0 || t.kslice % TBK != 0 || t.kslice <= 0 || (int64_t)S * t.kslice < t.K ||
       (int64_t)(S - 1) * t.kslice >= t.K || t.M <= 0 || t.N <= 0 || t.nseg < 1 || t.nseg > MAX_SEG)
     return hipErrorInvalidValue;
+  // the fused logits need whole 64-entry chunks per wave (128 x 128 tiles)
+  // and the final product (one K slice)
+  if (t.lm && (tile != TALL_128 || S != 1 || t.N % 64 != 0 || !t.lohi || t.ldt != t.N)) return hipErrorInvalidValue;
   const int bm = tile == TALL_128 ? 128 : 64, bn = bm;
   const dim3 grid((t.N + bn - 1) / bn, (t.M + bm - 1) / bm, S);
   if (tile == TALL_128) {

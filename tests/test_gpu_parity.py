@@ -253,6 +253,34 @@ def test_tiled_path_round_small_ragged(gpu_lib):
     assert rel_err(logits, z0.cpu().numpy()) <= 1e-3
 
 
+def test_tiled_path_fused_logits(gpu_lib):
+    """lm_head on 128 x 128 tiles with one K slice (16 rows = 256 block rows,
+    the full 32768-entry vocabulary: 512 tiles), so softcap and the walk's
+    chunk bounds are formed in the tiled kernel itself; an active Markov head
+    makes the walk depend on those bounds.  Oracle parity, and agreement with
+    the weight-streaming path."""
+    import torch
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=1)
+    lens = [0, 1, 31, 64, 100, 7, 250, 33, 12, 96, 5, 300, 2, 40, 128, 77]
+    w = synth.Workload("tall_lm", cfg, rows=len(lens), ctx_lens=tuple(lens))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    try:
+        case.gm.set_tall_rows(0)
+        t0, z0 = gpu_lib.draft_rows(case.gm, k_rows, v_rows, lens, anchors, lens, collect_logits=True)
+        torch.cuda.synchronize()
+        case.gm.set_tall_rows(1)
+        toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    finally:
+        case.gm.set_tall_rows(256)
+    for a in range(len(lens)):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 64
+    assert rel_err(logits, z0.cpu().numpy()) <= 1e-3
+
+
 @pytest.mark.parametrize("kind", ["target_features", "context_hidden"])
 def test_tiled_path_projection_small_ragged(gpu_lib, kind):
     """The context projection on the tiled path (threshold 1 row) over 2 x 100
