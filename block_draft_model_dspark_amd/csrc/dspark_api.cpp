@@ -260,6 +260,14 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.NC = e.NC;
     return launch_tall(t, p.tall, p.np, p.S, st);
   }
+  // gate|up: gelu_tanh(gate) * up in the tiled kernel itself when its
+  // 128 x 128 tiles hold the final product of hi + lo planes
+  if (epi == EPI_GELU && p.tall == TALL_128 && p.S == 1 && p.np == 2 && a.N % 128 == 0) {
+    t.gelu = 1;
+    t.act = e.act;
+    t.ld_act = e.ld_act;
+    return launch_tall(t, p.tall, p.np, p.S, st);
+  }
   hipError_t r = launch_tall(t, p.tall, p.np, p.S, st);
   if (r != hipSuccess) return r;
   return launch_gemm_epi(a, e, epi, t.T, t.ldt, p.S, t.tstride, st);

@@ -120,6 +120,12 @@ struct TallArgs {
   const float* aux;
   float2* lohi;       // [M, NC]
   int NC;
+  // gate|up in the tiled kernel itself (128 x 128 tiles, hi + lo planes, one
+  // K slice): tile x multiplies gate rows 64x.. and up rows I + 64x.. (N = 2I)
+  // and writes act[m, 64x + c] = gelu_tanh(gate) * up
+  int gelu;
+  float* act;
+  int64_t ld_act;
 };
 
 // per-row data of a draft round

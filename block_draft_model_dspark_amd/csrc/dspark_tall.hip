@@ -147,7 +147,9 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
 #pragma unroll
   for (int j = 0; j < BIT; ++j) {
     const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
-    const int n = min(n0 + r, t.N - 1);
+    // gate|up pairing: tile rows 0..63 are gate rows 64x.., 64..127 up rows
+    const int n = (BN == 128 && t.gelu) ? (r < 64 ? 64 * blockIdx.x + r : t.N / 2 + 64 * blockIdx.x + r - 64)
+                                        : min(n0 + r, t.N - 1);
     // segment lookup with uniform (scalar) reads of the argument array
     const void* w = t.seg[0].w;
     int nb = t.seg[0].n0;
@@ -238,6 +240,34 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   }
   float* const T = t.T + blockIdx.z * t.tstride;
 
+  if constexpr (WN == 64 && NP == 2) {
+    if (t.gelu) {  // uniform: waves wn = 1 hold the up columns of the gate columns of waves wn = 0
+      float* ex = (float*)&As[0][0];  // 2 x 64 x 64 floats (32 KiB) of the staging planes
+      __syncthreads();                // every wave is done with the last step's operands
+      if (wn == 1)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) ex[(wm * 64 + 16 * i + 4 * gq + q) * 64 + 16 * j + ln] = acc[i][j][q];
+      __syncthreads();
+      if (wn == 0)
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 16 * i + 4 * gq + q, m = m0 + WM * wm + r;
+            if (m < t.M)
+#pragma unroll
+              for (int j = 0; j < FN; ++j) {
+                const int c = 16 * j + ln;
+                t.act[(int64_t)m * t.ld_act + 64 * blockIdx.x + c] = gelu_tanh(acc[i][j][q]) * ex[(wm * 64 + r) * 64 + c];
+              }
+          }
+      return;
+    }
+  }
   if constexpr (WN == 64) {
     if (t.lm) {  // uniform: the wave's 64 columns are one walk chunk
       const int nc0 = n0 + WN * wn;
@@ -303,6 +333,8 @@ hipError_t launch_tall(const TallArgs& t, int tile, int np, int S, hipStream_t s
   // the fused logits need whole 64-entry chunks per wave (128 x 128 tiles)
   // and the final product (one K slice)
   if (t.lm && (tile != TALL_128 || S != 1 || t.N % 64 != 0 || !t.lohi || t.ldt != t.N)) return hipErrorInvalidValue;
+  // the fused gate|up pairs 64 gate with 64 up columns per tile
+  if (t.gelu && (tile != TALL_128 || S != 1 || np != 2 || t.N % 128 != 0 || !t.act || t.lm)) return hipErrorInvalidValue;
   const int bm = tile == TALL_128 ? 128 : 64, bn = bm;
   const dim3 grid((t.N + bn - 1) / bn, (t.M + bm - 1) / bm, S);
   if (tile == TALL_128) {
