@@ -205,8 +205,10 @@ struct TallBufs {
   float* T = nullptr;
 };
 
+// x_planes: the tiled path's input planes are already in tb.xop (the
+// attention merge wrote them), so no input preparation runs
 hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st,
-                    const TallBufs& tb = TallBufs{}) {
+                    const TallBufs& tb = TallBufs{}, bool x_planes = false) {
   a.kslice = p.kslice;
   a.kc = p.kc;
   if (p.tall == TALL_NONE) return launch_gemm(a, e, epi, wk, p.xmode, p.mt, p.S, st);
@@ -217,8 +219,10 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.plane = 0;
   } else {
     if (!tb.xop) return hipErrorInvalidValue;
-    const hipError_t r = launch_xprep(a, p.xmode, tb.xop, (int64_t)a.M * a.K, st);
-    if (r != hipSuccess) return r;
+    if (!x_planes) {
+      const hipError_t r = launch_xprep(a, p.xmode, tb.xop, (int64_t)a.M * a.K, st);
+      if (r != hipSuccess) return r;
+    }
     t.X = tb.xop;
     t.ldx = a.K;
     t.plane = (int64_t)a.M * a.K;
@@ -836,6 +840,12 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   mg.ml = at.ml;
   mg.O = O;
   mg.ldo = d.ldo;
+  // a tiled o projection over hi + lo planes reads them straight from the merge
+  const bool o_planes = d.o.tall != TALL_NONE && d.o.np == 2;
+  if (o_planes) {
+    mg.planes = tb.xop;
+    mg.plane = (int64_t)M * nH * hd;
+  }
 
   EmbedArgs em{};
   em.E = m->embed.w;
@@ -940,7 +950,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     e.Y = Y;
     e.h = hB;
     e.w1 = W.pa;
-    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream, tb); }));
+    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream, tb, o_planes); }));
 
     g = GemmArgs{};
     g.ldx = H;

@@ -180,6 +180,10 @@ struct MergeArgs {
   const void* opart; const float* ml;
   float* O;           // [A*gamma, nH*hd], row pitch ldo
   int64_t ldo;
+  // non-null: O goes out as the bf16 hi / lo planes [2][A*gamma, nH*hd]
+  // (plane stride `plane`) that the tiled o projection reads, instead of fp32
+  uint16_t* planes;
+  int64_t plane;
 };
 
 struct WalkArgs {

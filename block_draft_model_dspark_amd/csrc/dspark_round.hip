@@ -144,7 +144,19 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
   const float rd = 1.f / den;
-  float* dst = a.O + ((int64_t)row * a.gamma + g) * a.ldo + h * a.hd + d0;
+  const int64_t m = (int64_t)row * a.gamma + g;
+  if (a.planes) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = num[e] * rd;
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
+    uint16_t* dst = a.planes + m * (a.nH * a.hd) + h * a.hd + d0;
+    *(u32x4*)dst = __builtin_bit_cast(u32x4, hi);
+    *(u32x4*)(dst + a.plane) = __builtin_bit_cast(u32x4, lo);
+    return;
+  }
+  float* dst = a.O + m * a.ldo + h * a.hd + d0;
   *(f32x4*)dst = f32x4{num[0] * rd, num[1] * rd, num[2] * rd, num[3] * rd};
   *(f32x4*)(dst + 4) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
 }
@@ -198,7 +210,16 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
   }
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
-  a.O[((int64_t)row * a.gamma + g) * a.ldo + h * a.hd + tid] = num / den;
+  const int64_t m = (int64_t)row * a.gamma + g;
+  const float x = num / den;
+  if (a.planes) {
+    const __bf16 hi = (__bf16)x;
+    const __bf16 lo = (__bf16)(x - (float)hi);
+    a.planes[m * (a.nH * a.hd) + h * a.hd + tid] = __builtin_bit_cast(uint16_t, hi);
+    a.planes[a.plane + m * (a.nH * a.hd) + h * a.hd + tid] = __builtin_bit_cast(uint16_t, lo);
+    return;
+  }
+  a.O[m * a.ldo + h * a.hd + tid] = x;
 }
 
 // markov_w1 / markov_w2 element (table_elem with the head's own storage)
