@@ -205,8 +205,11 @@ struct TallBufs {
   float* T = nullptr;
 };
 
+// gate|up whose tiles form gelu_tanh(gate) * up themselves (tiled path)
+bool fused_gelu(const GemmPlan& p, int64_t N) { return p.tall == TALL_128 && p.S == 1 && p.np == 2 && N % 128 == 0; }
+
 // x_planes: the tiled path's input planes are already in tb.xop (the
-// attention merge wrote them), so no input preparation runs
+// attention merge or the fused gate|up wrote them), so no input preparation runs
 hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st,
                     const TallBufs& tb = TallBufs{}, bool x_planes = false) {
   a.kslice = p.kslice;
@@ -266,10 +269,12 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
   }
   // gate|up: gelu_tanh(gate) * up in the tiled kernel itself when its
   // 128 x 128 tiles hold the final product of hi + lo planes
-  if (epi == EPI_GELU && p.tall == TALL_128 && p.S == 1 && p.np == 2 && a.N % 128 == 0) {
+  if (epi == EPI_GELU && fused_gelu(p, a.N)) {
     t.gelu = 1;
     t.act = e.act;
     t.ld_act = e.ld_act;
+    t.act_planes = e.act_planes;
+    t.act_plane = e.act_plane;
     return launch_tall(t, p.tall, p.np, p.S, st);
   }
   hipError_t r = launch_tall(t, p.tall, p.np, p.S, st);
@@ -293,7 +298,8 @@ GemmSeg seg_of(const Mat& w, int n0) {
 constexpr int ROW_PAD = 64;
 
 struct DraftLayout {
-  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, xop, T, total;
+  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, xop, xop2, T, total;
+  bool dn_planes;  // the fused gate|up writes the tiled down projection's input planes (xop2)
   int64_t ldh, ldo, ldact;
   GemmPlan qk, o, gu, dn, lm;
   size_t cwords;
@@ -367,6 +373,8 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
   d.lohi = take((size_t)M * NC * 8);
   d.xop = take(std::max({d.qk.xbytes, d.o.xbytes, d.gu.xbytes, d.dn.xbytes, d.lm.xbytes, (size_t)4}));
+  d.dn_planes = fused_gelu(d.gu, 2 * (int64_t)I) && d.dn.tall != TALL_NONE && d.dn.np == 2;
+  d.xop2 = take(d.dn_planes ? (size_t)2 * M * I * 2 : 4);
   d.T = take(std::max({d.qk.tall ? (size_t)M * (nH + nKv) * hd * 4 : 0, d.gu.tall ? (size_t)M * 2 * I * 4 : 0,
                        d.qk.tbytes, d.o.tbytes, d.gu.tbytes, d.dn.tbytes, d.lm.tbytes, (size_t)4}));
   d.total = off;
@@ -962,6 +970,10 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     g.seg[1] = seg_of(W.u, I);
     g.P = P;
     g.nin = norm_in(hB, Y, W.pa, scal, W.pf, hA);
+    if (d.dn_planes) {
+      e.act_planes = (uint16_t*)(ws + d.xop2);
+      e.act_plane = (int64_t)M * I;
+    }
     HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream, tb); }));
 
     g = GemmArgs{};
@@ -976,7 +988,9 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
     e.Y = Y;
     e.h = hA;
     e.w1 = W.pff;
-    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream, tb); }));
+    TallBufs tb_dn = tb;
+    if (d.dn_planes) tb_dn.xop = (uint16_t*)(ws + d.xop2);
+    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream, tb_dn, d.dn_planes); }));
     y_prev = Y;
     w1_prev = W.pff;
     sc_prev = scal + 1 + l;

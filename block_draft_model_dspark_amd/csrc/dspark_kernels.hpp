@@ -87,6 +87,8 @@ struct EpiArgs {
   // EPI_GELU
   float* act;         // [M, N/2], row pitch ld_act
   int64_t ld_act;
+  uint16_t* act_planes;  // tiled gate|up only: act as bf16 hi / lo planes (see TallArgs)
+  int64_t act_plane;
   // EPI_SUMS
   int64_t ldy;        // row pitch (floats) of Y and h
   const float* h;     // residual [M, N] or null
@@ -126,6 +128,10 @@ struct TallArgs {
   int gelu;
   float* act;
   int64_t ld_act;
+  // non-null: act goes out as the bf16 hi / lo planes [2][M, N/2] (plane
+  // stride act_plane) that a tiled down projection reads, instead of fp32
+  uint16_t* act_planes;
+  int64_t act_plane;
 };
 
 // per-row data of a draft round

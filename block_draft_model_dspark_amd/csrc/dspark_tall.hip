@@ -258,13 +258,35 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const int r = 16 * i + 4 * gq + q, m = m0 + WM * wm + r;
-            if (m < t.M)
 #pragma unroll
-              for (int j = 0; j < FN; ++j) {
-                const int c = 16 * j + ln;
-                t.act[(int64_t)m * t.ld_act + 64 * blockIdx.x + c] = gelu_tanh(acc[i][j][q]) * ex[(wm * 64 + r) * 64 + c];
-              }
+            for (int j = 0; j < FN; ++j) {
+              const int c = 16 * j + ln;
+              float* xe = &ex[(wm * 64 + r) * 64 + c];
+              const float x = gelu_tanh(acc[i][j][q]) * *xe;
+              if (t.act_planes) *xe = x;  // (this thread's own element)
+              else if (m < t.M) t.act[(int64_t)m * t.ld_act + 64 * blockIdx.x + c] = x;
+            }
           }
+      if (t.act_planes) {
+        // the 128 x 64 products as hi / lo planes, eight columns (16 bytes) per store
+        __syncthreads();
+        const int64_t I = t.N / 2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int idx = tid + 256 * k, rr = idx >> 3, c8 = idx & 7;  // rr: row of the 128-row tile
+          const int m = m0 + rr;
+          if (m < t.M) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = ex[rr * 64 + 8 * c8 + e];
+            bf16x8 hi, lo;
+            split8(v, hi, lo);
+            uint16_t* dst = t.act_planes + (int64_t)m * I + 64 * blockIdx.x + 8 * c8;
+            *(u32x4*)dst = __builtin_bit_cast(u32x4, hi);
+            *(u32x4*)(dst + t.act_plane) = __builtin_bit_cast(u32x4, lo);
+          }
+        }
+      }
       return;
     }
   }
