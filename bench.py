@@ -32,20 +32,22 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 # WRITE_SIZE passes over a short run of the same workload, each scaled by what
 # the same counter reads for a plain copy of known size (--calibrate-copy-mib:
 # FETCH_SIZE x 2.0, WRITE_SIZE x 1.0).  Valid only for the sources the
-# counters were taken on (their sha256): otherwise the traffic is unknown.
+# counters were taken on (their sha256, the launch planner included):
+# otherwise the traffic is unknown.
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
-    "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
-                  "sha256": "8896025cae467c440c54539c92c416ac076b00b897b434a498adc0cf4e4f3a18",
-                  "bytes_per_step": 713367756},
+    "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
+                  "sha256": "f4b6ec8397a45c6293f41afa985cba190f3609cae4e85af016f3130af96baaba",
+                  "bytes_per_step": 713362022},
     # rows_a32: the 4 wide-attention launches of one round
-    "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
-                  "sha256": "aad7c175ce097a39d9fa6665ac74fb3068619a3874527eebde8a51b4476da755",
-                  "bytes_per_step": 387748326},
-    # rows_a32: the 17 tiled-GEMM launches of one round (their epilogues excluded)
-    "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp"),
-                  "sha256": "64d1e9cab26eee92879a6fbee18c53871fccdfe9c644634353d5e860d2126537",
-                  "bytes_per_step": 2577942425},
+    "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
+                  "sha256": "a479109a16e0bd96889181540356476ce43fb021b50c079ddb5646cf01e26d2e",
+                  "bytes_per_step": 387687424},
+    # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
+    # separate epilogues excluded)
+    "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
+                  "sha256": "01b274b2bfd9d1c8fd7652270ef733087d2844411ca1f50464a55c8a26ac9709",
+                  "bytes_per_step": 2529535852},
 }
 
 
