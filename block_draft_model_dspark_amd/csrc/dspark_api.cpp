@@ -368,7 +368,8 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.kb = take((size_t)A * nKv * c.block_size * hd * 4);
   d.vb = take((size_t)A * nKv * c.block_size * hd * 4);
   d.ssq = take((size_t)(nH + nKv) * (hd / 64) * M * 4);
-  d.opart = take((size_t)d.nsplit_max * nKv * m->nq * hd * 4);
+  // fp32 partials [split, kvh, nq, hd], or fp16 ones in groups of 16 query rows
+  d.opart = take((size_t)d.nsplit_max * nKv * std::max((size_t)m->nq * hd * 4, (size_t)((m->nq + 15) / 16) * 16 * hd * 2));
   d.ml = take((size_t)d.nsplit_max * nKv * m->nq * 2 * 4);
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
   d.lohi = take((size_t)M * NC * 8);
@@ -845,6 +846,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   mg.hd = hd;
   mg.opart = at.opart;
   mg.part_f16 = c.act_dtype == DSPARK_BF16 ? 1 : 0;  // the attention kernels' KVB variant
+  mg.lane_order = wide ? 1 : 0;                         // the wide kernel stores fp16 partials in lane order
   mg.ml = at.ml;
   mg.O = O;
   mg.ldo = d.ldo;

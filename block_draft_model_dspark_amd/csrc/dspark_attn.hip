@@ -220,21 +220,43 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
   }
 }
 
-// this lane's output tiles t0.. (dims 16 t + 4 (lane / 16) .. + 3 of its
-// query) at element offset off: a bf16 cache stores fp16 O / l (bounded by
-// the largest |v|, so in range, and half the bytes of fp32), an fp32 cache
-// the fp32 sums themselves
-template <bool F16, int NTW>
-__device__ __forceinline__ void store_part(void* opart, int64_t off, int t0, const f32x4 (&o)[NTW], float l) {
-  if constexpr (F16) {
+// This lane's output tiles t0.. (dims 16 t + 4 (lane / 16) .. + 3 of its
+// query).  An fp32 cache stores the fp32 sums at [split, kvh, nq, hd] (element
+// offset off32 of this lane's first dim).  A bf16 cache stores fp16 O / l
+// (bounded by the largest |v|, so in range; half the bytes): LANE = false at
+// [split, kvh, nq, hd] like the fp32 sums; LANE = true in the lanes' own
+// order, [split, kvh, query group of 16, tile pair, lane, 8] with tile 2j in
+// halves 0..3 and tile 2j + 1 in halves 4..7 (element offset offp of this
+// (split, kvh, group), pair 0, lane 0), so a wave's store of a tile pair is
+// 1 KiB contiguous (the merge then reads 16-byte pieces of several rows).
+template <bool F16, bool LANE, int HD, int NTW>
+__device__ __forceinline__ void store_part(void* opart, int64_t off32, int64_t offp, int t0, const f32x4 (&o)[NTW],
+                                           float l) {
+  if constexpr (F16 && !LANE) {
     const float rl = 1.f / l;
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
-      *(u32x2*)((uint16_t*)opart + off + 16 * (t0 + t)) =
+      *(u32x2*)((uint16_t*)opart + off32 + 16 * (t0 + t)) =
           u32x2{pack_f16x2(o[t][0] * rl, o[t][1] * rl), pack_f16x2(o[t][2] * rl, o[t][3] * rl)};
+  } else if constexpr (F16) {
+    const float rl = 1.f / l;
+    const int lane = threadIdx.x & 63;
+    uint16_t* const base = (uint16_t*)opart + offp + 8 * lane;
+    if constexpr (NTW % 2 == 0) {  // t0 even: whole pairs
+#pragma unroll
+      for (int t = 0; t < NTW; t += 2)
+        *(u32x4*)(base + (int64_t)((t0 + t) / 2) * 512) =
+            u32x4{pack_f16x2(o[t][0] * rl, o[t][1] * rl), pack_f16x2(o[t][2] * rl, o[t][3] * rl),
+                  pack_f16x2(o[t + 1][0] * rl, o[t + 1][1] * rl), pack_f16x2(o[t + 1][2] * rl, o[t + 1][3] * rl)};
+    } else {
+#pragma unroll
+      for (int t = 0; t < NTW; ++t)
+        *(u32x2*)(base + (int64_t)((t0 + t) / 2) * 512 + 4 * ((t0 + t) & 1)) =
+            u32x2{pack_f16x2(o[t][0] * rl, o[t][1] * rl), pack_f16x2(o[t][2] * rl, o[t][3] * rl)};
+    }
   } else {
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) *(f32x4*)((float*)opart + off + 16 * (t0 + t)) = o[t];
+    for (int t = 0; t < NTW; ++t) *(f32x4*)((float*)opart + off32 + 16 * (t0 + t)) = o[t];
   }
 }
 
@@ -339,7 +361,8 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
   const int qrow = q0 + ln;
   if (qrow < a.nq) {
     const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qrow;
-    store_part<KVB>(a.opart, base * HD + 4 * gq, t0, o, l);
+    const int64_t grp = ((int64_t)sg * a.nKv + kvh) * ((a.nq + 15) / 16) + blockIdx.z;
+    store_part<KVB, false, HD>(a.opart, base * HD + 4 * gq, grp * 16 * HD, t0, o, l);
     if (wave == 0 && gq == 0) {
       a.ml[base * 2] = m_run;
       a.ml[base * 2 + 1] = l;
@@ -440,7 +463,8 @@ __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
   l += __shfl_xor(l, 16);
   l += __shfl_xor(l, 32);
   const int64_t base = ((int64_t)sg * a.nKv + kvh) * a.nq + qr;
-  store_part<KVB>(a.opart, base * HD + 4 * gq, 0, o, l);
+  const int64_t grp = ((int64_t)sg * a.nKv + kvh) * (a.nq / 16) + wave;
+  store_part<KVB, true, HD>(a.opart, base * HD + 4 * gq, grp * 16 * HD, 0, o, l);
   if (gq == 0) {
     a.ml[base * 2] = m_run;
     a.ml[base * 2 + 1] = l;

@@ -183,6 +183,7 @@ struct MergeArgs {
   int split_off[MAX_ROWS + 1];
   int A, gamma, nKv, nq, nH, hd;
   int part_f16;       // partials are fp16 O / sum (else fp32 unnormalised)
+  int lane_order;     // fp16 partials in the wide attention's lane order (else [split, kvh, nq, hd])
   const void* opart; const float* ml;
   float* O;           // [A*gamma, nH*hd], row pitch ldo
   int64_t ldo;

@@ -81,21 +81,51 @@ __global__ __launch_bounds__(256) void k_zero(unsigned* p, int64_t n) {
 // ---------------------------------------------------------------------------
 // split-softmax merge: O = sum_s e^{m_s - M} O_s / sum_s e^{m_s - M} l_s with
 // M = max_s m_s; F16: the partials hold O_s / l_s in fp16 (weight e^{m_s-M} l_s).
-// Each thread owns 8 head dims of one query row (hd / 8 threads per row), so
-// a split's partial row is one 16-byte (fp16) or 32-byte (fp32) load per
-// thread, eight splits in flight.  grid ceil(A*nKv*nq / (256 / (hd / 8))), block 256
+// Each thread owns 8 head dims of one query row, so a split's partial is one
+// 16-byte (fp16) or 32-byte (fp32) load per thread, eight splits in flight.
+// fp32: dims 8c.. of the row, hd / 8 threads per row, grid
+// ceil(A*nKv*nq / (256 / (hd / 8))).  fp16 (the attention's lane order
+// [split, kvh, group of 16 rows, tile pair j, lane, 8]): thread (row group,
+// j, lane) owns dims 32j + 4 (lane / 16) .. + 3 and the same + 16 of row
+// 16 group + lane mod 16, so 64 threads read 1 KiB contiguous per split;
+// grid A*nKv*ceil(nq/16)*(hd/32)*64 / 256.  block 256
 // ---------------------------------------------------------------------------
 constexpr int MERGE_SB = 8;          // splits loaded per batch
 constexpr int MERGE_FEW_ROWS = 512;  // up to this many query rows: k_merge_rows
 
-template <bool F16>
+template <bool F16, bool LANE>
 __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
-  const int tid = threadIdx.x, lpq = a.hd >> 3;
-  const int nrows = a.A * a.nKv * a.nq;
-  const int qg = blockIdx.x * (256 / lpq) + tid / lpq;
-  if (qg >= nrows) return;
-  const int d0 = 8 * (tid - (tid / lpq) * lpq);
-  const int j = qg % a.nq, kvh = (qg / a.nq) % a.nKv, row = qg / (a.nq * a.nKv);
+  const int tid = threadIdx.x;
+  int j, kvh, row, d0, d1;  // query row, kv head, draft row; this thread's two runs of four dims
+  int64_t pbase;            // fp16: halves offset of (split 0, kvh, group, pair, lane)
+  const int ng = (a.nq + 15) / 16, np2 = a.hd / 32;
+  if constexpr (F16 && LANE) {
+    const int64_t gt = (int64_t)blockIdx.x * 256 + tid;
+    const int lane = (int)(gt & 63);
+    const int64_t rest = gt >> 6;  // ((row * nKv + kvh) * ng + group) * np2 + pair
+    const int pair = (int)(rest % np2);
+    const int64_t rg = rest / np2;  // (row * nKv + kvh) * ng + group
+    const int grp = (int)(rg % ng);
+    kvh = (int)((rg / ng) % a.nKv);
+    row = (int)(rg / ((int64_t)ng * a.nKv));
+    if (row >= a.A) return;
+    j = grp * 16 + (lane & 15);
+    if (j >= a.nq) return;
+    d0 = 32 * pair + 4 * (lane >> 4);
+    d1 = d0 + 16;
+    pbase = (((int64_t)kvh * ng + grp) * np2 + pair) * 512 + 8 * lane;
+  } else {
+    const int lpq = a.hd >> 3;
+    const int nrows = a.A * a.nKv * a.nq;
+    const int qg = blockIdx.x * (256 / lpq) + tid / lpq;
+    if (qg >= nrows) return;
+    d0 = 8 * (tid - (tid / lpq) * lpq);
+    d1 = d0 + 4;
+    j = qg % a.nq;
+    kvh = (qg / a.nq) % a.nKv;
+    row = qg / (a.nq * a.nKv);
+    pbase = 0;
+  }
   const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
   auto mli = [&](int s) { return ((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + j; };
@@ -108,10 +138,13 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
 #pragma unroll
     for (int q = 0; q < MERGE_SB; ++q) {
       const int s = c0 + min(q, ns - c0 - 1);
-      const int64_t i = mli(s) * a.hd + d0;
-      if constexpr (F16) {
-        raw[q][0] = *(const u32x4*)((const uint16_t*)a.opart + i);
+      if constexpr (F16 && LANE) {
+        // split stride: nKv * ng groups of 16 rows x hd halves
+        raw[q][0] = *(const u32x4*)((const uint16_t*)a.opart + (int64_t)(s0 + s) * a.nKv * ng * 16 * a.hd + pbase);
+      } else if constexpr (F16) {
+        raw[q][0] = *(const u32x4*)((const uint16_t*)a.opart + mli(s) * a.hd + d0);
       } else {
+        const int64_t i = mli(s) * a.hd + d0;
         raw[q][0] = *(const u32x4*)((const float*)a.opart + i);
         raw[q][1] = *(const u32x4*)((const float*)a.opart + i + 4);
       }
@@ -145,20 +178,24 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const int h = kvh * rep + hl;
   const float rd = 1.f / den;
   const int64_t m = (int64_t)row * a.gamma + g;
+  // dims d0.. (values 0..3) and d1.. (values 4..7)
   if (a.planes) {
     float v[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = num[e] * rd;
     bf16x8 hi, lo;
     split8(v, hi, lo);
-    uint16_t* dst = a.planes + m * (a.nH * a.hd) + h * a.hd + d0;
-    *(u32x4*)dst = __builtin_bit_cast(u32x4, hi);
-    *(u32x4*)(dst + a.plane) = __builtin_bit_cast(u32x4, lo);
+    const u32x4 hw = __builtin_bit_cast(u32x4, hi), lw = __builtin_bit_cast(u32x4, lo);
+    uint16_t* dst = a.planes + m * (a.nH * a.hd) + h * a.hd;
+    *(u32x2*)(dst + d0) = u32x2{hw[0], hw[1]};
+    *(u32x2*)(dst + d1) = u32x2{hw[2], hw[3]};
+    *(u32x2*)(dst + a.plane + d0) = u32x2{lw[0], lw[1]};
+    *(u32x2*)(dst + a.plane + d1) = u32x2{lw[2], lw[3]};
     return;
   }
-  float* dst = a.O + m * a.ldo + h * a.hd + d0;
-  *(f32x4*)dst = f32x4{num[0] * rd, num[1] * rd, num[2] * rd, num[3] * rd};
-  *(f32x4*)(dst + 4) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
+  float* dst = a.O + m * a.ldo + h * a.hd;
+  *(f32x4*)(dst + d0) = f32x4{num[0] * rd, num[1] * rd, num[2] * rd, num[3] * rd};
+  *(f32x4*)(dst + d1) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
 }
 
 // Few query rows (a single draft row): one workgroup per query row, one
@@ -166,7 +203,7 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
 // load of a pass in flight.  grid A*nKv*nq, block hd (>= 64)
 constexpr int MERGE_RB = 32;
 
-template <bool F16>
+template <bool F16, bool LANE>
 __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
   __shared__ float2 wl[MERGE_RB];
   __shared__ float cmax;
@@ -174,6 +211,12 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
   const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
+  // fp16 lane order: thread tid reads half (tid mod 8) of lane j mod 16 +
+  // 16 ((tid mod 32) / 8) in tile pair tid / 32 (eight threads per 16-byte
+  // piece), which is dim 16 (2 pair + half / 4) + 4 ((tid mod 32) / 8) + half mod 4
+  const int pr = tid >> 5, gq8 = (tid & 31) >> 3, hv = tid & 7;
+  const int dim = F16 && LANE ? 16 * (2 * pr + (hv >> 2)) + 4 * gq8 + (hv & 3) : tid;
+  const int ng = (a.nq + 15) / 16;
   float num = 0.f, den = 0.f, mrun = -INFINITY;
   for (int c0 = 0; c0 < ns; c0 += MERGE_RB) {
     const int cn = min(MERGE_RB, ns - c0);
@@ -181,8 +224,15 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
 #pragma unroll
     for (int q = 0; q < MERGE_RB; ++q) {
       const int s = s0 + c0 + min(q, cn - 1);
-      const int64_t i = (((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid;
-      o[q] = F16 ? f16_to_f32(((const uint16_t*)a.opart)[i]) : ((const float*)a.opart)[i];
+      if constexpr (F16 && LANE) {
+        const int64_t i = ((((int64_t)s * a.nKv + kvh) * ng + j / 16) * (a.hd / 32) + pr) * 512 +
+                          8 * ((j & 15) + 16 * gq8) + hv;
+        o[q] = f16_to_f32(((const uint16_t*)a.opart)[i]);
+      } else if constexpr (F16) {
+        o[q] = f16_to_f32(((const uint16_t*)a.opart)[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid]);
+      } else {
+        o[q] = ((const float*)a.opart)[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
+      }
     }
     const float2 v = ml[((int64_t)(s0 + c0 + min(tid, cn - 1)) * a.nKv + kvh) * a.nq + j];
     if (tid < 64) {
@@ -215,11 +265,11 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
   if (a.planes) {
     const __bf16 hi = (__bf16)x;
     const __bf16 lo = (__bf16)(x - (float)hi);
-    a.planes[m * (a.nH * a.hd) + h * a.hd + tid] = __builtin_bit_cast(uint16_t, hi);
-    a.planes[a.plane + m * (a.nH * a.hd) + h * a.hd + tid] = __builtin_bit_cast(uint16_t, lo);
+    a.planes[m * (a.nH * a.hd) + h * a.hd + dim] = __builtin_bit_cast(uint16_t, hi);
+    a.planes[a.plane + m * (a.nH * a.hd) + h * a.hd + dim] = __builtin_bit_cast(uint16_t, lo);
     return;
   }
-  a.O[m * a.ldo + h * a.hd + tid] = x;
+  a.O[m * a.ldo + h * a.hd + dim] = x;
 }
 
 // markov_w1 / markov_w2 element (table_elem with the head's own storage)
@@ -536,14 +586,20 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int nrows = a.A * a.nKv * a.nq;
   if (nrows <= MERGE_FEW_ROWS) {
     // few rows: a workgroup per row keeps enough of the chip busy
-    if (a.part_f16) hipLaunchKernelGGL(k_merge_rows<true>, dim3(nrows), dim3(a.hd), 0, st, a);
-    else hipLaunchKernelGGL(k_merge_rows<false>, dim3(nrows), dim3(a.hd), 0, st, a);
+    if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else hipLaunchKernelGGL((k_merge_rows<false, false>), dim3(nrows), dim3(a.hd), 0, st, a);
     return hipGetLastError();
   }
-  const int per = 256 / (a.hd / 8);  // query rows per workgroup
-  const dim3 grid((nrows + per - 1) / per);
-  if (a.part_f16) hipLaunchKernelGGL(k_merge<true>, grid, dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_merge<false>, grid, dim3(256), 0, st, a);
+  const int per = 256 / (a.hd / 8);  // query rows per workgroup (row-major partials)
+  if (a.part_f16 && a.lane_order) {
+    const int64_t threads = (int64_t)a.A * a.nKv * ((a.nq + 15) / 16) * (a.hd / 32) * 64;
+    hipLaunchKernelGGL((k_merge<true, true>), dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, a);
+  } else if (a.part_f16) {
+    hipLaunchKernelGGL((k_merge<true, false>), dim3((nrows + per - 1) / per), dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL((k_merge<false, false>), dim3((nrows + per - 1) / per), dim3(256), 0, st, a);
+  }
   return hipGetLastError();
 }
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st) {

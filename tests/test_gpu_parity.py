@@ -213,6 +213,22 @@ def test_wide_attention_ragged_rows(gpu_lib):
     assert checked >= 40
 
 
+def test_wide_attention_single_row(gpu_lib):
+    """One row with 2100 context keys: the attention kernel that holds every
+    query row of the kv head (fp16 partials in its lanes' order) followed by
+    the merge that gives each query row a workgroup."""
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=1, vocab_size=4096, mask_token_id=4095)
+    w = synth.Workload("wide_one", cfg, rows=1, ctx_lens=(2100,))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    assert rel_err(logits[0], ref["logits"][0]) <= 2e-2
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 8
+
+
 def test_rows_a32_ragged_full_size(gpu_lib):
     """32 rows, context lengths uniform in [1024, 4096], stored per row."""
     w = synth.WORKLOADS["rows_a32"]
