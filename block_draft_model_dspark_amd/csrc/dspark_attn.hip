@@ -100,9 +100,16 @@ __device__ __forceinline__ void attn_pass(const uint16_t* Ks, const uint16_t* Vt
 #pragma unroll
   for (int t = 0; t < NTW; ++t) {
     const int hr = 16 * (t0 + t) + ln;
-    const u32x2 va = *(const u32x2*)&Vt[hr * VSTR + 4 * gq];
-    const u32x2 vb = *(const u32x2*)&Vt[hr * VSTR + 16 + 4 * gq];
-    const bf16x8 vop = __builtin_bit_cast(bf16x8, u32x4{va[0], va[1], vb[0], vb[1]});
+    bf16x8 vop;
+    if constexpr (ONE) {
+      // one-plane chunks store V^T with keys in the score layout's k-slot
+      // order (slot 8g + e: key 4g + e, then 16 + 4g + e - 4), one 16-byte read
+      vop = __builtin_bit_cast(bf16x8, *(const u32x4*)&Vt[hr * VSTR + 8 * gq]);
+    } else {
+      const u32x2 va = *(const u32x2*)&Vt[hr * VSTR + 4 * gq];
+      const u32x2 vb = *(const u32x2*)&Vt[hr * VSTR + 16 + 4 * gq];
+      vop = __builtin_bit_cast(bf16x8, u32x4{va[0], va[1], vb[0], vb[1]});
+    }
     o[t] = mfma16(vop, ph, o[t]);
     o[t] = mfma16(vop, pl, o[t]);
   }
@@ -169,7 +176,10 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
         const uint32_t r1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
         const uint32_t m0 = odd ? vw[2] : vw[0], m1 = odd ? vw[3] : vw[1];  // this lane's four dims
         const int e0 = odd ? 4 : 0;
-        uint32_t* vrow = (uint32_t*)&Vt[(8 * c8 + e0) * VSTR + (key & ~1)];
+        // k-slot of the pair's even key: keys 4g.. of each half of the chunk
+        // take slots 8g.. (first half) and 8g + 4.. (second half)
+        const int k2 = key & ~1, slot = 8 * ((k2 & 15) >> 2) + 4 * (k2 >> 4) + (k2 & 3);
+        uint32_t* vrow = (uint32_t*)&Vt[(8 * c8 + e0) * VSTR + slot];
         const uint32_t mine[4] = {m0 & 0xFFFFu, m0 >> 16, m1 & 0xFFFFu, m1 >> 16};
         const uint32_t part[4] = {r0 & 0xFFFFu, r0 >> 16, r1 & 0xFFFFu, r1 >> 16};
 #pragma unroll
