@@ -37,17 +37,17 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "f4b6ec8397a45c6293f41afa985cba190f3609cae4e85af016f3130af96baaba",
-                  "bytes_per_step": 713362022},
+                  "sha256": "90a089ff39aa48026c8a38c8d4dc44964a7b2515829c4288578a3f1c3a4bf4b5",
+                  "bytes_per_step": 713364480},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "a479109a16e0bd96889181540356476ce43fb021b50c079ddb5646cf01e26d2e",
-                  "bytes_per_step": 387687424},
+                  "sha256": "225e1604246d04b7cdc611ea9d7bd2d3781cdbc923289f1c0840302f1bfe6530",
+                  "bytes_per_step": 387673676},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "01b274b2bfd9d1c8fd7652270ef733087d2844411ca1f50464a55c8a26ac9709",
-                  "bytes_per_step": 2529535852},
+                  "sha256": "775ba5b1271d4e0e1c532b027cef420bc48aa224addfec9a0be6a406f5acd9ac",
+                  "bytes_per_step": 2529527507},
 }
 
 
