@@ -129,8 +129,9 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
   auto mli = [&](int s) { return ((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + j; };
+  // running max over batches of MERGE_SB splits (all loads of a batch in
+  // flight; a separate pass over the maxima would wait on each in turn)
   float mx = -INFINITY;
-  for (int s = 0; s < ns; ++s) mx = fmaxf(mx, ml[mli(s)].x);
   float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, den = 0.f;
   for (int c0 = 0; c0 < ns; c0 += MERGE_SB) {
     u32x4 raw[MERGE_SB][F16 ? 1 : 2];
@@ -149,6 +150,16 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
         raw[q][1] = *(const u32x4*)((const float*)a.opart + i + 4);
       }
       wv[q] = ml[mli(s)];
+    }
+    float bm = mx;
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q) bm = fmaxf(bm, wv[q].x);  // repeats of the last split change nothing
+    if (bm > mx) {
+      const float r = expf(mx - bm);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] *= r;
+      den *= r;
+      mx = bm;
     }
 #pragma unroll
     for (int q = 0; q < MERGE_SB; ++q)
