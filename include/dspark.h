@@ -102,8 +102,9 @@ void dspark_model_destroy(dspark_model* m);
 
 /* GEMMs over at least `rows` activation rows (a batch of draft rows, a long
  * context to project) run as a tiled bf16 MFMA GEMM over a product buffer in
- * the workspace, followed by the GEMM's epilogue; fewer rows stream the
- * weights once per 16-row tile.  Both compute the same product (fp32
+ * the workspace, followed by the GEMM's epilogue (gate|up and lm_head form
+ * theirs in the tiled kernel's store when one K slice holds the product);
+ * fewer rows stream the weights once per 16-row tile.  Both compute the same product (fp32
  * activations as bf16 hi + lo planes); the context projection of bf16 rows
  * switches at four times `rows`.  rows <= 0 keeps every GEMM on the
  * weight-streaming kernel.  Default 256.  Workspace sizes depend on it: set it
