@@ -229,6 +229,24 @@ def test_wide_attention_single_row(gpu_lib):
     assert checked >= 8
 
 
+def test_max_rows_a64(gpu_lib):
+    """The largest batch a call takes (64 rows = 1024 block rows): tiled GEMMs
+    (gate|up fused on one K slice), the attention that holds every query row
+    of a kv head with the splits of row a on XCD a mod 8, the merge over many
+    rows; contexts of 0..79 keys, 2512 in total; Markov head active."""
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=1, vocab_size=4096, mask_token_id=4095)
+    lens = [(a * 37) % 80 for a in range(64)]
+    w = synth.Workload("rows_a64", cfg, rows=64, ctx_lens=tuple(lens))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(64):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 256
+
+
 def test_rows_a32_ragged_full_size(gpu_lib):
     """32 rows, context lengths uniform in [1024, 4096], stored per row."""
     w = synth.WORKLOADS["rows_a32"]
