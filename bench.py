@@ -37,17 +37,17 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "90a089ff39aa48026c8a38c8d4dc44964a7b2515829c4288578a3f1c3a4bf4b5",
-                  "bytes_per_step": 713364480},
+                  "sha256": "1f3e5cd268c1fe9bd6c0d98cbc7eb8a8a9cf6ef7873740638c78264e5a96518c",
+                  "bytes_per_step": 713362176},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "225e1604246d04b7cdc611ea9d7bd2d3781cdbc923289f1c0840302f1bfe6530",
-                  "bytes_per_step": 387673676},
+                  "sha256": "83e5838c2569dbbc0845712d210f16f49bbb7a862288361a67ebcbb0dc04a335",
+                  "bytes_per_step": 387676083},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "775ba5b1271d4e0e1c532b027cef420bc48aa224addfec9a0be6a406f5acd9ac",
-                  "bytes_per_step": 2529527507},
+                  "sha256": "a3a40ca766981a12f05e3ccfbb69eda83df2b4c0c54ea0cdcebae617574b2dab",
+                  "bytes_per_step": 2530180665},
 }
 
 

@@ -77,10 +77,11 @@ template <class F>
 hipError_t timed(const char* name, hipStream_t st, F&& launch) {
   if (!g_prof) return launch();
   ProfEntry e{name, prof_event(), prof_event()};
-  if (e.a) hipEventRecord(e.a, st);
+  // timing is best effort: a launch whose events cannot be recorded is not logged
+  const bool ra = e.a && hipEventRecord(e.a, st) == hipSuccess;
   hipError_t r = launch();
-  if (e.b) hipEventRecord(e.b, st);
-  if (e.a && e.b) g_prof_log.push_back(e);
+  const bool rb = e.b && hipEventRecord(e.b, st) == hipSuccess;
+  if (ra && rb) g_prof_log.push_back(e);
   return r;
 }
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
@@ -493,8 +494,7 @@ int dspark_profile_read(dspark_kernel_time* out, int max) {
   std::vector<dspark_kernel_time> acc;
   for (const ProfEntry& e : g_prof_log) {
     float ms = 0.f;
-    hipEventSynchronize(e.b);
-    hipEventElapsedTime(&ms, e.a, e.b);
+    if (hipEventSynchronize(e.b) != hipSuccess || hipEventElapsedTime(&ms, e.a, e.b) != hipSuccess) ms = 0.f;
     size_t i = 0;
     while (i < acc.size() && std::strcmp(acc[i].name, e.name) != 0) ++i;
     if (i == acc.size()) acc.push_back(dspark_kernel_time{e.name, 0, 0.0});
