@@ -37,17 +37,17 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "1f3e5cd268c1fe9bd6c0d98cbc7eb8a8a9cf6ef7873740638c78264e5a96518c",
-                  "bytes_per_step": 713362176},
+                  "sha256": "ce0c76f5b59dacd04fe9d1694e4ec90a2575bb6fb2bb17822657054602b636d0",
+                  "bytes_per_step": 713366298},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "83e5838c2569dbbc0845712d210f16f49bbb7a862288361a67ebcbb0dc04a335",
-                  "bytes_per_step": 387676083},
+                  "sha256": "531300d380d7048787b1bbd5ece24c7c6928b83d59269c979c3e2bd39fcd5055",
+                  "bytes_per_step": 387663258},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "a3a40ca766981a12f05e3ccfbb69eda83df2b4c0c54ea0cdcebae617574b2dab",
-                  "bytes_per_step": 2530180665},
+                  "sha256": "3fb49e67cc81f629db1cb60690af5dbd154a56e297629022a7d8b02f271e6b44",
+                  "bytes_per_step": 2515317318},
 }
 
 

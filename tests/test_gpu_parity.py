@@ -313,7 +313,11 @@ def test_tiled_path_fused_logits(gpu_lib):
         assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
     checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
     assert checked >= 128
-    assert rel_err(logits, z0.cpu().numpy()) <= 1e-3
+    # the fused tiled lm_head multiplies the final hidden rows rounded to bf16
+    # (relative error <= 2**-9 per element) where the streaming path keeps them
+    # to ~16 bits, so the paths differ by that rounding: about 1e-3 of the
+    # largest logit at RMS, a few times that at the maximum over 1M logits
+    assert rel_err(logits, z0.cpu().numpy()) <= 5e-3
 
 
 @pytest.mark.parametrize("kind", ["target_features", "context_hidden"])
