@@ -37,17 +37,17 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "ce0c76f5b59dacd04fe9d1694e4ec90a2575bb6fb2bb17822657054602b636d0",
-                  "bytes_per_step": 713366298},
+                  "sha256": "fb44c067f2d74d2def348e9d6f4b53a9141479a5cf6f16289cc99d6ad481079e",
+                  "bytes_per_step": 713345638},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "531300d380d7048787b1bbd5ece24c7c6928b83d59269c979c3e2bd39fcd5055",
-                  "bytes_per_step": 387663258},
+                  "sha256": "346337f59d17af04f2bc511de9d8fdc2f7d2fddb9a20e37db1009271e81e0b36",
+                  "bytes_per_step": 387682534},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "3fb49e67cc81f629db1cb60690af5dbd154a56e297629022a7d8b02f271e6b44",
-                  "bytes_per_step": 2515317318},
+                  "sha256": "53d9f3ec81c5089d4ff5b15e01288afa1d70f4a85dc367c8971751d33be9ca64",
+                  "bytes_per_step": 2099728934},
 }
 
 

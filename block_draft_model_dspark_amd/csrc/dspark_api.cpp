@@ -180,7 +180,7 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols, int t
     const int64_t tiles = (int64_t)ceil_div(M, bt) * ceil_div(N, bt);
     const int steps = K / 64;
     int S = 1;
-    if (tiles < 512 && group_cols == 0) S = (int)std::min<int64_t>(4, (768 + tiles - 1) / tiles);
+    if (tiles < 512 && group_cols == 0) S = (int)std::min<int64_t>(8, (768 + tiles - 1) / tiles);
     S = std::max(1, std::min(S, steps / 2));
     const int sl = 2 * ceil_div(ceil_div(steps, S), 2);  // steps per slice, even
     p.kslice = std::min(K, 64 * sl);

@@ -132,7 +132,17 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   __shared__ __align__(16) uint16_t Bs[BN * TLD];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  // Tile order: workgroups go round-robin over the 8 XCDs in launch order, so
+  // column tile bx always runs on XCD bx mod 8; when the column tiles are a
+  // multiple of 8, each XCD takes the row tiles of one weight tile back to
+  // back, so they stream that weight tile through its L2 together.
+  int bx = blockIdx.x, by = blockIdx.y;
+  if ((gridDim.x & 7) == 0) {
+    const int w = blockIdx.x + gridDim.x * blockIdx.y, s = w >> 3;
+    bx = (s / gridDim.y) * 8 + (w & 7);
+    by = s % gridDim.y;
+  }
+  const int m0 = by * BM, n0 = bx * BN;
   const int kb = blockIdx.z * t.kslice, ke = min(t.K, kb + t.kslice);  // this slice of K (multiples of 64)
 
   // this thread's rows of the two tiles (clamped: rows past M or N repeat
@@ -148,7 +158,7 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   for (int j = 0; j < BIT; ++j) {
     const int it = tid + 256 * j, r = it >> 3, c8 = it & 7;
     // gate|up pairing: tile rows 0..63 are gate rows 64x.., 64..127 up rows
-    const int n = (BN == 128 && t.gelu) ? (r < 64 ? 64 * blockIdx.x + r : t.N / 2 + 64 * blockIdx.x + r - 64)
+    const int n = (BN == 128 && t.gelu) ? (r < 64 ? 64 * bx + r : t.N / 2 + 64 * bx + r - 64)
                                         : min(n0 + r, t.N - 1);
     // segment lookup with uniform (scalar) reads of the argument array
     const void* w = t.seg[0].w;
@@ -264,7 +274,7 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
               float* xe = &ex[(wm * 64 + r) * 64 + c];
               const float x = gelu_tanh(acc[i][j][q]) * *xe;
               if (t.act_planes) *xe = x;  // (this thread's own element)
-              else if (m < t.M) t.act[(int64_t)m * t.ld_act + 64 * blockIdx.x + c] = x;
+              else if (m < t.M) t.act[(int64_t)m * t.ld_act + 64 * bx + c] = x;
             }
           }
       if (t.act_planes) {
@@ -281,7 +291,7 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
             for (int e = 0; e < 8; ++e) v[e] = ex[rr * 64 + 8 * c8 + e];
             bf16x8 hi, lo;
             split8(v, hi, lo);
-            uint16_t* dst = t.act_planes + (int64_t)m * I + 64 * blockIdx.x + 8 * c8;
+            uint16_t* dst = t.act_planes + (int64_t)m * I + 64 * bx + 8 * c8;
             *(u32x4*)dst = __builtin_bit_cast(u32x4, hi);
             *(u32x4*)(dst + t.act_plane) = __builtin_bit_cast(u32x4, lo);
           }
