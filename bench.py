@@ -38,16 +38,16 @@ TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "fb44c067f2d74d2def348e9d6f4b53a9141479a5cf6f16289cc99d6ad481079e",
-                  "bytes_per_step": 713345638},
+                  "bytes_per_step": 713365171},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "346337f59d17af04f2bc511de9d8fdc2f7d2fddb9a20e37db1009271e81e0b36",
-                  "bytes_per_step": 387682534},
+                  "bytes_per_step": 387669018},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "53d9f3ec81c5089d4ff5b15e01288afa1d70f4a85dc367c8971751d33be9ca64",
-                  "bytes_per_step": 2099728934},
+                  "sha256": "e5dada7bd155f9185a0df8146b059e430ee3dbddc8298ff0f7d19f63fda4bc2f",
+                  "bytes_per_step": 2101155270},
 }
 
 

@@ -133,11 +133,14 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   // Tile order: workgroups go round-robin over the 8 XCDs in launch order, so
-  // column tile bx always runs on XCD bx mod 8; when the column tiles are a
-  // multiple of 8, each XCD takes the row tiles of one weight tile back to
-  // back, so they stream that weight tile through its L2 together.
+  // column tile bx always runs on XCD bx mod 8. When the weights are the big
+  // operand (at most 8 row tiles) and the column tiles are a multiple of 8,
+  // each XCD takes the row tiles of one weight tile back to back, so they
+  // stream that weight tile through its L2 together; with many row tiles the
+  // plain order keeps two column tiles of the same rows together instead,
+  // which shares the (then bigger) activation rows.
   int bx = blockIdx.x, by = blockIdx.y;
-  if ((gridDim.x & 7) == 0) {
+  if ((gridDim.x & 7) == 0 && gridDim.y <= 8) {
     const int w = blockIdx.x + gridDim.x * blockIdx.y, s = w >> 3;
     bx = (s / gridDim.y) * 8 + (w & 7);
     by = s % gridDim.y;
