@@ -132,18 +132,22 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   __shared__ __align__(16) uint16_t Bs[BN * TLD];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  // Tile order: workgroups go round-robin over the 8 XCDs in launch order, so
-  // column tile bx always runs on XCD bx mod 8. When the weights are the big
-  // operand (at most 8 row tiles) and the column tiles are a multiple of 8,
-  // each XCD takes the row tiles of one weight tile back to back, so they
-  // stream that weight tile through its L2 together; with many row tiles the
-  // plain order keeps two column tiles of the same rows together instead,
-  // which shares the (then bigger) activation rows.
+  // Tile order: workgroups go round-robin over the 8 XCDs in launch order
+  // (linear id w runs on XCD w mod 8), and each XCD has its own L2. When the
+  // weights are the big operand (at most 8 row tiles) and the column tiles
+  // are a multiple of 8, XCD x takes the row tiles of column tile x, x + 8, ...
+  // back to back, so they stream that weight tile through its L2 together.
+  // With more than 8 row tiles, a multiple of 8, the activation rows are the big
+  // operand: XCD x takes row tiles x, x + 8, ... each across every column
+  // tile, so each activation row is read by one XCD only.
   int bx = blockIdx.x, by = blockIdx.y;
+  const int w = blockIdx.x + gridDim.x * blockIdx.y, s = w >> 3;
   if ((gridDim.x & 7) == 0 && gridDim.y <= 8) {
-    const int w = blockIdx.x + gridDim.x * blockIdx.y, s = w >> 3;
     bx = (s / gridDim.y) * 8 + (w & 7);
     by = s % gridDim.y;
+  } else if ((gridDim.y & 7) == 0 && gridDim.y > 8) {
+    by = (s / gridDim.x) * 8 + (w & 7);
+    bx = s % gridDim.x;
   }
   const int m0 = by * BM, n0 = bx * BN;
   const int kb = blockIdx.z * t.kslice, ke = min(t.K, kb + t.kslice);  // this slice of K (multiples of 64)
