@@ -38,16 +38,16 @@ TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "fb44c067f2d74d2def348e9d6f4b53a9141479a5cf6f16289cc99d6ad481079e",
-                  "bytes_per_step": 713357594},
+                  "bytes_per_step": 713350733},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "346337f59d17af04f2bc511de9d8fdc2f7d2fddb9a20e37db1009271e81e0b36",
-                  "bytes_per_step": 387672550},
+                  "bytes_per_step": 387662976},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "b9d1b9c63b9ccaa802e2075a68fcdcaae0b2a9c7d0d796149c6c09a46a825d07",
-                  "bytes_per_step": 2100560352},
+                  "sha256": "d93481b5fd71a0b6dda0f3c5ea70d8633f8153bea0e1ecf9472421d6f4c18e41",
+                  "bytes_per_step": 2106370067},
 }
 
 

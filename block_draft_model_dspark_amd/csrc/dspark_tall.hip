@@ -146,8 +146,16 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
     bx = (s / gridDim.y) * 8 + (w & 7);
     by = s % gridDim.y;
   } else if ((gridDim.y & 7) == 0 && gridDim.y > 8) {
-    by = (s / gridDim.x) * 8 + (w & 7);
-    bx = s % gridDim.x;
+    if ((gridDim.x & 7) == 0) {
+      // its row tiles against 8 column tiles at a time, so that the tiles in
+      // flight on the XCD share weight tiles as well
+      const int R = gridDim.y >> 3, inner = s % (8 * R), outer = s / (8 * R);
+      by = 8 * (inner >> 3) + (w & 7);
+      bx = 8 * outer + (inner & 7);
+    } else {
+      by = (s / gridDim.x) * 8 + (w & 7);
+      bx = s % gridDim.x;
+    }
   }
   const int m0 = by * BM, n0 = bx * BN;
   const int kb = blockIdx.z * t.kslice, ke = min(t.K, kb + t.kslice);  // this slice of K (multiples of 64)
