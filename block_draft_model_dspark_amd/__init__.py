@@ -25,7 +25,7 @@ EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tal
             "dspark_model_prepare",
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
-            "dspark_last_error")
+            "dspark_tall_tile_of", "dspark_last_error")
 
 
 class DsparkError(RuntimeError):
@@ -91,6 +91,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_profile_enable.restype = None
     lib.dspark_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
     lib.dspark_profile_read.restype = ctypes.c_int
+    lib.dspark_tall_tile_of.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                                        ctypes.POINTER(ctypes.c_int)]
+    lib.dspark_tall_tile_of.restype = ctypes.c_int
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
     for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
@@ -113,6 +116,20 @@ def _stream_handle(stream=None) -> int:
 
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
+
+
+def _keep_for(stream, *tensors) -> None:
+    """Tensors allocated on the current stream but read or written by work
+    enqueued on another `stream`: tell PyTorch's caching allocator not to
+    hand their memory out again before that stream's work is done."""
+    if stream is None:
+        return
+    import torch
+    if stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
 
 
 def _torch_dtype(kind: str):
@@ -205,6 +222,7 @@ class Model:
         n = _lib.dspark_model_aux_bytes(self.handle)
         self.aux = torch.empty(n, dtype=torch.uint8, device="cuda")
         _check(_lib.dspark_model_prepare(self.handle, self.aux.data_ptr(), n, _stream_handle(stream)))
+        _keep_for(stream, self.aux)
         return self
 
     def set_tall_rows(self, rows: int):
@@ -257,6 +275,7 @@ def project_context_kv(model: Model, x, pos0: Sequence[int], input_kind: int = I
     vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_out])
     _check(_lib.dspark_project_context_kv(model.handle, input_kind, x.data_ptr(), B, L, pos, kp, vp,
                                           workspace.data_ptr(), n, _stream_handle(stream)))
+    _keep_for(stream, workspace, *k_out, *v_out)
     return k_out, v_out
 
 
@@ -291,6 +310,7 @@ class DraftCall:
         _check(_lib.dspark_draft_rows(m.handle, self.A, self.kp, self.vp, self.lens, self.anchors, self.positions,
                                       self.tokens.data_ptr(), _ptr(self.logits),
                                       _ptr(m.aux), self.ws.data_ptr(), self.nbytes, _stream_handle(stream)))
+        _keep_for(stream, self.ws, self.tokens, self.logits)
         return self.tokens
 
 
@@ -320,4 +340,5 @@ def draft_block(model: Model, k_ctx, v_ctx, anchor: int, position: int, collect_
     vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_ctx])
     _check(_lib.dspark_draft_block(model.handle, kp, vp, L, int(anchor), int(position), tokens.data_ptr(),
                                    _ptr(logits), _ptr(model.aux), ws.data_ptr(), n, _stream_handle(stream)))
+    _keep_for(stream, ws, tokens, logits)
     return tokens, logits

@@ -477,11 +477,11 @@ dspark_status check_config(const dspark_config& c) {
   if (c.weight_dtype != DSPARK_F32 && c.weight_dtype != DSPARK_BF16 && c.weight_dtype != DSPARK_Q4)
     return fail(DSPARK_ERR_UNSUPPORTED, "weight_dtype must be F32, BF16 or Q4");
   if (c.weight_dtype == DSPARK_Q4) {
+    if (c.group_size != 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 group size %d not built (64)", c.group_size);
+    if (c.markov_rank % 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 Markov tables need rank %% 64 == 0");
     // The first GPU run of a 4-bit round faulted and no cause has been shown
     // yet; the path stays switched off until one is.
     return fail(DSPARK_ERR_UNSUPPORTED, "4-bit weights are disabled in this build (GPU fault under analysis)");
-    if (c.group_size != 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 group size %d not built (64)", c.group_size);
-    if (c.markov_rank % 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 Markov tables need rank %% 64 == 0");
   }
   return DSPARK_OK;
 }
@@ -491,6 +491,14 @@ dspark_status check_config(const dspark_config& c) {
 extern "C" {
 
 const char* dspark_last_error(void) { return g_err.c_str(); }
+
+dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by) {
+  g_err.clear();
+  if (gx <= 0 || gy <= 0 || !bx || !by || w < 0 || (int64_t)w >= (int64_t)gx * gy)
+    return fail(DSPARK_ERR_INVALID_ARG, "grid %d x %d, workgroup %d", gx, gy, w);
+  tall_tile_of(gx, gy, w, *bx, *by);
+  return DSPARK_OK;
+}
 
 void dspark_profile_enable(int on) { g_prof = on != 0; }
 
@@ -739,9 +747,8 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
 }
 
 size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, int64_t total_ctx) {
-  (void)max_ctx;
-  (void)total_ctx;
-  if (!m || A <= 0 || A > MAX_ROWS) return 0;
+  // the layout does not depend on the context lengths (see draft_layout)
+  if (!m || A <= 0 || A > MAX_ROWS || max_ctx < 0 || total_ctx < 0) return 0;
   return draft_layout(m, A, true).total;
 }
 

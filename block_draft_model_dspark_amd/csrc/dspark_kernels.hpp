@@ -134,6 +134,40 @@ struct TallArgs {
   int64_t act_plane;
 };
 
+// Tile order of the tiled GEMM: workgroups go round-robin over the 8 XCDs
+// in launch order (linear id w runs on XCD w mod 8), and each XCD has its own
+// L2.  Maps the linear workgroup id w of a gx x gy grid (column tiles x row
+// tiles) to the output tile (bx, by) it computes:
+//  - the weights are the big operand (at most 8 row tiles) and the column
+//    tiles are a multiple of 8: XCD x takes the row tiles of column tile
+//    x, x + 8, ... back to back, so they stream that weight tile through its
+//    L2 together;
+//  - more than 8 row tiles, a multiple of 8 (the activation rows are the big
+//    operand): XCD x takes row tiles x, x + 8, ... each across every column
+//    tile, so each activation row is read by one XCD only; when the column
+//    tiles are a multiple of 8 too, against 8 column tiles at a time, so the
+//    tiles in flight on the XCD share weight tiles as well;
+//  - otherwise the plain order bx = w mod gx, by = w / gx.
+// A bijection of [0, gx gy) onto the tiles in every case.
+__host__ __device__ inline void tall_tile_of(int gx, int gy, int w, int& bx, int& by) {
+  bx = w % gx;
+  by = w / gx;
+  const int s = w >> 3;
+  if ((gx & 7) == 0 && gy <= 8) {
+    bx = (s / gy) * 8 + (w & 7);
+    by = s % gy;
+  } else if ((gy & 7) == 0 && gy > 8) {
+    if ((gx & 7) == 0) {
+      const int R = gy >> 3, inner = s % (8 * R), outer = s / (8 * R);
+      by = 8 * (inner >> 3) + (w & 7);
+      bx = 8 * outer + (inner & 7);
+    } else {
+      by = (s / gx) * 8 + (w & 7);
+      bx = s % gx;
+    }
+  }
+}
+
 // per-row data of a draft round
 struct RowTab {
   int A, gamma;

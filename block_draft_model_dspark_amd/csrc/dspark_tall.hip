@@ -132,31 +132,9 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
   __shared__ __align__(16) uint16_t Bs[BN * TLD];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, ln = lane & 15, gq = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
-  // Tile order: workgroups go round-robin over the 8 XCDs in launch order
-  // (linear id w runs on XCD w mod 8), and each XCD has its own L2. When the
-  // weights are the big operand (at most 8 row tiles) and the column tiles
-  // are a multiple of 8, XCD x takes the row tiles of column tile x, x + 8, ...
-  // back to back, so they stream that weight tile through its L2 together.
-  // With more than 8 row tiles, a multiple of 8, the activation rows are the big
-  // operand: XCD x takes row tiles x, x + 8, ... each across every column
-  // tile, so each activation row is read by one XCD only.
-  int bx = blockIdx.x, by = blockIdx.y;
-  const int w = blockIdx.x + gridDim.x * blockIdx.y, s = w >> 3;
-  if ((gridDim.x & 7) == 0 && gridDim.y <= 8) {
-    bx = (s / gridDim.y) * 8 + (w & 7);
-    by = s % gridDim.y;
-  } else if ((gridDim.y & 7) == 0 && gridDim.y > 8) {
-    if ((gridDim.x & 7) == 0) {
-      // its row tiles against 8 column tiles at a time, so that the tiles in
-      // flight on the XCD share weight tiles as well
-      const int R = gridDim.y >> 3, inner = s % (8 * R), outer = s / (8 * R);
-      by = 8 * (inner >> 3) + (w & 7);
-      bx = 8 * outer + (inner & 7);
-    } else {
-      by = (s / gridDim.x) * 8 + (w & 7);
-      bx = s % gridDim.x;
-    }
-  }
+  // tile order: see tall_tile_of (XCD-aware renumbering of the grid)
+  int bx, by;
+  tall_tile_of(gridDim.x, gridDim.y, blockIdx.x + gridDim.x * blockIdx.y, bx, by);
   const int m0 = by * BM, n0 = bx * BN;
   const int kb = blockIdx.z * t.kslice, ke = min(t.K, kb + t.kslice);  // this slice of K (multiples of 64)
 

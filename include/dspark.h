@@ -140,8 +140,12 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
                                         const int32_t* pos0_host, void* const* k_out_dev, void* const* v_out_dev,
                                         void* ws_dev, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace for dspark_draft_rows with A rows whose context lengths sum to at
- * most total_ctx and none exceeds max_ctx. */
+/* Workspace for dspark_draft_rows with A rows (1..64) whose context lengths
+ * sum to at most total_ctx and none exceeds max_ctx.  The size depends on
+ * the model and A only: the attention split plan holds at most 512 + 2A
+ * splits whatever the context lengths, and no other buffer scales with
+ * them.  The context arguments are checked (0 for negative values) so that
+ * a later plan may use them.  0 for an invalid model or A. */
 size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, int64_t total_ctx);
 
 /* deepspec.ts, draftRows at temperature 0 with confidence truncation off
@@ -183,6 +187,14 @@ typedef struct {
 } dspark_kernel_time;
 void dspark_profile_enable(int on);
 int dspark_profile_read(dspark_kernel_time* out, int max);
+
+/* Diagnostic (host only, no HIP call): the output tile (column tile *bx,
+ * row tile *by) that workgroup `w` of a gx x gy grid of the tiled GEMM
+ * computes.  The tiled kernel renumbers its workgroups so that the tiles
+ * dealt to one XCD share operands in that XCD's L2; the map is a bijection
+ * of [0, gx*gy) onto the tiles.  DSPARK_ERR_INVALID_ARG for non-positive
+ * sizes, w outside [0, gx*gy) or null outputs. */
+dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by);
 
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* dspark_last_error(void);

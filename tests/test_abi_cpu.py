@@ -156,3 +156,30 @@ def test_draft_rows_host_validation(dsp):
     assert lib.dspark_project_context_kv(h, 0, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws - 1, None) == 4
     assert lib.dspark_project_context_kv(h, 7, FAKE, 1, 32, p0, outs, outs, FAKE * 16, n_ws, None) == 1
     lib.dspark_model_destroy(h)
+
+
+@pytest.mark.parametrize("gx,gy", [(1, 1), (3, 5), (8, 1), (8, 8), (16, 4), (256, 4), (16, 64), (8, 64),
+                                   (36, 16), (12, 24), (24, 16), (7, 9), (64, 8), (128, 128)])
+def test_tall_tile_order_is_a_bijection(dsp, gx, gy):
+    """The tiled GEMM's XCD-aware renumbering covers every output tile once
+    (for the grid shapes of the round and the projection and odd ones)."""
+    lib = dsp._lib
+    bx, by = ctypes.c_int(), ctypes.c_int()
+    seen = set()
+    for w in range(gx * gy):
+        assert lib.dspark_tall_tile_of(gx, gy, w, ctypes.byref(bx), ctypes.byref(by)) == 0
+        assert 0 <= bx.value < gx and 0 <= by.value < gy
+        seen.add((bx.value, by.value))
+    assert len(seen) == gx * gy
+    assert lib.dspark_tall_tile_of(gx, gy, gx * gy, ctypes.byref(bx), ctypes.byref(by)) == 1
+
+
+def test_tall_tile_order_keeps_a_row_tile_on_one_xcd(dsp):
+    """More than 8 row tiles: every tile of row tile r runs on XCD r mod 8
+    (workgroup w on XCD w mod 8), so an activation row is fetched by one L2."""
+    lib = dsp._lib
+    bx, by = ctypes.c_int(), ctypes.c_int()
+    for gx, gy in [(16, 64), (8, 64), (12, 24)]:
+        for w in range(gx * gy):
+            lib.dspark_tall_tile_of(gx, gy, w, ctypes.byref(bx), ctypes.byref(by))
+            assert by.value % 8 == w % 8

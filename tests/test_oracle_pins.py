@@ -271,6 +271,30 @@ def test_teacher_forced_matches_free_walk():
     assert np.array_equal(tf, toks) and np.allclose(tmg, mg)
 
 
+def test_teacher_forced_scores_with_the_given_previous_tokens():
+    """In the chain construction (W1 = I, W2 = c P) the step-k winner is
+    P(previous token), so a checker fed tokens that depart from the free walk
+    must answer perm[tokens[k-1]] at step k (the anchor's image at k = 0), not
+    the free walk's token."""
+    V = 7
+    cfg = synth.scaled(SMALL, vocab_size=V, markov_rank=V, mask_token_id=V - 1, block_size=6)
+    m = small_model(cfg)
+    perm = np.array([3, 5, 0, 6, 1, 2, 4])
+    P = np.zeros((V, V))
+    P[perm, np.arange(V)] = 1.0
+    m.w1 = np.eye(V)
+    m.w2 = 1000.0 * P
+    z = rand((cfg.gamma, V), 17)
+    anchor = 2
+    free, _ = O.markov_walk(m, z, anchor)
+    given = [4, 4, 0, 6, 1, 5]  # departs from the free walk at step 0
+    assert given[0] != free[0]
+    tf, mg = O.teacher_forced(m, z, anchor, given)
+    prevs = [anchor] + given[:-1]
+    assert tf.tolist() == [int(perm[p]) for p in prevs]
+    assert np.all(mg > 900.0)  # the chain term dominates every step
+
+
 # ---------------------------------------------------------------- 4-bit
 
 
@@ -297,18 +321,43 @@ def test_q4_oracle_equals_dense_oracle_on_dequantized_weights():
     cfg = synth.scaled(SMALL, weight_dtype=synth.Q4, act_dtype=synth.BF16, hidden_size=64,
                        global_head_dim=32, intermediate_size=128, markov_rank=64, group_size=64,
                        target_hidden_size=64)
-    st = synth.make_model(cfg)
+    st = synth.make_model(cfg, markov_active=True)
     mq = O.OracleModel(cfg, st)
-    md = O.OracleModel(cfg, st)
-    # a dense copy: every 4-bit tensor replaced by float64 values of w_hat
+    # A dense checkpoint: every 4-bit tensor replaced by float32 storage of
+    # w_hat = s * q + b, with the codes unpacked here by shifts and masks and
+    # s, b decoded from their bf16 bits (not through the oracle's decoder).
+    # s * q + b needs at most ~13 significant bits, so float32 holds it exactly.
+    dense = {}
+    n_q4 = 0
     for name, t in st.items():
-        if t.kind == "q4":
-            assert np.array_equal(O.decode(t), O.dequant_q4(t.data, t.scales, t.biases, t.shape[1], 64))
-    kv = [O.project_context_kv(mq, rand((1, 5, 64), 14), 0)]
-    kv_rows = [[(K[0], V[0]) for K, V in kv[0]]]
-    r1 = O.draft_rows(mq, kv_rows, [7], [5])
-    r2 = O.draft_rows(md, kv_rows, [7], [5])
-    assert np.array_equal(r1["logits"], r2["logits"])
+        if t.kind != "q4":
+            dense[name] = t
+            continue
+        n_q4 += 1
+        rows, cols = t.shape
+        words = np.asarray(t.data, dtype=np.uint64)
+        codes = np.stack([(words >> np.uint64(4 * j)) & np.uint64(15) for j in range(8)], axis=-1)
+        codes = codes.reshape(rows, cols).astype(np.float64)
+        s = np.repeat(synth.bf16_bits_as_f32(t.scales).astype(np.float64), 64, axis=1)
+        b = np.repeat(synth.bf16_bits_as_f32(t.biases).astype(np.float64), 64, axis=1)
+        w_hat = codes * s + b
+        assert np.array_equal(w_hat.astype(np.float32).astype(np.float64), w_hat)
+        dense[name] = synth.Stored("f32", (rows, cols), w_hat.astype(np.float32))
+    assert n_q4 == len([n for n in st if synth.gen.is_matrix(n)])  # every matrix was 4-bit (S16)
+    md = O.OracleModel(cfg, dense)
+    ctx = rand((1, 5, 64), 14)
+    kvq = O.project_context_kv(mq, ctx, 0)
+    kvd = O.project_context_kv(md, ctx, 0)
+    for (Kq, Vq), (Kd, Vd) in zip(kvq, kvd):
+        assert np.allclose(Kq, Kd, rtol=1e-12, atol=1e-12) and np.allclose(Vq, Vd, rtol=1e-12, atol=1e-12)
+    rows_q = [[(K[0], V[0]) for K, V in kvq]]
+    r1 = O.draft_rows(mq, rows_q * 2, [7, 30], [5, 9])
+    r2 = O.draft_rows(md, rows_q * 2, [7, 30], [5, 9])
+    assert np.allclose(r1["logits"], r2["logits"], rtol=1e-12, atol=1e-12)
+    assert np.array_equal(r1["tokens"], r2["tokens"])
+    # and the 4-bit model is not the bf16-free identity: w_hat differs from the draw
+    assert not np.allclose(O.decode(st["lm_head.weight"]),
+                           synth.normal(cfg.seed, "lm_head.weight", (cfg.V, cfg.H), cfg.weight_std), atol=1e-6)
 
 
 # ---------------------------------------------------------------- whole round
