@@ -330,7 +330,16 @@ int attn_split_wide(int64_t total_ctx, int A) {
 // contexts long enough in total for the wide attention kernel
 constexpr int64_t ATTN_WIDE_MIN_KEYS = 2048;
 
-DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
+// Attention splits of a round over A rows whose contexts hold total_ctx keys:
+// each row has ceil(L_a / split) context splits and one block split, with
+// split >= ATT_KEYS and split >= total_ctx / 512 (attn_split; the wide plan's
+// splits are longer still), so sum_a ceil(L_a / split) < total_ctx / split + A
+// and there are at most min(512, ceil(total_ctx / ATT_KEYS)) + 2A of them.
+int64_t nsplit_bound(int64_t total_ctx, int A) {
+  return std::min<int64_t>(512, (total_ctx + ATT_KEYS - 1) / ATT_KEYS) + 2 * (int64_t)A;
+}
+
+DraftLayout draft_layout(const dspark_model* m, int A, bool with_z, int64_t total_ctx) {
   const dspark_config& c = m->c;
   const int M = A * c.block_size, H = c.hidden_size, I = c.intermediate_size, hd = c.global_head_dim;
   const int nH = c.num_attention_heads, nKv = c.num_global_key_value_heads;
@@ -348,7 +357,7 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   if (d.lm.tall == TALL_128 && d.lm.S == 1 && d.lm.np == 2 && c.vocab_size % 64 == 0) d.lm.np = 1;
   const size_t pmax = std::max({d.qk.pbytes, d.o.pbytes, d.gu.pbytes, d.dn.pbytes, d.lm.pbytes, (size_t)4});
   d.cwords = std::max({d.qk.cwords, d.o.cwords, d.gu.cwords, d.dn.cwords, d.lm.cwords});
-  d.nsplit_max = 512 + 2 * A;
+  d.nsplit_max = (int)nsplit_bound(total_ctx, A);
   const int NC = nc_of(m);
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -373,8 +382,11 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z) {
   d.kb = take((size_t)A * nKv * c.block_size * hd * 4);
   d.vb = take((size_t)A * nKv * c.block_size * hd * 4);
   d.ssq = take((size_t)(nH + nKv) * (hd / 64) * M * 4);
-  // fp32 partials [split, kvh, nq, hd], or fp16 ones in groups of 16 query rows
-  d.opart = take((size_t)d.nsplit_max * nKv * std::max((size_t)m->nq * hd * 4, (size_t)((m->nq + 15) / 16) * 16 * hd * 2));
+  // fp32 partials [split, kvh, nq, hd] (fp32 cache), or fp16 ones in groups
+  // of 16 query rows (bf16 cache)
+  const size_t part_bytes = c.act_dtype == DSPARK_BF16 ? (size_t)((m->nq + 15) / 16) * 16 * hd * 2
+                                                       : (size_t)m->nq * hd * 4;
+  d.opart = take((size_t)d.nsplit_max * nKv * part_bytes);
   d.ml = take((size_t)d.nsplit_max * nKv * m->nq * 2 * 4);
   d.z = with_z ? take((size_t)M * c.vocab_size * 4) : 0;
   d.lohi = take((size_t)M * NC * 8);
@@ -747,9 +759,8 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
 }
 
 size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, int64_t total_ctx) {
-  // the layout does not depend on the context lengths (see draft_layout)
-  if (!m || A <= 0 || A > MAX_ROWS || max_ctx < 0 || total_ctx < 0) return 0;
-  return draft_layout(m, A, true).total;
+  if (!m || A <= 0 || A > MAX_ROWS || max_ctx < 0 || total_ctx < 0 || total_ctx > (int64_t)A * max_ctx) return 0;
+  return draft_layout(m, A, true, total_ctx).total;
 }
 
 dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const* k_ctx_dev,
@@ -783,7 +794,7 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
       if (ctx_len_host[a] > 0 && (!k_ctx_dev[l * A + a] || !v_ctx_dev[l * A + a]))
         return fail(DSPARK_ERR_INVALID_ARG, "null context K/V for layer %d row %d", l, a);
   }
-  const DraftLayout d = draft_layout(m, A, logits_dev == nullptr);
+  const DraftLayout d = draft_layout(m, A, logits_dev == nullptr, total_keys - (int64_t)A * G);
   if (ws_bytes < d.total) return fail(DSPARK_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, d.total);
   if ((uintptr_t)ws_dev & 255) return fail(DSPARK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 

@@ -141,11 +141,11 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
                                         void* ws_dev, size_t ws_bytes, hipStream_t stream);
 
 /* Workspace for dspark_draft_rows with A rows (1..64) whose context lengths
- * sum to at most total_ctx and none exceeds max_ctx.  The size depends on
- * the model and A only: the attention split plan holds at most 512 + 2A
- * splits whatever the context lengths, and no other buffer scales with
- * them.  The context arguments are checked (0 for negative values) so that
- * a later plan may use them.  0 for an invalid model or A. */
+ * sum to at most total_ctx and none exceeds max_ctx.  Only the attention
+ * partials scale with the contexts: a round holds at most
+ * min(512, ceil(total_ctx / 32)) + 2A key splits.  A workspace sized for
+ * total_ctx serves every call whose contexts sum to at most total_ctx.
+ * 0 for an invalid model, A, negative lengths or total_ctx > A * max_ctx. */
 size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, int64_t total_ctx);
 
 /* deepspec.ts, draftRows at temperature 0 with confidence truncation off

@@ -183,3 +183,21 @@ def test_tall_tile_order_keeps_a_row_tile_on_one_xcd(dsp):
         for w in range(gx * gy):
             lib.dspark_tall_tile_of(gx, gy, w, ctypes.byref(bx), ctypes.byref(by))
             assert by.value % 8 == w % 8
+
+
+def test_draft_workspace_scales_with_context_up_to_the_split_cap(dsp):
+    """Only the attention partials scale with the contexts: at most
+    min(512, ceil(total / 32)) + 2A splits, so the size grows with total_ctx
+    and stops growing once 512 context splits are reached."""
+    cfg = synth.FULL
+    c = make_config(dsp, cfg)
+    table, n, keep = fake_table(dsp, cfg)
+    st, h = create(dsp, c, table, n)
+    assert st == 0
+    f = dsp._lib.dspark_draft_workspace_bytes
+    sizes = [f(h, 2, t, t) for t in (0, 32, 512, 4096, 16384, 32768, 65536)]
+    assert all(s > 0 for s in sizes)
+    assert sizes == sorted(sizes) and sizes[1] > sizes[0]
+    assert sizes[-1] == sizes[-2] == f(h, 2, 10 ** 6, 10 ** 6)  # >= 512 * 32 keys: capped
+    assert f(h, 2, 100, 201) == 0 and f(h, 2, -1, 0) == 0 and f(h, 0, 10, 10) == 0
+    dsp._lib.dspark_model_destroy(h)
