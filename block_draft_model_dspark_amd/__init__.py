@@ -25,7 +25,8 @@ EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tal
             "dspark_model_prepare",
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
-            "dspark_tall_tile_of", "dspark_last_error")
+            "dspark_tall_tile_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
+            "dspark_last_error")
 
 
 class DsparkError(RuntimeError):
@@ -87,6 +88,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_draft_rows.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(I32),
                                       ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, P, P, SZ, P]
     lib.dspark_draft_block.argtypes = [P, ctypes.POINTER(P), ctypes.POINTER(P), I32, I32, I32, P, P, P, P, SZ, P]
+    lib.dspark_draft_rows_noalloc.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P),
+                                              ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, P,
+                                              P]
+    lib.dspark_draft_noalloc_max_bytes.argtypes = []
+    lib.dspark_draft_noalloc_max_bytes.restype = SZ
     lib.dspark_profile_enable.argtypes = [ctypes.c_int]
     lib.dspark_profile_enable.restype = None
     lib.dspark_profile_read.argtypes = [ctypes.POINTER(KernelTime), ctypes.c_int]
@@ -97,7 +103,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
     for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
-               "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block"):
+               "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block", "dspark_draft_rows_noalloc"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -322,6 +328,29 @@ def draft_rows(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: S
     call = DraftCall(model, k_rows, v_rows, ctx_lens, anchors, positions, collect_logits)
     call(stream)
     return call.tokens, call.logits
+
+
+def draft_rows_noalloc(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+                       positions: Sequence[int], tokens, logits=None, stream=None):
+    """draft_rows on the library's fixed per-GPU scratch array instead of a
+    workspace (for callers that cannot allocate): the caller passes the
+    outputs, tokens [A, gamma] int32 and optionally logits [A, gamma, V]
+    fp32, both on the GPU.  Calls that overlap on one GPU race."""
+    cfg = model.cfg
+    A = len(anchors)
+    nL = cfg.num_hidden_layers
+    kp = (ctypes.c_void_p * (nL * A))(*[k_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+    vp = (ctypes.c_void_p * (nL * A))(*[v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+    lens = (ctypes.c_int32 * A)(*[int(v) for v in ctx_lens])
+    anc = (ctypes.c_int32 * A)(*[int(v) for v in anchors])
+    pos = (ctypes.c_int32 * A)(*[int(v) for v in positions])
+    _check(_lib.dspark_draft_rows_noalloc(model.handle, A, kp, vp, lens, anc, pos, tokens.data_ptr(), _ptr(logits),
+                                          _ptr(model.aux), _stream_handle(stream)))
+    return tokens, logits
+
+
+def draft_noalloc_max_bytes() -> int:
+    return int(load_library().dspark_draft_noalloc_max_bytes())
 
 
 def draft_block(model: Model, k_ctx, v_ctx, anchor: int, position: int, collect_logits: bool = True,

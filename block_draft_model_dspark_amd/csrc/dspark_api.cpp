@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -498,6 +499,35 @@ dspark_status check_config(const dspark_config& c) {
   return DSPARK_OK;
 }
 
+// ---- fixed scratch for callers that cannot allocate ------------------------
+// The workspace of dspark_draft_rows_noalloc: one array per GPU in the
+// library's own code object (each GPU the library runs on holds it until the
+// process ends).  In host code `scratch` is only a host-side stand-in; its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is ever handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[NOALLOC_MAX_DEVICES] = {};
+
+// the device address of the current device's scratch array
+dspark_status scratch_address(void** out) {
+  int dev = -1;
+  HIPCHECK(hipGetDevice(&dev));
+  if (dev < 0 || dev >= NOALLOC_MAX_DEVICES) return fail(DSPARK_ERR_UNSUPPORTED, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    HIPCHECK(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)));
+    if (!ptr || ((uintptr_t)ptr & 255)) return fail(DSPARK_ERR_HIP, "scratch array has no usable device address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return DSPARK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -763,13 +793,20 @@ size_t dspark_draft_workspace_bytes(const dspark_model* m, int A, int max_ctx, i
   return draft_layout(m, A, true, total_ctx).total;
 }
 
-dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const* k_ctx_dev,
-                                const void* const* v_ctx_dev, const int32_t* ctx_len_host,
-                                const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
-                                float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
-                                hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// dspark_draft_rows on the caller's workspace (use_scratch false), or on this
+// device's fixed scratch array (use_scratch true; ws_dev and ws_bytes unused)
+dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                              const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                              const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
+                              float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
+                              hipStream_t stream, bool use_scratch) {
   g_err.clear();
-  if (!m || !k_ctx_dev || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host || !tokens_dev || !ws_dev)
+  if (!m || !k_ctx_dev || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host || !tokens_dev ||
+      (!ws_dev && !use_scratch))
     return fail(DSPARK_ERR_INVALID_ARG, "null argument");
   const dspark_config& c = m->c;
   if (A <= 0) return fail(DSPARK_ERR_INVALID_ARG, "A must be positive");
@@ -795,6 +832,16 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
         return fail(DSPARK_ERR_INVALID_ARG, "null context K/V for layer %d row %d", l, a);
   }
   const DraftLayout d = draft_layout(m, A, logits_dev == nullptr, total_keys - (int64_t)A * G);
+  if (use_scratch) {
+    if (d.total > NOALLOC_SCRATCH_BYTES)
+      return fail(DSPARK_ERR_WORKSPACE,
+                  "this round needs %zu bytes of scratch, above the %zu-byte fixed array of "
+                  "dspark_draft_rows_noalloc (use dspark_draft_rows with a workspace)",
+                  d.total, NOALLOC_SCRATCH_BYTES);
+    const dspark_status sst = scratch_address(&ws_dev);
+    if (sst) return sst;
+    ws_bytes = NOALLOC_SCRATCH_BYTES;
+  }
   if (ws_bytes < d.total) return fail(DSPARK_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, d.total);
   if ((uintptr_t)ws_dev & 255) return fail(DSPARK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
 
@@ -1053,6 +1100,30 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
   HIPCHECK(timed("markov_walk", stream, [&] { return launch_walk(w, stream); }));
   return DSPARK_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
+                                float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
+                                hipStream_t stream) {
+  return draft_rows_impl(m, A, k_ctx_dev, v_ctx_dev, ctx_len_host, anchors_host, positions_host, tokens_dev,
+                         logits_dev, aux_dev, ws_dev, ws_bytes, stream, false);
+}
+
+dspark_status dspark_draft_rows_noalloc(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                        const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                        const int32_t* anchors_host, const int32_t* positions_host,
+                                        int32_t* tokens_dev, float* logits_dev, const void* aux_dev,
+                                        hipStream_t stream) {
+  return draft_rows_impl(m, A, k_ctx_dev, v_ctx_dev, ctx_len_host, anchors_host, positions_host, tokens_dev,
+                         logits_dev, aux_dev, nullptr, 0, stream, true);
+}
+
+size_t dspark_draft_noalloc_max_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 dspark_status dspark_draft_block(const dspark_model* m, const void* const* k_ctx_dev, const void* const* v_ctx_dev,
                                  int32_t ctx_len, int32_t anchor, int32_t position, int32_t* tokens_dev,

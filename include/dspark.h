@@ -169,6 +169,27 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
                                 float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
                                 hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * dspark_draft_rows with its workspace taken from a fixed scratch array that
+ * the library holds on each GPU (dspark_draft_noalloc_max_bytes() bytes,
+ * 64 MiB, held from the library's load until the process ends).  Arguments
+ * as for dspark_draft_rows; the caller still passes every input and output.
+ * A round whose workspace (dspark_draft_workspace_bytes for these contexts;
+ * less when logits_dev is given) exceeds the array fails with
+ * DSPARK_ERR_WORKSPACE before anything is enqueued.  The call allocates
+ * nothing: its first call on a GPU only looks up the array's device address
+ * there.  Every call on one GPU shares that GPU's array and the array keeps
+ * the last call's contents (the round clears what it needs itself), so
+ * calls that overlap on one GPU (several streams or threads) race and must
+ * not be issued. */
+dspark_status dspark_draft_rows_noalloc(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                        const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                        const int32_t* anchors_host, const int32_t* positions_host,
+                                        int32_t* tokens_dev, float* logits_dev, const void* aux_dev,
+                                        hipStream_t stream);
+size_t dspark_draft_noalloc_max_bytes(void);
+
 /* deepspec-module.ts, draftBlock: draftRows with one row. */
 dspark_status dspark_draft_block(const dspark_model* m, const void* const* k_ctx_dev, const void* const* v_ctx_dev,
                                  int32_t ctx_len, int32_t anchor, int32_t position, int32_t* tokens_dev,
