@@ -1,19 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the DSpark draft round on one MI355X.
 
-Default step (--workload full_bf16_a1) = the whole hot path for one batch of
-the full-size workload: context K/V projection of the 512 context rows
-(4 layers of k_proj, k/v norms, RoPE) followed by one draft round (embedding,
-4 backbone layers, lm_head with softcap, Markov walk) for A = 1 block of
-gamma = 16 tokens.  --workload prefill_8192 times the K/V projection of 8192
-target-feature rows (fc, hidden_norm, 4-layer k_proj) in context rows/s;
---workload rows_a32 times one round over 32 ragged rows with per-row context
-K/V.  Inputs and weights are seeded synthetic data resident in HBM before
-timing.
+The headline step (full_bf16_a1) = the whole hot path for one batch of the
+full-size workload: context K/V projection of the 512 context rows (4 layers
+of k_proj, k/v norms, RoPE) followed by one draft round (embedding, 4 backbone
+layers, lm_head with softcap, Markov walk) for A = 1 block of gamma = 16
+tokens.  The default run adds two sub-measurements on the same model under
+"workloads": rows_a32 (one round over 32 ragged rows with per-row context
+K/V, blocks/s) and prefill_8192 (the K/V projection of 8192 target-feature
+rows: fc, hidden_norm, 4-layer k_proj; context rows/s).  --workload NAME
+measures one of them alone.  Inputs and weights are seeded synthetic data
+resident in HBM before timing.
 
 Prints one JSON line: the throughput, the roofline of the dominant kernel
 measured with HIP events on the launch stream, and the CPU oracle timed on a
-bounded sample of the same workload.
+bounded sample of the same workload (per workload).
 """
 import argparse
 import json
@@ -115,12 +116,11 @@ def oracle_threads():
     return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, seconds):
-    """The CPU oracle (as it stands) on the same step, bounded in time."""
+def cpu_baseline(w, seconds, om):
+    """The CPU oracle (as it stands) on the same step, bounded in time
+    (`om`: the decoded oracle model; decoding is excluded from the timing)."""
     import synth
     from oracle import dspark_oracle as O
-    cfg = w.model
-    om = O.OracleModel(cfg, synth.make_model(cfg, with_fc=False))  # decoding excluded from timing
     L = w.fixed_ctx_len
     ctx = O.decode(synth.ctx_hidden(w, 0, L))[None]
     anchors = synth.anchors(w)
@@ -139,13 +139,11 @@ def cpu_baseline(w, seconds):
                       f"{el:.1f} s, float64 NumPy"}
 
 
-def cpu_baseline_prefill(w, seconds):
+def cpu_baseline_prefill(w, seconds, om):
     """The oracle's fc + hidden_norm + 4-layer K/V projection on a bounded
     sample of the 8192 rows (the step is row-wise), scaled to rows/s."""
     import synth
     from oracle import dspark_oracle as O
-    cfg = w.model
-    om = O.OracleModel(cfg, synth.make_model(cfg, with_fc=True))
     x = O.decode(synth.target_features(w))
     rows = 256
     n = 0
@@ -163,13 +161,12 @@ def cpu_baseline_prefill(w, seconds):
                       f"the 4-layer K/V projection, {el:.1f} s, float64 NumPy"}
 
 
-def cpu_baseline_rows(w, lens, seconds):
+def cpu_baseline_rows(w, lens, seconds, om):
     """The oracle's draft round on the first rows of the batch (their own
     direct K/V and lengths), one row at a time until the time bound."""
     import synth
     from oracle import dspark_oracle as O
     cfg = w.model
-    om = O.OracleModel(cfg, synth.make_model(cfg, with_fc=False))
     anchors = synth.anchors(w)
     n = 0
     el = 0.0
@@ -218,13 +215,30 @@ def run_timed(step, args):
     return ms, prof, nprof
 
 
-def bench_full(args, dsp, synth, torch):
+class Shared:
+    """The full-size bf16 model (with fc and hidden_norm) on the GPU and, for
+    the CPU baselines, its float64 oracle copy: built once and used by every
+    workload of a run (C1, C2 and C3 share the model shapes)."""
+
+    def __init__(self, dsp, synth):
+        self.dsp, self.synth = dsp, synth
+        self.cfg = synth.WORKLOADS["full_bf16_a1"].model
+        self.stored = synth.make_model(self.cfg, with_fc=True)
+        self.model = dsp.Model(self.cfg, dsp.upload(self.stored)).prepare()
+        self._om = None
+
+    def oracle(self):
+        if self._om is None:
+            from oracle import dspark_oracle as O
+            self._om = O.OracleModel(self.cfg, self.stored)
+        return self._om
+
+
+def bench_full(args, dsp, synth, torch, sh):
     """Context K/V projection of 512 rows + one draft round of one block."""
     w = synth.WORKLOADS["full_bf16_a1"]
     cfg = w.model
-    stored = synth.make_model(cfg, with_fc=False)
-    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
-    del stored
+    model = sh.model
     L, A = w.fixed_ctx_len, w.rows
     x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
     anchors = synth.anchors(w)
@@ -270,17 +284,15 @@ def bench_full(args, dsp, synth, torch):
         "kernel_sum_us_per_step": round(kern_sum_us, 2),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, sh.oracle())
     return out
 
 
-def bench_prefill(args, dsp, synth, torch):
+def bench_prefill(args, dsp, synth, torch, sh):
     """fc + hidden_norm + 4-layer K/V projection of 8192 target-feature rows."""
     w = synth.WORKLOADS["prefill_8192"]
     cfg = w.model
-    stored = synth.make_model(cfg, with_fc=True)
-    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
-    del stored
+    model = sh.model
     B, L = w.prefill_batch, w.prefill_rows
     x = dsp.act_tensor(synth.target_features(w))
     k_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=torch.bfloat16, device="cuda") for _ in range(cfg.L)]
@@ -317,17 +329,15 @@ def bench_prefill(args, dsp, synth, torch):
         "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_prefill(w, args.cpu_seconds, sh.oracle())
     return out
 
 
-def bench_rows(args, dsp, synth, torch):
+def bench_rows(args, dsp, synth, torch, sh):
     """One draft round over 32 ragged rows whose context K/V is stored per row."""
     w = synth.WORKLOADS["rows_a32"]
     cfg = w.model
-    stored = synth.make_model(cfg, with_fc=False)
-    model = dsp.Model(cfg, dsp.upload(stored)).prepare()
-    del stored
+    model = sh.model
     lens = synth.ctx_lens(w)
     A = w.rows
     k_rows = [[None] * A for _ in range(cfg.L)]
@@ -371,7 +381,7 @@ def bench_rows(args, dsp, synth, torch):
         "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline_rows(w, lens, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline_rows(w, lens, args.cpu_seconds, sh.oracle())
     return out
 
 
@@ -384,8 +394,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--profile-steps", type=int, default=50)
-    ap.add_argument("--workload", choices=sorted(BENCHES), default="full_bf16_a1",
-                    help="full_bf16_a1 (default) is the headline line; the others are per-workload measurements")
+    ap.add_argument("--workload", choices=sorted(BENCHES) + ["all"], default="all",
+                    help="all (default): the headline full_bf16_a1 line with the rows_a32 and prefill_8192 "
+                         "measurements as sub-objects; a single name measures that workload alone")
+    ap.add_argument("--sub-steps", type=int, default=50,
+                    help="timed steps of each sub-workload in the default run")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -406,7 +419,22 @@ def main():
         calibrate_copy(args.calibrate_copy_mib, 4)
         return
     dsp.load_library()
-    print(json.dumps(BENCHES[args.workload](args, dsp, synth, torch)))
+    sh = Shared(dsp, synth)
+    if args.workload != "all":
+        print(json.dumps(BENCHES[args.workload](args, dsp, synth, torch, sh)), flush=True)
+        return
+    out = bench_full(args, dsp, synth, torch, sh)
+    print(f"full_bf16_a1: {out['value']} blocks/s", file=sys.stderr, flush=True)
+    sub = argparse.Namespace(**vars(args))
+    sub.steps, sub.warmup, sub.profile_steps = args.sub_steps, max(2, args.warmup // 4), min(args.profile_steps, 5)
+    out["workloads"] = {}
+    for name in ("rows_a32", "prefill_8192"):
+        r = BENCHES[name](sub, dsp, synth, torch, sh)
+        print(f"{name}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
+        for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "dtype"):
+            r.pop(k, None)
+        out["workloads"][name] = r
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":
