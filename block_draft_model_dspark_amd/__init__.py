@@ -26,6 +26,7 @@ EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tal
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
             "dspark_tall_tile_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
+            "dspark_draft_rows_conf",
             "dspark_last_error")
 
 
@@ -45,7 +46,9 @@ class Config(ctypes.Structure):
                 ("fc_in", ctypes.c_int32), ("rope_theta", ctypes.c_double),
                 ("partial_rotary_factor", ctypes.c_double), ("rms_norm_eps", ctypes.c_double),
                 ("final_logit_softcapping", ctypes.c_double), ("weight_dtype", ctypes.c_int32),
-                ("act_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("act_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32),
+                ("enable_confidence_head", ctypes.c_int32), ("confidence_head_with_markov", ctypes.c_int32),
+                ("confidence_threshold", ctypes.c_double)]
 
 
 class KernelTime(ctypes.Structure):
@@ -91,6 +94,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_draft_rows_noalloc.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P),
                                               ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32), P, P, P,
                                               P]
+    lib.dspark_draft_rows_conf.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P),
+                                           ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
+                                           ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, SZ, P]
     lib.dspark_draft_noalloc_max_bytes.argtypes = []
     lib.dspark_draft_noalloc_max_bytes.restype = SZ
     lib.dspark_profile_enable.argtypes = [ctypes.c_int]
@@ -103,7 +109,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
     for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
-               "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block", "dspark_draft_rows_noalloc"):
+               "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block", "dspark_draft_rows_noalloc",
+               "dspark_draft_rows_conf"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -199,6 +206,9 @@ class Model:
         c.weight_dtype = _KIND[cfg.weight_dtype]
         c.act_dtype = _KIND[cfg.act_dtype]
         c.group_size = cfg.group_size
+        c.enable_confidence_head = int(bool(getattr(cfg, "enable_confidence_head", False)))
+        c.confidence_head_with_markov = int(bool(getattr(cfg, "confidence_head_with_markov", False)))
+        c.confidence_threshold = float(getattr(cfg, "confidence_threshold", 0.0) or 0.0)
         self._c = c
         names = list(weights)
         self._names = [n.encode() for n in names]
@@ -328,6 +338,37 @@ def draft_rows(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: S
     call = DraftCall(model, k_rows, v_rows, ctx_lens, anchors, positions, collect_logits)
     call(stream)
     return call.tokens, call.logits
+
+
+def draft_rows_conf(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+                    positions: Sequence[int], thresholds: Optional[Sequence[float]] = None,
+                    collect_logits: bool = False, collect_conf: bool = True, stream=None):
+    """deepspec.ts, draftRows with the confidence head: returns a dict of
+    device tensors tokens [A, gamma] (the whole block), lengths [A] (each
+    row's confident prefix), conf [A, gamma] (when collect_conf) and logits
+    [A, gamma, V] (when collect_logits).  thresholds: gamma per-slot values,
+    or None for the config's confidence_threshold."""
+    import torch
+    cfg = model.cfg
+    A = len(anchors)
+    nL = cfg.num_hidden_layers
+    kp = (ctypes.c_void_p * (nL * A))(*[k_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+    vp = (ctypes.c_void_p * (nL * A))(*[v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+    lens = (ctypes.c_int32 * A)(*[int(v) for v in ctx_lens])
+    anc = (ctypes.c_int32 * A)(*[int(v) for v in anchors])
+    pos = (ctypes.c_int32 * A)(*[int(v) for v in positions])
+    thr = None if thresholds is None else (ctypes.c_float * cfg.gamma)(*[float(t) for t in thresholds])
+    out = {"tokens": torch.empty(A, cfg.gamma, dtype=torch.int32, device="cuda"),
+           "lengths": torch.empty(A, dtype=torch.int32, device="cuda")}
+    out["conf"] = torch.empty(A, cfg.gamma, dtype=torch.float32, device="cuda") if collect_conf else None
+    out["logits"] = torch.empty(A, cfg.gamma, cfg.V, dtype=torch.float32, device="cuda") if collect_logits else None
+    n = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _check(_lib.dspark_draft_rows_conf(model.handle, A, kp, vp, lens, anc, pos, thr, out["tokens"].data_ptr(),
+                                       _ptr(out["logits"]), _ptr(out["conf"]), out["lengths"].data_ptr(),
+                                       _ptr(model.aux), ws.data_ptr(), n, _stream_handle(stream)))
+    _keep_for(stream, ws, *[t for t in out.values() if t is not None])
+    return out
 
 
 def draft_rows_noalloc(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],

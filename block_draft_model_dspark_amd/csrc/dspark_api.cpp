@@ -91,7 +91,8 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct dspark_model {
   dspark_config c;
-  Mat embed, fc, lm, w1, w2;
+  Mat embed, fc, lm, w1, w2, conf;
+  const void* conf_b = nullptr;
   const void* hidden_norm = nullptr;
   const void* norm = nullptr;
   std::vector<LayerW> L;
@@ -300,7 +301,7 @@ GemmSeg seg_of(const Mat& w, int n0) {
 constexpr int ROW_PAD = 64;
 
 struct DraftLayout {
-  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, xop, xop2, T, total;
+  size_t hA, hB, Y, sums, rt, scal, O, act, P, cnt, q, kb, vb, ssq, opart, ml, z, lohi, xop, xop2, T, conf, total;
   bool dn_planes;  // the fused gate|up writes the tiled down projection's input planes (xop2)
   int64_t ldh, ldo, ldact;
   GemmPlan qk, o, gu, dn, lm;
@@ -396,6 +397,7 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z, int64_t tota
   d.xop2 = take(d.dn_planes ? (size_t)2 * M * I * 2 : 4);
   d.T = take(std::max({d.qk.tall ? (size_t)M * (nH + nKv) * hd * 4 : 0, d.gu.tall ? (size_t)M * 2 * I * 4 : 0,
                        d.qk.tbytes, d.o.tbytes, d.gu.tbytes, d.dn.tbytes, d.lm.tbytes, (size_t)4}));
+  d.conf = take((size_t)M * 4);
   d.total = off;
   return d;
 }
@@ -483,6 +485,9 @@ dspark_status check_config(const dspark_config& c) {
     return fail(DSPARK_ERR_UNSUPPORTED, "markov_rank must be a multiple of 8 and at most 256");
   if (c.mask_token_id < 0 || c.mask_token_id >= c.vocab_size)
     return fail(DSPARK_ERR_INVALID_ARG, "mask_token_id out of range");
+  if (c.enable_confidence_head && c.confidence_head_with_markov && c.markov_rank == 0)
+    return fail(DSPARK_ERR_INVALID_ARG, "confidence_head_with_markov requires markov_rank > 0");
+  if (c.block_size > CONF_MAX_GAMMA) return fail(DSPARK_ERR_UNSUPPORTED, "block_size > %d not built", CONF_MAX_GAMMA);
   if (!(c.rope_theta > 0) || !(c.partial_rotary_factor >= 0 && c.partial_rotary_factor <= 1) || !(c.rms_norm_eps >= 0))
     return fail(DSPARK_ERR_INVALID_ARG, "rope_theta, partial_rotary_factor or rms_norm_eps out of range");
   if (c.act_dtype != DSPARK_F32 && c.act_dtype != DSPARK_BF16)
@@ -622,6 +627,10 @@ dspark_status dspark_model_create(const dspark_config* cfg, const dspark_weight*
   if (c.markov_rank > 0) {
     mat("markov_head.markov_w1.weight", c.vocab_size, c.markov_rank, m->w1);
     mat("markov_head.markov_w2.weight", c.vocab_size, c.markov_rank, m->w2);
+  }
+  if (c.enable_confidence_head) {
+    mat("confidence_head.proj.weight", 1, H + (c.confidence_head_with_markov ? c.markov_rank : 0), m->conf);
+    m->conf_b = vec("confidence_head.proj.bias", 1);
   }
   for (int i = 0; i < c.num_hidden_layers && !err; ++i) {
     const std::string p = "layers." + std::to_string(i) + ".";
@@ -803,11 +812,15 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
                               const void* const* v_ctx_dev, const int32_t* ctx_len_host,
                               const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
                               float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
-                              hipStream_t stream, bool use_scratch) {
+                              hipStream_t stream, bool use_scratch, const float* thresholds_host = nullptr,
+                              float* conf_dev = nullptr, int32_t* lengths_dev = nullptr) {
   g_err.clear();
   if (!m || !k_ctx_dev || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host || !tokens_dev ||
       (!ws_dev && !use_scratch))
     return fail(DSPARK_ERR_INVALID_ARG, "null argument");
+  const bool head = m->c.enable_confidence_head != 0;
+  if (conf_dev && !head) return fail(DSPARK_ERR_INVALID_ARG, "confidence requested from a model without the head");
+  const bool need_conf = head && (conf_dev || lengths_dev);
   const dspark_config& c = m->c;
   if (A <= 0) return fail(DSPARK_ERR_INVALID_ARG, "A must be positive");
   if (A > MAX_ROWS) return fail(DSPARK_ERR_UNSUPPORTED, "A > %d not built", MAX_ROWS);
@@ -1075,7 +1088,8 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   g.nseg = 1;
   g.seg[0] = seg_of(m->lm, 0);
   g.P = P;
-  g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, m->norm, nullptr);
+  // the confidence head reads the final residual rows (hB is free by now)
+  g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, m->norm, need_conf ? hB : nullptr);
   float* z = logits_dev ? logits_dev : (float*)(ws + d.z);
   e.Y = z;
   e.cap = c.final_logit_softcapping > 0 ? (float)c.final_logit_softcapping : 0.f;
@@ -1098,6 +1112,31 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   w.w2 = m->w2.w; w.w2s = m->w2.s; w.w2b = m->w2.b;
   w.tokens = tokens_dev;
   HIPCHECK(timed("markov_walk", stream, [&] { return launch_walk(w, stream); }));
+
+  if (conf_dev || lengths_dev) {
+    ConfArgs cf{};
+    cf.rows = rows;
+    cf.head = need_conf ? 1 : 0;
+    cf.H = H;
+    cf.rank = c.markov_rank;
+    cf.with_markov = c.confidence_head_with_markov ? 1 : 0;
+    cf.wkind = m->conf.kind;
+    cf.group = c.group_size;
+    cf.act_bf16 = abf;
+    cf.hn = hB;
+    cf.ldh = d.ldh;
+    cf.wnorm = m->norm;
+    cf.eps = eps;
+    cf.pw = m->conf.w; cf.ps = m->conf.s; cf.pb = m->conf.b;
+    cf.bias = m->conf_b;
+    cf.w1 = m->w1.w; cf.w1s = m->w1.s; cf.w1b = m->w1.b;
+    cf.tokens = tokens_dev;
+    for (int k = 0; k < G; ++k)
+      cf.thr[k] = thresholds_host ? thresholds_host[k] : (float)c.confidence_threshold;
+    cf.conf = conf_dev ? conf_dev : (float*)(ws + d.conf);
+    cf.lengths = lengths_dev;
+    HIPCHECK(timed("confidence", stream, [&] { return launch_conf(cf, stream); }));
+  }
   return DSPARK_OK;
 }
 
@@ -1112,6 +1151,17 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
                                 hipStream_t stream) {
   return draft_rows_impl(m, A, k_ctx_dev, v_ctx_dev, ctx_len_host, anchors_host, positions_host, tokens_dev,
                          logits_dev, aux_dev, ws_dev, ws_bytes, stream, false);
+}
+
+dspark_status dspark_draft_rows_conf(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                     const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                     const int32_t* anchors_host, const int32_t* positions_host,
+                                     const float* thresholds_host, int32_t* tokens_dev, float* logits_dev,
+                                     float* conf_dev, int32_t* lengths_dev, const void* aux_dev, void* ws_dev,
+                                     size_t ws_bytes, hipStream_t stream) {
+  return draft_rows_impl(m, A, k_ctx_dev, v_ctx_dev, ctx_len_host, anchors_host, positions_host, tokens_dev,
+                         logits_dev, aux_dev, ws_dev, ws_bytes, stream, false, thresholds_host, conf_dev,
+                         lengths_dev);
 }
 
 dspark_status dspark_draft_rows_noalloc(const dspark_model* m, int A, const void* const* k_ctx_dev,

@@ -236,6 +236,25 @@ struct WalkArgs {
   int32_t* tokens;
 };
 
+// deepspec.ts, #confidence and draftRows truncation (see k_conf)
+constexpr int CONF_MAX_GAMMA = 32;
+struct ConfArgs {
+  RowTab rows;
+  int H, rank, with_markov, wkind, group, act_bf16;
+  int head;               // 0: no confidence head (lengths = gamma, conf untouched)
+  const float* hn;        // [A*gamma, H] final residual rows (before the final norm), row pitch ldh
+  int64_t ldh;
+  const void* wnorm;      // final norm weight [H], act dtype
+  float eps;
+  const void* pw; const void* ps; const void* pb;  // proj weight [1, H (+ rank)] (q4: scales, biases)
+  const void* bias;       // [1] act dtype
+  const void* w1; const void* w1s; const void* w1b;  // markov_w1 [V, rank]
+  const int32_t* tokens;  // [A, gamma] the walk's tokens
+  float thr[CONF_MAX_GAMMA];  // per-slot thresholds; <= 0: slot not tested
+  float* conf;            // [A, gamma]
+  int32_t* lengths;       // [A] confident prefix lengths, or null
+};
+
 struct AuxArgs {
   int V, rank, wkind, group;
   const void* w1; const void* w1s; const void* w1b;
@@ -265,5 +284,6 @@ hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);
 hipError_t launch_walk(const WalkArgs& a, hipStream_t st);
 hipError_t launch_aux(const AuxArgs& a, hipStream_t st);
+hipError_t launch_conf(const ConfArgs& a, hipStream_t st);
 
 }  // namespace dsp

@@ -584,6 +584,67 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// deepspec.ts, #confidence and the draftRows truncation rule
+// (_confident_prefix_length):
+//   c_k = sigmoid(proj . [x_k ; markov_w1[prev_k]] + bias),  x_k = rms(h_k; norm)
+//   prev_0 = anchor, prev_k = token k - 1 (the walk's);
+//   length = first k with c_k < thr_k (thr_k > 0), else gamma.
+// x_k is formed here from the final residual row h_k exactly (its own sum of
+// squares), so the head reads the same final-normed rows as lm_head.
+// One workgroup per draft row, wave w takes slots w, w + 16, ...; every lane
+// holds H / 64 entries of the row.  grid A, block 1024
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_conf(const ConfArgs a) {
+  __shared__ float cs[CONF_MAX_GAMMA];
+  const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma;
+  if (a.head) {
+    const float b = ld_act(a.bias, 0, a.act_bf16);
+    for (int k = wave; k < G; k += 16) {
+      const int64_t m = (int64_t)row * G + k;
+      const float* h = a.hn + m * a.ldh;
+      float ss = 0.f, dot = 0.f;
+      for (int i = lane; i < a.H; i += 64) {
+        const float v = h[i];
+        ss += v * v;
+        dot += v * ld_act(a.wnorm, i, a.act_bf16) * table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, a.H + (a.with_markov ? a.rank : 0), i);
+      }
+      ss = wave_sum(ss);
+      dot = wave_sum(dot) / sqrtf(ss / a.H + a.eps);
+      if (a.with_markov) {
+        const int prev = k == 0 ? a.rows.anchor[row] : a.tokens[m - 1];
+        float dm = 0.f;
+        if (prev >= 0)  // a walk step without a finite candidate reports -1 (no Markov feature)
+          for (int j = lane; j < a.rank; j += 64)
+            dm += table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, a.H + a.rank, a.H + j) *
+                  table_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+        dot += wave_sum(dm);
+      }
+      const float c = 1.f / (1.f + expf(-(dot + b)));
+      if (lane == 0) {
+        cs[k] = c;
+        a.conf[m] = c;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0 && a.lengths) {
+    int len = G;
+    if (a.head)
+      for (int k = 0; k < G; ++k)
+        if (a.thr[k] > 0.f && cs[k] < a.thr[k]) {
+          len = k;
+          break;
+        }
+    a.lengths[row] = len;
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_conf(const ConfArgs& a, hipStream_t st) {
+  if (a.rows.gamma > CONF_MAX_GAMMA || a.rows.A < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_conf, dim3(a.rows.A), dim3(1024), 0, st, a);
+  return hipGetLastError();
+}
 hipError_t launch_embed(const EmbedArgs& a, int M, hipStream_t st) {
   hipLaunchKernelGGL(k_embed, dim3(M), dim3(256), 0, st, a);
   return hipGetLastError();

@@ -73,6 +73,14 @@ typedef struct {
   int32_t weight_dtype;               /* matmul weights and gather tables: F32, BF16 or Q4 */
   int32_t act_dtype;                  /* norm vectors, layer_scalar, context K/V, X inputs: F32 or BF16 */
   int32_t group_size;                 /* Q4 group along the input axis (64) */
+  /* deepspec.ts, DeepspecConfig: the confidence head (a Linear(confDim, 1)
+   * with bias, "confidence_head.proj.weight" [1, confDim] in the weight dtype
+   * and "confidence_head.proj.bias" [1] in the act dtype; confDim = H, plus
+   * markov_rank when it also reads markov_w1[previous token]) and the
+   * truncation threshold (<= 0: every row keeps its whole block). */
+  int32_t enable_confidence_head;
+  int32_t confidence_head_with_markov;  /* needs markov_rank > 0 */
+  double confidence_threshold;
 } dspark_config;
 
 /* One checkpoint tensor (deepspec.ts, DeepspecDrafter constructor keys, e.g.
@@ -168,6 +176,29 @@ dspark_status dspark_draft_rows(const dspark_model* m, int A, const void* const*
                                 const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
                                 float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
                                 hipStream_t stream);
+
+/* deepspec.ts, draftRows with the confidence head (its #confidence and the
+ * _confident_prefix_length rule in the draftRows doc comment): after the walk,
+ *   c[a, k] = sigmoid(proj . [x_k ; markov_w1[prev_k]] + bias),
+ * x_k the final-normed hidden row of block slot k, prev_0 = anchor,
+ * prev_k = token k - 1, and each row's proposal length is the first slot k
+ * with c[a, k] < thr[k] (slots with thr[k] <= 0 are not tested), else gamma;
+ * 0 is an empty proposal.  Other arguments as dspark_draft_rows (tokens_dev
+ * always receives the whole block).
+ *   thresholds_host  NULL: the config's confidence_threshold for every slot;
+ *                    else gamma per-slot thresholds (the per-position form
+ *                    of calibrated draft-length pruning)
+ *   conf_dev         NULL, or float [A, gamma]: every slot's confidence
+ *                    (requires the head: DSPARK_ERR_INVALID_ARG otherwise)
+ *   lengths_dev      NULL, or int32 [A]: the proposal lengths (gamma for
+ *                    every row when the model has no confidence head)
+ * The workspace is dspark_draft_workspace_bytes's. */
+dspark_status dspark_draft_rows_conf(const dspark_model* m, int A, const void* const* k_ctx_dev,
+                                     const void* const* v_ctx_dev, const int32_t* ctx_len_host,
+                                     const int32_t* anchors_host, const int32_t* positions_host,
+                                     const float* thresholds_host, int32_t* tokens_dev, float* logits_dev,
+                                     float* conf_dev, int32_t* lengths_dev, const void* aux_dev, void* ws_dev,
+                                     size_t ws_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):

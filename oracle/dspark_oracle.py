@@ -19,7 +19,9 @@ notes): rotate-half RoPE pairing (k, k + hd/2); norm weights multiply (no 1+w);
 context rows of draft row a sit at positions 0..L_a-1 and its block at
 L_a..L_a+gamma-1 unless a position is given; row a attends only its own
 context rows plus its own block rows; argmax ties go to the lowest index;
-the Markov sum is float64 here (the page sums in the model dtype).
+the Markov sum is float64 here (the page sums in the model dtype), and so is
+the confidence head's linear map (the page runs it in the model dtype, then
+casts to float32).
 """
 from __future__ import annotations
 
@@ -187,6 +189,11 @@ class OracleModel:
         self.lm_head = d("lm_head.weight")
         self.w1 = d("markov_head.markov_w1.weight") if cfg.markov_rank > 0 else None
         self.w2 = d("markov_head.markov_w2.weight") if cfg.markov_rank > 0 else None
+        # deepspec.ts, DeepspecDrafter constructor: the confidence head is a
+        # Linear(confDim, 1) with bias, present when enable_confidence_head
+        conf = getattr(cfg, "enable_confidence_head", False)
+        self.conf_w = d("confidence_head.proj.weight") if conf else None
+        self.conf_b = d("confidence_head.proj.bias") if conf else None
         self.layers: List[Layer] = []
         for i in range(cfg.num_hidden_layers):
             p = f"layers.{i}."
@@ -334,13 +341,53 @@ def markov_walk(m: OracleModel, z: np.ndarray, anchor: int) -> Tuple[np.ndarray,
     return np.array(toks, dtype=np.int64), np.array(margins)
 
 
+def sigmoid(z):
+    return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+
+def confidence(m: OracleModel, h: np.ndarray, prev: int) -> float:
+    """deepspec.ts, #confidence: c_k = sigmoid(proj([h_k; markov_w1[prev]]) +
+    bias), the Markov part only when confidence_head_with_markov.  h is the
+    final-normed hidden row of block slot k (the backbone output)."""
+    feat = h
+    if m.cfg.confidence_head_with_markov:
+        feat = np.concatenate([h, m.w1[prev]])
+    return float(sigmoid(m.conf_w[0] @ feat + m.conf_b.reshape(-1)[0]))
+
+
+def block_confidence(m: OracleModel, hidden: np.ndarray, anchor: int, tokens: Sequence[int]) -> np.ndarray:
+    """deepspec.ts, draftRows: confidence over the full block after the walk,
+    step k scored with previous token anchor (k = 0) or tokens[k-1]
+    (prev_token_ids = [anchor, sampled[:-1]])."""
+    prevs = [int(anchor)] + [int(t) for t in tokens[:-1]]
+    return np.array([confidence(m, hidden[k], prevs[k]) for k in range(hidden.shape[0])])
+
+
+def confident_prefix_length(conf: Sequence[float], thresholds) -> int:
+    """deepspec.ts, draftRows doc comment (_confident_prefix_length): the
+    first slot whose confidence falls below the threshold, or gamma when
+    none does; a threshold <= 0 disables truncation (gamma).  The length can
+    be 0 (an empty proposal).  `thresholds` is one value for every slot, as on
+    that page, or one per slot (the per-position thresholds of the
+    calibrated-pruning drafter on the mlx-bun 0.2.0 -> 0.4.0 page); a slot
+    whose threshold is <= 0 is not tested."""
+    g = len(conf)
+    thr = np.broadcast_to(np.asarray(thresholds, dtype=np.float64), (g,))
+    for k in range(g):
+        if thr[k] > 0 and conf[k] < thr[k]:
+            return k
+    return g
+
+
 def draft_rows(m: OracleModel, ctx_kv_rows: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]],
-               anchors: Sequence[int], positions: Sequence[int]) -> Dict[str, np.ndarray]:
-    """deepspec.ts, draftRows (confidence truncation disabled, so every row
-    keeps its full block).  ctx_kv_rows[a][l] = (K, V) [nKv, L_a, hd].
+               anchors: Sequence[int], positions: Sequence[int], thresholds=None) -> Dict[str, np.ndarray]:
+    """deepspec.ts, draftRows.  ctx_kv_rows[a][l] = (K, V) [nKv, L_a, hd].
     Returns tokens [A, gamma], margins [A, gamma], logits z [A, gamma, V],
-    hidden [A, gamma, H]."""
-    hid, zs, toks, mgs = [], [], [], []
+    hidden [A, gamma, H]; with a confidence head also conf [A, gamma] (the
+    full block) and lengths [A] (the confident prefix under `thresholds`,
+    default the config's confidence_threshold; gamma when it is <= 0)."""
+    hid, zs, toks, mgs, confs, lens = [], [], [], [], [], []
+    thr = getattr(m.cfg, "confidence_threshold", 0.0) if thresholds is None else thresholds
     for a, anchor in enumerate(anchors):
         h = backbone_row(m, ctx_kv_rows[a], int(anchor), int(positions[a]))
         z = compute_logits(m, h)
@@ -349,8 +396,15 @@ def draft_rows(m: OracleModel, ctx_kv_rows: Sequence[Sequence[Tuple[np.ndarray, 
         zs.append(z)
         toks.append(t)
         mgs.append(mg)
-    return {"tokens": np.stack(toks), "margins": np.stack(mgs), "logits": np.stack(zs),
-            "hidden": np.stack(hid)}
+        if m.conf_w is not None:
+            c = block_confidence(m, h, int(anchor), t)
+            confs.append(c)
+            lens.append(confident_prefix_length(c, thr))
+    out = {"tokens": np.stack(toks), "margins": np.stack(mgs), "logits": np.stack(zs), "hidden": np.stack(hid)}
+    if m.conf_w is not None:
+        out["conf"] = np.stack(confs)
+        out["lengths"] = np.array(lens, dtype=np.int64)
+    return out
 
 
 def draft_block(m: OracleModel, ctx_kv: Sequence[Tuple[np.ndarray, np.ndarray]], anchor: int,

@@ -47,6 +47,10 @@ class ModelConfig:
     weight_dtype: str = BF16
     act_dtype: str = BF16
     group_size: int = 64
+    # confidence head (deepspec.ts, DeepspecConfig): sigmoid(proj [h; w1[prev]])
+    enable_confidence_head: bool = False
+    confidence_head_with_markov: bool = False
+    confidence_threshold: float = 0.0
     # distributions
     weight_std: float = 0.02
     norm_std: float = 0.02

@@ -139,6 +139,10 @@ def tensor_shape(cfg: ModelConfig, name: str) -> tuple:
         return (V, H)
     if name in ("markov_head.markov_w1.weight", "markov_head.markov_w2.weight"):
         return (V, r)
+    if name == "confidence_head.proj.weight":
+        return (1, H + (r if cfg.confidence_head_with_markov else 0))
+    if name == "confidence_head.proj.bias":
+        return (1,)
     if name.startswith("layers."):
         suffix = name.split(".", 2)[2]
         return {
@@ -169,20 +173,23 @@ def tensor_names(cfg: ModelConfig, with_fc: bool = True) -> List[str]:
         names += [p + s for s in MATMUL_SUFFIXES] + [p + s for s in NORM_SUFFIXES] + [p + "layer_scalar"]
     if cfg.markov_rank > 0:
         names += ["markov_head.markov_w1.weight", "markov_head.markov_w2.weight"]
+    if cfg.enable_confidence_head:
+        names += ["confidence_head.proj.weight", "confidence_head.proj.bias"]
     return names
 
 
 def is_matrix(name: str) -> bool:
     return (name in ("embed_tokens.weight", "fc.weight", "lm_head.weight",
-                     "markov_head.markov_w1.weight", "markov_head.markov_w2.weight")
+                     "markov_head.markov_w1.weight", "markov_head.markov_w2.weight",
+                     "confidence_head.proj.weight")
             or any(name.endswith(s) for s in MATMUL_SUFFIXES))
 
 
 def make_tensor(cfg: ModelConfig, name: str, markov_active: bool = False,
                 overrides: Optional[Dict[str, float]] = None) -> Stored:
     """One model tensor in its storage format.  Matrices ~ N(0, weight_std^2)
-    (Markov tables N(0, 0.35^2) when markov_active); norm weights and
-    layer_scalar ~ 1 + N(0, norm_std^2)."""
+    (Markov tables N(0, 0.35^2) when markov_active); biases ~ N(0,
+    weight_std^2); norm weights and layer_scalar ~ 1 + N(0, norm_std^2)."""
     shape = tensor_shape(cfg, name)
     if is_matrix(name):
         std = cfg.weight_std
@@ -194,6 +201,10 @@ def make_tensor(cfg: ModelConfig, name: str, markov_active: bool = False,
         if cfg.weight_dtype == Q4:
             return quantize_q4(w, cfg.group_size)
         return store(w, cfg.weight_dtype)
+    if name.endswith(".bias"):
+        # a linear layer's bias (the confidence head's): N(0, weight_std^2)
+        std = overrides[name] if overrides and name in overrides else cfg.weight_std
+        return store(normal(cfg.seed, name, shape, std), cfg.act_dtype)
     w = normal(cfg.seed, name, shape, cfg.norm_std, mean=1.0)
     return store(w, cfg.act_dtype)
 

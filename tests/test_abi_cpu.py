@@ -201,3 +201,31 @@ def test_draft_workspace_scales_with_context_up_to_the_split_cap(dsp):
     assert sizes[-1] == sizes[-2] == f(h, 2, 10 ** 6, 10 ** 6)  # >= 512 * 32 keys: capped
     assert f(h, 2, 100, 201) == 0 and f(h, 2, -1, 0) == 0 and f(h, 0, 10, 10) == 0
     dsp._lib.dspark_model_destroy(h)
+
+
+def test_confidence_head_guards(dsp):
+    base = synth.scaled(synth.TINY, enable_confidence_head=True, confidence_head_with_markov=True)
+    table, n, keep = fake_table(dsp, base)
+    st, h = create(dsp, make_config(dsp, base), table, n)
+    assert st == 0, dsp._lib.dspark_last_error()
+    dsp._lib.dspark_model_destroy(h)
+    # the Markov feature needs a Markov head
+    st, _ = create(dsp, make_config(dsp, base, markov_rank=0), table, n)
+    assert st == 1 and b"markov" in dsp._lib.dspark_last_error()
+    # a missing head tensor
+    table, n, keep = fake_table(dsp, base, drop="confidence_head.proj.bias")
+    st, _ = create(dsp, make_config(dsp, base), table, n)
+    assert st == 2 and b"confidence_head" in dsp._lib.dspark_last_error()
+    # confidences requested from a model without the head
+    plain = synth.TINY
+    table, n, keep = fake_table(dsp, plain)
+    st, h = create(dsp, make_config(dsp, plain), table, n)
+    assert st == 0
+    P = ctypes.c_void_p
+    kp = (P * 1)(FAKE)
+    one = (ctypes.c_int32 * 1)(32)
+    anc = (ctypes.c_int32 * 1)(5)
+    ws = dsp._lib.dspark_draft_workspace_bytes(h, 1, 32, 32)
+    assert dsp._lib.dspark_draft_rows_conf(h, 1, kp, kp, one, anc, one, None, FAKE, None, FAKE, None, FAKE,
+                                           FAKE * 16, ws, None) == 1
+    dsp._lib.dspark_model_destroy(h)

@@ -531,3 +531,81 @@ def test_mlp_gate_takes_activation_brute_force():
         hms = sum(t * t for t in h1) / cfg.H
         ref = [h1[o] / math.sqrt(hms + eps) * m.norm[o] for o in range(cfg.H)]
         assert np.allclose(hid[g], ref, atol=1e-12)
+
+
+# ---------------------------------------------------------------- confidence head
+
+
+def test_confident_prefix_length_rule():
+    c = [0.9, 0.8, 0.2, 0.95, 0.1]
+    assert O.confident_prefix_length(c, 0.0) == 5           # threshold <= 0: full block
+    assert O.confident_prefix_length(c, -1.0) == 5
+    assert O.confident_prefix_length(c, 0.5) == 2           # first slot below, later ones ignored
+    assert O.confident_prefix_length(c, 0.95) == 0          # empty proposal
+    assert O.confident_prefix_length(c, 0.05) == 5          # none below
+    assert O.confident_prefix_length(c, 0.2) == 4           # strictly below (0.2 is not < 0.2)
+    # per-position thresholds: a slot whose threshold is <= 0 is not tested
+    assert O.confident_prefix_length(c, [0.0, 0.0, 0.1, 0.99, 0.5]) == 3
+    assert O.confident_prefix_length(c, [0.95, 0, 0, 0, 0]) == 0
+
+
+def _conf_cfg(with_markov):
+    return synth.scaled(SMALL, enable_confidence_head=True, confidence_head_with_markov=with_markov,
+                        confidence_threshold=0.4)
+
+
+def test_confidence_sigmoid_closed_form_and_feature():
+    """proj = 0: every slot's confidence is sigmoid(bias), by hand; proj = unit
+    vector at hidden index j: sigmoid(h_k[j] + bias), with h_k the
+    final-normed backbone output (unit RMS after dividing by the norm weight)."""
+    cfg = _conf_cfg(False)
+    m = small_model(cfg)
+    kv = _kv_rows(m, [rand((6, cfg.H), 40)], [0])
+    b = 0.37
+    m.conf_b = np.array([b])
+    m.conf_w = np.zeros((1, cfg.H))
+    r = O.draft_rows(m, kv, [3], [6])
+    assert np.allclose(r["conf"][0], 1.0 / (1.0 + math.exp(-b)), rtol=0, atol=1e-15)
+    j = 5
+    m.conf_w[0, j] = 1.0
+    r = O.draft_rows(m, kv, [3], [6])
+    h = r["hidden"][0]
+    assert np.allclose(np.mean((h / m.norm) ** 2, axis=-1), 1.0, atol=1e-4)
+    assert np.allclose(r["conf"][0], [1.0 / (1.0 + math.exp(-(h[k, j] + b))) for k in range(cfg.gamma)], atol=1e-15)
+
+
+def test_confidence_with_markov_scores_previous_tokens():
+    """With the Markov feature and proj zero on the hidden part, slot k's
+    confidence is sigmoid(proj_m . w1[prev_k] + b) with prev_0 the anchor and
+    prev_k the walk's token k - 1."""
+    cfg = _conf_cfg(True)
+    m = small_model(cfg, markov_active=True)
+    kv = _kv_rows(m, [rand((6, cfg.H), 41)], [0])
+    pm = rand(cfg.markov_rank, 42)
+    m.conf_w = np.concatenate([np.zeros(cfg.H), pm])[None]
+    b = float(m.conf_b.reshape(-1)[0])
+    anchor = 11
+    r = O.draft_rows(m, kv, [anchor], [6])
+    toks = r["tokens"][0]
+    prev = anchor
+    for k in range(cfg.gamma):
+        z = sum(pm[j] * m.w1[prev][j] for j in range(cfg.markov_rank)) + b
+        assert math.isclose(r["conf"][0][k], 1.0 / (1.0 + math.exp(-z)), rel_tol=1e-12)
+        prev = int(toks[k])
+
+
+def test_round_lengths_follow_the_config_threshold():
+    cfg = _conf_cfg(True)
+    m = small_model(cfg, markov_active=True)
+    rows = [rand((5 + a, cfg.H), 43 + a) for a in range(3)]
+    kv = _kv_rows(m, rows, [0, 0, 0])
+    r = O.draft_rows(m, kv, [1, 2, 3], [5, 6, 7])
+    for a in range(3):
+        assert r["lengths"][a] == O.confident_prefix_length(r["conf"][a], 0.4)
+    # threshold 0 (the page's default): the full block
+    r0 = O.draft_rows(m, kv, [1, 2, 3], [5, 6, 7], thresholds=0.0)
+    assert r0["lengths"].tolist() == [cfg.gamma] * 3
+    # a bias far below zero: every confidence ~ 0, an empty proposal
+    m.conf_b = np.array([-50.0])
+    r1 = O.draft_rows(m, kv, [1, 2, 3], [5, 6, 7])
+    assert r1["lengths"].tolist() == [0, 0, 0] and np.array_equal(r1["tokens"], r["tokens"])
