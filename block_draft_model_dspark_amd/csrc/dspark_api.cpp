@@ -476,8 +476,10 @@ dspark_status check_config(const dspark_config& c) {
   if (c.hidden_size > 8192 || c.intermediate_size > (1 << 20))
     return fail(DSPARK_ERR_UNSUPPORTED, "hidden_size > 8192 not built");
   if (c.num_hidden_layers > MAX_LAYERS) return fail(DSPARK_ERR_UNSUPPORTED, "more than %d layers not built", MAX_LAYERS);
-  if (c.vocab_size % 64 || c.vocab_size > 1024 * WALK_CHUNK)
-    return fail(DSPARK_ERR_UNSUPPORTED, "vocab_size must be a multiple of 64 and at most %d", 1024 * WALK_CHUNK);
+  // the walk packs (step, chunk) into one word with 24 bits for the chunk;
+  // 2^22 keeps every vocabulary product in int32 range as well
+  if (c.vocab_size % 64 || c.vocab_size > (1 << 22))
+    return fail(DSPARK_ERR_UNSUPPORTED, "vocab_size must be a multiple of 64 and at most %d", 1 << 22);
   if (c.block_size > 32) return fail(DSPARK_ERR_UNSUPPORTED, "block_size > 32 not built");
   if ((c.num_attention_heads / c.num_global_key_value_heads) * c.block_size > 128)
     return fail(DSPARK_ERR_UNSUPPORTED, "more than 128 query rows per kv head not built");

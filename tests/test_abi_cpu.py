@@ -93,7 +93,7 @@ def create(dsp, c, table, n):
 @pytest.mark.parametrize("field,value,status", [
     ("attention_k_eq_v", 0, 3), ("markov_head_vanilla", 0, 3), ("activation_gelu_tanh", 0, 3),
     ("global_head_dim", 96, 3), ("num_global_key_value_heads", 3, 2), ("block_size", 0, 1),
-    ("mask_token_id", 5000, 1), ("vocab_size", 1000, 3)])
+    ("mask_token_id", 5000, 1), ("vocab_size", 1000, 3), ("vocab_size", (1 << 22) + 64, 3)])
 def test_config_guards(dsp, field, value, status):
     cfg = synth.TINY
     table, n, keep = fake_table(dsp, cfg)

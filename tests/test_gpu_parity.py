@@ -270,6 +270,24 @@ def test_rows_a32_ragged_full_size(gpu_lib, markov_active):
     assert checked >= 256
 
 
+def test_long_context_large_vocab_rows(gpu_lib):
+    """The 4-bit workload's shapes with bf16 weights: V = 262144 (4096 walk
+    chunks of 64), 4 rows of 32768 context keys each (the wide attention
+    over 131072 keys), one layer; Markov head active."""
+    cfg = synth.scaled(synth.FULL_Q4, weight_dtype="bf16", num_hidden_layers=1)
+    assert cfg.V == 262144
+    w = synth.Workload("long_vocab", cfg, rows=4, ctx_lens=(32768,) * 4)
+    case = Case(cfg, markov_active=True, with_fc=False)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(4):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 32
+
+
 def test_tiled_path_round_small_ragged(gpu_lib):
     """Every GEMM of the round on the tiled path (threshold 1 row): 3 rows =
     48 block rows, a partial tile, ragged contexts, an active Markov head.
