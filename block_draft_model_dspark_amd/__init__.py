@@ -26,7 +26,7 @@ EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tal
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
             "dspark_tall_tile_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
-            "dspark_draft_rows_conf",
+            "dspark_draft_rows_conf", "dspark_draft_rows_ex",
             "dspark_last_error")
 
 
@@ -49,6 +49,15 @@ class Config(ctypes.Structure):
                 ("act_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("enable_confidence_head", ctypes.c_int32), ("confidence_head_with_markov", ctypes.c_int32),
                 ("confidence_threshold", ctypes.c_double)]
+
+
+class DraftArgs(ctypes.Structure):
+    _fields_ = [("A", ctypes.c_int32), ("k_ctx_dev", ctypes.c_void_p), ("v_ctx_dev", ctypes.c_void_p),
+                ("ctx_len_host", ctypes.c_void_p), ("ctx_pos0_host", ctypes.c_void_p),
+                ("anchors_host", ctypes.c_void_p), ("positions_host", ctypes.c_void_p),
+                ("thresholds_host", ctypes.c_void_p), ("tokens_dev", ctypes.c_void_p),
+                ("logits_dev", ctypes.c_void_p), ("conf_dev", ctypes.c_void_p), ("lengths_dev", ctypes.c_void_p),
+                ("aux_dev", ctypes.c_void_p)]
 
 
 class KernelTime(ctypes.Structure):
@@ -97,6 +106,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_draft_rows_conf.argtypes = [P, ctypes.c_int, ctypes.POINTER(P), ctypes.POINTER(P),
                                            ctypes.POINTER(I32), ctypes.POINTER(I32), ctypes.POINTER(I32),
                                            ctypes.POINTER(ctypes.c_float), P, P, P, P, P, P, SZ, P]
+    lib.dspark_draft_rows_ex.argtypes = [P, ctypes.POINTER(DraftArgs), P, SZ, P]
     lib.dspark_draft_noalloc_max_bytes.argtypes = []
     lib.dspark_draft_noalloc_max_bytes.restype = SZ
     lib.dspark_profile_enable.argtypes = [ctypes.c_int]
@@ -110,7 +120,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_last_error.restype = ctypes.c_char_p
     for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
                "dspark_project_context_kv", "dspark_draft_rows", "dspark_draft_block", "dspark_draft_rows_noalloc",
-               "dspark_draft_rows_conf"):
+               "dspark_draft_rows_conf", "dspark_draft_rows_ex"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -272,26 +282,29 @@ def draft_workspace_bytes(model: Model, A: int, max_ctx: int, total_ctx: int) ->
 
 
 def project_context_kv(model: Model, x, pos0: Sequence[int], input_kind: int = INPUT_CONTEXT_HIDDEN,
-                       k_out=None, v_out=None, workspace=None, stream=None):
+                       k_out=None, v_out=None, workspace=None, stream=None, v_only: bool = False):
     """deepspec.ts, #projectContextKVRows.  x [B, L, H] (or [B, L, fc_in] for
     target features), act dtype, on the GPU.  Returns per-layer (K, V) lists,
-    each [B, nKv, L, hd]."""
+    each [B, nKv, L, hd]; with v_only the K list is None (a V-only cache)."""
     import torch
     cfg = model.cfg
     B, L = int(x.shape[0]), int(x.shape[1])
     nL = cfg.num_hidden_layers
-    if k_out is None:
-        k_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
+    if v_out is None:
         v_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
+    if k_out is None and not v_only:
+        k_out = [torch.empty(B, cfg.nKv, L, cfg.hd, dtype=model.act_dtype, device=x.device) for _ in range(nL)]
+    if v_only:
+        k_out = None
     n = project_workspace_bytes(model, input_kind, B, L)
     if workspace is None or workspace.numel() < n:
         workspace = torch.empty(n, dtype=torch.uint8, device=x.device)
     pos = (ctypes.c_int32 * B)(*[int(p) for p in pos0])
-    kp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in k_out])
+    kp = None if k_out is None else (ctypes.c_void_p * nL)(*[t.data_ptr() for t in k_out])
     vp = (ctypes.c_void_p * nL)(*[t.data_ptr() for t in v_out])
     _check(_lib.dspark_project_context_kv(model.handle, input_kind, x.data_ptr(), B, L, pos, kp, vp,
                                           workspace.data_ptr(), n, _stream_handle(stream)))
-    _keep_for(stream, workspace, *k_out, *v_out)
+    _keep_for(stream, workspace, *(k_out or []), *v_out)
     return k_out, v_out
 
 
@@ -367,6 +380,51 @@ def draft_rows_conf(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], ancho
     _check(_lib.dspark_draft_rows_conf(model.handle, A, kp, vp, lens, anc, pos, thr, out["tokens"].data_ptr(),
                                        _ptr(out["logits"]), _ptr(out["conf"]), out["lengths"].data_ptr(),
                                        _ptr(model.aux), ws.data_ptr(), n, _stream_handle(stream)))
+    _keep_for(stream, ws, *[t for t in out.values() if t is not None])
+    return out
+
+
+def draft_rows_ex(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+                  positions: Sequence[int], ctx_pos0: Optional[Sequence[int]] = None,
+                  thresholds: Optional[Sequence[float]] = None, collect_logits: bool = False,
+                  collect_conf: bool = False, lengths: bool = False, stream=None):
+    """deepspec.ts, draftRows through dspark_draft_rows_ex.  k_rows None: a
+    V-only context cache (v_rows[l][a] only; the attention rebuilds the keys
+    at positions ctx_pos0[a] + j).  Returns a dict of device tensors: tokens,
+    and logits / conf / lengths when asked for."""
+    import torch
+    cfg = model.cfg
+    A = len(anchors)
+    nL = cfg.num_hidden_layers
+    keep = []
+
+    def arr(ctype, vals):
+        a = (ctype * len(vals))(*vals)
+        keep.append(a)
+        return ctypes.cast(a, ctypes.c_void_p)
+
+    out = {"tokens": torch.empty(A, cfg.gamma, dtype=torch.int32, device="cuda")}
+    out["logits"] = torch.empty(A, cfg.gamma, cfg.V, dtype=torch.float32, device="cuda") if collect_logits else None
+    out["conf"] = torch.empty(A, cfg.gamma, dtype=torch.float32, device="cuda") if collect_conf else None
+    out["lengths"] = torch.empty(A, dtype=torch.int32, device="cuda") if lengths else None
+    x = DraftArgs()
+    x.A = A
+    x.k_ctx_dev = None if k_rows is None else arr(ctypes.c_void_p, [k_rows[l][a].data_ptr() for l in range(nL)
+                                                                    for a in range(A)])
+    x.v_ctx_dev = arr(ctypes.c_void_p, [v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+    x.ctx_len_host = arr(ctypes.c_int32, [int(v) for v in ctx_lens])
+    x.ctx_pos0_host = None if ctx_pos0 is None else arr(ctypes.c_int32, [int(v) for v in ctx_pos0])
+    x.anchors_host = arr(ctypes.c_int32, [int(v) for v in anchors])
+    x.positions_host = arr(ctypes.c_int32, [int(v) for v in positions])
+    x.thresholds_host = None if thresholds is None else arr(ctypes.c_float, [float(t) for t in thresholds])
+    x.tokens_dev = out["tokens"].data_ptr()
+    x.logits_dev = _ptr(out["logits"])
+    x.conf_dev = _ptr(out["conf"])
+    x.lengths_dev = _ptr(out["lengths"])
+    x.aux_dev = _ptr(model.aux)
+    n = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    _check(_lib.dspark_draft_rows_ex(model.handle, ctypes.byref(x), ws.data_ptr(), n, _stream_handle(stream)))
     _keep_for(stream, ws, *[t for t in out.values() if t is not None])
     return out
 

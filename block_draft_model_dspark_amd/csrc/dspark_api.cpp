@@ -705,8 +705,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
                                         const int32_t* pos0_host, void* const* k_out_dev, void* const* v_out_dev,
                                         void* ws_dev, size_t ws_bytes, hipStream_t stream) {
   g_err.clear();
-  if (!m || !x_dev || !pos0_host || !k_out_dev || !v_out_dev || !ws_dev)
-    return fail(DSPARK_ERR_INVALID_ARG, "null argument");
+  if (!m || !x_dev || !pos0_host || !v_out_dev || !ws_dev) return fail(DSPARK_ERR_INVALID_ARG, "null argument");
   if (B <= 0 || L <= 0) return fail(DSPARK_ERR_INVALID_ARG, "B and L must be positive");
   if (B > MAX_ROWS) return fail(DSPARK_ERR_UNSUPPORTED, "B > %d not built", MAX_ROWS);
   if ((int64_t)B * L > (1 << 24)) return fail(DSPARK_ERR_UNSUPPORTED, "B*L too large");
@@ -718,7 +717,8 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   for (int b = 0; b < B; ++b)
     if (pos0_host[b] < 0) return fail(DSPARK_ERR_INVALID_ARG, "pos0[%d] < 0", b);
   for (int l = 0; l < c.num_hidden_layers; ++l)
-    if (!k_out_dev[l] || !v_out_dev[l]) return fail(DSPARK_ERR_INVALID_ARG, "null K/V output for layer %d", l);
+    if ((k_out_dev && !k_out_dev[l]) || !v_out_dev[l])
+      return fail(DSPARK_ERR_INVALID_ARG, "null K/V output for layer %d", l);
   const ProjLayout p = proj_layout(m, input_kind, B, L);
   if (ws_bytes < p.total) return fail(DSPARK_ERR_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, p.total);
   if ((uintptr_t)ws_dev & 255) return fail(DSPARK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
@@ -791,7 +791,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     for (int b = 0; b < B; ++b) e.pos0[b] = pos0_host[b];
     for (int i = 0; i < nl; ++i) {
       e.kn_l[i] = m->L[l0 + i].kn;
-      e.kout[i] = k_out_dev[l0 + i];
+      e.kout[i] = k_out_dev ? k_out_dev[l0 + i] : nullptr;  // null: V-only cache
       e.vout[i] = v_out_dev[l0 + i];
     }
     HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream, tb); }));
@@ -815,10 +815,12 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
                               const int32_t* anchors_host, const int32_t* positions_host, int32_t* tokens_dev,
                               float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
                               hipStream_t stream, bool use_scratch, const float* thresholds_host = nullptr,
-                              float* conf_dev = nullptr, int32_t* lengths_dev = nullptr) {
+                              float* conf_dev = nullptr, int32_t* lengths_dev = nullptr, bool allow_vonly = false,
+                              const int32_t* ctx_pos0_host = nullptr) {
   g_err.clear();
-  if (!m || !k_ctx_dev || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host || !tokens_dev ||
-      (!ws_dev && !use_scratch))
+  const bool vonly = allow_vonly && !k_ctx_dev;  // a V-only context cache
+  if (!m || (!k_ctx_dev && !vonly) || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host ||
+      !tokens_dev || (!ws_dev && !use_scratch))
     return fail(DSPARK_ERR_INVALID_ARG, "null argument");
   const bool head = m->c.enable_confidence_head != 0;
   if (conf_dev && !head) return fail(DSPARK_ERR_INVALID_ARG, "confidence requested from a model without the head");
@@ -843,9 +845,12 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     rows.len[a] = ctx_len_host[a];
     total_keys += ctx_len_host[a] + G;
     for (int l = 0; l < nL; ++l)
-      if (ctx_len_host[a] > 0 && (!k_ctx_dev[l * A + a] || !v_ctx_dev[l * A + a]))
+      if (ctx_len_host[a] > 0 && ((!vonly && !k_ctx_dev[l * A + a]) || !v_ctx_dev[l * A + a]))
         return fail(DSPARK_ERR_INVALID_ARG, "null context K/V for layer %d row %d", l, a);
+    if (ctx_pos0_host && ctx_pos0_host[a] < 0) return fail(DSPARK_ERR_INVALID_ARG, "ctx_pos0[%d] < 0", a);
   }
+  if (vonly && c.act_dtype != DSPARK_BF16)
+    return fail(DSPARK_ERR_UNSUPPORTED, "a V-only context cache is built for bf16 caches");
   const DraftLayout d = draft_layout(m, A, logits_dev == nullptr, total_keys - (int64_t)A * G);
   if (use_scratch) {
     if (d.total > NOALLOC_SCRATCH_BYTES)
@@ -883,8 +888,15 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   // attention split plan: context splits of `split` keys, then the block split
   const int64_t total_ctx = total_keys - (int64_t)A * G;
   const bool wide = total_ctx >= ATTN_WIDE_MIN_KEYS && attn_wide_ok(m->nq, hd);
+  if (vonly && !attn_vonly_ok(m->nq, hd, wide))
+    return fail(DSPARK_ERR_UNSUPPORTED, "a V-only context cache is not built for head_dim %d with %d query rows",
+                hd, m->nq);
   const int split = wide ? attn_split_wide(total_ctx, A) : attn_split(total_ctx);
   AttnArgs at{};
+  at.vonly = vonly ? 1 : 0;
+  at.theta = c.rope_theta;
+  at.nrot = m->nrot;
+  for (int a = 0; a < A; ++a) at.ctx_pos0[a] = ctx_pos0_host ? ctx_pos0_host[a] : 0;
   MergeArgs mg{};
   int nsplit = 0;
   for (int a = 0; a < A; ++a) {
@@ -1023,9 +1035,10 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream, tb); }));
 
     for (int a = 0; a < A; ++a) {
-      at.row[a].k = k_ctx_dev[l * A + a];
+      at.row[a].k = vonly ? nullptr : k_ctx_dev[l * A + a];
       at.row[a].v = v_ctx_dev[l * A + a];
     }
+    at.kn = W.kn;  // a V-only cache rebuilds the context keys with this layer's k_norm
     HIPCHECK(timed("attn", stream, [&] {
       return wide ? launch_attn_wide(at, c.act_dtype == DSPARK_BF16, attn_grid, stream)
                   : launch_attn(at, c.act_dtype == DSPARK_BF16, nsplit, stream);
@@ -1164,6 +1177,15 @@ dspark_status dspark_draft_rows_conf(const dspark_model* m, int A, const void* c
   return draft_rows_impl(m, A, k_ctx_dev, v_ctx_dev, ctx_len_host, anchors_host, positions_host, tokens_dev,
                          logits_dev, aux_dev, ws_dev, ws_bytes, stream, false, thresholds_host, conf_dev,
                          lengths_dev);
+}
+
+dspark_status dspark_draft_rows_ex(const dspark_model* m, const dspark_draft_args* x, void* ws_dev, size_t ws_bytes,
+                                   hipStream_t stream) {
+  g_err.clear();
+  if (!x) return fail(DSPARK_ERR_INVALID_ARG, "null arguments");
+  return draft_rows_impl(m, x->A, x->k_ctx_dev, x->v_ctx_dev, x->ctx_len_host, x->anchors_host, x->positions_host,
+                         x->tokens_dev, x->logits_dev, x->aux_dev, ws_dev, ws_bytes, stream, false,
+                         x->thresholds_host, x->conf_dev, x->lengths_dev, true, x->ctx_pos0_host);
 }
 
 dspark_status dspark_draft_rows_noalloc(const dspark_model* m, int A, const void* const* k_ctx_dev,

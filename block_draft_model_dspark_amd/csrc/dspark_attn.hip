@@ -124,13 +124,31 @@ __device__ __forceinline__ uint16_t half_of(const u32x4& w, int e) { return (uin
 // block's own, scaled by their RMS factor: rkey for this thread's key, or an
 // fp32 cache: 1) in two 16-key passes of hi / lo planes.  NTH threads stage;
 // each wave accumulates NTW output tiles from t0.
-template <int HD, bool ONE, int NTH, int NTW, class Prep>
+// V-only cache (VO): the keys are rebuilt while staging as
+// K = RoPE(V * k_norm, pos0 + j) (deepspec.ts, #projectContextKVRows: V is
+// the weightless norm of the same k whose k_norm'd, roped form is K).  Thread
+// items c8 = tid / 32 + (NTH / 32) i hold dims 8 c8..; items i and i + PI are
+// the two halves of the same RoPE pairs when (HD / 16) is a multiple of
+// NTH / 32 (vo_layout_ok), so each thread rotates its own values.
+template <int HD, int NTH>
+__host__ __device__ constexpr bool vo_layout_ok() {
+  return (HD / 16) % (NTH / ATT_KEYS) == 0 && ATT_KEYS * (HD / 8) % NTH == 0;
+}
+struct VoCtx {
+  const uint32_t* knw;  // LDS: k_norm as bf16 pairs [HD / 2]
+  const double* inv;    // LDS: 1 / wavelength per pair [HD / 2] (0: identity)
+  int64_t pos0;         // absolute position of context key 0 of the row
+};
+
+template <int HD, bool ONE, int NTH, int NTW, bool VO = false, class Prep>
 __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, int j0, int j1, float rkey,
                                           Prep&& prep, const bf16x8* qh, const bf16x8* ql, f32x4* o, int t0,
-                                          float& m_run, float& l_part, uint16_t* Ks, uint16_t* Vt) {
+                                          float& m_run, float& l_part, uint16_t* Ks, uint16_t* Vt,
+                                          const VoCtx& vo = VoCtx{}) {
   constexpr int KSTR = HD + 8, VSTR = 40;
   constexpr int IPT = ATT_KEYS * (HD / 8) / NTH;  // staging items (key, 8 dims) per thread
   static_assert(IPT >= 1 && ATT_KEYS * (HD / 8) % NTH == 0 && NTH % ATT_KEYS == 0, "staging layout");
+  static_assert(!VO || (ONE && vo_layout_ok<HD, NTH>()), "V-only staging: bf16 cache, pairs within a thread");
   const int tid = threadIdx.x;
   const int key = tid & (ATT_KEYS - 1);  // the key this thread stages (all its items)
   u32x4 kk[ONE ? IPT : 1], vv[ONE ? IPT : 1];
@@ -141,7 +159,7 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
     for (int i = 0; i < IPT; ++i) {
       const int c8 = (tid + NTH * i) / ATT_KEYS;
       if constexpr (ONE) {
-        kk[i] = *(const u32x4*)((const uint16_t*)kbase + (int64_t)kc * HD + 8 * c8);
+        if constexpr (!VO) kk[i] = *(const u32x4*)((const uint16_t*)kbase + (int64_t)kc * HD + 8 * c8);
         vv[i] = *(const u32x4*)((const uint16_t*)vbase + (int64_t)kc * HD + 8 * c8);
       } else {
         const float* kp = (const float*)kbase + (int64_t)kc * HD + 8 * c8;
@@ -159,6 +177,32 @@ __device__ __forceinline__ void attn_keys(const void* kbase, const void* vbase, 
     const int nk = min(ATT_KEYS, j1 - jc);
     const bool ok = key < nk;
     if constexpr (ONE) {
+      if constexpr (VO) {
+        // K of this thread's key from its V: items i < PI hold dims
+        // [0, HD/2) of the pairs, items i + PI the partner dims
+        constexpr int PI = (HD / 16) / (NTH / ATT_KEYS);
+        const int64_t pos = vo.pos0 + jc + min(key, j1 - jc - 1);
+#pragma unroll
+        for (int i = 0; i < PI; ++i) {
+          const int c8 = (tid + NTH * i) / ATT_KEYS;  // dims 8 c8 .. in the first half
+          const u32x4 wl = *(const u32x4*)&vo.knw[4 * c8], wh = *(const u32x4*)&vo.knw[HD / 4 + 4 * c8];
+          float klo[8], khi[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t sh = (e & 1) ? 0u : 16u;  // bf16 e of a word: low half first
+            const float vlo = __uint_as_float((vv[i][e >> 1] << sh) & 0xFFFF0000u);
+            const float vhi = __uint_as_float((vv[i + PI][e >> 1] << sh) & 0xFFFF0000u);
+            const float tl = vlo * __uint_as_float((wl[e >> 1] << sh) & 0xFFFF0000u);
+            const float th = vhi * __uint_as_float((wh[e >> 1] << sh) & 0xFFFF0000u);
+            float c, sn;
+            rope_cs_hw(pos, vo.inv[8 * c8 + e], c, sn);
+            klo[e] = tl * c - th * sn;
+            khi[e] = th * c + tl * sn;
+          }
+          kk[i] = __builtin_bit_cast(u32x4, to_bf16x8(klo));
+          kk[i + PI] = __builtin_bit_cast(u32x4, to_bf16x8(khi));
+        }
+      }
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < IPT; ++i) {
@@ -270,13 +314,38 @@ __device__ __forceinline__ void store_part(void* opart, int64_t off32, int64_t o
   }
 }
 
-template <int HD, bool KVB>
+// V-only cache: the workgroup's RoPE inverse wavelengths and k_norm weight
+// in LDS (filled before the first barrier of the key loop)
+template <int HD, bool VO>
+struct VoTables {
+  __align__(16) uint32_t knw[VO ? HD / 2 : 1];
+  double inv[VO ? HD / 2 : 1];
+};
+template <int HD, bool VO>
+__device__ __forceinline__ VoCtx vo_setup(VoTables<HD, VO>& t, const AttnArgs& a, int row) {
+  VoCtx v{};
+  if constexpr (VO) {
+    const int tid = threadIdx.x;
+    if (tid < HD / 2) {
+      t.knw[tid] = ((const uint32_t*)a.kn)[tid];
+      t.inv[tid] = rope_inv(tid, HD, a.theta, a.nrot);
+    }
+    __syncthreads();  // (called by every thread of the workgroup: the split kind is uniform)
+    v.knw = t.knw;
+    v.inv = t.inv;
+    v.pos0 = a.ctx_pos0[row];
+  }
+  return v;
+}
+
+template <int HD, bool KVB, bool VO>
 __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
   constexpr int NS = HD / 32, NTW = HD / 64, HJ = HD / 64;
   static_assert(ATT_KEYS * (HD / 8) / ATT_NTH >= 1 && ATT_NTH % ATT_KEYS == 0, "staging layout");
   __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
   __shared__ __align__(16) uint16_t Vt[HD * 40];
   __shared__ __align__(16) u32x4 qop[2][NS][64];  // q hi / lo in B-operand order
+  __shared__ VoTables<HD, VO> vot;
 
   const int sg = blockIdx.x, kvh = blockIdx.y;
   int row = 0;
@@ -360,9 +429,14 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
                                        o, t0, m_run, l_part, Ks, Vt);
   } else {
     const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
-    const char* kb = (const char*)a.row[row].k + kvoff;
     const char* vb = (const char*)a.row[row].v + kvoff;
-    attn_keys<HD, KVB, ATT_NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt);
+    if constexpr (VO) {
+      const VoCtx vo = vo_setup<HD, VO>(vot, a, row);
+      attn_keys<HD, KVB, ATT_NTH, NTW, true>(vb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt, vo);
+    } else {
+      const char* kb = (const char*)a.row[row].k + kvoff;
+      attn_keys<HD, KVB, ATT_NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, t0, m_run, l_part, Ks, Vt);
+    }
   }
 
   float l = l_part;
@@ -386,11 +460,12 @@ __global__ __launch_bounds__(ATT_NTH) void k_attn(const AttnArgs a) {
 // query rows, and no wave repeats another's scores.  The query operand is
 // loaded straight into B-operand order (lane: query l mod 16, dims
 // 32s + 8(l / 16) ..), scaled by its RMS factor and split into hi / lo.
-template <int HD, bool KVB, int NQT>
+template <int HD, bool KVB, int NQT, bool VO>
 __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
   constexpr int NTH = 64 * NQT, NS = HD / 32, NTW = HD / 16, HJ = HD / 64;
   __shared__ __align__(16) uint16_t Ks[32 * (HD + 8)];
   __shared__ __align__(16) uint16_t Vt[HD * 40];
+  __shared__ VoTables<HD, VO> vot;
 
   const int kvh = blockIdx.y;
   int sg = blockIdx.x, row = 0;
@@ -464,9 +539,14 @@ __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
                                    m_run, l_part, Ks, Vt);
   } else {
     const int64_t kvoff = (int64_t)kvh * len * HD * (KVB ? 2 : 4);
-    const char* kb = (const char*)a.row[row].k + kvoff;
     const char* vb = (const char*)a.row[row].v + kvoff;
-    attn_keys<HD, KVB, NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, 0, m_run, l_part, Ks, Vt);
+    if constexpr (VO) {
+      const VoCtx vo = vo_setup<HD, VO>(vot, a, row);
+      attn_keys<HD, KVB, NTH, NTW, true>(vb, vb, j0, j1, 1.f, prep, qh, ql, o, 0, m_run, l_part, Ks, Vt, vo);
+    } else {
+      const char* kb = (const char*)a.row[row].k + kvoff;
+      attn_keys<HD, KVB, NTH, NTW>(kb, vb, j0, j1, 1.f, prep, qh, ql, o, 0, m_run, l_part, Ks, Vt);
+    }
   }
 
   float l = l_part;
@@ -479,6 +559,12 @@ __global__ __launch_bounds__(64 * NQT) void k_attn_wide(const AttnArgs a) {
     a.ml[base * 2] = m_run;
     a.ml[base * 2 + 1] = l;
   }
+}
+
+bool attn_vonly_ok(int nq, int hd, bool wide) {
+  const int nth = wide ? 4 * nq : ATT_NTH;
+  if (hd != 64 && hd != 128 && hd != 256) return false;
+  return (hd / 16) % (nth / ATT_KEYS) == 0 && ATT_KEYS * (hd / 8) % nth == 0;
 }
 
 bool attn_wide_ok(int nq, int hd) {
@@ -495,8 +581,15 @@ hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStre
   const dim3 grid(nsplit, a.nKv);  // nsplit: the split count, or 8 * slots per XCD (xcd_rows)
   const int nqt = a.nq / 16;
 #define DSP_WIDE(H, Q)                                                                                    \
-  if (kv_bf16) hipLaunchKernelGGL((k_attn_wide<H, true, Q>), grid, dim3(64 * Q), 0, st, a);              \
-  else hipLaunchKernelGGL((k_attn_wide<H, false, Q>), grid, dim3(64 * Q), 0, st, a);
+  if (a.vonly) {                                                                                          \
+    if constexpr (vo_layout_ok<H, 64 * Q>()) {                                                            \
+      if (!kv_bf16) return hipErrorInvalidValue;                                                          \
+      hipLaunchKernelGGL((k_attn_wide<H, true, Q, true>), grid, dim3(64 * Q), 0, st, a);                  \
+    } else {                                                                                              \
+      return hipErrorInvalidValue;                                                                        \
+    }                                                                                                     \
+  } else if (kv_bf16) hipLaunchKernelGGL((k_attn_wide<H, true, Q, false>), grid, dim3(64 * Q), 0, st, a); \
+  else hipLaunchKernelGGL((k_attn_wide<H, false, Q, false>), grid, dim3(64 * Q), 0, st, a);
   if (a.hd == 64) {
     if (nqt == 2) { DSP_WIDE(64, 2) }
     else { DSP_WIDE(64, 4) }
@@ -511,8 +604,15 @@ hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStre
 hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st) {
   dim3 grid(nsplit, a.nKv, (a.nq + 15) / 16), block(ATT_NTH);
 #define DSP_ATTN(H)                                                                            \
-  if (kv_bf16) hipLaunchKernelGGL((k_attn<H, true>), grid, block, 0, st, a);                   \
-  else hipLaunchKernelGGL((k_attn<H, false>), grid, block, 0, st, a);
+  if (a.vonly) {                                                                               \
+    if constexpr (vo_layout_ok<H, ATT_NTH>()) {                                                \
+      if (!kv_bf16) return hipErrorInvalidValue;                                               \
+      hipLaunchKernelGGL((k_attn<H, true, true>), grid, block, 0, st, a);                      \
+    } else {                                                                                   \
+      return hipErrorInvalidValue;                                                             \
+    }                                                                                          \
+  } else if (kv_bf16) hipLaunchKernelGGL((k_attn<H, true, false>), grid, block, 0, st, a);     \
+  else hipLaunchKernelGGL((k_attn<H, false, false>), grid, block, 0, st, a);
   if (a.hd == 64) { DSP_ATTN(64) }
   else if (a.hd == 128) { DSP_ATTN(128) }
   else { DSP_ATTN(256) }

@@ -424,6 +424,7 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
       kv[j] = d < half ? t[j] * cs.x - partner * cs.y : t[j] * cs.x + partner * cs.y;
     }
     const int64_t off = (((int64_t)b * e.nKv + kvh) * e.L + i) * hd;
+    // (kout null: a V-only cache, K is rebuilt from V where it is read)
     if (bf) {
       uint16_t* const vo = (uint16_t*)vout + off;
       uint16_t* const ko = (uint16_t*)kout + off;
@@ -431,7 +432,7 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
       for (int j = 0; j < 4; ++j)
         if (j < HJ) {
           vo[lane + 64 * j] = f2bf(vv[j]);
-          ko[lane + 64 * j] = f2bf(kv[j]);
+          if (kout) ko[lane + 64 * j] = f2bf(kv[j]);
         }
     } else {
       float* const vo = (float*)vout + off;
@@ -440,7 +441,7 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
       for (int j = 0; j < 4; ++j)
         if (j < HJ) {
           vo[lane + 64 * j] = vv[j];
-          ko[lane + 64 * j] = kv[j];
+          if (kout) ko[lane + 64 * j] = kv[j];
         }
     }
   }

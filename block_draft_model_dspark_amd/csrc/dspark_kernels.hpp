@@ -207,6 +207,13 @@ struct AttnArgs {
   int xcd_rows;
   float eps;
   const float* q; const float* kb; const float* vb; const float* ssq;
+  // V-only context cache (row[a].k unused): the context keys are rebuilt as
+  // K = RoPE(V * k_norm) at positions ctx_pos0[a] + j while they are staged
+  int vonly;
+  const void* kn;        // this layer's k_norm weight [hd], bf16
+  double theta;
+  int nrot;
+  int ctx_pos0[MAX_ROWS];
   // [nsplit, nKv, nq, hd]: fp32 unnormalised for an fp32 cache; for a bf16
   // cache, fp16 of O / sum (|O / sum| <= max |v|, unit-RMS value rows)
   void* opart;
@@ -279,6 +286,9 @@ hipError_t launch_attn(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t 
 // one workgroup per (row, split, kv head) with every query row (nq = 32, 64
 // or 128 rows, staging layout permitting)
 bool attn_wide_ok(int nq, int hd);
+// whether the kernel that takes these shapes can rebuild context keys from a
+// V-only cache (each staging thread must hold both halves of its RoPE pairs)
+bool attn_vonly_ok(int nq, int hd, bool wide);
 hipError_t launch_attn_wide(const AttnArgs& a, bool kv_bf16, int nsplit, hipStream_t st);
 hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st);

@@ -141,7 +141,10 @@ size_t dspark_project_workspace_bytes(const dspark_model* m, int input_kind, int
  * RMSNorm(k); K = RoPE(RMSNorm(k; k_norm)) at positions pos0[b] + i.
  *   x_dev        input per `input_kind`, row-major, act dtype
  *   pos0_host[B] first absolute position of each batch row (>= 0)
- *   k_out_dev[l], v_out_dev[l]  per layer, [B, nKv, L, hd] act dtype
+ *   k_out_dev[l], v_out_dev[l]  per layer, [B, nKv, L, hd] act dtype;
+ *                k_out_dev may be NULL: a V-only cache (V is the weightless
+ *                norm of the same k, so K = RoPE(V * k_norm) can be rebuilt
+ *                where it is read; dspark_draft_rows_ex takes such a cache)
  * Workspace: dspark_project_workspace_bytes(m, input_kind, B, L) bytes,
  * 256-byte aligned, any contents (the call clears what it needs). */
 dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, const void* x_dev, int B, int L,
@@ -199,6 +202,36 @@ dspark_status dspark_draft_rows_conf(const dspark_model* m, int A, const void* c
                                      const float* thresholds_host, int32_t* tokens_dev, float* logits_dev,
                                      float* conf_dev, int32_t* lengths_dev, const void* aux_dev, void* ws_dev,
                                      size_t ws_bytes, hipStream_t stream);
+
+/* Every input and output of one draft round, for dspark_draft_rows_ex.
+ * Fields as the arguments of the same names of dspark_draft_rows_conf, plus:
+ *   k_ctx_dev      NULL: a V-only context cache (dspark_project_context_kv
+ *                  with k_out_dev NULL).  The attention rebuilds each context
+ *                  key as K = RoPE(V * k_norm) at position ctx_pos0[a] + j
+ *                  (V is the weightless norm of the same k, so this is the
+ *                  stored K up to the rounding of V): half the context bytes.
+ *                  Built for bf16 caches (DSPARK_ERR_UNSUPPORTED otherwise,
+ *                  and for head_dim 64).
+ *   ctx_pos0_host  [A] absolute position of each row's first context row
+ *                  (the pos0 the projection used), or NULL: 0.  Only read
+ *                  for a V-only cache. */
+typedef struct {
+  int32_t A;
+  const void* const* k_ctx_dev;   /* [layers * A] or NULL (V-only) */
+  const void* const* v_ctx_dev;   /* [layers * A] */
+  const int32_t* ctx_len_host;    /* [A] */
+  const int32_t* ctx_pos0_host;   /* [A] or NULL */
+  const int32_t* anchors_host;    /* [A] */
+  const int32_t* positions_host;  /* [A] */
+  const float* thresholds_host;   /* [gamma] or NULL */
+  int32_t* tokens_dev;            /* [A, gamma] */
+  float* logits_dev;              /* [A, gamma, V] or NULL */
+  float* conf_dev;                /* [A, gamma] or NULL */
+  int32_t* lengths_dev;           /* [A] or NULL */
+  const void* aux_dev;
+} dspark_draft_args;
+dspark_status dspark_draft_rows_ex(const dspark_model* m, const dspark_draft_args* args, void* ws_dev,
+                                   size_t ws_bytes, hipStream_t stream);
 
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc):

@@ -239,6 +239,14 @@ def context_kv_layer(m: OracleModel, layer: Layer, ctx: np.ndarray, positions: n
     return K, v.transpose(1, 0, 2)
 
 
+def keys_from_values(m: OracleModel, layer: Layer, V: np.ndarray, positions: np.ndarray) -> np.ndarray:
+    """The context keys of a V-only cache: deepspec.ts, #projectContextKVRows
+    makes V = rms(k) and K = RoPE(rms(k) * k_norm) from the same k, so
+    K = RoPE(V * k_norm) at the rows' positions.  V [nKv, L, hd] (the stored
+    values), positions [L] -> K [nKv, L, hd]."""
+    return rope(V * layer.k_norm, positions, m.wavelengths)
+
+
 def project_context_kv(m: OracleModel, ctx: np.ndarray, pos0) -> List[Tuple[np.ndarray, np.ndarray]]:
     """deepspec.ts, #projectContextKVRows: ctx [B, L, H]; row b's rows start at
     absolute position pos0[b] (a scalar applies to every row).  Returns per

@@ -609,3 +609,25 @@ def test_round_lengths_follow_the_config_threshold():
     m.conf_b = np.array([-50.0])
     r1 = O.draft_rows(m, kv, [1, 2, 3], [5, 6, 7])
     assert r1["lengths"].tolist() == [0, 0, 0] and np.array_equal(r1["tokens"], r["tokens"])
+
+
+# ---------------------------------------------------------------- V-only context cache
+
+
+def test_keys_rebuilt_from_values_equal_projected_keys():
+    """A V-only cache loses nothing: K rebuilt from V (RoPE(V * k_norm) at the
+    rows' positions) equals the projected K, at any offset, for a partial
+    rotary factor too."""
+    for cfg in (SMALL, synth.scaled(SMALL, partial_rotary_factor=0.25)):
+        m = small_model(cfg)
+        ctx = rand((2, 9, cfg.H), 50)
+        for pos0 in ([0, 0], [7, 40000]):
+            kv = O.project_context_kv(m, ctx, pos0)
+            for layer, (K, V) in zip(m.layers, kv):
+                for b in range(2):
+                    Kr = O.keys_from_values(m, layer, V[b], pos0[b] + np.arange(9))
+                    assert np.allclose(Kr, K[b], rtol=1e-12, atol=1e-12)
+    # and the rebuild is not the identity: without k_norm or RoPE it differs
+    m = small_model()
+    K, V = O.project_context_kv(m, rand((1, 5, SMALL.H), 51), 3)[0]
+    assert not np.allclose(V[0], K[0], atol=1e-3)
