@@ -52,10 +52,17 @@ TRAFFIC = {
 }
 
 
+def dom_traffic_key(role):
+    """The TRAFFIC record of one GEMM role of the headline step, if taken."""
+    return "gemm_" + role[5:] if ("gemm_" + role[5:]) in TRAFFIC else "none"
+
+
 def traffic(key):
     """The recorded bytes per step of a kernel group while its sources are
     unchanged, else None."""
     import hashlib
+    if key not in TRAFFIC:
+        return None
     t = TRAFFIC[key]
     h = hashlib.sha256()
     for f in t["sources"]:
@@ -222,7 +229,11 @@ class Shared:
 
     def __init__(self, dsp, synth):
         self.dsp, self.synth = dsp, synth
-        self.cfg = synth.WORKLOADS["full_bf16_a1"].model
+        # the full model plus its optional heads (fc/hidden_norm for the
+        # target-feature projection, the confidence head for the truncation
+        # measurement); the headline round reads neither
+        self.cfg = synth.scaled(synth.WORKLOADS["full_bf16_a1"].model, enable_confidence_head=True,
+                                confidence_head_with_markov=True, confidence_threshold=0.3)
         self.stored = synth.make_model(self.cfg, with_fc=True)
         self.model = dsp.Model(self.cfg, dsp.upload(self.stored)).prepare()
         self._om = None
@@ -266,6 +277,10 @@ def bench_full(args, dsp, synth, torch, sh):
         if k in roles:
             v["algorithmic_GBs"] = round(roles[k][0] * roles[k][1] / (v["us_per_step"] * 1e3), 1)
     traffic_b = traffic("gemm_full")
+    # the dominant kernel: the GEMM role with the largest time per step
+    dom = max((k for k in roles if k in kernels), key=lambda k: kernels[k]["us_per_step"])
+    dom_us = kernels[dom]["us_per_step"] / kernels[dom]["launches_per_step"]
+    dom_gbs = roles[dom][0] / (dom_us * 1e3)
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -275,11 +290,15 @@ def bench_full(args, dsp, synth, torch, sh):
                    "rows": A, "gamma": cfg.gamma, "ctx_len": L,
                    "step": "context K/V projection of 512 rows + one draft round",
                    "tokens_per_s": round(value * cfg.gamma, 1)},
-        "roofline": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_b,
-                     "bytes_per_step": g_bytes, "launches_per_step": g_launch,
-                     "us_per_step": round(1e3 * g_ms, 2)},
+        "roofline": {"bound": "hbm", "kernel": f"k_gemm {dom[5:]} role (weight-streaming bf16 MFMA GEMM)",
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic(dom_traffic_key(dom)),
+                     "bytes_per_launch": roles[dom][0], "us_per_launch": round(dom_us, 2)},
+        "roofline_gemm_all": {"bound": "hbm", "kernel": "k_gemm (weight-streaming bf16 MFMA GEMM, all roles)",
+                              "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic_b,
+                              "bytes_per_step": g_bytes, "launches_per_step": g_launch,
+                              "us_per_step": round(1e3 * g_ms, 2)},
         "kernels": kernels,
         "kernel_sum_us_per_step": round(kern_sum_us, 2),
     }
@@ -333,8 +352,9 @@ def bench_prefill(args, dsp, synth, torch, sh):
     return out
 
 
-def bench_rows(args, dsp, synth, torch, sh):
-    """One draft round over 32 ragged rows whose context K/V is stored per row."""
+def bench_rows(args, dsp, synth, torch, sh, vonly=False):
+    """One draft round over 32 ragged rows whose context K/V is stored per
+    row (vonly: a V-only cache, K rebuilt in the attention)."""
     w = synth.WORKLOADS["rows_a32"]
     cfg = w.model
     model = sh.model
@@ -348,7 +368,10 @@ def bench_rows(args, dsp, synth, torch, sh):
             k_rows[li][a] = dsp.act_tensor(kv["k"])
             v_rows[li][a] = dsp.act_tensor(kv["v"])
     anchors = synth.anchors(w)
-    call = dsp.DraftCall(model, k_rows, v_rows, lens, anchors, lens)
+    if vonly:
+        call = dsp.DraftCallEx(model, None, v_rows, lens, anchors, lens)
+    else:
+        call = dsp.DraftCall(model, k_rows, v_rows, lens, anchors, lens)
 
     ms, prof, nprof = run_timed(call, args)
     kernels = kernel_table(prof, nprof)
@@ -356,7 +379,7 @@ def bench_rows(args, dsp, synth, torch, sh):
     fl = gemm_flops_round(cfg, M)
     g_ms = sum(v[1] for k, v in prof.items() if k.startswith("gemm.")) / nprof
     g_tflops = fl / (g_ms * 1e-3) / 1e12
-    ab = attn_bytes(cfg, lens)
+    ab = attn_bytes(cfg, lens) // (2 if vonly else 1)  # a V-only cache streams V alone
     at_us = kernels["attn"]["us_per_step"]
     kernels["attn"]["algorithmic_GBs"] = round(ab / (at_us * 1e3), 1)
     value = A * args.steps / (ms / 1e3)
@@ -365,7 +388,8 @@ def bench_rows(args, dsp, synth, torch, sh):
         "warmup": args.warmup, "ms_per_step": round(ms / args.steps, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "rows_a32: full_bf16 model, A=32 blocks of gamma 16, per-row context "
-                               "lengths uniform in [1024, 4096] stored per row",
+                               "lengths uniform in [1024, 4096] stored per row"
+                               + (" as a V-only cache (keys rebuilt from values in the attention)" if vonly else ""),
                    "rows": A, "gamma": cfg.gamma, "ctx_lens_sum": sum(lens),
                    "step": "one dspark_draft_rows call",
                    "tokens_per_s": round(value * cfg.gamma, 1)},
@@ -373,19 +397,53 @@ def bench_rows(args, dsp, synth, torch, sh):
                      "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic("tall_rows"),
                      "flops_per_step": fl, "us_per_step": round(1e3 * g_ms, 2)},
-        "roofline_attn": {"bound": "hbm", "kernel": "ctx++block attention (context K/V streaming)",
+        "roofline_attn": {"bound": "hbm", "kernel": "ctx++block attention (context " + ("V" if vonly else "K/V")
+                                                     + " streaming)",
                           "achieved": round(ab / (at_us * 1e3), 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": round(ab / (at_us * 1e3) / HBM_PEAK_GBS, 4), "traffic": traffic("attn_rows"),
+                          "frac": round(ab / (at_us * 1e3) / HBM_PEAK_GBS, 4),
+                          "traffic": None if vonly else traffic("attn_rows"),
                           "bytes_per_step": ab, "us_per_step": round(at_us, 2)},
         "kernels": kernels,
         "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not vonly:
         out["cpu_baseline"] = cpu_baseline_rows(w, lens, args.cpu_seconds, sh.oracle())
     return out
 
 
-BENCHES = {"full_bf16_a1": bench_full, "prefill_8192": bench_prefill, "rows_a32": bench_rows}
+def bench_rows_vonly(args, dsp, synth, torch, sh):
+    return bench_rows(args, dsp, synth, torch, sh, vonly=True)
+
+
+def bench_conf(args, dsp, synth, torch, sh):
+    """The one-block round (512 context rows, as the headline) with the
+    confidence head scoring every slot and the rows' confident-prefix lengths
+    (threshold 0.3) returned: the round alone, no context projection."""
+    w = synth.WORKLOADS["full_bf16_a1"]
+    cfg = sh.cfg
+    model = sh.model
+    L, A = w.fixed_ctx_len, w.rows
+    x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
+    ks, vs = dsp.project_context_kv(model, x, [0])
+    anchors = synth.anchors(w)
+    call = dsp.DraftCallEx(model, [[k[0]] for k in ks], [[v[0]] for v in vs], [L], anchors, [L],
+                           collect_conf=True, lengths=True)
+    ms, prof, nprof = run_timed(call, args)
+    kernels = kernel_table(prof, nprof)
+    value = A * args.steps / (ms / 1e3)
+    return {"value": round(value, 2), "unit": "blocks/s", "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms / args.steps, 4),
+            "config": {"workload": "full_bf16_a1 round with the confidence head (with the Markov feature), "
+                                   "threshold 0.3, lengths and every slot's confidence returned",
+                       "rows": A, "gamma": cfg.gamma, "ctx_len": L,
+                       "step": "one dspark_draft_rows_ex call (no context projection)"},
+            "confidence_us_per_step": round(kernels.get("confidence", {}).get("us_per_step", 0.0), 2),
+            "lengths": call.out["lengths"].cpu().tolist(),
+            "kernels": kernels}
+
+
+BENCHES = {"full_bf16_a1": bench_full, "prefill_8192": bench_prefill, "rows_a32": bench_rows,
+           "rows_a32_vonly": bench_rows_vonly, "full_bf16_a1_conf": bench_conf}
 
 
 def main():
@@ -428,7 +486,7 @@ def main():
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.profile_steps = args.sub_steps, max(2, args.warmup // 4), min(args.profile_steps, 5)
     out["workloads"] = {}
-    for name in ("rows_a32", "prefill_8192"):
+    for name in ("rows_a32", "prefill_8192", "rows_a32_vonly", "full_bf16_a1_conf"):
         r = BENCHES[name](sub, dsp, synth, torch, sh)
         print(f"{name}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
         for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "dtype"):

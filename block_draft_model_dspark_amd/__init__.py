@@ -343,6 +343,57 @@ class DraftCall:
         return self.tokens
 
 
+class DraftCallEx:
+    """Marshalled arguments of one dspark_draft_rows_ex call (reusable, like
+    DraftCall): k_rows None for a V-only cache; optional confidence outputs."""
+
+    def __init__(self, model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
+                 positions: Sequence[int], ctx_pos0: Optional[Sequence[int]] = None,
+                 thresholds: Optional[Sequence[float]] = None, collect_logits: bool = False,
+                 collect_conf: bool = False, lengths: bool = False):
+        import torch
+        cfg = model.cfg
+        A = len(anchors)
+        nL = cfg.num_hidden_layers
+        self.model = model
+        self.keep_t = (k_rows, v_rows)
+        self._keep = []
+
+        def arr(ctype, vals):
+            a = (ctype * len(vals))(*vals)
+            self._keep.append(a)
+            return ctypes.cast(a, ctypes.c_void_p)
+
+        self.out = {"tokens": torch.empty(A, cfg.gamma, dtype=torch.int32, device="cuda"),
+                    "logits": torch.empty(A, cfg.gamma, cfg.V, device="cuda") if collect_logits else None,
+                    "conf": torch.empty(A, cfg.gamma, device="cuda") if collect_conf else None,
+                    "lengths": torch.empty(A, dtype=torch.int32, device="cuda") if lengths else None}
+        x = DraftArgs()
+        x.A = A
+        x.k_ctx_dev = None if k_rows is None else arr(ctypes.c_void_p, [k_rows[l][a].data_ptr() for l in range(nL)
+                                                                        for a in range(A)])
+        x.v_ctx_dev = arr(ctypes.c_void_p, [v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
+        x.ctx_len_host = arr(ctypes.c_int32, [int(v) for v in ctx_lens])
+        x.ctx_pos0_host = None if ctx_pos0 is None else arr(ctypes.c_int32, [int(v) for v in ctx_pos0])
+        x.anchors_host = arr(ctypes.c_int32, [int(v) for v in anchors])
+        x.positions_host = arr(ctypes.c_int32, [int(v) for v in positions])
+        x.thresholds_host = None if thresholds is None else arr(ctypes.c_float, [float(t) for t in thresholds])
+        x.tokens_dev = self.out["tokens"].data_ptr()
+        x.logits_dev = _ptr(self.out["logits"])
+        x.conf_dev = _ptr(self.out["conf"])
+        x.lengths_dev = _ptr(self.out["lengths"])
+        x.aux_dev = _ptr(model.aux)
+        self.args = x
+        self.nbytes = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
+        self.ws = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
+
+    def __call__(self, stream=None):
+        _check(_lib.dspark_draft_rows_ex(self.model.handle, ctypes.byref(self.args), self.ws.data_ptr(), self.nbytes,
+                                         _stream_handle(stream)))
+        _keep_for(stream, self.ws, *[t for t in self.out.values() if t is not None])
+        return self.out
+
+
 def draft_rows(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
                positions: Sequence[int], collect_logits: bool = False, stream=None):
     """deepspec.ts, draftRows.  k_rows[l][a], v_rows[l][a]: row a's layer-l
@@ -391,42 +442,9 @@ def draft_rows_ex(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors
     """deepspec.ts, draftRows through dspark_draft_rows_ex.  k_rows None: a
     V-only context cache (v_rows[l][a] only; the attention rebuilds the keys
     at positions ctx_pos0[a] + j).  Returns a dict of device tensors: tokens,
-    and logits / conf / lengths when asked for."""
-    import torch
-    cfg = model.cfg
-    A = len(anchors)
-    nL = cfg.num_hidden_layers
-    keep = []
-
-    def arr(ctype, vals):
-        a = (ctype * len(vals))(*vals)
-        keep.append(a)
-        return ctypes.cast(a, ctypes.c_void_p)
-
-    out = {"tokens": torch.empty(A, cfg.gamma, dtype=torch.int32, device="cuda")}
-    out["logits"] = torch.empty(A, cfg.gamma, cfg.V, dtype=torch.float32, device="cuda") if collect_logits else None
-    out["conf"] = torch.empty(A, cfg.gamma, dtype=torch.float32, device="cuda") if collect_conf else None
-    out["lengths"] = torch.empty(A, dtype=torch.int32, device="cuda") if lengths else None
-    x = DraftArgs()
-    x.A = A
-    x.k_ctx_dev = None if k_rows is None else arr(ctypes.c_void_p, [k_rows[l][a].data_ptr() for l in range(nL)
-                                                                    for a in range(A)])
-    x.v_ctx_dev = arr(ctypes.c_void_p, [v_rows[l][a].data_ptr() for l in range(nL) for a in range(A)])
-    x.ctx_len_host = arr(ctypes.c_int32, [int(v) for v in ctx_lens])
-    x.ctx_pos0_host = None if ctx_pos0 is None else arr(ctypes.c_int32, [int(v) for v in ctx_pos0])
-    x.anchors_host = arr(ctypes.c_int32, [int(v) for v in anchors])
-    x.positions_host = arr(ctypes.c_int32, [int(v) for v in positions])
-    x.thresholds_host = None if thresholds is None else arr(ctypes.c_float, [float(t) for t in thresholds])
-    x.tokens_dev = out["tokens"].data_ptr()
-    x.logits_dev = _ptr(out["logits"])
-    x.conf_dev = _ptr(out["conf"])
-    x.lengths_dev = _ptr(out["lengths"])
-    x.aux_dev = _ptr(model.aux)
-    n = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
-    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
-    _check(_lib.dspark_draft_rows_ex(model.handle, ctypes.byref(x), ws.data_ptr(), n, _stream_handle(stream)))
-    _keep_for(stream, ws, *[t for t in out.values() if t is not None])
-    return out
+    and logits / conf / lengths when asked for (None otherwise)."""
+    return DraftCallEx(model, k_rows, v_rows, ctx_lens, anchors, positions, ctx_pos0, thresholds, collect_logits,
+                       collect_conf, lengths)(stream)
 
 
 def draft_rows_noalloc(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],

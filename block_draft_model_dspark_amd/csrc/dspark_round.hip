@@ -594,19 +594,47 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
 // One workgroup per draft row, wave w takes slots w, w + 16, ...; every lane
 // holds H / 64 entries of the row.  grid A, block 1024
 // ---------------------------------------------------------------------------
+constexpr int CONF_NV = 4;  // 8-element pieces per lane and pass (H up to 64 * 8 * CONF_NV per pass)
+
 __global__ __launch_bounds__(1024) void k_conf(const ConfArgs a) {
   __shared__ float cs[CONF_MAX_GAMMA];
   const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma;
   if (a.head) {
     const float b = ld_act(a.bias, 0, a.act_bf16);
+    const bool bf = a.act_bf16 != 0, wbf = a.wkind == WK_BF16;
+    const int cols = a.H + (a.with_markov ? a.rank : 0);
     for (int k = wave; k < G; k += 16) {
       const int64_t m = (int64_t)row * G + k;
       const float* h = a.hn + m * a.ldh;
       float ss = 0.f, dot = 0.f;
-      for (int i = lane; i < a.H; i += 64) {
-        const float v = h[i];
-        ss += v * v;
-        dot += v * ld_act(a.wnorm, i, a.act_bf16) * table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, a.H + (a.with_markov ? a.rank : 0), i);
+      // pieces of eight: every load of a pass issued before the first use
+      for (int p0 = 0; p0 < a.H; p0 += 64 * 8 * CONF_NV) {
+        f32x4 hv[CONF_NV][2];
+        Raw8 wn[CONF_NV];
+        u32x4 pw[CONF_NV];
+#pragma unroll
+        for (int q = 0; q < CONF_NV; ++q) {
+          const int i0 = min(p0 + 8 * (lane + 64 * q), a.H - 8);
+          hv[q][0] = *(const f32x4*)(h + i0);
+          hv[q][1] = *(const f32x4*)(h + i0 + 4);
+          wn[q] = ld_act8(a.wnorm, i0, bf);
+          if (wbf) pw[q] = *(const u32x4*)((const uint16_t*)a.pw + i0);
+        }
+#pragma unroll
+        for (int q = 0; q < CONF_NV; ++q) {
+          const int i0 = p0 + 8 * (lane + 64 * q);
+          if (i0 >= a.H) break;
+          float w8[8];
+          cvt_act8(wn[q], bf, w8);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = hv[q][e >> 2][e & 3];
+            const float p = wbf ? __uint_as_float((pw[q][e >> 1] << ((e & 1) ? 0 : 16)) & 0xFFFF0000u)
+                                : table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, cols, i0 + e);
+            ss += v * v;
+            dot += v * w8[e] * p;
+          }
+        }
       }
       ss = wave_sum(ss);
       dot = wave_sum(dot) / sqrtf(ss / a.H + a.eps);
@@ -615,7 +643,7 @@ __global__ __launch_bounds__(1024) void k_conf(const ConfArgs a) {
         float dm = 0.f;
         if (prev >= 0)  // a walk step without a finite candidate reports -1 (no Markov feature)
           for (int j = lane; j < a.rank; j += 64)
-            dm += table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, a.H + a.rank, a.H + j) *
+            dm += table_elem(a.pw, a.ps, a.pb, a.wkind, a.group, 0, cols, a.H + j) *
                   table_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
         dot += wave_sum(dm);
       }
