@@ -189,6 +189,11 @@ class OracleModel:
         self.lm_head = d("lm_head.weight")
         self.w1 = d("markov_head.markov_w1.weight") if cfg.markov_rank > 0 else None
         self.w2 = d("markov_head.markov_w2.weight") if cfg.markov_rank > 0 else None
+        # the RNN head's recurrence (mlx-bun 0.2.0 -> 0.4.0, forwardRows: rnn.wH
+        # [r, r] applied as s @ wH, rnn.bH [r])
+        self.rnn = getattr(cfg, "markov_head_type", "vanilla") == "rnn" and cfg.markov_rank > 0
+        self.wh = d("markov_head.rnn_wh.weight") if self.rnn else None
+        self.bh = d("markov_head.rnn_bh.bias") if self.rnn else None
         # deepspec.ts, DeepspecDrafter constructor: the confidence head is a
         # Linear(confDim, 1) with bias, present when enable_confidence_head
         conf = getattr(cfg, "enable_confidence_head", False)
@@ -335,18 +340,26 @@ def top2(u: np.ndarray) -> Tuple[int, float]:
     return t, float(u[t] - rest.max())
 
 
+def rnn_state(m: OracleModel, s_prev: np.ndarray, prev: int) -> np.ndarray:
+    """The RNN head's state update (mlx-bun 0.2.0 -> 0.4.0, forwardRows, the
+    rnn sequential head): s_k = tanh(s_{k-1} @ wH + w1[prev] + bH)."""
+    return np.tanh(s_prev @ m.wh + m.w1[prev] + m.bh)
+
+
+def rnn_scores(m: OracleModel, z_step: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Base logits plus the RNN head's bias from its state: the output
+    projection is markov_w2 (deepspec.ts readConfig: the gated / rnn heads
+    ship markov_w1 and markov_w2 too), bias_v = w2[v] . s."""
+    return z_step + m.w2 @ s
+
+
 def markov_walk(m: OracleModel, z: np.ndarray, anchor: int) -> Tuple[np.ndarray, np.ndarray]:
     """deepspec.ts, draftRows sequential Markov sampling at temperature 0:
     prev = anchor; for each block slot k: tok = argmax(z[k] + bias(prev));
-    prev = tok.  z [gamma, V].  Returns (tokens [gamma], margins [gamma])."""
-    prev = anchor
-    toks, margins = [], []
-    for k in range(z.shape[0]):
-        t, mg = top2(step_scores(m, z[k], prev))
-        toks.append(t)
-        margins.append(mg)
-        prev = t
-    return np.array(toks, dtype=np.int64), np.array(margins)
+    prev = tok.  z [gamma, V].  Returns (tokens [gamma], margins [gamma]).
+    With the RNN head the bias comes from a state carried across the block
+    (s_{-1} = 0)."""
+    return teacher_forced(m, z, anchor, None)
 
 
 def sigmoid(z):
@@ -422,17 +435,23 @@ def draft_block(m: OracleModel, ctx_kv: Sequence[Tuple[np.ndarray, np.ndarray]],
     return {k: v[0] for k, v in r.items()}
 
 
-def teacher_forced(m: OracleModel, z: np.ndarray, anchor: int, tokens: Sequence[int]
+def teacher_forced(m: OracleModel, z: np.ndarray, anchor: int, tokens: Optional[Sequence[int]]
                    ) -> Tuple[np.ndarray, np.ndarray]:
     """Per-step check of a walk produced elsewhere: step k is scored with the
-    previous token taken from `tokens` (the anchor at k = 0), so one early
-    near-tie cannot hide later steps.  Returns (argmax [gamma],
-    margin [gamma])."""
+    previous tokens taken from `tokens` (the anchor at k = 0; the RNN head's
+    state follows the same given prefix), so one early near-tie cannot hide
+    later steps.  tokens None: the free walk (each step's own argmax feeds
+    the next).  Returns (argmax [gamma], margin [gamma])."""
     out, mgs = [], []
     prev = anchor
+    s = np.zeros(m.cfg.markov_rank) if m.rnn else None
     for k in range(z.shape[0]):
-        t, mg = top2(step_scores(m, z[k], prev))
+        if m.rnn:
+            s = rnn_state(m, s, prev)
+            t, mg = top2(rnn_scores(m, z[k], s))
+        else:
+            t, mg = top2(step_scores(m, z[k], prev))
         out.append(t)
         mgs.append(mg)
-        prev = int(tokens[k])
+        prev = t if tokens is None else int(tokens[k])
     return np.array(out, dtype=np.int64), np.array(mgs)

@@ -47,6 +47,9 @@ class ModelConfig:
     weight_dtype: str = BF16
     act_dtype: str = BF16
     group_size: int = 64
+    # sequential head: "vanilla" (bias = w2 w1[prev]) or "rnn" (a tanh state
+    # carried across the block, the mlx-bun 0.2.0 -> 0.4.0 drafter's form)
+    markov_head_type: str = "vanilla"
     # confidence head (deepspec.ts, DeepspecConfig): sigmoid(proj [h; w1[prev]])
     enable_confidence_head: bool = False
     confidence_head_with_markov: bool = False

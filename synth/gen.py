@@ -139,6 +139,10 @@ def tensor_shape(cfg: ModelConfig, name: str) -> tuple:
         return (V, H)
     if name in ("markov_head.markov_w1.weight", "markov_head.markov_w2.weight"):
         return (V, r)
+    if name == "markov_head.rnn_wh.weight":
+        return (r, r)
+    if name == "markov_head.rnn_bh.bias":
+        return (r,)
     if name == "confidence_head.proj.weight":
         return (1, H + (r if cfg.confidence_head_with_markov else 0))
     if name == "confidence_head.proj.bias":
@@ -173,6 +177,8 @@ def tensor_names(cfg: ModelConfig, with_fc: bool = True) -> List[str]:
         names += [p + s for s in MATMUL_SUFFIXES] + [p + s for s in NORM_SUFFIXES] + [p + "layer_scalar"]
     if cfg.markov_rank > 0:
         names += ["markov_head.markov_w1.weight", "markov_head.markov_w2.weight"]
+        if cfg.markov_head_type == "rnn":
+            names += ["markov_head.rnn_wh.weight", "markov_head.rnn_bh.bias"]
     if cfg.enable_confidence_head:
         names += ["confidence_head.proj.weight", "confidence_head.proj.bias"]
     return names
@@ -181,7 +187,7 @@ def tensor_names(cfg: ModelConfig, with_fc: bool = True) -> List[str]:
 def is_matrix(name: str) -> bool:
     return (name in ("embed_tokens.weight", "fc.weight", "lm_head.weight",
                      "markov_head.markov_w1.weight", "markov_head.markov_w2.weight",
-                     "confidence_head.proj.weight")
+                     "confidence_head.proj.weight", "markov_head.rnn_wh.weight")
             or any(name.endswith(s) for s in MATMUL_SUFFIXES))
 
 
@@ -195,6 +201,8 @@ def make_tensor(cfg: ModelConfig, name: str, markov_active: bool = False,
         std = cfg.weight_std
         if name.startswith("markov_head."):
             std = 0.35 if markov_active else cfg.markov_std
+        if name == "markov_head.rnn_wh.weight":
+            std = 0.1  # a recurrence that matters without saturating the state
         if overrides and name in overrides:
             std = overrides[name]
         w = normal(cfg.seed, name, shape, std)

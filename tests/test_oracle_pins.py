@@ -631,3 +631,114 @@ def test_keys_rebuilt_from_values_equal_projected_keys():
     m = small_model()
     K, V = O.project_context_kv(m, rand((1, 5, SMALL.H), 51), 3)[0]
     assert not np.allclose(V[0], K[0], atol=1e-3)
+
+
+# ---------------------------------------------------------------- RNN sequential head
+
+
+RNN = synth.scaled(SMALL, markov_head_type="rnn")
+
+
+def test_rnn_head_brute_force_loops():
+    """s_k = tanh(s_{k-1} wH + w1[prev] + bH) from s_{-1} = 0, scores
+    z + w2 s_k, written out with scalar loops and math.tanh."""
+    m = small_model(RNN, markov_active=True)
+    r, V = RNN.markov_rank, RNN.V
+    z = rand((RNN.gamma, V), 60)
+    toks, margins = O.markov_walk(m, z, 9)
+    s = [0.0] * r
+    prev = 9
+    for k in range(RNN.gamma):
+        s = [math.tanh(sum(s[i] * m.wh[i][j] for i in range(r)) + m.w1[prev][j] + m.bh[j]) for j in range(r)]
+        u = [z[k, v] + sum(m.w2[v][j] * s[j] for j in range(r)) for v in range(V)]
+        best = max(range(V), key=lambda i: (u[i], -i))
+        second = max(u[i] for i in range(V) if i != best)
+        assert toks[k] == best and math.isclose(margins[k], u[best] - second, rel_tol=1e-9)
+        prev = best
+
+
+def test_rnn_head_chain_construction():
+    """w1 = c I, wH = 0, bH = 0: s_k = tanh(c) e_prev, and w2 = d P turns the
+    bias into d tanh(c) P e_prev, so the walk follows the permutation."""
+    V = 7
+    cfg = synth.scaled(RNN, vocab_size=V, markov_rank=V, mask_token_id=V - 1, block_size=6)
+    m = small_model(cfg)
+    perm = np.array([3, 5, 0, 6, 1, 2, 4])
+    P = np.zeros((V, V))
+    P[perm, np.arange(V)] = 1.0
+    m.w1 = 2.0 * np.eye(V)
+    m.wh = np.zeros((V, V))
+    m.bh = np.zeros(V)
+    m.w2 = 1000.0 * P
+    toks, _ = O.markov_walk(m, rand((cfg.gamma, V), 61), 2)
+    expect, cur = [], 2
+    for _ in range(cfg.gamma):
+        cur = perm[cur]
+        expect.append(cur)
+    assert toks.tolist() == expect
+
+
+def test_rnn_state_carries_across_steps():
+    """With w1 = 0 the tokens do not feed the state; s_k = tanh(a s_{k-1} + b)
+    per component with wH = a I, bH = b (a scalar recursion by hand), and a
+    single-entry w2 makes the step-k winner that entry whenever its bias
+    s_k[0] exceeds the logit gap."""
+    cfg = synth.scaled(RNN, markov_rank=4)
+    m = small_model(cfg)
+    r = cfg.markov_rank
+    m.w1 = np.zeros((cfg.V, r))
+    a, b = 0.9, 0.3
+    m.wh = a * np.eye(r)
+    m.bh = np.full(r, b)
+    m.w2 = np.zeros((cfg.V, r))
+    m.w2[5, 0] = 100.0
+    z = np.zeros((cfg.gamma, cfg.V))
+    z[:, 7] = 1.0  # entry 7 wins unless the state's bias lifts entry 5
+    _, mg = O.markov_walk(m, z, 0)
+    toks, _ = O.markov_walk(m, z, 0)
+    s = 0.0
+    for k in range(cfg.gamma):
+        s = math.tanh(a * s + b)
+        assert toks[k] == (5 if 100.0 * s > 1.0 else 7)
+        assert math.isclose(mg[k], abs(100.0 * s - 1.0), rel_tol=1e-9)
+
+
+def test_rnn_teacher_forced_follows_the_given_prefix():
+    """The state of the teacher-forced check is driven by the given tokens:
+    in the chain construction, step k's winner is perm[tokens[k-1]]."""
+    V = 7
+    cfg = synth.scaled(RNN, vocab_size=V, markov_rank=V, mask_token_id=V - 1, block_size=6)
+    m = small_model(cfg)
+    perm = np.array([3, 5, 0, 6, 1, 2, 4])
+    P = np.zeros((V, V))
+    P[perm, np.arange(V)] = 1.0
+    m.w1 = 2.0 * np.eye(V)
+    m.wh = np.zeros((V, V))
+    m.bh = np.zeros(V)
+    m.w2 = 1000.0 * P
+    given = [4, 4, 0, 6, 1, 5]
+    tf, _ = O.teacher_forced(m, rand((cfg.gamma, V), 62), 2, given)
+    assert tf.tolist() == [int(perm[p]) for p in [2] + given[:-1]]
+
+
+def test_rnn_recurrent_matrix_orientation():
+    """wH with one entry, wH[0, 1] = a, and bH = b e_0: s_0 = (tanh b, 0, ..),
+    and s_1[1] = tanh(a tanh b) only if the state multiplies from the left
+    (s @ wH, the forwardRows form); the transposed product leaves s_1[1] = 0.
+    w2 reads component 1, so step 1's winner tells them apart."""
+    cfg = synth.scaled(RNN, markov_rank=4)
+    m = small_model(cfg)
+    r = cfg.markov_rank
+    a, b = 1.5, 0.8
+    m.w1 = np.zeros((cfg.V, r))
+    m.wh = np.zeros((r, r))
+    m.wh[0, 1] = a
+    m.bh = np.zeros(r)
+    m.bh[0] = b
+    m.w2 = np.zeros((cfg.V, r))
+    m.w2[5, 1] = 100.0
+    z = np.zeros((cfg.gamma, cfg.V))
+    z[:, 7] = 1.0
+    toks, mg = O.markov_walk(m, z, 0)
+    assert toks[0] == 7 and math.isclose(mg[0], 1.0, rel_tol=1e-12)
+    assert toks[1] == 5 and math.isclose(mg[1], 100.0 * math.tanh(a * math.tanh(b)) - 1.0, rel_tol=1e-12)
