@@ -48,7 +48,7 @@ class Config(ctypes.Structure):
                 ("final_logit_softcapping", ctypes.c_double), ("weight_dtype", ctypes.c_int32),
                 ("act_dtype", ctypes.c_int32), ("group_size", ctypes.c_int32),
                 ("enable_confidence_head", ctypes.c_int32), ("confidence_head_with_markov", ctypes.c_int32),
-                ("confidence_threshold", ctypes.c_double)]
+                ("confidence_threshold", ctypes.c_double), ("markov_head_rnn", ctypes.c_int32)]
 
 
 class DraftArgs(ctypes.Structure):
@@ -219,6 +219,7 @@ class Model:
         c.enable_confidence_head = int(bool(getattr(cfg, "enable_confidence_head", False)))
         c.confidence_head_with_markov = int(bool(getattr(cfg, "confidence_head_with_markov", False)))
         c.confidence_threshold = float(getattr(cfg, "confidence_threshold", 0.0) or 0.0)
+        c.markov_head_rnn = int(getattr(cfg, "markov_head_type", "vanilla") == "rnn")
         self._c = c
         names = list(weights)
         self._names = [n.encode() for n in names]

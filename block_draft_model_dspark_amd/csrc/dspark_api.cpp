@@ -91,8 +91,10 @@ int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 struct dspark_model {
   dspark_config c;
-  Mat embed, fc, lm, w1, w2, conf;
+  Mat embed, fc, lm, w1, w2, conf, wh;
   const void* conf_b = nullptr;
+  const void* bh = nullptr;  // RNN head bias
+  bool rnn = false;
   const void* hidden_norm = nullptr;
   const void* norm = nullptr;
   std::vector<LayerW> L;
@@ -459,8 +461,10 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
 dspark_status check_config(const dspark_config& c) {
   if (!c.attention_k_eq_v)
     return fail(DSPARK_ERR_UNSUPPORTED, "attention_k_eq_v=false needs a v_proj path; only V == K is implemented");
-  if (c.markov_rank > 0 && !c.markov_head_vanilla)
-    return fail(DSPARK_ERR_UNSUPPORTED, "only the vanilla Markov head is implemented");
+  if (c.markov_rank > 0 && !c.markov_head_vanilla && !c.markov_head_rnn)
+    return fail(DSPARK_ERR_UNSUPPORTED, "only the vanilla and rnn Markov heads are implemented");
+  if (c.markov_head_vanilla && c.markov_head_rnn)
+    return fail(DSPARK_ERR_INVALID_ARG, "markov_head_vanilla and markov_head_rnn both set");
   if (!c.activation_gelu_tanh)
     return fail(DSPARK_ERR_UNSUPPORTED, "only the gelu_pytorch_tanh activation is implemented");
   if (c.hidden_size <= 0 || c.num_hidden_layers <= 0 || c.num_attention_heads <= 0 || c.global_head_dim <= 0 ||
@@ -629,6 +633,11 @@ dspark_status dspark_model_create(const dspark_config* cfg, const dspark_weight*
   if (c.markov_rank > 0) {
     mat("markov_head.markov_w1.weight", c.vocab_size, c.markov_rank, m->w1);
     mat("markov_head.markov_w2.weight", c.vocab_size, c.markov_rank, m->w2);
+    if (c.markov_head_rnn) {
+      mat("markov_head.rnn_wh.weight", c.markov_rank, c.markov_rank, m->wh);
+      m->bh = vec("markov_head.rnn_bh.bias", c.markov_rank);
+      m->rnn = true;
+    }
   }
   if (c.enable_confidence_head) {
     mat("confidence_head.proj.weight", 1, H + (c.confidence_head_with_markov ? c.markov_rank : 0), m->conf);
@@ -692,6 +701,7 @@ dspark_status dspark_model_prepare(dspark_model* m, void* aux_dev, size_t aux_by
   a.w1 = m->w1.w; a.w1s = m->w1.s; a.w1b = m->w1.b;
   a.w2 = m->w2.w; a.w2s = m->w2.s; a.w2b = m->w2.b;
   a.aux = (float*)aux_dev;
+  a.rnn = m->rnn ? 1 : 0;
   HIPCHECK(launch_aux(a, stream));
   return DSPARK_OK;
 }
@@ -1125,6 +1135,10 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   w.aux = e.aux;
   w.w1 = m->w1.w; w.w1s = m->w1.s; w.w1b = m->w1.b;
   w.w2 = m->w2.w; w.w2s = m->w2.s; w.w2b = m->w2.b;
+  w.rnn = m->rnn ? 1 : 0;
+  w.wh = m->wh.w; w.whs = m->wh.s; w.whb = m->wh.b;
+  w.bh = m->bh;
+  w.act_bf16 = abf;
   w.tokens = tokens_dev;
   HIPCHECK(timed("markov_walk", stream, [&] { return launch_walk(w, stream); }));
 

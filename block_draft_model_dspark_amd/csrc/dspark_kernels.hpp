@@ -240,6 +240,10 @@ struct WalkArgs {
   const float* z; const float2* lohi; const float* aux;
   const void* w1; const void* w1s; const void* w1b;
   const void* w2; const void* w2s; const void* w2b;
+  // RNN head: s_k = tanh(s_{k-1} wh + w1[prev] + bh), bias = w2 s_k
+  int rnn, act_bf16;
+  const void* wh; const void* whs; const void* whb;  // [rank, rank], weight dtype
+  const void* bh;                                      // [rank], act dtype
   int32_t* tokens;
 };
 
@@ -267,6 +271,7 @@ struct AuxArgs {
   const void* w1; const void* w1s; const void* w1b;
   const void* w2; const void* w2s; const void* w2b;
   float* aux;
+  int rnn;  // aux[V] bounds the RNN state's norm (sqrt(rank)) instead of the markov_w1 rows'
 };
 
 // launchers (return hipGetLastError())

@@ -365,14 +365,18 @@ __device__ __forceinline__ float w1w2_dot_part(const WalkArgs& a, int64_t prev, 
 }
 
 // the per-step path: every entry of a passing chunk is scored against the
-// actual previous token
+// actual previous token (vanilla head: e = markov_w1[prev]) or the state
+// that the previous tokens drove (RNN head: e = s_k)
 __device__ void walk_per_step(const WalkArgs& a, int row) {
   __shared__ float redu[WALK_NT / 64];
   __shared__ int redi[WALK_NT / 64];
   __shared__ float e[256];
+  __shared__ float st[256];  // RNN head: s_{k-1}
   __shared__ int prev_s;
   const int tid = threadIdx.x, G = a.rows.gamma;
   if (tid == 0) prev_s = a.rows.anchor[row];
+  if (a.rnn)
+    for (int j = tid; j < a.rank; j += WALK_NT) st[j] = 0.f;
   __syncthreads();
   for (int k = 0; k < G; ++k) {
     const int64_t m = (int64_t)row * G + k;
@@ -382,8 +386,18 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
     lm = block_max(lm, redu);
     const float thr = lm - 1e-4f * (1.f + fabsf(lm));
     const int prev = prev_s;
-    if (a.rank > 0)
+    if (a.rnn) {
+      // s_k = tanh(s_{k-1} wh + w1[prev] + bh): entry j is column j of s wh
+      for (int j = tid; j < a.rank; j += WALK_NT) {
+        float acc = ld_act(a.bh, j, a.act_bf16) + head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+        for (int i = 0; i < a.rank; ++i) acc += st[i] * head_elem(a.wh, a.whs, a.whb, a.wkind, a.group, i, a.rank, j);
+        e[j] = tanhf(acc);
+      }
+      __syncthreads();
+      for (int j = tid; j < a.rank; j += WALK_NT) st[j] = e[j];
+    } else if (a.rank > 0) {
       for (int j = tid; j < a.rank; j += WALK_NT) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+    }
     __syncthreads();
     float bu = -INFINITY;
     int bi = 0x7fffffff;
@@ -420,6 +434,12 @@ __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
   __shared__ int nflag, slow;
   const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma;
   const int NC = a.NC;
+  if (a.rnn) {
+    // the RNN head's bias depends on the whole prefix, not only on the
+    // previous token: no per-(step, previous candidate) table
+    walk_per_step(a, row);
+    return;
+  }
   if (tid < WALK_GMAX) ncand[tid] = 0;
   if (tid == 0) {
     nflag = 0;
@@ -577,9 +597,12 @@ __global__ __launch_bounds__(256) void k_aux(const AuxArgs a) {
   }
   s2 = wave_sum(s2);
   s1 = wave_sum(s1);
+  // |markov_w2[v] . x| <= ||markov_w2[v]|| ||x||; x = markov_w1[prev] (vanilla
+  // head) or the RNN state, whose entries are tanh values (||s|| <= sqrt(rank))
+  const float xb = a.rnn ? sqrtf((float)a.rank) : sqrtf(s1);
   if (l == 0) {
     a.aux[v] = sqrtf(s2) * (1.f + 1e-5f);
-    atomicMax((unsigned int*)&a.aux[a.V], __float_as_uint(sqrtf(s1) * (1.f + 1e-5f)));
+    atomicMax((unsigned int*)&a.aux[a.V], __float_as_uint(xb * (1.f + 1e-5f)));
   }
 }
 

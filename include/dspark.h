@@ -50,7 +50,7 @@ typedef enum { DSPARK_F32 = 0, DSPARK_BF16 = 1, DSPARK_Q4 = 2 } dspark_dtype;
  * readConfig.  readConfig refuses attention_k_eq_v == 0, a Markov head other
  * than "vanilla" when markov_rank > 0, and any activation other than
  * gelu_pytorch_tanh; dspark_model_create refuses the same with
- * DSPARK_ERR_UNSUPPORTED. */
+ * DSPARK_ERR_UNSUPPORTED, except the RNN head (markov_head_rnn below). */
 typedef struct {
   int32_t hidden_size;                /* H */
   int32_t num_hidden_layers;
@@ -81,6 +81,15 @@ typedef struct {
   int32_t enable_confidence_head;
   int32_t confidence_head_with_markov;  /* needs markov_rank > 0 */
   double confidence_threshold;
+  /* The RNN sequential head (markov_head_type "rnn"; markov_head_vanilla 0):
+   * the bias of block slot k is markov_w2 s_k with
+   * s_k = tanh(s_{k-1} W_H + markov_w1[prev_k] + b_H), s_{-1} = 0
+   * (the rnn head of the mlx-bun 0.2.0 -> 0.4.0 drafter, forwardRows; P1's
+   * readConfig notes such heads ship markov_w1/w2 too).  Extra tensors:
+   * "markov_head.rnn_wh.weight" [r, r] (weight dtype, applied as s @ W_H)
+   * and "markov_head.rnn_bh.bias" [r] (act dtype).  Other non-vanilla heads
+   * (the gated one, whose form the pages do not print) are refused. */
+  int32_t markov_head_rnn;
 } dspark_config;
 
 /* One checkpoint tensor (deepspec.ts, DeepspecDrafter constructor keys, e.g.

@@ -229,3 +229,19 @@ def test_confidence_head_guards(dsp):
     assert dsp._lib.dspark_draft_rows_conf(h, 1, kp, kp, one, anc, one, None, FAKE, None, FAKE, None, FAKE,
                                            FAKE * 16, ws, None) == 1
     dsp._lib.dspark_model_destroy(h)
+
+
+def test_rnn_head_guards(dsp):
+    base = synth.scaled(synth.TINY, markov_head_type="rnn")
+    table, n, keep = fake_table(dsp, base)
+    st, h = create(dsp, make_config(dsp, base, markov_head_vanilla=0, markov_head_rnn=1), table, n)
+    assert st == 0, dsp._lib.dspark_last_error()
+    dsp._lib.dspark_model_destroy(h)
+    # both head kinds at once, and a head that is neither (the gated one)
+    st, _ = create(dsp, make_config(dsp, base, markov_head_vanilla=1, markov_head_rnn=1), table, n)
+    assert st == 1
+    st, _ = create(dsp, make_config(dsp, base, markov_head_vanilla=0, markov_head_rnn=0), table, n)
+    assert st == 3
+    table, n, keep = fake_table(dsp, base, drop="markov_head.rnn_wh.weight")
+    st, _ = create(dsp, make_config(dsp, base, markov_head_vanilla=0, markov_head_rnn=1), table, n)
+    assert st == 2 and b"rnn_wh" in dsp._lib.dspark_last_error()
