@@ -235,8 +235,20 @@ class Shared:
         self.cfg = synth.scaled(synth.WORKLOADS["full_bf16_a1"].model, enable_confidence_head=True,
                                 confidence_head_with_markov=True, confidence_threshold=0.3)
         self.stored = synth.make_model(self.cfg, with_fc=True)
-        self.model = dsp.Model(self.cfg, dsp.upload(self.stored)).prepare()
+        # the RNN head's two extra tensors, for a second handle over the same
+        # uploaded weights
+        self.cfg_rnn = synth.scaled(self.cfg, markov_head_type="rnn")
+        for n in ("markov_head.rnn_wh.weight", "markov_head.rnn_bh.bias"):
+            self.stored[n] = synth.make_tensor(self.cfg_rnn, n)
+        self.weights = dsp.upload(self.stored)
+        self.model = dsp.Model(self.cfg, self.weights).prepare()
+        self._model_rnn = None
         self._om = None
+
+    def model_rnn(self):
+        if self._model_rnn is None:
+            self._model_rnn = self.dsp.Model(self.cfg_rnn, self.weights).prepare()
+        return self._model_rnn
 
     def oracle(self):
         if self._om is None:
@@ -442,8 +454,29 @@ def bench_conf(args, dsp, synth, torch, sh):
             "kernels": kernels}
 
 
+def bench_rnn(args, dsp, synth, torch, sh):
+    """The one-block round (512 context rows) with the RNN sequential head
+    instead of the vanilla one: the round alone, no context projection."""
+    w = synth.WORKLOADS["full_bf16_a1"]
+    model = sh.model_rnn()
+    L, A = w.fixed_ctx_len, w.rows
+    x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
+    ks, vs = dsp.project_context_kv(model, x, [0])
+    call = dsp.DraftCall(model, [[k[0]] for k in ks], [[v[0]] for v in vs], [L], synth.anchors(w), [L])
+    ms, prof, nprof = run_timed(call, args)
+    kernels = kernel_table(prof, nprof)
+    value = A * args.steps / (ms / 1e3)
+    return {"value": round(value, 2), "unit": "blocks/s", "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms / args.steps, 4),
+            "config": {"workload": "full_bf16_a1 round with the RNN sequential head (rank 64)",
+                       "rows": A, "gamma": sh.cfg.gamma, "ctx_len": L,
+                       "step": "one dspark_draft_rows call (no context projection)"},
+            "walk_us_per_step": round(kernels["markov_walk"]["us_per_step"], 2),
+            "kernels": kernels}
+
+
 BENCHES = {"full_bf16_a1": bench_full, "prefill_8192": bench_prefill, "rows_a32": bench_rows,
-           "rows_a32_vonly": bench_rows_vonly, "full_bf16_a1_conf": bench_conf}
+           "rows_a32_vonly": bench_rows_vonly, "full_bf16_a1_conf": bench_conf, "full_bf16_a1_rnn": bench_rnn}
 
 
 def main():
@@ -486,7 +519,7 @@ def main():
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.profile_steps = args.sub_steps, max(2, args.warmup // 4), min(args.profile_steps, 5)
     out["workloads"] = {}
-    for name in ("rows_a32", "prefill_8192", "rows_a32_vonly", "full_bf16_a1_conf"):
+    for name in ("rows_a32", "prefill_8192", "rows_a32_vonly", "full_bf16_a1_conf", "full_bf16_a1_rnn"):
         r = BENCHES[name](sub, dsp, synth, torch, sh)
         print(f"{name}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
         for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "dtype"):

@@ -400,9 +400,94 @@ def confident_prefix_length(conf: Sequence[float], thresholds) -> int:
     return g
 
 
+# ---------------------------------------------------------------------------
+# temperature > 0: sampling with per-row key streams
+# ---------------------------------------------------------------------------
+#
+# The mlx-bun 0.2.0 -> 0.4.0 drafter (forwardRows) samples each step's token
+# from processLogits(scores, sample) with the row's KeyStream(seed).next();
+# the pages do not print those helpers.  Reading: a token is a draw from
+# softmax(u / T) over the step's Markov-corrected scores u, and a row's key
+# stream is a counter-based generator keyed by the row's seed whose counter
+# advances with the step.  The draw is the Gumbel-max rule
+#     t_k = argmax_v (u_v + T g_v),   g_v = -log(-log U_v),
+# with U_v uniform from Philox4x64-10 (Salmon, Moraes, Dror, Shaw,
+# "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): key (seed, 0),
+# counter (v // 4, k, 0, 0), output word v mod 4, U = (top 24 bits + 1/2) / 2^24.
+
+M64 = (1 << 64) - 1
+PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
+PHILOX_W = (0x9E3779B97F4A7C15, 0xBB67AE8584CAA73B)
+
+
+def _mulhilo64(a: np.ndarray, b: int) -> Tuple[np.ndarray, np.ndarray]:
+    """(high, low) 64-bit halves of a * b for uint64 arrays a (schoolbook on
+    32-bit limbs; numpy uint64 arithmetic wraps mod 2^64)."""
+    m32 = np.uint64(0xFFFFFFFF)
+    s32 = np.uint64(32)
+    a0, a1 = a & m32, a >> s32
+    b0, b1 = np.uint64(b & 0xFFFFFFFF), np.uint64(b >> 32)
+    p00, p01, p10, p11 = a0 * b0, a0 * b1, a1 * b0, a1 * b1
+    mid = (p00 >> s32) + (p01 & m32) + (p10 & m32)
+    lo = (p00 & m32) | (mid << s32)
+    hi = p11 + (p01 >> s32) + (p10 >> s32) + (mid >> s32)
+    return hi, lo
+
+
+def philox4x64_10(counter: Sequence, key: Sequence) -> List[np.ndarray]:
+    """Philox4x64 with 10 rounds (the SC 2011 definition): counter words
+    (arrays or ints, uint64), key (k0, k1) -> four uint64 output words."""
+    with np.errstate(over="ignore"):
+        c = [np.asarray(x, dtype=np.uint64) for x in counter]
+        k0, k1 = int(key[0]) & M64, int(key[1]) & M64
+        for r in range(10):
+            if r:
+                k0 = (k0 + PHILOX_W[0]) & M64
+                k1 = (k1 + PHILOX_W[1]) & M64
+            hi0, lo0 = _mulhilo64(c[0], PHILOX_M[0])
+            hi1, lo1 = _mulhilo64(c[2], PHILOX_M[1])
+            c = [hi1 ^ c[1] ^ np.uint64(k0), lo1, hi0 ^ c[3] ^ np.uint64(k1), lo0]
+    return c
+
+
+def gumbel_noise(seed: int, step: int, V: int) -> np.ndarray:
+    """g_v = -log(-log U_v) for v < V at `step` of the key stream `seed`."""
+    b = np.arange((V + 3) // 4, dtype=np.uint64)
+    z = np.zeros_like(b)
+    words = philox4x64_10([b, np.full_like(b, step), z, z], (seed, 0))
+    x = np.stack(words, axis=1).reshape(-1)[:V]
+    u = ((x >> np.uint64(40)).astype(np.float64) + 0.5) * 2.0 ** -24
+    return -np.log(-np.log(u))
+
+
+def sampled_walk(m: OracleModel, z: np.ndarray, anchor: int, temperature: float, seed: int,
+                 tokens: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """The walk at temperature T > 0: t_k = argmax_v (u_v + T g_v) with u the
+    step's scores (base logits plus the head's bias, as in the greedy walk)
+    and g the step's Gumbel noise of the row's key stream.  tokens: drive the
+    previous tokens (teacher-forced check) instead of the walk's own."""
+    out, mgs = [], []
+    prev = anchor
+    s = np.zeros(m.cfg.markov_rank) if m.rnn else None
+    for k in range(z.shape[0]):
+        if m.rnn:
+            s = rnn_state(m, s, prev)
+            u = rnn_scores(m, z[k], s)
+        else:
+            u = step_scores(m, z[k], prev)
+        t, mg = top2(u + temperature * gumbel_noise(seed, k, z.shape[1]))
+        out.append(t)
+        mgs.append(mg)
+        prev = t if tokens is None else int(tokens[k])
+    return np.array(out, dtype=np.int64), np.array(mgs)
+
+
 def draft_rows(m: OracleModel, ctx_kv_rows: Sequence[Sequence[Tuple[np.ndarray, np.ndarray]]],
-               anchors: Sequence[int], positions: Sequence[int], thresholds=None) -> Dict[str, np.ndarray]:
+               anchors: Sequence[int], positions: Sequence[int], thresholds=None, temperature: float = 0.0,
+               seeds: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """deepspec.ts, draftRows.  ctx_kv_rows[a][l] = (K, V) [nKv, L_a, hd].
+    temperature > 0: each row samples with its key stream seeds[a] (default
+    0), see sampled_walk.
     Returns tokens [A, gamma], margins [A, gamma], logits z [A, gamma, V],
     hidden [A, gamma, H]; with a confidence head also conf [A, gamma] (the
     full block) and lengths [A] (the confident prefix under `thresholds`,
@@ -412,7 +497,10 @@ def draft_rows(m: OracleModel, ctx_kv_rows: Sequence[Sequence[Tuple[np.ndarray, 
     for a, anchor in enumerate(anchors):
         h = backbone_row(m, ctx_kv_rows[a], int(anchor), int(positions[a]))
         z = compute_logits(m, h)
-        t, mg = markov_walk(m, z, int(anchor))
+        if temperature > 0:
+            t, mg = sampled_walk(m, z, int(anchor), temperature, 0 if seeds is None else int(seeds[a]))
+        else:
+            t, mg = markov_walk(m, z, int(anchor))
         hid.append(h)
         zs.append(z)
         toks.append(t)
