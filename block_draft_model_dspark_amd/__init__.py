@@ -57,7 +57,7 @@ class DraftArgs(ctypes.Structure):
                 ("anchors_host", ctypes.c_void_p), ("positions_host", ctypes.c_void_p),
                 ("thresholds_host", ctypes.c_void_p), ("tokens_dev", ctypes.c_void_p),
                 ("logits_dev", ctypes.c_void_p), ("conf_dev", ctypes.c_void_p), ("lengths_dev", ctypes.c_void_p),
-                ("aux_dev", ctypes.c_void_p)]
+                ("aux_dev", ctypes.c_void_p), ("temperature", ctypes.c_float), ("seeds_host", ctypes.c_void_p)]
 
 
 class KernelTime(ctypes.Structure):
@@ -351,7 +351,8 @@ class DraftCallEx:
     def __init__(self, model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
                  positions: Sequence[int], ctx_pos0: Optional[Sequence[int]] = None,
                  thresholds: Optional[Sequence[float]] = None, collect_logits: bool = False,
-                 collect_conf: bool = False, lengths: bool = False):
+                 collect_conf: bool = False, lengths: bool = False, temperature: float = 0.0,
+                 seeds: Optional[Sequence[int]] = None):
         import torch
         cfg = model.cfg
         A = len(anchors)
@@ -384,6 +385,8 @@ class DraftCallEx:
         x.conf_dev = _ptr(self.out["conf"])
         x.lengths_dev = _ptr(self.out["lengths"])
         x.aux_dev = _ptr(model.aux)
+        x.temperature = float(temperature)
+        x.seeds_host = None if seeds is None else arr(ctypes.c_uint64, [int(v) for v in seeds])
         self.args = x
         self.nbytes = draft_workspace_bytes(model, A, max(ctx_lens), sum(ctx_lens))
         self.ws = torch.empty(self.nbytes, dtype=torch.uint8, device="cuda")
@@ -439,13 +442,15 @@ def draft_rows_conf(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], ancho
 def draft_rows_ex(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],
                   positions: Sequence[int], ctx_pos0: Optional[Sequence[int]] = None,
                   thresholds: Optional[Sequence[float]] = None, collect_logits: bool = False,
-                  collect_conf: bool = False, lengths: bool = False, stream=None):
+                  collect_conf: bool = False, lengths: bool = False, temperature: float = 0.0,
+                  seeds: Optional[Sequence[int]] = None, stream=None):
     """deepspec.ts, draftRows through dspark_draft_rows_ex.  k_rows None: a
     V-only context cache (v_rows[l][a] only; the attention rebuilds the keys
-    at positions ctx_pos0[a] + j).  Returns a dict of device tensors: tokens,
-    and logits / conf / lengths when asked for (None otherwise)."""
+    at positions ctx_pos0[a] + j).  temperature > 0 samples with the rows'
+    key streams (seeds).  Returns a dict of device tensors: tokens, and
+    logits / conf / lengths when asked for (None otherwise)."""
     return DraftCallEx(model, k_rows, v_rows, ctx_lens, anchors, positions, ctx_pos0, thresholds, collect_logits,
-                       collect_conf, lengths)(stream)
+                       collect_conf, lengths, temperature, seeds)(stream)
 
 
 def draft_rows_noalloc(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], anchors: Sequence[int],

@@ -826,12 +826,15 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
                               float* logits_dev, const void* aux_dev, void* ws_dev, size_t ws_bytes,
                               hipStream_t stream, bool use_scratch, const float* thresholds_host = nullptr,
                               float* conf_dev = nullptr, int32_t* lengths_dev = nullptr, bool allow_vonly = false,
-                              const int32_t* ctx_pos0_host = nullptr) {
+                              const int32_t* ctx_pos0_host = nullptr, float temperature = 0.f,
+                              const uint64_t* seeds_host = nullptr) {
   g_err.clear();
   const bool vonly = allow_vonly && !k_ctx_dev;  // a V-only context cache
   if (!m || (!k_ctx_dev && !vonly) || !v_ctx_dev || !ctx_len_host || !anchors_host || !positions_host ||
       !tokens_dev || (!ws_dev && !use_scratch))
     return fail(DSPARK_ERR_INVALID_ARG, "null argument");
+  if (!(temperature >= 0.f) || temperature > 1e30f)  // NaN or infinite
+    return fail(DSPARK_ERR_INVALID_ARG, "temperature must be finite and >= 0");
   const bool head = m->c.enable_confidence_head != 0;
   if (conf_dev && !head) return fail(DSPARK_ERR_INVALID_ARG, "confidence requested from a model without the head");
   const bool need_conf = head && (conf_dev || lengths_dev);
@@ -1139,6 +1142,8 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   w.wh = m->wh.w; w.whs = m->wh.s; w.whb = m->wh.b;
   w.bh = m->bh;
   w.act_bf16 = abf;
+  w.temperature = temperature;
+  for (int a = 0; a < A; ++a) w.seeds[a] = seeds_host ? seeds_host[a] : 0ull;
   w.tokens = tokens_dev;
   HIPCHECK(timed("markov_walk", stream, [&] { return launch_walk(w, stream); }));
 
@@ -1199,7 +1204,8 @@ dspark_status dspark_draft_rows_ex(const dspark_model* m, const dspark_draft_arg
   if (!x) return fail(DSPARK_ERR_INVALID_ARG, "null arguments");
   return draft_rows_impl(m, x->A, x->k_ctx_dev, x->v_ctx_dev, x->ctx_len_host, x->anchors_host, x->positions_host,
                          x->tokens_dev, x->logits_dev, x->aux_dev, ws_dev, ws_bytes, stream, false,
-                         x->thresholds_host, x->conf_dev, x->lengths_dev, true, x->ctx_pos0_host);
+                         x->thresholds_host, x->conf_dev, x->lengths_dev, true, x->ctx_pos0_host, x->temperature,
+                         x->seeds_host);
 }
 
 dspark_status dspark_draft_rows_noalloc(const dspark_model* m, int A, const void* const* k_ctx_dev,

@@ -244,6 +244,11 @@ struct WalkArgs {
   int rnn, act_bf16;
   const void* wh; const void* whs; const void* whb;  // [rank, rank], weight dtype
   const void* bh;                                      // [rank], act dtype
+  // temperature > 0: each step samples softmax(u / T) by the Gumbel-max rule
+  // with the row's Philox4x64-10 key stream (key (seed, 0), counter
+  // (entry / 4, step, 0, 0))
+  float temperature;
+  uint64_t seeds[MAX_ROWS];
   int32_t* tokens;
 };
 

@@ -238,6 +238,17 @@ typedef struct {
   float* conf_dev;                /* [A, gamma] or NULL */
   int32_t* lengths_dev;           /* [A] or NULL */
   const void* aux_dev;
+  /* Sampling (the mlx-bun 0.2.0 -> 0.4.0 drafter's temperature > 0 path with
+   * per-row key streams): temperature <= 0 is the greedy walk.  Otherwise
+   * step k of row a draws from softmax(u / temperature), u the step's scores
+   * (base logits plus the head's bias), by the Gumbel-max rule
+   * argmax_v (u_v + T g_v), g_v = -log(-log U_v), U_v from Philox4x64-10
+   * (Salmon et al., SC 2011) with key (seeds_host[a], 0) and counter
+   * (v / 4, k, 0, 0), word v mod 4, U = (top 23 bits + 1/2) / 2^23.
+   * seeds_host NULL: seed 0 for every row.  The confidence head, when asked
+   * for, scores the sampled tokens. */
+  float temperature;
+  const uint64_t* seeds_host;     /* [A] or NULL */
 } dspark_draft_args;
 dspark_status dspark_draft_rows_ex(const dspark_model* m, const dspark_draft_args* args, void* ws_dev,
                                    size_t ws_bytes, hipStream_t stream);

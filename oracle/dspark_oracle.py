@@ -413,7 +413,8 @@ def confident_prefix_length(conf: Sequence[float], thresholds) -> int:
 #     t_k = argmax_v (u_v + T g_v),   g_v = -log(-log U_v),
 # with U_v uniform from Philox4x64-10 (Salmon, Moraes, Dror, Shaw,
 # "Parallel Random Numbers: As Easy as 1, 2, 3", SC 2011): key (seed, 0),
-# counter (v // 4, k, 0, 0), output word v mod 4, U = (top 24 bits + 1/2) / 2^24.
+# counter (v // 4, k, 0, 0), output word v mod 4, U = (top 23 bits + 1/2) / 2^23
+# (exact in float32, so both sides draw the same uniforms).
 
 M64 = (1 << 64) - 1
 PHILOX_M = (0xD2E7470EE14C6C93, 0xCA5A826395121157)
@@ -456,7 +457,7 @@ def gumbel_noise(seed: int, step: int, V: int) -> np.ndarray:
     z = np.zeros_like(b)
     words = philox4x64_10([b, np.full_like(b, step), z, z], (seed, 0))
     x = np.stack(words, axis=1).reshape(-1)[:V]
-    u = ((x >> np.uint64(40)).astype(np.float64) + 0.5) * 2.0 ** -24
+    u = ((x >> np.uint64(41)).astype(np.float64) + 0.5) * 2.0 ** -23
     return -np.log(-np.log(u))
 
 
