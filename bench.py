@@ -475,8 +475,31 @@ def bench_rnn(args, dsp, synth, torch, sh):
             "kernels": kernels}
 
 
+def bench_sampled(args, dsp, synth, torch, sh):
+    """The one-block round (512 context rows) sampled at temperature 1 with a
+    per-row key stream instead of the greedy walk: the round alone."""
+    w = synth.WORKLOADS["full_bf16_a1"]
+    model = sh.model
+    L, A = w.fixed_ctx_len, w.rows
+    x = dsp.act_tensor(synth.ctx_hidden(w, 0, L))[None]
+    ks, vs = dsp.project_context_kv(model, x, [0])
+    call = dsp.DraftCallEx(model, [[k[0]] for k in ks], [[v[0]] for v in vs], [L], synth.anchors(w), [L],
+                           temperature=1.0, seeds=[7])
+    ms, prof, nprof = run_timed(call, args)
+    kernels = kernel_table(prof, nprof)
+    value = A * args.steps / (ms / 1e3)
+    return {"value": round(value, 2), "unit": "blocks/s", "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms / args.steps, 4),
+            "config": {"workload": "full_bf16_a1 round sampled at temperature 1.0 (Gumbel-max, Philox4x64-10 "
+                                   "key stream of seed 7)", "rows": A, "gamma": sh.cfg.gamma, "ctx_len": L,
+                       "step": "one dspark_draft_rows_ex call (no context projection)"},
+            "walk_us_per_step": round(kernels["markov_walk"]["us_per_step"], 2),
+            "kernels": kernels}
+
+
 BENCHES = {"full_bf16_a1": bench_full, "prefill_8192": bench_prefill, "rows_a32": bench_rows,
-           "rows_a32_vonly": bench_rows_vonly, "full_bf16_a1_conf": bench_conf, "full_bf16_a1_rnn": bench_rnn}
+           "rows_a32_vonly": bench_rows_vonly, "full_bf16_a1_conf": bench_conf, "full_bf16_a1_rnn": bench_rnn,
+           "full_bf16_a1_sampled": bench_sampled}
 
 
 def main():
@@ -519,7 +542,8 @@ def main():
     sub = argparse.Namespace(**vars(args))
     sub.steps, sub.warmup, sub.profile_steps = args.sub_steps, max(2, args.warmup // 4), min(args.profile_steps, 5)
     out["workloads"] = {}
-    for name in ("rows_a32", "prefill_8192", "rows_a32_vonly", "full_bf16_a1_conf", "full_bf16_a1_rnn"):
+    for name in ("rows_a32", "prefill_8192", "rows_a32_vonly", "full_bf16_a1_conf", "full_bf16_a1_rnn",
+                 "full_bf16_a1_sampled"):
         r = BENCHES[name](sub, dsp, synth, torch, sh)
         print(f"{name}: {r['value']} {r['unit']}", file=sys.stderr, flush=True)
         for k in ("metric", "n_gpus", "higher_is_better", "scaling", "data", "dtype"):

@@ -270,6 +270,7 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.aux = e.aux;
     t.lohi = e.lohi;
     t.NC = e.NC;
+    t.smp = e.smp;
     return launch_tall(t, p.tall, p.np, p.S, st);
   }
   // gate|up: gelu_tanh(gate) * up in the tiled kernel itself when its
@@ -864,7 +865,9 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   }
   if (vonly && c.act_dtype != DSPARK_BF16)
     return fail(DSPARK_ERR_UNSUPPORTED, "a V-only context cache is built for bf16 caches");
-  const DraftLayout d = draft_layout(m, A, logits_dev == nullptr, total_keys - (int64_t)A * G);
+  // sampling keeps the noisy scores in the workspace's logits buffer
+  const bool sampled = temperature > 0.f;
+  const DraftLayout d = draft_layout(m, A, logits_dev == nullptr || sampled, total_keys - (int64_t)A * G);
   if (use_scratch) {
     if (d.total > NOALLOC_SCRATCH_BYTES)
       return fail(DSPARK_ERR_WORKSPACE,
@@ -1124,6 +1127,12 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   e.aux = c.markov_rank > 0 ? (const float*)aux_dev : nullptr;
   e.lohi = (float2*)(ws + d.lohi);
   e.NC = NC;
+  if (sampled) {
+    e.smp.temperature = temperature;
+    e.smp.gamma = G;
+    e.smp.zs = (float*)(ws + d.z);
+    for (int a = 0; a < A; ++a) e.smp.seeds[a] = seeds_host ? seeds_host[a] : 0ull;
+  }
   HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream, tb); }));
 
   WalkArgs w{};
@@ -1133,7 +1142,7 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   w.rank = c.markov_rank;
   w.wkind = m->w1.kind;
   w.group = c.group_size;
-  w.z = z;
+  w.z = sampled ? e.smp.zs : z;  // the walk draws from the noisy scores when sampling
   w.lohi = e.lohi;
   w.aux = e.aux;
   w.w1 = m->w1.w; w.w1s = m->w1.s; w.w1b = m->w1.b;
@@ -1142,8 +1151,6 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   w.wh = m->wh.w; w.whs = m->wh.s; w.whb = m->wh.b;
   w.bh = m->bh;
   w.act_bf16 = abf;
-  w.temperature = temperature;
-  for (int a = 0; a < A; ++a) w.seeds[a] = seeds_host ? seeds_host[a] : 0ull;
   w.tokens = tokens_dev;
   HIPCHECK(timed("markov_walk", stream, [&] { return launch_walk(w, stream); }));
 

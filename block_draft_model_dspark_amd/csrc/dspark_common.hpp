@@ -226,6 +226,40 @@ __device__ __forceinline__ float walk_bound(const float* aux, int64_t v, int V) 
   return aux[v] * aux[V] * (1.f + 1e-5f);
 }
 
+// Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011): four 64-bit words of counter c
+// under key (k0, k1)
+__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
+  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += W0;
+      k1 += W1;
+    }
+    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
+    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
+    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
+    c[0] = n0;
+    c[1] = lo1;
+    c[2] = n2;
+    c[3] = lo0;
+  }
+}
+// The Gumbel noise of vocabulary entry v at block slot `step` of the key
+// stream `seed`: g = -log(-log U), U = (top 23 bits + 1/2) / 2^23 (exact in
+// float32) of word v mod 4 of Philox4x64-10 at key (seed, 0), counter
+// (v / 4, step, 0, 0)
+__device__ __forceinline__ float gumbel_noise(uint64_t seed, int step, int v) {
+  uint64_t c[4] = {(uint64_t)(v >> 2), (uint64_t)step, 0ull, 0ull};
+  philox4x64_10(c, seed, 0ull);
+  const int j = v & 3;
+  const uint64_t x = j == 0 ? c[0] : (j == 1 ? c[1] : (j == 2 ? c[2] : c[3]));
+  const float u = ((float)(uint32_t)(x >> 41) + 0.5f) * 1.1920928955078125e-07f;  // 2^-23
+  return -logf(-logf(u));
+}
+
 // gelu_pytorch_tanh in fp32
 __device__ __forceinline__ float gelu_tanh(float x) {
   const float k0 = 0.7978845608028654f;  // sqrt(2/pi)

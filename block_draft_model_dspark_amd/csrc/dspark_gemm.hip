@@ -287,7 +287,18 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
       const int r = t * 16 + 4 * gq + i, m = mbase + r;
       float z = acc[t][i];
       if (e.cap > 0.f) z = e.cap * tanhf(z / e.cap);
-      if (m < g.M) e.Y[(int64_t)m * V + n] = z;
+      if (e.smp.temperature > 0.f) {
+        // sampling: the walk and its bounds see z + T g (base z to the logits)
+        const int mr = min(m, g.M - 1), row = mr / e.smp.gamma;
+        const float zs = z + e.smp.temperature * gumbel_noise(e.smp.seeds[row], mr - row * e.smp.gamma, n);
+        if (m < g.M) {
+          if (e.smp.zs != e.Y) e.Y[(int64_t)m * V + n] = z;
+          e.smp.zs[(int64_t)m * V + n] = zs;
+        }
+        z = zs;
+      } else if (m < g.M) {
+        e.Y[(int64_t)m * V + n] = z;
+      }
       // per 16-column tile: max over the tile's columns of z - b and z + b
       const float lo = row16_max(z - b), hi = row16_max(z + b);
       if ((lane & 15) == 0) {

@@ -65,6 +65,17 @@ struct RopeCfg {
   int hd, nrot;       // rotated pairs: k < nrot turn, the rest pass through
 };
 
+// Sampling at temperature > 0 (see dspark.h, dspark_draft_args): the
+// logits epilogue also writes zs = z + T g, g the Gumbel noise of row
+// m / gamma's key stream at slot m mod gamma, and forms the walk's chunk
+// bounds on zs, so the greedy walk over zs draws from softmax(u / T)
+struct SampleArgs {
+  float temperature;  // <= 0: no sampling
+  int gamma;
+  float* zs;          // [M, V]; may equal the logits buffer (then only zs is stored)
+  uint64_t seeds[MAX_ROWS];
+};
+
 struct EpiArgs {
   float* Y;           // [M, N] fp32 result (EPI_Y, EPI_SUMS, EPI_LM, EPI_KV)
   unsigned* cnt;      // reduction counters, zero on entry, left zero
@@ -99,6 +110,7 @@ struct EpiArgs {
   const float* aux;   // [V] markov_w2 row norms, aux[V] = max markov_w1 row norm; null when rank 0
   float2* lohi;       // [M, NC] (max z - B, max z + B) per chunk
   int NC;
+  SampleArgs smp;
 };
 
 // tiled GEMM over many rows (dspark_tall.hip): T[m, n] = sum over the np
@@ -132,6 +144,7 @@ struct TallArgs {
   // stride act_plane) that a tiled down projection reads, instead of fp32
   uint16_t* act_planes;
   int64_t act_plane;
+  SampleArgs smp;     // lm: sampling noise (see SampleArgs)
 };
 
 // Tile order of the tiled GEMM: workgroups go round-robin over the 8 XCDs
@@ -244,11 +257,6 @@ struct WalkArgs {
   int rnn, act_bf16;
   const void* wh; const void* whs; const void* whb;  // [rank, rank], weight dtype
   const void* bh;                                      // [rank], act dtype
-  // temperature > 0: each step samples softmax(u / T) by the Gumbel-max rule
-  // with the row's Philox4x64-10 key stream (key (seed, 0), counter
-  // (entry / 4, step, 0, 0))
-  float temperature;
-  uint64_t seeds[MAX_ROWS];
   int32_t* tokens;
 };
 

@@ -422,108 +422,6 @@ __device__ void walk_per_step(const WalkArgs& a, int row) {
   }
 }
 
-// Philox4x64 with 10 rounds (Salmon, Moraes, Dror, Shaw, "Parallel Random
-// Numbers: As Easy as 1, 2, 3", SC 2011): four 64-bit words of counter c
-// under key (k0, k1)
-__device__ __forceinline__ void philox4x64_10(uint64_t c[4], uint64_t k0, uint64_t k1) {
-  constexpr uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
-  constexpr uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
-#pragma unroll
-  for (int r = 0; r < 10; ++r) {
-    if (r) {
-      k0 += W0;
-      k1 += W1;
-    }
-    const uint64_t hi0 = __umul64hi(M0, c[0]), lo0 = M0 * c[0];
-    const uint64_t hi1 = __umul64hi(M1, c[2]), lo1 = M1 * c[2];
-    const uint64_t n0 = hi1 ^ c[1] ^ k0, n2 = hi0 ^ c[3] ^ k1;
-    c[0] = n0;
-    c[1] = lo1;
-    c[2] = n2;
-    c[3] = lo0;
-  }
-}
-// Gumbel noise -log(-log U) of a 64-bit word: U = (top 23 bits + 1/2) / 2^23,
-// exact in float32
-__device__ __forceinline__ float gumbel_of(uint64_t x) {
-  const float u = ((float)(uint32_t)(x >> 41) + 0.5f) * 1.1920928955078125e-07f;  // 2^-23
-  return -logf(-logf(u));
-}
-
-// Sampling at temperature T > 0 (the per-row key streams of the drafter's
-// forwardRows): t_k = argmax_v (u_v + T g_v), u the step's scores (logits
-// plus the head's bias), g the row's Gumbel noise of step k.  Two passes
-// over the vocabulary per step: the threshold max_v (z_v - B_v + T g_v)
-// (B the walk bound), then the exact scores of the entries that reach it.
-__device__ void walk_sampled(const WalkArgs& a, int row) {
-  __shared__ float redu[WALK_NT / 64];
-  __shared__ int redi[WALK_NT / 64];
-  __shared__ float e[256];
-  __shared__ float st[256];  // RNN head: s_{k-1}
-  __shared__ int prev_s;
-  const int tid = threadIdx.x, G = a.rows.gamma;
-  const float T = a.temperature;
-  const uint64_t seed = a.seeds[row];
-  const int nb = (a.V + 3) >> 2;
-  if (tid == 0) prev_s = a.rows.anchor[row];
-  if (a.rnn)
-    for (int j = tid; j < a.rank; j += WALK_NT) st[j] = 0.f;
-  __syncthreads();
-  for (int k = 0; k < G; ++k) {
-    const int64_t m = (int64_t)row * G + k;
-    const int prev = prev_s;
-    if (a.rnn) {
-      for (int j = tid; j < a.rank; j += WALK_NT) {
-        float acc = ld_act(a.bh, j, a.act_bf16) + head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
-        for (int i = 0; i < a.rank; ++i) acc += st[i] * head_elem(a.wh, a.whs, a.whb, a.wkind, a.group, i, a.rank, j);
-        e[j] = tanhf(acc);
-      }
-      __syncthreads();
-      for (int j = tid; j < a.rank; j += WALK_NT) st[j] = e[j];
-    } else if (a.rank > 0) {
-      for (int j = tid; j < a.rank; j += WALK_NT) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
-    }
-    __syncthreads();
-    float lm = -INFINITY;
-    for (int b = tid; b < nb; b += WALK_NT) {
-      uint64_t c[4] = {(uint64_t)b, (uint64_t)k, 0ull, 0ull};
-      philox4x64_10(c, seed, 0ull);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = 4 * b + j;
-        if (v < a.V) lm = fmaxf(lm, a.z[m * a.V + v] - (a.aux ? walk_bound(a.aux, v, a.V) : 0.f) + T * gumbel_of(c[j]));
-      }
-    }
-    lm = block_max(lm, redu);
-    const float thr = lm - 1e-4f * (1.f + fabsf(lm));
-    float bu = -INFINITY;
-    int bi = 0x7fffffff;
-    for (int b = tid; b < nb; b += WALK_NT) {
-      uint64_t c[4] = {(uint64_t)b, (uint64_t)k, 0ull, 0ull};
-      philox4x64_10(c, seed, 0ull);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int v = 4 * b + j;
-        if (v >= a.V) continue;
-        const float zg = a.z[m * a.V + v] + T * gumbel_of(c[j]);
-        if (!(zg + (a.aux ? walk_bound(a.aux, v, a.V) : 0.f) >= thr)) continue;
-        const float u = a.rank > 0 ? zg + w2_dot(a, v, e) : zg;
-        if (better(u, v, bu, bi)) {
-          bu = u;
-          bi = v;
-        }
-      }
-    }
-    block_argmax(bu, bi, redu, redi);
-    if (tid == 0) {
-      const bool ok = bi >= 0 && bi < a.V;
-      a.tokens[m] = ok ? bi : -1;
-      prev_s = ok ? bi : 0;
-    }
-    __syncthreads();
-  }
-}
-
 __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
   __shared__ int cand[WALK_GMAX][WALK_CMAX];
   __shared__ float candz[WALK_GMAX][WALK_CMAX];  // the candidates' logits
@@ -536,10 +434,6 @@ __global__ __launch_bounds__(WALK_NT) void k_walk(const WalkArgs a) {
   __shared__ int nflag, slow;
   const int row = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma;
   const int NC = a.NC;
-  if (a.temperature > 0.f) {
-    walk_sampled(a, row);
-    return;
-  }
   if (a.rnn) {
     // the RNN head's bias depends on the whole prefix, not only on the
     // previous token: no per-(step, previous candidate) table

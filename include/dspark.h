@@ -245,8 +245,9 @@ typedef struct {
    * argmax_v (u_v + T g_v), g_v = -log(-log U_v), U_v from Philox4x64-10
    * (Salmon et al., SC 2011) with key (seeds_host[a], 0) and counter
    * (v / 4, k, 0, 0), word v mod 4, U = (top 23 bits + 1/2) / 2^23.
-   * seeds_host NULL: seed 0 for every row.  The confidence head, when asked
-   * for, scores the sampled tokens. */
+   * seeds_host NULL: seed 0 for every row.  logits_dev receives the base
+   * logits, without the noise.  The confidence head, when asked for, scores
+   * the sampled tokens. */
   float temperature;
   const uint64_t* seeds_host;     /* [A] or NULL */
 } dspark_draft_args;
