@@ -364,59 +364,124 @@ __device__ __forceinline__ float w1w2_dot_part(const WalkArgs& a, int64_t prev, 
   return dot;
 }
 
-// the per-step path: every entry of a passing chunk is scored against the
-// actual previous token (vanilla head: e = markov_w1[prev]) or the state
-// that the previous tokens drove (RNN head: e = s_k)
+// The per-step path: each step scores every entry that can still win against
+// the actual previous token (vanilla head: e = markov_w1[prev]) or the state
+// the previous tokens drove (RNN head: e = s_k).  With n = ||e|| the bias of
+// entry v is at most n ||markov_w2[v]|| = t B_v, t = n / (the model-wide
+// bound of ||e|| that B uses) <= 1, and over a chunk
+// z_v + t B_v <= ((1 + t) hi + (1 - t) lo) / 2 by the epilogue's statistics.
+// The exact best score of the chunk with the largest such bound is a
+// threshold; the chunks whose bound reaches it are scored one wave per
+// chunk, one lane per entry.
 __device__ void walk_per_step(const WalkArgs& a, int row) {
   __shared__ float redu[WALK_NT / 64];
   __shared__ int redi[WALK_NT / 64];
   __shared__ float e[256];
-  __shared__ float st[256];  // RNN head: s_{k-1}
-  __shared__ int prev_s;
-  const int tid = threadIdx.x, G = a.rows.gamma;
+  __shared__ float st[256];         // RNN head: s_{k-1}
+  __shared__ float part[WALK_NT];   // RNN head: partial sums of s_{k-1} wh
+  __shared__ int clist[WALK_NT];    // chunks to score
+  __shared__ int ncl, prev_s;
+  __shared__ float thr_s;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, G = a.rows.gamma, r = a.rank, NC = a.NC;
+  const bool rnn = a.rnn && r > 0;
   if (tid == 0) prev_s = a.rows.anchor[row];
-  if (a.rnn)
-    for (int j = tid; j < a.rank; j += WALK_NT) st[j] = 0.f;
+  if (rnn)
+    for (int j = tid; j < r; j += WALK_NT) st[j] = 0.f;
   __syncthreads();
+  const float nb = a.aux ? a.aux[a.V] : 0.f;
   for (int k = 0; k < G; ++k) {
     const int64_t m = (int64_t)row * G + k;
-    const float2* lh = a.lohi + m * a.NC;
-    float lm = -INFINITY;
-    for (int c = tid; c < a.NC; c += WALK_NT) lm = fmaxf(lm, lh[c].x);
-    lm = block_max(lm, redu);
-    const float thr = lm - 1e-4f * (1.f + fabsf(lm));
+    const float2* lh = a.lohi + m * NC;
     const int prev = prev_s;
-    if (a.rnn) {
-      // s_k = tanh(s_{k-1} wh + w1[prev] + bh): entry j is column j of s wh
-      for (int j = tid; j < a.rank; j += WALK_NT) {
-        float acc = ld_act(a.bh, j, a.act_bf16) + head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
-        for (int i = 0; i < a.rank; ++i) acc += st[i] * head_elem(a.wh, a.whs, a.whb, a.wkind, a.group, i, a.rank, j);
-        e[j] = tanhf(acc);
+    if (rnn) {
+      // s_k = tanh(s_{k-1} wh + w1[prev] + bh): entry j is column j of s wh,
+      // its sum split over P groups of rows
+      const int P = min(WALK_NT / r, r), j = tid % r, p = tid / r;
+      if (p < P) {
+        float acc = 0.f;
+        for (int i = p; i < r; i += P) acc += st[i] * head_elem(a.wh, a.whs, a.whb, a.wkind, a.group, i, r, j);
+        part[p * r + j] = acc;
       }
       __syncthreads();
-      for (int j = tid; j < a.rank; j += WALK_NT) st[j] = e[j];
-    } else if (a.rank > 0) {
-      for (int j = tid; j < a.rank; j += WALK_NT) e[j] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, a.rank, j);
+      if (tid < r) {
+        float acc = ld_act(a.bh, tid, a.act_bf16) + head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, r, tid);
+        for (int q = 0; q < P; ++q) acc += part[q * r + tid];
+        const float s = tanhf(acc);
+        e[tid] = s;
+        st[tid] = s;
+      }
+    } else if (tid < r) {
+      e[tid] = head_elem(a.w1, a.w1s, a.w1b, a.wkind, a.group, prev, r, tid);
     }
-    __syncthreads();
+    // t from ||e|| (a relative margin for its rounding; t <= 1 always holds
+    // mathematically, the clamp only absorbs that margin)
+    const float n2 = block_sum(tid < r ? e[tid] * e[tid] : 0.f, redu);
+    const float t = nb > 0.f ? fminf(1.f, sqrtf(n2) * (1.f + 1e-4f) / nb) : 0.f;
+    const float wt = 0.5f * (1.f + t), wl = 0.5f * (1.f - t);
+    // seed chunk: the largest bound
     float bu = -INFINITY;
     int bi = 0x7fffffff;
-    for (int c = tid; c < a.NC; c += WALK_NT) {
-      if (!(lh[c].y >= thr)) continue;
-      for (int v = c * WALK_CHUNK; v < min(c * WALK_CHUNK + WALK_CHUNK, a.V); ++v) {
-        const float zv = a.z[m * a.V + v];
-        if (!(zv + (a.aux ? walk_bound(a.aux, v, a.V) : 0.f) >= thr)) continue;
-        float u = zv;
-        if (a.rank > 0) u += w2_dot(a, v, e);
-        if (better(u, v, bu, bi)) { bu = u; bi = v; }
+    for (int c = tid; c < NC; c += WALK_NT) {
+      const float2 q = lh[c];
+      const float ub = wt * q.y + wl * q.x;
+      if (better(ub, c, bu, bi)) {
+        bu = ub;
+        bi = c;
       }
     }
     block_argmax(bu, bi, redu, redi);
+    if (wave == 0) {
+      const int v = (bi >= 0 && bi < NC ? bi : 0) * WALK_CHUNK + lane;
+      float u = -INFINITY;
+      if (v < a.V) {
+        u = a.z[m * a.V + v];
+        if (r > 0) u += w2_dot(a, v, e);
+      }
+      u = wave_max(u);
+      if (lane == 0) {
+        float th = u - 1e-4f * (1.f + fabsf(u));
+        if (!(th > -INFINITY)) th = -INFINITY;  // non-finite seed scores: keep every finite entry
+        thr_s = th;
+        ncl = 0;
+      }
+    }
+    __syncthreads();
+    const float thr = thr_s;
+    float wu = -INFINITY;
+    int wi = 0x7fffffff;
+    for (int c0 = 0; c0 < NC; c0 += WALK_NT) {
+      const int c = c0 + tid;
+      if (c < NC) {
+        const float2 q = lh[c];
+        if (wt * q.y + wl * q.x >= thr) clist[atomicAdd(&ncl, 1)] = c;
+      }
+      __syncthreads();
+      const int nl = ncl;
+      for (int l = wave; l < nl; l += WALK_NT / 64) {
+        const int v = clist[l] * WALK_CHUNK + lane;
+        if (v < a.V) {
+          const float zv = a.z[m * a.V + v];
+          if (zv + t * (a.aux ? walk_bound(a.aux, v, a.V) : 0.f) >= thr) {
+            const float u = r > 0 ? zv + w2_dot(a, v, e) : zv;
+            if (better(u, v, wu, wi)) {
+              wu = u;
+              wi = v;
+            }
+          }
+        }
+      }
+      if (c0 + WALK_NT < NC) {
+        __syncthreads();
+        if (tid == 0) ncl = 0;
+        __syncthreads();
+      }
+    }
+    block_argmax(wu, wi, redu, redi);
     if (tid == 0) {
       // no finite candidate (non-finite logits): report -1 and keep a valid row index
-      const bool ok = bi >= 0 && bi < a.V;
-      a.tokens[m] = ok ? bi : -1;
-      prev_s = ok ? bi : 0;
+      const bool ok = wi >= 0 && wi < a.V;
+      a.tokens[m] = ok ? wi : -1;
+      prev_s = ok ? wi : 0;
     }
     __syncthreads();
   }
