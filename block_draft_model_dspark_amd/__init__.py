@@ -26,6 +26,7 @@ EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tal
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
             "dspark_tall_tile_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
+            "dspark_q4_address_check",
             "dspark_draft_rows_conf", "dspark_draft_rows_ex",
             "dspark_last_error")
 
@@ -116,6 +117,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_tall_tile_of.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int)]
     lib.dspark_tall_tile_of.restype = ctypes.c_int
+    lib.dspark_q4_address_check.argtypes = [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
+                                            I64, ctypes.c_int, ctypes.POINTER(I64)]
+    lib.dspark_q4_address_check.restype = ctypes.c_int
     lib.dspark_last_error.argtypes = []
     lib.dspark_last_error.restype = ctypes.c_char_p
     for fn in ("dspark_model_create", "dspark_model_set_tall_rows", "dspark_model_prepare",
@@ -187,6 +191,38 @@ def act_tensor(st, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(st.data).view(np.int16)).to(device).view(torch.bfloat16)
 
 
+def make_config(cfg, with_fc: bool) -> Config:
+    """The library's config struct for a model config (fc / hidden_norm present
+    or not)."""
+    c = Config()
+    c.hidden_size = cfg.hidden_size
+    c.num_hidden_layers = cfg.num_hidden_layers
+    c.num_attention_heads = cfg.num_attention_heads
+    c.global_head_dim = cfg.global_head_dim
+    c.num_global_key_value_heads = cfg.num_global_key_value_heads
+    c.intermediate_size = cfg.intermediate_size
+    c.vocab_size = cfg.vocab_size
+    c.block_size = cfg.block_size
+    c.mask_token_id = cfg.mask_token_id
+    c.markov_rank = cfg.markov_rank
+    c.attention_k_eq_v = int(getattr(cfg, "attention_k_eq_v", True))
+    c.markov_head_vanilla = int(getattr(cfg, "markov_head_type", "vanilla") == "vanilla")
+    c.activation_gelu_tanh = int(getattr(cfg, "hidden_activation", "gelu_pytorch_tanh") == "gelu_pytorch_tanh")
+    c.fc_in = cfg.num_taps * cfg.target_hidden_size if with_fc else 0
+    c.rope_theta = cfg.rope_theta
+    c.partial_rotary_factor = cfg.partial_rotary_factor
+    c.rms_norm_eps = cfg.rms_norm_eps
+    c.final_logit_softcapping = cfg.final_logit_softcapping or 0.0
+    c.weight_dtype = _KIND[cfg.weight_dtype]
+    c.act_dtype = _KIND[cfg.act_dtype]
+    c.group_size = cfg.group_size
+    c.enable_confidence_head = int(bool(getattr(cfg, "enable_confidence_head", False)))
+    c.confidence_head_with_markov = int(bool(getattr(cfg, "confidence_head_with_markov", False)))
+    c.confidence_threshold = float(getattr(cfg, "confidence_threshold", 0.0) or 0.0)
+    c.markov_head_rnn = int(getattr(cfg, "markov_head_type", "vanilla") == "rnn")
+    return c
+
+
 class Model:
     """A drafter whose weights live in device tensors owned by this object."""
 
@@ -194,32 +230,7 @@ class Model:
         lib = load_library()
         self.cfg = cfg
         self.weights = weights  # keeps the device tensors alive
-        c = Config()
-        c.hidden_size = cfg.hidden_size
-        c.num_hidden_layers = cfg.num_hidden_layers
-        c.num_attention_heads = cfg.num_attention_heads
-        c.global_head_dim = cfg.global_head_dim
-        c.num_global_key_value_heads = cfg.num_global_key_value_heads
-        c.intermediate_size = cfg.intermediate_size
-        c.vocab_size = cfg.vocab_size
-        c.block_size = cfg.block_size
-        c.mask_token_id = cfg.mask_token_id
-        c.markov_rank = cfg.markov_rank
-        c.attention_k_eq_v = int(getattr(cfg, "attention_k_eq_v", True))
-        c.markov_head_vanilla = int(getattr(cfg, "markov_head_type", "vanilla") == "vanilla")
-        c.activation_gelu_tanh = int(getattr(cfg, "hidden_activation", "gelu_pytorch_tanh") == "gelu_pytorch_tanh")
-        c.fc_in = cfg.num_taps * cfg.target_hidden_size if "fc.weight" in weights else 0
-        c.rope_theta = cfg.rope_theta
-        c.partial_rotary_factor = cfg.partial_rotary_factor
-        c.rms_norm_eps = cfg.rms_norm_eps
-        c.final_logit_softcapping = cfg.final_logit_softcapping or 0.0
-        c.weight_dtype = _KIND[cfg.weight_dtype]
-        c.act_dtype = _KIND[cfg.act_dtype]
-        c.group_size = cfg.group_size
-        c.enable_confidence_head = int(bool(getattr(cfg, "enable_confidence_head", False)))
-        c.confidence_head_with_markov = int(bool(getattr(cfg, "confidence_head_with_markov", False)))
-        c.confidence_threshold = float(getattr(cfg, "confidence_threshold", 0.0) or 0.0)
-        c.markov_head_rnn = int(getattr(cfg, "markov_head_type", "vanilla") == "rnn")
+        c = make_config(cfg, "fc.weight" in weights)
         self._c = c
         names = list(weights)
         self._names = [n.encode() for n in names]
@@ -470,6 +481,19 @@ def draft_rows_noalloc(model: Model, k_rows, v_rows, ctx_lens: Sequence[int], an
     _check(_lib.dspark_draft_rows_noalloc(model.handle, A, kp, vp, lens, anc, pos, tokens.data_ptr(), _ptr(logits),
                                           _ptr(model.aux), _stream_handle(stream)))
     return tokens, logits
+
+
+def q4_address_check(cfg, A: int, anchors: Sequence[int], ctx_rows: int, input_kind: int = INPUT_CONTEXT_HIDDEN,
+                     with_fc: bool = False) -> int:
+    """Host replay of every 4-bit address a round and projection of these
+    sizes form (dspark_q4_address_check); returns the number checked and
+    raises DsparkError naming the first address out of range."""
+    lib = load_library()
+    c = make_config(cfg, with_fc)
+    an = (ctypes.c_int32 * A)(*anchors)
+    n = ctypes.c_int64()
+    _check(lib.dspark_q4_address_check(ctypes.byref(c), A, an, ctx_rows, input_kind, ctypes.byref(n)))
+    return n.value
 
 
 def draft_noalloc_max_bytes() -> int:

@@ -459,7 +459,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
 }
 
 // ---- model creation --------------------------------------------------------
-dspark_status check_config(const dspark_config& c) {
+dspark_status check_shapes(const dspark_config& c) {
   if (!c.attention_k_eq_v)
     return fail(DSPARK_ERR_UNSUPPORTED, "attention_k_eq_v=false needs a v_proj path; only V == K is implemented");
   if (c.markov_rank > 0 && !c.markov_head_vanilla && !c.markov_head_rnn)
@@ -504,10 +504,17 @@ dspark_status check_config(const dspark_config& c) {
   if (c.weight_dtype == DSPARK_Q4) {
     if (c.group_size != 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 group size %d not built (64)", c.group_size);
     if (c.markov_rank % 64) return fail(DSPARK_ERR_UNSUPPORTED, "Q4 Markov tables need rank %% 64 == 0");
-    // The first GPU run of a 4-bit round faulted and no cause has been shown
-    // yet; the path stays switched off until one is.
-    return fail(DSPARK_ERR_UNSUPPORTED, "4-bit weights are disabled in this build (GPU fault under analysis)");
   }
+  return DSPARK_OK;
+}
+
+dspark_status check_config(const dspark_config& c) {
+  const dspark_status st = check_shapes(c);
+  if (st) return st;
+  // The first GPU run of a 4-bit round faulted and no cause has been shown
+  // yet; the path stays switched off until one is.
+  if (c.weight_dtype == DSPARK_Q4)
+    return fail(DSPARK_ERR_UNSUPPORTED, "4-bit weights are disabled in this build (GPU fault under analysis)");
   return DSPARK_OK;
 }
 
@@ -552,6 +559,218 @@ dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by) {
     return fail(DSPARK_ERR_INVALID_ARG, "grid %d x %d, workgroup %d", gx, gy, w);
   tall_tile_of(gx, gy, w, *bx, *by);
   return DSPARK_OK;
+}
+
+// ---- host replay of the 4-bit weight addresses ------------------------------
+// Every address that the 4-bit branches of the kernels form, evaluated on the
+// host with the kernels' own index functions (q4_word, q4_group,
+// q4_gemm_word, q4_gemm_group, wave_col, xsum_offset, xbuf_bytes) over the
+// launch plans the library makes, each checked against the buffer it reads.
+extern "C++" {
+namespace {
+struct Q4Replay {
+  int64_t n = 0;
+  dspark_status st = DSPARK_OK;
+};
+
+// k_gemm's weight loads and per-group activation sums: the only GEMM variant
+// built for 4-bit weights is the streaming one with one 16-row tile and four
+// waves per workgroup, sub-slices of kc (KCMAX 256, SMAX = 8 steps of 32)
+template <int EPI>
+void q4_replay_gemm(Q4Replay& r, const char* role, const GemmPlan& p, int N, int K, int hd, int nseg,
+                    const int64_t* seg_rows, const int* seg_n0) {
+  if (r.st) return;
+  constexpr int KCMAX = 256, SMAX = KCMAX / 32;
+  if (p.tall != TALL_NONE || p.mt != 1 || p.kc > KCMAX || p.kc % 64 || p.kslice % 64 || K % 64 || N % 64) {
+    r.st = fail(DSPARK_ERR_SHAPE, "%s: plan tall %d mt %d kc %d kslice %d K %d N %d outside the 4-bit GEMM's domain",
+                role, p.tall, p.mt, p.kc, p.kslice, K, N);
+    return;
+  }
+  const int KC = p.kc, ngmax = KC >> 6;
+  // the sums sit after the activation planes and inside one staging buffer;
+  // a 16-row tile double-buffers within the launch's dynamic LDS
+  if (xsum_offset(p.xmode, 1, KC) + (size_t)16 * ngmax * 4 > xbuf_bytes(WK_Q4, p.xmode, 1, KC) ||
+      2 * xbuf_bytes(WK_Q4, p.xmode, 1, KC) > gemm_lds_bytes(WK_Q4, p.xmode, 1, KC) ||
+      gemm_lds_bytes(WK_Q4, p.xmode, 1, KC) > 65536) {
+    r.st = fail(DSPARK_ERR_SHAPE, "%s: 4-bit staging buffers exceed the launch's LDS", role);
+    return;
+  }
+  // how often each word and each scale of every segment is read by one row
+  // block of the grid: every word once, every scale once per lane group
+  std::vector<std::vector<uint8_t>> wcount(nseg), gcount(nseg);
+  for (int i = 0; i < nseg; ++i) {
+    wcount[i].assign((size_t)(seg_rows[i] * (K >> 3)), 0);
+    gcount[i].assign((size_t)(seg_rows[i] * (K / 64)), 0);
+  }
+  for (int cb = 0; cb < N / 64; ++cb)
+    for (int w = 0; w < 4; ++w) {
+      const int n0w = wave_col<EPI>(cb, w, N, hd);
+      int si = 0;
+      for (int i = 1; i < nseg; ++i)
+        if (n0w >= seg_n0[i]) si = i;
+      const int64_t rows = seg_rows[si];
+      const int64_t words = rows * (K >> 3), groups = rows * (K / 64);
+      for (int col = 0; col < 16; ++col) {
+        const int64_t wrow = (int64_t)(n0w - seg_n0[si] + col);
+        if (wrow < 0 || wrow >= rows) {
+          r.st = fail(DSPARK_ERR_SHAPE, "%s: column block %d wave %d reads weight row %lld of %lld", role, cb, w,
+                      (long long)wrow, (long long)rows);
+          return;
+        }
+        for (int y = 0; y < p.S; ++y) {
+          const int kbeg = y * p.kslice, kend = std::min(K, kbeg + p.kslice);
+          for (int kc = kbeg; kc < kend; kc += KC) {
+            const int len = std::min(KC, kend - kc), nsteps = len >> 5;
+            if (len % 64) {
+              r.st = fail(DSPARK_ERR_SHAPE, "%s: sub-slice of %d codes (not whole 64-groups)", role, len);
+              return;
+            }
+            for (int gq = 0; gq < 4; ++gq)
+              for (int j = 0; j < SMAX / 2; ++j) {
+                if (2 * j >= nsteps) continue;
+                const int64_t wd = q4_gemm_word(wrow, K, kc, gq, j), gi = q4_gemm_group(wrow, K, kc, j);
+                // both words hold codes of this row inside the sub-slice
+                const int64_t k0 = (wd - wrow * (K >> 3)) * 8;
+                r.n += 3;
+                if (wd < 0 || wd + 1 >= words || k0 < kc || k0 + 16 > kc + len || gi < 0 || gi >= groups ||
+                    gi - wrow * (K / 64) != (kc + 64 * j) / 64) {
+                  r.st = fail(DSPARK_ERR_SHAPE, "%s: row %lld k %d lane group %d group %d: word %lld of %lld, "
+                              "scale %lld of %lld", role, (long long)wrow, kc, gq, j, (long long)wd,
+                              (long long)words, (long long)gi, (long long)groups);
+                  return;
+                }
+                wcount[si][wd] += 1;
+                wcount[si][wd + 1] += 1;
+                gcount[si][gi] += 1;
+              }
+            // the staging's group sums: row ml < 16, group of the 8-code piece k8
+            for (int k8 = 0; k8 < (len >> 3); ++k8) {
+              const int idx = 15 * ngmax + (k8 >> 3);
+              ++r.n;
+              if ((k8 >> 3) >= ngmax || idx >= 16 * ngmax) {
+                r.st = fail(DSPARK_ERR_SHAPE, "%s: group sum %d of %d", role, idx, 16 * ngmax);
+                return;
+              }
+            }
+          }
+        }
+      }
+    }
+  for (int i = 0; i < nseg; ++i) {
+    for (size_t x = 0; x < wcount[i].size(); ++x)
+      if (wcount[i][x] != 1) {
+        r.st = fail(DSPARK_ERR_SHAPE, "%s: segment %d word %zu read %d times by one row block", role, i, x,
+                    (int)wcount[i][x]);
+        return;
+      }
+    for (size_t x = 0; x < gcount[i].size(); ++x)
+      if (gcount[i][x] != 4) {
+        r.st = fail(DSPARK_ERR_SHAPE, "%s: segment %d scale %zu read %d times by one row block", role, i, x,
+                    (int)gcount[i][x]);
+        return;
+      }
+  }
+}
+
+// element reads of a 4-bit table (embedding, Markov tables, the RNN matrix,
+// the confidence projection): rows [r0, r1) and every column
+void q4_replay_table(Q4Replay& r, const char* role, int64_t rows, int cols, int group, int64_t r0, int64_t r1) {
+  if (r.st) return;
+  const int64_t words = rows * (cols >> 3), groups = rows * (cols / group);
+  for (int64_t row = r0; row < r1; ++row)
+    for (int k = 0; k < cols; ++k) {
+      const int64_t wd = q4_word(row, cols, k), gi = q4_group(row, cols, group, k);
+      ++r.n;
+      if (row < 0 || row >= rows || wd < 0 || wd >= words || gi < 0 || gi >= groups) {
+        r.st = fail(DSPARK_ERR_SHAPE, "%s: element (%lld, %d): word %lld of %lld, scale %lld of %lld", role,
+                    (long long)row, k, (long long)wd, (long long)words, (long long)gi, (long long)groups);
+        return;
+      }
+    }
+}
+}  // namespace
+}  // extern "C++"
+
+dspark_status dspark_q4_address_check(const dspark_config* cfg, int A, const int32_t* anchors_host, int64_t ctx_rows,
+                                      int input_kind, int64_t* n_checked) {
+  g_err.clear();
+  if (!cfg || !anchors_host || A <= 0 || A > MAX_ROWS || ctx_rows <= 0 || ctx_rows > (1 << 24))
+    return fail(DSPARK_ERR_INVALID_ARG, "null config or anchors, or A / ctx_rows out of range");
+  const dspark_config& c = *cfg;
+  if (c.weight_dtype != DSPARK_Q4) return fail(DSPARK_ERR_INVALID_ARG, "not a 4-bit config");
+  dspark_status st = check_shapes(c);
+  if (st) return st;
+  if (input_kind == DSPARK_INPUT_TARGET_FEATURES && c.fc_in == 0)
+    return fail(DSPARK_ERR_UNSUPPORTED, "model has no fc / hidden_norm");
+  for (int a = 0; a < A; ++a)
+    if (anchors_host[a] < 0 || anchors_host[a] >= c.vocab_size)
+      return fail(DSPARK_ERR_INVALID_ARG, "anchor %d out of range", a);
+  // a model with the config's sizes and no tensors: the layouts read sizes only
+  dspark_model m;
+  m.c = c;
+  const int rotated = (int)std::floor(c.global_head_dim * c.partial_rotary_factor);
+  m.nrot = std::min((rotated + 1) / 2, c.global_head_dim / 2);
+  m.nq = (c.num_attention_heads / c.num_global_key_value_heads) * c.block_size;
+  const int H = c.hidden_size, I = c.intermediate_size, hd = c.global_head_dim, V = c.vocab_size;
+  const int nH = c.num_attention_heads, nKv = c.num_global_key_value_heads, G = c.group_size, r = c.markov_rank;
+  Q4Replay rp;
+  // the round's GEMMs (weights [out, in]; segments as the round passes them)
+  const DraftLayout d = draft_layout(&m, A, true, 1);
+  {
+    const int64_t rows[2] = {(int64_t)nH * hd, (int64_t)nKv * hd};
+    const int n0[2] = {0, nH * hd};
+    q4_replay_gemm<EPI_QK>(rp, "q|k", d.qk, (nH + nKv) * hd, H, hd, 2, rows, n0);
+  }
+  {
+    const int64_t rows[1] = {H};
+    const int n0[1] = {0};
+    q4_replay_gemm<EPI_SUMS>(rp, "o", d.o, H, nH * hd, hd, 1, rows, n0);
+    q4_replay_gemm<EPI_SUMS>(rp, "down", d.dn, H, I, hd, 1, rows, n0);
+  }
+  {
+    const int64_t rows[2] = {I, I};
+    const int n0[2] = {0, I};
+    q4_replay_gemm<EPI_GELU>(rp, "gate|up", d.gu, 2 * I, H, hd, 2, rows, n0);
+  }
+  {
+    const int64_t rows[1] = {V};
+    const int n0[1] = {0};
+    q4_replay_gemm<EPI_LM>(rp, "lm_head", d.lm, V, H, hd, 1, rows, n0);
+  }
+  // the context projection: fc, then k_proj over groups of layers
+  const ProjLayout pl = proj_layout(&m, input_kind, 1, (int)ctx_rows);
+  if (input_kind == DSPARK_INPUT_TARGET_FEATURES) {
+    const int64_t rows[1] = {H};
+    const int n0[1] = {0};
+    q4_replay_gemm<EPI_SUMS>(rp, "fc", pl.fc, H, c.fc_in, hd, 1, rows, n0);
+  }
+  for (int l0 = 0; l0 < c.num_hidden_layers; l0 += pl.lay_per_gemm) {
+    const int nl = std::min(pl.lay_per_gemm, c.num_hidden_layers - l0);
+    const GemmPlan gp = nl == pl.lay_per_gemm ? pl.kp
+                                              : plan_gemm(c.weight_dtype, pl.kp.xmode, (int)ctx_rows, nl * nKv * hd, H,
+                                                          hd, m.tall_rows);
+    int64_t rows[MAX_SEG];
+    int n0[MAX_SEG];
+    for (int i = 0; i < nl; ++i) {
+      rows[i] = (int64_t)nKv * hd;
+      n0[i] = i * nKv * hd;
+    }
+    q4_replay_gemm<EPI_KV>(rp, "k_proj", gp, nl * nKv * hd, H, hd, nl, rows, n0);
+  }
+  // element reads: the embedding rows of the anchors and the mask id, the
+  // Markov tables (walk bound over every row, walk and confidence over any
+  // previous token), the RNN matrix, the confidence projection
+  for (int a = 0; a < A; ++a) q4_replay_table(rp, "embed", V, H, G, anchors_host[a], anchors_host[a] + 1);
+  q4_replay_table(rp, "embed", V, H, G, c.mask_token_id, c.mask_token_id + 1);
+  if (r > 0) {
+    q4_replay_table(rp, "markov_w1", V, r, G, 0, V);
+    q4_replay_table(rp, "markov_w2", V, r, G, 0, V);
+    if (c.markov_head_rnn) q4_replay_table(rp, "rnn_wh", r, r, G, 0, r);
+  }
+  if (c.enable_confidence_head)
+    q4_replay_table(rp, "confidence proj", 1, H + (c.confidence_head_with_markov ? r : 0), G, 0, 1);
+  if (n_checked) *n_checked = rp.n;
+  return rp.st;
 }
 
 void dspark_profile_enable(int on) { g_prof = on != 0; }

@@ -81,20 +81,6 @@ __device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned total, int* 
   return *flag != 0;
 }
 
-// first output column of wave w in column block c.  gate|up: waves 0,1 take
-// gate columns 32c.., waves 2,3 the matching up columns.  q|k heads: waves
-// 0,1 take head dims [32c', 32c'+32), waves 2,3 their RoPE partners + hd/2
-// (c' = c mod hd/64), so a workgroup holds whole rotation pairs.
-template <int EPI>
-__device__ __forceinline__ int wave_col(int c, int w, int N, int hd) {
-  if constexpr (EPI == EPI_GELU) return (w >> 1) * (N >> 1) + 32 * c + 16 * (w & 1);
-  if constexpr (EPI == EPI_QK) {
-    const int hj = hd >> 6, head = c / hj, cp = c - head * hj;
-    return head * hd + (w >> 1) * (hd >> 1) + 32 * cp + 16 * (w & 1);
-  }
-  return 64 * c + 16 * w;
-}
-
 // ---------------------------------------------------------------------------
 // input rows (XM_NORM): per-row factors (r1, r2) and sc from the statistics
 // ---------------------------------------------------------------------------
@@ -660,15 +646,16 @@ __device__ __forceinline__ void load_w(const GemmArgs& g, int si, int64_t wrow, 
       w.v[2 * s + 1] = *(const u32x4*)(p + 32 * min(s, nsteps - 1) + 4);
     }
   } else {
-    const uint32_t* p = (const uint32_t*)g.seg[si].w + wrow * (g.K >> 3) + (kc >> 3) + 2 * gq;
-    const uint16_t* ps = (const uint16_t*)g.seg[si].s + wrow * (g.K >> 6) + (kc >> 6);
-    const uint16_t* pb = (const uint16_t*)g.seg[si].b + wrow * (g.K >> 6) + (kc >> 6);
+    const uint32_t* p = (const uint32_t*)g.seg[si].w;
+    const uint16_t* ps = (const uint16_t*)g.seg[si].s;
+    const uint16_t* pb = (const uint16_t*)g.seg[si].b;
 #pragma unroll
     for (int j = 0; j < SMAX / 2; ++j)
       if (2 * j < nsteps) {
-        w.q[j] = *(const u32x2*)(p + 8 * j);
-        w.qs[j] = bf2f(ps[j]);
-        w.qb[j] = bf2f(pb[j]);
+        const int64_t gi = q4_gemm_group(wrow, g.K, kc, j);
+        w.q[j] = *(const u32x2*)(p + q4_gemm_word(wrow, g.K, kc, gq, j));
+        w.qs[j] = bf2f(ps[gi]);
+        w.qb[j] = bf2f(pb[gi]);
       }
   }
 }
@@ -738,10 +725,6 @@ __device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, cons
 }
 
 // LDS bytes of one staged activation sub-slice (hi / lo planes + q4 row sums)
-__host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, int kc) {
-  return (size_t)mt * (kc / 32) * 64 * 16 * (xmode == XM_BF16 ? 1 : 2) +
-         (wkind == WK_Q4 ? (size_t)mt * 16 * (kc / 64) * 4 : 0);
-}
 
 // ---------------------------------------------------------------------------
 // NW = 8 (unrolled, no split-K): eight waves, two per SIMD, as two sets of
@@ -844,7 +827,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     const int kc = chunk_k(c), klen = chunk_len(c);
     u32x4* xhi = (u32x4*)(smem + (KH ? buf * 2 + half : buf) * xbuf);
     u32x4* xlo = xhi + MT * nfull * 64;
-    float* xsum = (float*)(xhi + (XM == XM_BF16 ? 1 : 2) * MT * nfull * 64);
+    float* xsum = (float*)((unsigned char*)xhi + xsum_offset(XM, MT, KC));
     if constexpr (WK == WK_Q4) {
       for (int i = tid; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
       __syncthreads();

@@ -60,6 +60,49 @@ struct GemmArgs {
 // what the GEMM does with its result (see dspark_gemm.hip)
 enum { EPI_Y = 0, EPI_QK = 1, EPI_GELU = 2, EPI_SUMS = 3, EPI_LM = 4, EPI_KV = 5 };
 
+// ---- address arithmetic shared by the kernels and the host ----------------
+// (host code replays the 4-bit kernels' addresses with these: see
+// dspark_q4_address_check)
+//
+// 4-bit storage, eight codes per uint32 word and groups of `group` codes
+// along each row: the word holding element (row, k) of a [rows, cols]
+// matrix, and the index of its scale / bias
+__host__ __device__ inline int64_t q4_word(int64_t row, int cols, int k) { return row * (cols >> 3) + (k >> 3); }
+__host__ __device__ inline int64_t q4_group(int64_t row, int cols, int group, int k) {
+  return row * (cols / group) + k / group;
+}
+// streaming GEMM: the first of the two words lane group gq loads for the j-th
+// 64-wide group of the sub-slice that starts at kc (codes kc + 64j + 16gq ..
+// kc + 64j + 16gq + 15 of weight row wrow), and that group's scale / bias
+__host__ __device__ inline int64_t q4_gemm_word(int64_t wrow, int K, int kc, int gq, int j) {
+  return q4_word(wrow, K, kc) + 2 * gq + 8 * j;
+}
+__host__ __device__ inline int64_t q4_gemm_group(int64_t wrow, int K, int kc, int j) {
+  return q4_group(wrow, K, 64, kc) + j;
+}
+// streaming GEMM staging buffer of one sub-slice of kc: the bf16 activation
+// planes (one for bf16 rows, hi and lo otherwise) of mt 16-row tiles, then,
+// for 4-bit weights, the per-(row, 64-group) activation sums
+__host__ __device__ constexpr size_t xsum_offset(int xmode, int mt, int kc) {
+  return (size_t)mt * (kc / 32) * 64 * 16 * (xmode == XM_BF16 ? 1 : 2);
+}
+__host__ __device__ constexpr size_t xbuf_bytes(int wkind, int xmode, int mt, int kc) {
+  return xsum_offset(xmode, mt, kc) + (wkind == WK_Q4 ? (size_t)mt * 16 * (kc / 64) * 4 : 0);
+}
+// first output column of wave w in column block c.  gate|up: waves 0,1 take
+// gate columns 32c.., waves 2,3 the matching up columns.  q|k heads: waves
+// 0,1 take head dims [32c', 32c'+32), waves 2,3 their RoPE partners + hd/2
+// (c' = c mod hd/64), so a workgroup holds whole rotation pairs.
+template <int EPI>
+__host__ __device__ inline int wave_col(int c, int w, int N, int hd) {
+  if constexpr (EPI == EPI_GELU) return (w >> 1) * (N >> 1) + 32 * c + 16 * (w & 1);
+  if constexpr (EPI == EPI_QK) {
+    const int hj = hd >> 6, head = c / hj, cp = c - head * hj;
+    return head * hd + (w >> 1) * (hd >> 1) + 32 * cp + 16 * (w & 1);
+  }
+  return 64 * c + 16 * w;
+}
+
 struct RopeCfg {
   double theta;
   int hd, nrot;       // rotated pairs: k < nrot turn, the rest pass through

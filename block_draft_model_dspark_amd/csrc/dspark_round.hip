@@ -12,9 +12,9 @@ __device__ __forceinline__ float table_elem(const void* E, const void* Es, const
                                             int64_t row, int cols, int k) {
   if (kind == WK_F32) return ((const float*)E)[row * cols + k];
   if (kind == WK_BF16) return bf2f(((const uint16_t*)E)[row * cols + k]);
-  const uint32_t w = ((const uint32_t*)E)[row * (cols >> 3) + (k >> 3)];
+  const uint32_t w = ((const uint32_t*)E)[q4_word(row, cols, k)];
   const float q = (float)((w >> (4 * (k & 7))) & 0xFu);
-  const int64_t gi = row * (cols / group) + k / group;
+  const int64_t gi = q4_group(row, cols, group, k);
   return bf2f(((const uint16_t*)Es)[gi]) * q + bf2f(((const uint16_t*)Eb)[gi]);
 }
 

@@ -302,6 +302,22 @@ int dspark_profile_read(dspark_kernel_time* out, int max);
  * sizes, w outside [0, gx*gy) or null outputs. */
 dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by);
 
+/* Diagnostic (host only, no HIP call): replays on the host every address
+ * that the 4-bit branches of the kernels form for a round of A rows with
+ * these anchors and a context projection of ctx_rows rows of input_kind
+ * (streaming GEMM weight words and scales for q|k, o, gate|up, down,
+ * lm_head, fc and k_proj under the launch plans the library makes; the
+ * GEMM's per-group activation sums in LDS; embedding, Markov, RNN and
+ * confidence table elements), using the kernels' own index functions, and
+ * checks each against the size of the buffer it reads ([rows, cols/8] words,
+ * [rows, cols/group] scales and biases).  DSPARK_OK when every address is in
+ * range (*n_checked = the number checked), DSPARK_ERR_SHAPE naming the first
+ * one that is not, DSPARK_ERR_INVALID_ARG for a config that is not 4-bit or
+ * arguments out of range.  The config is checked as dspark_model_create
+ * checks it, except that 4-bit weights are not refused. */
+dspark_status dspark_q4_address_check(const dspark_config* cfg, int A, const int32_t* anchors_host,
+                                      int64_t ctx_rows, int input_kind, int64_t* n_checked);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char* dspark_last_error(void);
 
