@@ -376,7 +376,7 @@ DraftLayout draft_layout(const dspark_model* m, int A, bool with_z, int64_t tota
   d.hA = take((size_t)M * d.ldh * 4);
   d.hB = take((size_t)M * d.ldh * 4);
   d.Y = take((size_t)M * d.ldh * 4);
-  d.sums = take((size_t)(H / 64) * M * 16);
+  d.sums = take((size_t)(H / 64) * M * sizeof(RowStats));
   d.rt = take((size_t)M * (hd / 2) * 8);
   d.scal = take((size_t)(c.num_hidden_layers + 1) * 4);
   d.O = take((size_t)M * d.ldo * 4);
@@ -450,7 +450,7 @@ ProjLayout proj_layout(const dspark_model* m, int input_kind, int B, int L) {
   p.P = take(pbytes);
   p.Y = take((size_t)M * Nk * 4);
   p.C = feats ? take((size_t)M * H * 4) : 0;
-  p.sums = feats ? take((size_t)(H / 64) * M * 16) : 0;
+  p.sums = feats ? take((size_t)(H / 64) * M * sizeof(RowStats)) : 0;
   p.cnt = take(p.cwords * 4);
   p.xop = take(std::max(xbytes, (size_t)4));
   p.T = take(std::max(tbytes, (size_t)4));
@@ -982,7 +982,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     e.h = nullptr;
     e.ldy = H;
     e.w1 = m->hidden_norm;
-    e.sums = (float4*)(ws + p.sums);
+    e.sums = (RowStats*)(ws + p.sums);
     HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream, tb); }));
     nin.y = e.Y;
     nin.sums = e.sums;
@@ -1108,7 +1108,7 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   float* hA = (float*)(ws + d.hA);  // the embedding, then each layer's post-attention residual
   float* hB = (float*)(ws + d.hB);  // the residual entering each layer
   float* Y = (float*)(ws + d.Y);
-  float4* sums = (float4*)(ws + d.sums);
+  RowStats* sums = (RowStats*)(ws + d.sums);
   float2* rt = (float2*)(ws + d.rt);
   float* O = (float*)(ws + d.O);
   float* act = (float*)(ws + d.act);

@@ -149,6 +149,57 @@ __device__ __forceinline__ float half_sum(float v) {
   return (threadIdx.x & 32) ? b : a;
 }
 
+// fp64 sums over a row of 16 lanes (the same DPP moves on both halves of
+// each double) and over the wave (every lane gets the result)
+template <int CTRL>
+__device__ __forceinline__ double dpp_mov_d(double v) {
+  const int2 p = __builtin_bit_cast(int2, v);
+  int2 r;
+  r.x = __builtin_amdgcn_mov_dpp(p.x, CTRL, 0xF, 0xF, false);
+  r.y = __builtin_amdgcn_mov_dpp(p.y, CTRL, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, r);
+}
+__device__ __forceinline__ double row16_sum_d(double v) {
+  v += dpp_mov_d<DPP_QUAD_1032>(v);
+  v += dpp_mov_d<DPP_QUAD_2301>(v);
+  v += dpp_mov_d<DPP_ROW_HALF_MIRROR>(v);
+  v += dpp_mov_d<DPP_ROW_MIRROR>(v);
+  return v;
+}
+// Reduce-scatter over the 16 lanes of a row: every lane brings v[0..15] and
+// lane l (= lane mod 16) gets the row's sum of v[l].  Four exchange steps
+// (partners differ in bit 3, 2, 1, 0 of l: row mirror, half-row mirror, quad
+// swaps); at each step a lane keeps the half of its values that its bit
+// selects and adds the partner's copy of that half (15 moves and adds
+// instead of 16 separate row sums).
+__device__ __forceinline__ double row16_reduce_scatter(const double* v) {
+  const int l = threadIdx.x & 15;
+  double a[8], b[4], c[2];
+  {
+    const bool up = l & 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = (up ? v[j + 8] : v[j]) + dpp_mov_d<DPP_ROW_MIRROR>(up ? v[j] : v[j + 8]);
+  }
+  {
+    const bool up = l & 4;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = (up ? a[j + 4] : a[j]) + dpp_mov_d<DPP_ROW_HALF_MIRROR>(up ? a[j] : a[j + 4]);
+  }
+  {
+    const bool up = l & 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) c[j] = (up ? b[j + 2] : b[j]) + dpp_mov_d<DPP_QUAD_2301>(up ? b[j] : b[j + 2]);
+  }
+  const bool up = l & 1;
+  return (up ? c[1] : c[0]) + dpp_mov_d<DPP_QUAD_1032>(up ? c[0] : c[1]);
+}
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = row16_sum_d(v);
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
 // block-wide sum; `red` holds >= blockDim/64 floats; all threads get the result
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63, nw = (blockDim.x + 63) >> 6;

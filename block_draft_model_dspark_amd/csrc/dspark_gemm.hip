@@ -90,9 +90,10 @@ __device__ __forceinline__ bool arrive_last(unsigned* ctr, unsigned total, int* 
 // loads (indices clamped, surplus parts masked when summing): a load under a
 // run-time condition would make the compiler wait for every load in flight.
 // norm_finish reduces them; further 16-row tiles (MT > 1) load theirs there.
-constexpr int NV = 8;  // parts per thread, 16 threads per row: K up to 16 * NV * 64 = 8192
+constexpr int NV = 2;  // parts each thread loads early (16 threads per row: K up to 16 * NV * 64 = 2048);
+                       // norm_finish reads the parts of wider rows
 
-__device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4* v, float& sc, int vt) {
+__device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, RowStats* v, float& sc, int vt) {
   const NormIn& n = g.nin;
   const int tid = vt, sub = tid & 15;
   const int m = min(mbase + (tid >> 4), g.M - 1);
@@ -102,38 +103,41 @@ __device__ __forceinline__ void norm_issue(const GemmArgs& g, int mbase, float4*
 }
 
 template <int MT>
-__device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const float4* v0, float sc, float2* rs,
+__device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const RowStats* v0, float sc, float2* rs,
                                             int vt) {
   const NormIn& n = g.nin;
   const int tid = vt, sub = tid & 15;
-  const float inv_k = 1.f / (float)g.K;
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int ml = 16 * t + (tid >> 4);
     const int m = min(mbase + ml, g.M - 1);
-    float4 v[NV];
+    RowStats s = {0.0, 0.0, 0.0, 0.0};
+    int p0 = sub;
+    if (t == 0) {
 #pragma unroll
-    for (int i = 0; i < NV; ++i)
-      v[i] = t == 0 ? v0[i] : n.sums[(int64_t)min(sub + 16 * i, n.nparts - 1) * g.M + m];
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int i = 0; i < NV; ++i)
-      if (sub + 16 * i < n.nparts) {
-        s.x += v[i].x;
-        s.y += v[i].y;
-        s.z += v[i].z;
-        s.w += v[i].w;
-      }
-    s.x = row16_sum(s.x);
-    s.y = row16_sum(s.y);
-    s.z = row16_sum(s.z);
-    s.w = row16_sum(s.w);
-    if (sub == 0) {
-      const float r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
-      const float t2 = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
-      const float r2 = 1.f / sqrtf(t2 * inv_k + n.eps);
-      rs[ml] = make_float2(r1, r2);
+      for (int i = 0; i < NV; ++i)
+        if (sub + 16 * i < n.nparts) {
+          s.x += v0[i].x;
+          s.y += v0[i].y;
+          s.z += v0[i].z;
+          s.w += v0[i].w;
+        }
+      p0 = sub + 16 * NV;
     }
+    // (rows wider than the early loads cover, and further 16-row tiles; the
+    // loads here wait for every load in flight, weights included)
+    for (int p = p0; p < n.nparts; p += 16) {
+      const RowStats v = n.sums[(int64_t)p * g.M + m];
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    s.x = row16_sum_d(s.x);
+    s.y = row16_sum_d(s.y);
+    s.z = row16_sum_d(s.z);
+    s.w = row16_sum_d(s.w);
+    if (sub == 0) rs[ml] = norm_factors(s, sc, g.K, n.eps);
   }
   if (tid == 0) rs[MT * 16] = make_float2(sc, 0.f);
 }
@@ -207,14 +211,22 @@ __device__ __forceinline__ void epi_sums(const GemmArgs& g, const EpiArgs& e, co
                          float* red) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4;
   const float w1 = ld_act_v(e.w1, n, e.act_bf16);
+  // residual loads issued together without a branch (a missing residual
+  // reads Y's rows, same shape, and is zeroed after the loads)
+  const float* hsrc = e.h ? e.h : e.Y;
   float hv[MT][4];
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = min(mbase + t * 16 + 4 * gq + i, g.M - 1);
-      hv[t][i] = e.h ? e.h[(int64_t)m * e.ldy + n] : 0.f;
+      hv[t][i] = hsrc[(int64_t)m * e.ldy + n];
     }
+  if (!e.h)
+#pragma unroll
+    for (int t = 0; t < MT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hv[t][i] = 0.f;
 #pragma unroll
   for (int t = 0; t < MT; ++t)
 #pragma unroll
@@ -222,28 +234,33 @@ __device__ __forceinline__ void epi_sums(const GemmArgs& g, const EpiArgs& e, co
       const int m = mbase + t * 16 + 4 * gq + i;
       if (m < g.M) e.Y[(int64_t)m * e.ldy + n] = acc[t][i];
     }
+  // fp64 products and sums (see RowStats)
+  double* redd = (double*)red;
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+  for (int t = 0; t < MT; ++t) {
+    // per lane: statistic q of row i at index 4 q + i; lane l of the row
+    // group gets the 16 lanes' sum of index l
+    double v[16];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float y = acc[t][i], wy = w1 * y, h = hv[t][i];
-      const float s0 = row16_sum(y * y), s1 = row16_sum(h * wy), s2 = row16_sum(wy * wy), s3 = row16_sum(h * h);
-      if ((lane & 15) == 0) {
-        float* p = red + ((wave * MT * 16) + t * 16 + 4 * gq + i) * 4;
-        p[0] = s0;
-        p[1] = s1;
-        p[2] = s2;
-        p[3] = s3;
-      }
+      const double y = acc[t][i], wy = (double)w1 * y, h = hv[t][i];
+      v[i] = y * y;
+      v[4 + i] = h * wy;
+      v[8 + i] = wy * wy;
+      v[12 + i] = h * h;
     }
+    const double sum = row16_reduce_scatter(v);
+    const int l = lane & 15;
+    redd[((wave * MT * 16) + t * 16 + 4 * gq + (l & 3)) * 4 + (l >> 2)] = sum;
+  }
   __syncthreads();
   for (int r = tid; r < MT * 16; r += 256) {
     const int m = mbase + r;
     if (m >= g.M) continue;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    RowStats s = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      const float* p = red + ((w * MT * 16) + r) * 4;
+      const double* p = redd + ((w * MT * 16) + r) * 4;
       s.x += p[0];
       s.y += p[1];
       s.z += p[2];
@@ -795,7 +812,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   // 1. the small loads first (a wave's loads complete in order): row
   //    statistics and norm weights of the slice, then chunk 0's activations
   //    and weights (and chunk 1's, double-buffered, for a 16-row tile)
-  float4 nv[NV];
+  RowStats nv[NV];
   float sc_in = 1.f;
   u32x4 wr[4];
   if constexpr (XM == XM_NORM) {

@@ -20,11 +20,28 @@ constexpr int ATT_KEYS = 32;    // keys staged per attention pass
 // residual h it is added to and the norm weight w1 of that sum:
 // (sum y^2, sum h*w1*y, sum (w1*y)^2, sum h^2).  Enough to form both RMSNorm
 // factors of the sandwich  hn = (h + rms(y)*w1) * sc,  x = rms(hn) * w2
-// without another pass over the row.
+// without another pass over the row.  The sum of hn^2 is formed as
+// sc^2 (S_hh + 2 r1 S_hwy + r1^2 S_wywy), which cancels when the normed
+// sublayer output nearly cancels the residual: the products and sums are
+// therefore taken in fp64 (a product of two fp32 values is exact there), so
+// the combination keeps its accuracy down to cancellations of ~1e8.
+struct RowStats {
+  double x, y, z, w;  // sum y^2, sum h w1 y, sum (w1 y)^2, sum h^2
+};
+
+// the sandwich's two RMS factors from a row's summed statistics over K
+// columns: r1 = rms factor of y, r2 = rms factor of hn = (h + r1 w1 y) sc
+__host__ __device__ inline float2 norm_factors(const RowStats& s, float sc, int K, float eps) {
+  const double r1 = 1.0 / sqrt(s.x / K + (double)eps);
+  const double t2 = (double)sc * sc * (s.w + 2.0 * r1 * s.y + r1 * r1 * s.z);
+  const double r2 = 1.0 / sqrt((t2 > 0.0 ? t2 : 0.0) / K + (double)eps);
+  return make_float2((float)r1, (float)r2);
+}
+
 struct NormIn {
   const float* h;      // [M, K] residual, or null (zero)
   const float* y;      // [M, K] sublayer output, or null (zero)
-  const float4* sums;  // [nparts, M] statistics of 64-column blocks
+  const RowStats* sums;  // [nparts, M] statistics of 64-column blocks
   int nparts;          // K / 64
   const void* w1;      // [K] act dtype (unused when y is null)
   const void* w2;      // [K] act dtype, or null: x = hn
@@ -147,7 +164,7 @@ struct EpiArgs {
   int64_t ldy;        // row pitch (floats) of Y and h
   const float* h;     // residual [M, N] or null
   const void* w1;     // norm weight [N]
-  float4* sums;       // [N/64, M]
+  RowStats* sums;     // [N/64, M]
   // EPI_LM
   float cap;          // <= 0: none
   const float* aux;   // [V] markov_w2 row norms, aux[V] = max markov_w1 row norm; null when rank 0
@@ -240,7 +257,7 @@ struct EmbedArgs {
   float* scal;        // [nL + 1]: 1, then the layer scalars as fp32
   float* h;           // [M, H] scaled embedding rows, row pitch ldh
   int64_t ldh;
-  float4* sums;       // [H/64, M] (0, 0, 0, sum h^2)
+  RowStats* sums;     // [H/64, M] (0, 0, 0, sum h^2)
   float2* rt;         // [M, hd/2] RoPE table of the block positions
   RopeCfg rope;
   unsigned* cnt; int ncnt;  // GEMM counters zeroed here

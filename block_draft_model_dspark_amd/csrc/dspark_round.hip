@@ -35,7 +35,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   const int64_t id = g == 0 ? a.rows.anchor[row] : a.mask_id;
   for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
     float v[8];
-    float ss = 0.f;
+    double ss = 0.0;
     if (a.ekind == WK_BF16) {
       // one 16-byte load of the eight bf16 values
       const u32x4 w = *(const u32x4*)((const uint16_t*)a.E + id * a.H + k0);
@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       v[q] *= a.scale;
-      ss += v[q] * v[q];
+      ss += (double)v[q] * v[q];
     }
     float* dst = a.h + (int64_t)m * a.ldh + k0;
     *(f32x4*)dst = f32x4{v[0], v[1], v[2], v[3]};
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
     ss += __shfl_xor(ss, 1);
     ss += __shfl_xor(ss, 2);
     ss += __shfl_xor(ss, 4);
-    if ((tid & 7) == 0) a.sums[(int64_t)(k0 >> 6) * M + m] = make_float4(0.f, 0.f, 0.f, ss);
+    if ((tid & 7) == 0) a.sums[(int64_t)(k0 >> 6) * M + m] = RowStats{0.0, 0.0, 0.0, ss};
   }
   const int half = a.rope.hd >> 1;
   const int64_t pos = (int64_t)a.rows.pos[row] + g;

@@ -31,24 +31,24 @@ namespace dsp {
 // hn written to hout when it is given.
 template <int XM>
 __global__ __launch_bounds__(256) void k_xprep(const GemmArgs g, uint16_t* xop, int64_t plane) {
-  __shared__ float4 red[4];
+  __shared__ RowStats red[4];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int K = g.K;
   float r1 = 1.f, r2 = 1.f, sc = 1.f;
   if constexpr (XM == XM_NORM) {
     const NormIn& n = g.nin;
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    RowStats s = {0.0, 0.0, 0.0, 0.0};
     for (int p = tid; p < n.nparts; p += 256) {
-      const float4 v = n.sums[(int64_t)p * g.M + m];
+      const RowStats v = n.sums[(int64_t)p * g.M + m];
       s.x += v.x;
       s.y += v.y;
       s.z += v.z;
       s.w += v.w;
     }
-    s.x = wave_sum(s.x);
-    s.y = wave_sum(s.y);
-    s.z = wave_sum(s.z);
-    s.w = wave_sum(s.w);
+    s.x = wave_sum_d(s.x);
+    s.y = wave_sum_d(s.y);
+    s.z = wave_sum_d(s.z);
+    s.w = wave_sum_d(s.w);
     if (lane == 0) red[wave] = s;
     __syncthreads();
     s = red[0];
@@ -60,10 +60,9 @@ __global__ __launch_bounds__(256) void k_xprep(const GemmArgs g, uint16_t* xop, 
       s.w += red[w].w;
     }
     sc = n.sc ? *n.sc : 1.f;
-    const float inv_k = 1.f / (float)K;
-    r1 = 1.f / sqrtf(s.x * inv_k + n.eps);
-    const float t2 = fmaxf(sc * sc * (s.w + 2.f * r1 * s.y + r1 * r1 * s.z), 0.f);
-    r2 = 1.f / sqrtf(t2 * inv_k + n.eps);
+    const float2 f = norm_factors(s, sc, K, n.eps);
+    r1 = f.x;
+    r2 = f.y;
   }
   for (int k8 = tid; k8 < (K >> 3); k8 += 256) {
     const int k = 8 * k8;
