@@ -846,7 +846,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     u32x4* xlo = xhi + MT * nfull * 64;
     float* xsum = (float*)((unsigned char*)xhi + xsum_offset(XM, MT, KC));
     if constexpr (WK == WK_Q4) {
-      for (int i = tid; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
+      // each set of four waves clears its own buffer's sums (vt: thread within the set)
+      for (int i = vt; i < MT * 16 * ngmax; i += 256) xsum[i] = 0.f;
       __syncthreads();
     }
     if (stager)
