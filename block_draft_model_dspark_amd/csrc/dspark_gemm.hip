@@ -555,6 +555,13 @@ __device__ __forceinline__ void stage_load(const GemmArgs& g, int mbase, int kc,
   }
 }
 
+// LDS position of staged 16-byte operand slot `slot` (16-slot groups hold one
+// A-operand column of 16 rows): the low four bits are xor-ed with bits 4..7,
+// so the staging stores (lanes along k, one row) spread over the banks
+// instead of landing 256 bytes apart, while each MFMA operand read (lanes
+// along the 16 rows of a group) stays a permutation within its group
+__device__ __forceinline__ int xslot(int slot) { return slot ^ ((slot >> 4) & 15); }
+
 template <int WK, int XM, int MT>
 __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc, int klen, int base,
                                             const XRegs<xbatch<XM, MT>()>& r,
@@ -624,12 +631,12 @@ __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc
     }
     const int slot = ((ml >> 4) * nfull + s) * 64 + qg * 16 + (ml & 15);
     if constexpr (XM == XM_BF16) {
-      xhi[slot] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
+      xhi[xslot(slot)] = __builtin_bit_cast(u32x4, to_bf16x8(e8));
     } else {
       bf16x8 h, l;
       split8(e8, h, l);
-      xhi[slot] = __builtin_bit_cast(u32x4, h);
-      xlo[slot] = __builtin_bit_cast(u32x4, l);
+      xhi[xslot(slot)] = __builtin_bit_cast(u32x4, h);
+      xlo[xslot(slot)] = __builtin_bit_cast(u32x4, l);
     }
   }
 }
@@ -689,7 +696,7 @@ __device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, cons
         const bf16x8 wb = __builtin_bit_cast(bf16x8, w.v[s]);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const int o = (t * nfull + s) * 64 + lane;
+          const int o = xslot((t * nfull + s) * 64 + lane);
           acc[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), wb, acc[t]);
           if constexpr (!XBF) acc[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wb, acc[t]);
         }
@@ -708,7 +715,7 @@ __device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, cons
         split8(w8, wh, wl);
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
-          const int o = (t * nfull + s) * 64 + lane;
+          const int o = xslot((t * nfull + s) * 64 + lane);
           const bf16x8 xh = __builtin_bit_cast(bf16x8, xhi[o]);
           acc[t] = mfma16(xh, wh, acc[t]);
           acc[t] = mfma16(xh, wl, acc[t]);
@@ -727,7 +734,7 @@ __device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, cons
           const bf16x8 wb = q4_decode(w.q[j][sub]);
 #pragma unroll
           for (int t = 0; t < MT; ++t) {
-            const int o = (t * nfull + 2 * j + sub) * 64 + lane;
+            const int o = xslot((t * nfull + 2 * j + sub) * 64 + lane);
             tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xhi[o]), wb, tmp[t]);
             if constexpr (!XBF) tmp[t] = mfma16(__builtin_bit_cast(bf16x8, xlo[o]), wb, tmp[t]);
           }
