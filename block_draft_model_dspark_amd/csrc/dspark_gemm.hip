@@ -137,7 +137,11 @@ __device__ __forceinline__ void norm_finish(const GemmArgs& g, int mbase, const 
     s.y = row16_sum_d(s.y);
     s.z = row16_sum_d(s.z);
     s.w = row16_sum_d(s.w);
-    if (sub == 0) rs[ml] = norm_factors(s, sc, g.K, n.eps);
+    if (sub == 0) {
+      // rows past M: r2 = 0, so the staged input of such a row is zero
+      const float2 f = norm_factors(s, sc, g.K, n.eps);
+      rs[ml] = mbase + ml < g.M ? f : make_float2(f.x, 0.f);
+    }
   }
   if (tid == 0) rs[MT * 16] = make_float2(sc, 0.f);
 }
@@ -586,13 +590,25 @@ __device__ __forceinline__ void stage_store(const GemmArgs& g, int mbase, int kc
       const f32x4 w1a = *(const f32x4*)&wn[8 * k8], w1b = *(const f32x4*)&wn[8 * k8 + 4];
       const f32x4 w2a = *(const f32x4*)&wn[kcmax + 8 * k8], w2b = *(const f32x4*)&wn[kcmax + 8 * k8 + 4];
       float hn[8];
+      if (n.h && n.y && n.w2) {
+        // the backbone's sandwich (every operand present): hn = h sc + y (r1 sc w1),
+        // x = hn (r2 w2); rows past M have r2 = 0 (norm_finish), so x = 0 there
+        const float a1 = rr.x * sc;
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const float w1 = q < 4 ? w1a[q & 3] : w1b[q & 3], w2 = q < 4 ? w2a[q & 3] : w2b[q & 3];
-        const float h = n.h ? r.a[b][q >> 2][q & 3] : 0.f;
-        const float y = n.y ? r.y[b][q >> 2][q & 3] * rr.x * w1 : 0.f;
-        hn[q] = (h + y) * sc;
-        v[q] = ok ? (n.w2 ? hn[q] * rr.y * w2 : hn[q]) : 0.f;
+        for (int q = 0; q < 8; ++q) {
+          const float w1 = q < 4 ? w1a[q & 3] : w1b[q & 3], w2 = q < 4 ? w2a[q & 3] : w2b[q & 3];
+          hn[q] = fmaf(r.y[b][q >> 2][q & 3], a1 * w1, r.a[b][q >> 2][q & 3] * sc);
+          v[q] = hn[q] * (rr.y * w2);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const float w1 = q < 4 ? w1a[q & 3] : w1b[q & 3], w2 = q < 4 ? w2a[q & 3] : w2b[q & 3];
+          const float h = n.h ? r.a[b][q >> 2][q & 3] : 0.f;
+          const float y = n.y ? r.y[b][q >> 2][q & 3] * rr.x * w1 : 0.f;
+          hn[q] = (h + y) * sc;
+          v[q] = ok ? (n.w2 ? hn[q] * rr.y * w2 : hn[q]) : 0.f;
+        }
       }
       if (write_h && ok) {
         float* dst = n.hout + (int64_t)m * n.ld + kc + 8 * k8;
