@@ -2,9 +2,11 @@
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+from typing import List, Tuple
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -20,14 +22,47 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", os.path.j
          "-Wno-unused-result"]
 
 
+# The compiler's per-kernel resource remarks: every kernel must run without
+# private (scratch) memory.  A spill, or a register array the compiler can no
+# longer index statically, lands there and costs a memory round trip per
+# access (a sampling branch inside the tiled GEMM's store loop once pushed its
+# accumulators to scratch and tripled the GEMM time of a 32-row round).
+RESOURCE_REMARKS = ["-Rpass-analysis=kernel-resource-usage"]
+# Known exception: the wide attention over an fp32 context cache at head dim
+# 256 (fp32 keys staged as bf16 hi + lo planes need more registers than the
+# kernel has); only fp32-cache models with >= 2048 context keys in a round
+# take it.
+SCRATCH_ALLOWED = {"_ZN3dsp11k_attn_wideILi256ELb0ELi8ELb0EEEvNS_8AttnArgsE"}
+_FN = re.compile(r"Function Name: (\S+)")
+_SCRATCH = re.compile(r"ScratchSize \[bytes/lane\]: (\d+)")
+
+
+def scratch_kernels(remarks: str) -> List[Tuple[str, int]]:
+    """(kernel, bytes per lane) for every kernel the remarks report with
+    private memory."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = _FN.search(line)
+        if m:
+            name = m.group(1)
+            continue
+        m = _SCRATCH.search(line)
+        if m and name is not None and int(m.group(1)) > 0 and name not in SCRATCH_ALLOWED:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *RESOURCE_REMARKS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
+    bad = scratch_kernels(r.stderr)
+    if bad:
+        raise RuntimeError(f"{src}: kernels using scratch memory: {bad}")
     return obj
 
 

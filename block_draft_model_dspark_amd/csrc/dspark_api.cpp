@@ -263,14 +263,15 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
     t.ldt = a.N;
   }
   // logits: softcap and the walk's chunk bounds in the tiled kernel itself
-  // when its 128 x 128 tiles hold the final product
-  if (epi == EPI_LM && p.tall == TALL_128 && p.S == 1 && a.N % 64 == 0) {
+  // when its 128 x 128 tiles hold the final product (not when sampling: the
+  // noise is added by the separate logits epilogue, which keeps the tiled
+  // kernel's store loop free of it)
+  if (epi == EPI_LM && p.tall == TALL_128 && p.S == 1 && a.N % 64 == 0 && !(e.smp.temperature > 0.f)) {
     t.lm = 1;
     t.cap = e.cap;
     t.aux = e.aux;
     t.lohi = e.lohi;
     t.NC = e.NC;
-    t.smp = e.smp;
     return launch_tall(t, p.tall, p.np, p.S, st);
   }
   // gate|up: gelu_tanh(gate) * up in the tiled kernel itself when its

@@ -293,7 +293,7 @@ __device__ __forceinline__ void epi_lm(const GemmArgs& g, const EpiArgs& e, cons
     for (int i = 0; i < 4; ++i) {
       const int r = t * 16 + 4 * gq + i, m = mbase + r;
       float z = acc[t][i];
-      if (e.cap > 0.f) z = e.cap * tanhf(z / e.cap);
+      if (e.cap > 0.f) z = e.cap * tanh_fast(z / e.cap);
       if (e.smp.temperature > 0.f) {
         // sampling: the walk and its bounds see z + T g (base z to the logits)
         const int mr = min(m, g.M - 1), row = mr / e.smp.gamma;

@@ -204,7 +204,6 @@ struct TallArgs {
   // stride act_plane) that a tiled down projection reads, instead of fp32
   uint16_t* act_planes;
   int64_t act_plane;
-  SampleArgs smp;     // lm: sampling noise (see SampleArgs)
 };
 
 // Tile order of the tiled GEMM: workgroups go round-robin over the 8 XCDs

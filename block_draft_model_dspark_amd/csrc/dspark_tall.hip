@@ -311,20 +311,9 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
           for (int j = 0; j < FN; ++j) {
             const int n = nc0 + 16 * j + ln;
             float z = acc[i][j][q];
-            if (t.cap > 0.f) z = t.cap * tanhf(z / t.cap);
+            if (t.cap > 0.f) z = t.cap * tanh_fast(z / t.cap);
             if (n < t.N) {
-              if (t.smp.temperature > 0.f) {
-                // sampling: the walk and its bounds see z + T g (base z to the logits)
-                const int mr = min(m, t.M - 1), row = mr / t.smp.gamma;
-                const float zs = z + t.smp.temperature * gumbel_noise(t.smp.seeds[row], mr - row * t.smp.gamma, n);
-                if (m < t.M) {
-                  if (t.smp.zs != T) T[(int64_t)m * t.ldt + n] = z;
-                  t.smp.zs[(int64_t)m * t.ldt + n] = zs;
-                }
-                z = zs;
-              } else if (m < t.M) {
-                T[(int64_t)m * t.ldt + n] = z;
-              }
+              if (m < t.M) T[(int64_t)m * t.ldt + n] = z;
               lo = fmaxf(lo, z - b[j]);
               hi = fmaxf(hi, z + b[j]);
             }

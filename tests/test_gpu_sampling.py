@@ -85,6 +85,24 @@ def test_sampling_full_size_a1(gpu_lib):
     assert check_sampled(case.om, ref["logits"], anchors, toks, 0.7, [2024]) >= 8
 
 
+def test_sampling_tiled_path(gpu_lib):
+    """Rows on the tiled GEMM path (threshold lowered to 16 rows): the 128 x 128
+    tiled lm_head leaves the noise to the separate logits epilogue."""
+    w0 = synth.WORKLOADS["full_bf16_a1"]
+    case = Case(w0.model, markov_active=True, with_fc=False)
+    case.gm.set_tall_rows(16)
+    lens = [0, 1, 37, 300, 700]
+    w = synth.Workload("sample_tiled", w0.model, rows=5, ctx_lens=tuple(lens))
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    seeds = [21, 22, 23, 24, 25]
+    toks, logits = _sample(case, k_rows, v_rows, lens, anchors, 1.0, seeds)
+    ref = O.draft_rows(case.om, o_rows, anchors, lens, temperature=1.0, seeds=seeds)
+    for a in range(5):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    assert check_sampled(case.om, ref["logits"], anchors, toks, 1.0, seeds) >= 40
+
+
 def test_sampling_refuses_bad_temperature(gpu_lib):
     w0 = synth.WORKLOADS["tiny_f32"]
     case = Case(w0.model, with_fc=False)
