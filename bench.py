@@ -38,17 +38,21 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "fb44c067f2d74d2def348e9d6f4b53a9141479a5cf6f16289cc99d6ad481079e",
-                  "bytes_per_step": 713350733},
+                  "sha256": "7a24e76fbb0afd8ab0e42825534e829695d59604bca32106710e5ac9617a2988",
+                  "bytes_per_step": 714371021},
+    # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
+    "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
+                     "sha256": "7a24e76fbb0afd8ab0e42825534e829695d59604bca32106710e5ac9617a2988",
+                     "bytes_per_launch": 70298195},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "346337f59d17af04f2bc511de9d8fdc2f7d2fddb9a20e37db1009271e81e0b36",
-                  "bytes_per_step": 387662976},
+                  "sha256": "4dc71ef091071fd890593555269dce6d0f72ce0fe51e8aae94d00dcab51bacce",
+                  "bytes_per_step": 387678259},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "d93481b5fd71a0b6dda0f3c5ea70d8633f8153bea0e1ecf9472421d6f4c18e41",
-                  "bytes_per_step": 2106370067},
+                  "sha256": "6d34e46aa8bb15100b564cd24b074e24740dfd34869a210edc420838d3ec869e",
+                  "bytes_per_step": 2101769773},
 }
 
 
@@ -68,7 +72,8 @@ def traffic(key):
     for f in t["sources"]:
         with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
-    return t["bytes_per_step"] if h.hexdigest() == t["sha256"] else None
+    n = t.get("bytes_per_step", t.get("bytes_per_launch"))
+    return n if h.hexdigest() == t["sha256"] else None
 
 
 def calibrate_copy(mib, reps):
