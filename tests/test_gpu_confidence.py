@@ -125,3 +125,26 @@ def test_confidence_full_size_a1(gpu_lib):
     assert _check(case, out, ref, anchors, 0.0, CONF_TOL["bf16"]) == 1
     out2, ref2 = _run(case, o_rows, k_rows, v_rows, [L], anchors, [0.9] * cfg.gamma)
     _check(case, out2, ref2, anchors, 0.9, CONF_TOL["bf16"])
+
+
+def test_confidence_with_sampling_tiny_f32(gpu_lib):
+    """The head scores the sampled tokens (its previous-token feature follows
+    the draws), and truncation applies to the sampled block."""
+    w0 = synth.WORKLOADS["tiny_f32"]
+    cfg = synth.scaled(w0.model, enable_confidence_head=True, confidence_head_with_markov=True,
+                       confidence_threshold=0.45)
+    lens = [32, 0, 7, 100]
+    w = synth.Workload("conf_sampled", cfg, rows=4, ctx_lens=tuple(lens))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    ctx = [O.decode(synth.ctx_hidden(w, a, L)) for a, L in enumerate(lens)]
+    o_rows, k_rows, v_rows = case.kv_rows_from_oracle(ctx, [0] * 4)
+    anchors = synth.anchors(w)
+    seeds = [5, 6, 7, 8]
+    thresholds = [0.45] * cfg.gamma
+    out = case.dsp.draft_rows_ex(case.gm, k_rows, v_rows, lens, anchors, lens, thresholds=thresholds,
+                                 collect_logits=True, collect_conf=True, lengths=True, temperature=0.9,
+                                 seeds=seeds)
+    ref = O.draft_rows(case.om, o_rows, anchors, lens, thresholds=thresholds, temperature=0.9, seeds=seeds)
+    greedy = case.dsp.draft_rows(case.gm, k_rows, v_rows, lens, anchors, lens)[0].cpu().numpy()
+    assert (out["tokens"].cpu().numpy() != greedy).sum() >= 4  # the draws differ from the greedy walk
+    assert _check(case, out, ref, anchors, thresholds, CONF_TOL["f32"]) >= 3

@@ -474,3 +474,24 @@ def test_draft_block_matches_draft_rows(gpu_lib):
     tr, zr = case.dsp.draft_rows(case.gm, k_rows, v_rows, [L], [anchor], [L], collect_logits=True)
     torch.cuda.synchronize()
     assert torch.equal(tb, tr[0]) and torch.equal(zb, zr[0])
+
+
+@pytest.mark.parametrize("wname", ["tiny_f32", "full_bf16_a1"])
+def test_walk_per_step_path(gpu_lib, wname):
+    """Markov tables large enough (std 3) that every entry survives the walk's
+    bound test: the walk leaves its candidate table for the per-step path,
+    which scores every surviving entry against the actual previous token."""
+    import torch
+    w0 = synth.WORKLOADS[wname]
+    cfg = w0.model
+    ov = {"markov_head.markov_w1.weight": 3.0, "markov_head.markov_w2.weight": 3.0}
+    case = Case(cfg, markov_active=True, with_fc=False, overrides=ov)
+    lens = [w0.fixed_ctx_len, 5]
+    w = synth.Workload("per_step", cfg, rows=2, ctx_lens=tuple(lens))
+    o_rows, k_rows, v_rows = case.kv_rows_from_oracle([_ctx(w, a, L) for a, L in enumerate(lens)], [0, 0])
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(2):
+        assert rel_err(logits[a], ref["logits"][a]) <= _tol(cfg), a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= cfg.gamma
