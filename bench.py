@@ -525,7 +525,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: the draft round is not sharded across GPUs in this build "
+        print("bench.py measures one GPU: the draft round is not sharded across GPUs by this library "
               "(rows would split across GPUs with no exchange); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

@@ -515,7 +515,7 @@ dspark_status check_config(const dspark_config& c) {
   // The first GPU run of a 4-bit round faulted and no cause has been shown
   // yet; the path stays switched off until one is.
   if (c.weight_dtype == DSPARK_Q4)
-    return fail(DSPARK_ERR_UNSUPPORTED, "4-bit weights are disabled in this build (GPU fault under analysis)");
+    return fail(DSPARK_ERR_UNSUPPORTED, "4-bit weights are disabled in this library version (an unexplained GPU fault)");
   return DSPARK_OK;
 }
 
