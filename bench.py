@@ -38,20 +38,20 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "7a24e76fbb0afd8ab0e42825534e829695d59604bca32106710e5ac9617a2988",
+                  "sha256": "e8657c796f61060be6f03e8b0206a3fcd37729289899d9bb31f908c26cdbcd94",
                   "bytes_per_step": 714371021},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "7a24e76fbb0afd8ab0e42825534e829695d59604bca32106710e5ac9617a2988",
+                     "sha256": "e8657c796f61060be6f03e8b0206a3fcd37729289899d9bb31f908c26cdbcd94",
                      "bytes_per_launch": 70298195},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "4dc71ef091071fd890593555269dce6d0f72ce0fe51e8aae94d00dcab51bacce",
+                  "sha256": "4da9ece3c2139ff7cb9dd6b97d4907b36b76ebe4c0e9837da05e0563d17ccb6d",
                   "bytes_per_step": 387678259},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "6d34e46aa8bb15100b564cd24b074e24740dfd34869a210edc420838d3ec869e",
+                  "sha256": "a8fb8bf2d53b1ce00e1713f95da1118b2a2ab62f59393b924a5812d9359bf7ce",
                   "bytes_per_step": 2101769773},
 }
 
