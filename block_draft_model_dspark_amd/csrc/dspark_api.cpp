@@ -210,6 +210,11 @@ struct TallBufs {
   float* T = nullptr;
 };
 
+// a weight-streaming context projection that leaves its K/V epilogue to a
+// separate launch (no split K, head groups k_kv_epi takes): it needs no
+// reduction counters
+bool kv_deferred(const GemmPlan& p) { return p.tall == TALL_NONE && p.S == 1; }
+
 // gate|up whose tiles form gelu_tanh(gate) * up themselves (tiled path)
 bool fused_gelu(const GemmPlan& p, int64_t N) { return p.tall == TALL_128 && p.S == 1 && p.np == 2 && N % 128 == 0; }
 
@@ -219,6 +224,15 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
                     const TallBufs& tb = TallBufs{}, bool x_planes = false) {
   a.kslice = p.kslice;
   a.kc = p.kc;
+  if (p.tall == TALL_NONE && epi == EPI_KV && kv_deferred(p)) {
+    // the context projection without split K: product to Y, then the
+    // norms and RoPE in their own launch
+    EpiArgs ed = e;
+    ed.kv_defer = 1;
+    const hipError_t r = launch_gemm(a, ed, epi, wk, p.xmode, p.mt, p.S, st);
+    if (r != hipSuccess) return r;
+    return launch_gemm_epi(a, ed, EPI_KV, nullptr, 0, 1, 0, st);
+  }
   if (p.tall == TALL_NONE) return launch_gemm(a, e, epi, wk, p.xmode, p.mt, p.S, st);
   TallArgs t{};
   if (p.xmode == XM_BF16) {
@@ -959,8 +973,17 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   // reduction counters, zeroed here: the workspace may hold other data (a
   // call of another input kind or shape lays it out differently)
   unsigned* cnt = (unsigned*)(ws + p.cnt);
-  HIPCHECK(timed("zero_counters", stream, [&] { return launch_zero(cnt, (int64_t)p.cwords, stream); }));
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
+  // counters are used by fc's split-K reduction and by a context projection
+  // that splits K or runs its K/V epilogue in the last-arriving workgroup
+  bool need_cnt = feats;
+  for (int l0 = 0; l0 < c.num_hidden_layers; l0 += p.lay_per_gemm) {
+    const int nl = std::min(p.lay_per_gemm, c.num_hidden_layers - l0);
+    const GemmPlan gp = nl == p.lay_per_gemm ? p.kp : plan_gemm(c.weight_dtype, p.kp.xmode, M, nl * nKv * hd, H, hd,
+                                                                 m->tall_rows);
+    if (gp.tall == TALL_NONE && !kv_deferred(gp)) need_cnt = true;
+  }
+  if (need_cnt) HIPCHECK(timed("zero_counters", stream, [&] { return launch_zero(cnt, (int64_t)p.cwords, stream); }));
   TallBufs tb;
   tb.xop = (uint16_t*)(ws + p.xop);
   tb.T = (float*)(ws + p.T);

@@ -360,9 +360,11 @@ __device__ __forceinline__ void epi_gelu(const GemmArgs& g, const EpiArgs& e, co
 // [m0, m1) of the row block: V = rms(k) (no weight, no RoPE);
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
 // rows is issued before the first use.
-template <int MT, int NT>
+// RINV: the caller has not formed rinv yet; it is formed here while the
+// loads are in flight.
+template <int MT, int NT, bool RINV = false>
 __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp,
-                                       const double* rinv, float2* rcs) {
+                                       double* rinv, float2* rcs) {
   // one wave per four rows of the tile
   static_assert(MT * 16 == 4 * (NT / 64), "the K/V epilogue gives each wave four rows");
   const int tid = threadIdx.x, lane = tid & 63;
@@ -396,6 +398,10 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
   // 2. while they are in flight: (cos, sin) of the tile's row positions and
   //    pairs.  The rows span batch rows b_first..b_last, whose starting
   //    positions are read with uniform (scalar) loads.
+  if constexpr (RINV) {
+    if (tid < half) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
+    __syncthreads();
+  }
   const int b_first = m0 / e.L, b_last = (m1 - 1) / e.L;
   for (int idx = tid; idx < MT * 16 * half; idx += NT) {
     const int r = idx / half, pr = idx - r * half;
@@ -991,6 +997,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] += *(const f32x4*)&ep[(t * 256 + vt) * 4];
     }
+    if (e.kv_defer) {
+      // the separate epilogue launch reads Y after this kernel has ended
+      if (half == 0)
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = mbase + t * 16 + 4 * gq + i;
+            if (m < g.M) e.Y[(int64_t)m * g.N + n] = acc[t][i];
+          }
+      return;
+    }
     if (half == 0)
 #pragma unroll
       for (int t = 0; t < MT; ++t)
@@ -1041,10 +1059,8 @@ __global__ __launch_bounds__(256) void k_gemm_epi(const GemmArgs g, const EpiArg
 __global__ __launch_bounds__(256) void k_kv_epi(const GemmArgs g, const EpiArgs e) {
   __shared__ double rinv[128];
   __shared__ float2 rcs[16 * 128];
-  if ((int)threadIdx.x < (e.hd >> 1)) rinv[threadIdx.x] = rope_inv(threadIdx.x, e.rope.hd, e.rope.theta, e.rope.nrot);
-  __syncthreads();
   const int mbase = blockIdx.y * 16;
-  epi_kv<1, 256>(g, e, mbase, min(g.M, mbase + 16), blockIdx.x, rinv, rcs);
+  epi_kv<1, 256, true>(g, e, mbase, min(g.M, mbase + 16), blockIdx.x, rinv, rcs);
 }
 
 hipError_t launch_gemm_epi(const GemmArgs& a, const EpiArgs& e, int epi, const float* T, int64_t ldt, int S,

@@ -155,6 +155,10 @@ struct EpiArgs {
   int pos0[MAX_ROWS];
   const void* kn_l[MAX_SEG];
   void* kout[MAX_SEG]; void* vout[MAX_SEG];  // [B, nKv, L, hd] act dtype
+  // EPI_KV on the weight-streaming kernel without split K: store the product
+  // to Y and leave the norms and RoPE to a separate k_kv_epi launch (no
+  // cross-workgroup arrival, so no counters)
+  int kv_defer;
   // EPI_GELU
   float* act;         // [M, N/2], row pitch ld_act
   int64_t ld_act;
