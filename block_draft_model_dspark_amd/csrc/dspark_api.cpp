@@ -220,8 +220,11 @@ bool fused_gelu(const GemmPlan& p, int64_t N) { return p.tall == TALL_128 && p.S
 
 // x_planes: the tiled path's input planes are already in tb.xop (the
 // attention merge or the fused gate|up wrote them), so no input preparation runs
+// next: on the tiled path, a split-K EPI_SUMS epilogue that also forms the
+// next GEMM's input planes (k_sums_prep) instead of the product's row
+// statistics (its T, S, M and K are filled in here)
 hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, int wk, hipStream_t st,
-                    const TallBufs& tb = TallBufs{}, bool x_planes = false) {
+                    const TallBufs& tb = TallBufs{}, bool x_planes = false, const SumsPrepArgs* next = nullptr) {
   a.kslice = p.kslice;
   a.kc = p.kc;
   if (p.tall == TALL_NONE && epi == EPI_KV && kv_deferred(p)) {
@@ -300,6 +303,16 @@ hipError_t run_gemm(const GemmPlan& p, GemmArgs a, const EpiArgs& e, int epi, in
   }
   hipError_t r = launch_tall(t, p.tall, p.np, p.S, st);
   if (r != hipSuccess) return r;
+  if (epi == EPI_SUMS && next) {
+    SumsPrepArgs sp = *next;
+    sp.T = t.T;
+    sp.ldt = t.ldt;
+    sp.tstride = t.tstride;
+    sp.S = p.S;
+    sp.M = a.M;
+    sp.K = a.N;
+    return launch_sums_prep(sp, st);
+  }
   return launch_gemm_epi(a, e, epi, t.T, t.ldt, p.S, t.tstride, st);
 }
 
@@ -1274,6 +1287,24 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   // The residual stream is formed lazily: a sublayer output y stays in Y
   // with its row statistics, and the next GEMM's staging adds it to the
   // residual it read and writes the sum (q|k writes hB, gate|up writes hA).
+  // the tiled o and down projections form the next GEMM's input planes in
+  // their epilogue when that GEMM is tiled too (no separate preparation)
+  auto sums_next = [&](const float* h, const void* w1, const float* sc, const void* w2, float* hout) {
+    SumsPrepArgs sp{};
+    sp.h = h;
+    sp.ldh = d.ldh;
+    sp.w1 = w1;
+    sp.sc = sc;
+    sp.w2 = w2;
+    sp.act_bf16 = abf;
+    sp.eps = eps;
+    sp.hout = hout;
+    sp.xop = tb.xop;
+    sp.plane = (int64_t)M * H;
+    return sp;
+  };
+  const bool fuse_prep = H <= SP_KMAX && H % 8 == 0;
+  bool planes_ready = false;  // the next GEMM's input planes are already in tb.xop
   const float* y_prev = nullptr;  // pending sublayer output folded into the next input norm
   const void* w1_prev = nullptr;
   const float* sc_prev = scal;
@@ -1291,7 +1322,8 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     g.nin = norm_in(hA, y_prev, w1_prev, sc_prev, W.in, hB);
     e.qn = W.qn;
     e.kn = W.kn;
-    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream, tb); }));
+    HIPCHECK(timed("gemm.qk", stream, [&] { return run_gemm(d.qk, g, e, EPI_QK, wk, stream, tb, planes_ready); }));
+    planes_ready = false;
 
     for (int a = 0; a < A; ++a) {
       at.row[a].k = vonly ? nullptr : k_ctx_dev[l * A + a];
@@ -1316,7 +1348,11 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     e.Y = Y;
     e.h = hB;
     e.w1 = W.pa;
-    HIPCHECK(timed("gemm.o", stream, [&] { return run_gemm(d.o, g, e, EPI_SUMS, wk, stream, tb, o_planes); }));
+    const bool fuse_o = fuse_prep && d.o.tall != TALL_NONE && d.gu.tall != TALL_NONE;
+    const SumsPrepArgs nx_o = sums_next(hB, W.pa, scal, W.pf, hA);
+    HIPCHECK(timed("gemm.o", stream, [&] {
+      return run_gemm(d.o, g, e, EPI_SUMS, wk, stream, tb, o_planes, fuse_o ? &nx_o : nullptr);
+    }));
 
     g = GemmArgs{};
     g.ldx = H;
@@ -1332,7 +1368,7 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
       e.act_planes = (uint16_t*)(ws + d.xop2);
       e.act_plane = (int64_t)M * I;
     }
-    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream, tb); }));
+    HIPCHECK(timed("gemm.gate_up", stream, [&] { return run_gemm(d.gu, g, e, EPI_GELU, wk, stream, tb, fuse_o); }));
 
     g = GemmArgs{};
     g.X = act;
@@ -1348,7 +1384,17 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     e.w1 = W.pff;
     TallBufs tb_dn = tb;
     if (d.dn_planes) tb_dn.xop = (uint16_t*)(ws + d.xop2);
-    HIPCHECK(timed("gemm.down", stream, [&] { return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream, tb_dn, d.dn_planes); }));
+    // the next GEMM: the next layer's q|k, or lm_head (whose hn rows feed
+    // the confidence head)
+    const bool last = l + 1 == nL;
+    const bool fuse_d = fuse_prep && d.dn.tall != TALL_NONE && (last ? d.lm.tall : d.qk.tall) != TALL_NONE &&
+                        (!d.dn_planes || tb_dn.xop != tb.xop);
+    const SumsPrepArgs nx_d = sums_next(hA, W.pff, scal + 1 + l, last ? m->norm : m->L[l + 1].in,
+                                        last ? (need_conf ? hB : nullptr) : hB);
+    HIPCHECK(timed("gemm.down", stream, [&] {
+      return run_gemm(d.dn, g, e, EPI_SUMS, wk, stream, tb_dn, d.dn_planes, fuse_d ? &nx_d : nullptr);
+    }));
+    planes_ready = fuse_d;
     y_prev = Y;
     w1_prev = W.pff;
     sc_prev = scal + 1 + l;
@@ -1376,7 +1422,7 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
     e.smp.zs = (float*)(ws + d.z);
     for (int a = 0; a < A; ++a) e.smp.seeds[a] = seeds_host ? seeds_host[a] : 0ull;
   }
-  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream, tb); }));
+  HIPCHECK(timed("gemm.lm_head", stream, [&] { return run_gemm(d.lm, g, e, EPI_LM, wk, stream, tb, planes_ready); }));
 
   WalkArgs w{};
   w.rows = rows;

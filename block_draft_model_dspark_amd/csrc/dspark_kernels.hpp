@@ -356,6 +356,29 @@ hipError_t launch_gemm(const GemmArgs& a, const EpiArgs& e, int epi, int wkind, 
 size_t gemm_lds_bytes(int wkind, int xmode, int mt, int kc);
 size_t gemm_counter_words(int M, int N, int mt, int group_cols);
 hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t plane, hipStream_t st);
+// The split-K epilogue of a tiled o or down projection fused with the next
+// GEMM's input preparation, one workgroup per row: y = sum of the S partial
+// products, hn = (h + rms(y) w1 y) sc (written to hout when given), and the
+// next GEMM's input x = rms(hn) w2 (x = hn without w2) as bf16 hi / lo planes.
+// The whole row is in the workgroup, so both RMS factors come from direct
+// fp64 sums of y^2 and hn^2.
+constexpr int SP_KMAX = 8192;  // row width (a multiple of 8)
+struct SumsPrepArgs {
+  const float* T;     // partial products [S][M][ldt] (slice stride tstride)
+  int64_t ldt, tstride;
+  int S, M, K;
+  const float* h;     // [M, ldh] residual
+  int64_t ldh;
+  const void* w1;     // [K] act dtype: norm weight of y
+  const float* sc;    // [1] residual scale, or null: 1
+  const void* w2;     // [K] act dtype: the next input norm weight, or null
+  int act_bf16;
+  float eps;
+  float* hout;        // [M, ldh] hn rows, or null
+  uint16_t* xop;      // [2][M, K] bf16 hi / lo planes (plane stride `plane`)
+  int64_t plane;
+};
+hipError_t launch_sums_prep(const SumsPrepArgs& a, hipStream_t st);
 hipError_t launch_tall(const TallArgs& t, int tile, int np, int S, hipStream_t st);
 // the epilogue of a GEMM whose product is the sum of S partial planes in T
 // (row pitch ldt, plane stride tstride); EPI_KV reads it from e.Y (pitch N,

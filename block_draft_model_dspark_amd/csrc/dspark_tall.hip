@@ -116,6 +116,98 @@ __global__ __launch_bounds__(256) void k_xprep(const GemmArgs g, uint16_t* xop, 
 }
 
 // ---------------------------------------------------------------------------
+// 1b. split-K epilogue of o / down fused with the next input preparation
+//     (deepspec.ts, #forwardBackbone sandwich norms): one workgroup per row,
+//     eight columns per thread and item
+// ---------------------------------------------------------------------------
+constexpr int SP_IT = SP_KMAX / 8 / 256;  // items per thread
+
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum_d(v);
+  __syncthreads();  // the previous use of red is complete
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void k_sums_prep(const SumsPrepArgs a) {
+  __shared__ double red[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const int nk8 = a.K >> 3;
+  const bool bf = a.act_bf16 != 0;
+  float y[SP_IT][8], hn[SP_IT][8];
+  // 1. y = sum of the slices, and sum y^2
+  double syy = 0.0;
+#pragma unroll
+  for (int it = 0; it < SP_IT; ++it) {
+    const int k = 8 * (tid + 256 * it);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) y[it][q] = 0.f;
+    if (k < a.K) {
+      const float* tp = a.T + (int64_t)m * a.ldt + k;
+      for (int s = 0; s < a.S; ++s) {
+        const f32x4 p0 = *(const f32x4*)(tp + s * a.tstride), p1 = *(const f32x4*)(tp + s * a.tstride + 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          y[it][q] += p0[q];
+          y[it][4 + q] += p1[q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) syy += (double)y[it][q] * y[it][q];
+    }
+  }
+  const float r1 = (float)(1.0 / sqrt(block_sum_d(syy, red) / a.K + (double)a.eps));
+  const float sc = a.sc ? *a.sc : 1.f;
+  // 2. hn = (h + r1 w1 y) sc, and sum hn^2
+  double shh = 0.0;
+#pragma unroll
+  for (int it = 0; it < SP_IT; ++it) {
+    const int k = 8 * (tid + 256 * it);
+    if (k < a.K) {
+      float w1[8];
+      cvt_act8(ld_act8(a.w1, k, bf), bf, w1);
+      const float* hp = a.h + (int64_t)m * a.ldh + k;
+      const f32x4 h0 = *(const f32x4*)hp, h1 = *(const f32x4*)(hp + 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const float hv = q < 4 ? h0[q] : h1[q - 4];
+        hn[it][q] = (hv + y[it][q] * r1 * w1[q]) * sc;
+        shh += (double)hn[it][q] * hn[it][q];
+      }
+      if (a.hout) {
+        float* dst = a.hout + (int64_t)m * a.ldh + k;
+        *(f32x4*)dst = f32x4{hn[it][0], hn[it][1], hn[it][2], hn[it][3]};
+        *(f32x4*)(dst + 4) = f32x4{hn[it][4], hn[it][5], hn[it][6], hn[it][7]};
+      }
+    }
+  }
+  const float r2 = (float)(1.0 / sqrt(block_sum_d(shh, red) / a.K + (double)a.eps));
+  // 3. x = hn r2 w2 as hi / lo planes
+#pragma unroll
+  for (int it = 0; it < SP_IT; ++it) {
+    const int k = 8 * (tid + 256 * it);
+    if (k < a.K) {
+      float v[8];
+      if (a.w2) {
+        float w2[8];
+        cvt_act8(ld_act8(a.w2, k, bf), bf, w2);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = hn[it][q] * r2 * w2[q];
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = hn[it][q];
+      }
+      bf16x8 hi, lo;
+      split8(v, hi, lo);
+      *(u32x4*)(a.xop + (int64_t)m * a.K + k) = __builtin_bit_cast(u32x4, hi);
+      *(u32x4*)(a.xop + a.plane + (int64_t)m * a.K + k) = __builtin_bit_cast(u32x4, lo);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 2. T = sum_p X_p W^T, BM x BN tiles, K steps of 64
 // ---------------------------------------------------------------------------
 constexpr int TBK = 64;        // K step
@@ -347,6 +439,13 @@ hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t pla
   } else {
     return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_sums_prep(const SumsPrepArgs& a, hipStream_t st) {
+  if (a.K <= 0 || a.K > SP_KMAX || a.K % 8 != 0 || a.S < 1 || a.M < 1 || !a.T || !a.h || !a.w1 || !a.xop)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sums_prep, dim3(a.M), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 
