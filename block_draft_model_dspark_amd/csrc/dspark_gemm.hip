@@ -360,9 +360,9 @@ __device__ __forceinline__ void epi_gelu(const GemmArgs& g, const EpiArgs& e, co
 // [m0, m1) of the row block: V = rms(k) (no weight, no RoPE);
 // K = RoPE(rms(k) * k_norm).  One wave per row; every load of a batch of
 // rows is issued before the first use.
-// RINV: the caller has not formed rinv yet; it is formed here while the
-// loads are in flight.
-template <int MT, int NT, bool RINV = false>
+// SEP: a launch of its own (k_kv_epi): Y was written by an earlier kernel,
+// so plain loads read it, and rinv is formed here while they are in flight.
+template <int MT, int NT, bool SEP = false>
 __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int m0, int m1, int grp,
                                        double* rinv, float2* rcs) {
   // one wave per four rows of the tile
@@ -392,13 +392,13 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int d = min(lane + 64 * j, hd - 1);
-      y[rr][j] = ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d);
+      y[rr][j] = SEP ? e.Y[(int64_t)m * g.N + grp * hd + d] : ld_coh(e.Y + (int64_t)m * g.N + grp * hd + d);
     }
   }
   // 2. while they are in flight: (cos, sin) of the tile's row positions and
   //    pairs.  The rows span batch rows b_first..b_last, whose starting
   //    positions are read with uniform (scalar) loads.
-  if constexpr (RINV) {
+  if constexpr (SEP) {
     if (tid < half) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
     __syncthreads();
   }

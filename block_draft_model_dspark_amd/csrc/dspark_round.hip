@@ -33,12 +33,23 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   if (m == 0 && tid <= a.nL) a.scal[tid] = tid == 0 ? 1.f : ld_act(a.scal_src[tid - 1], 0, a.act_bf16);
   const int row = m / a.rows.gamma, g = m - row * a.rows.gamma;
   const int64_t id = g == 0 ? a.rows.anchor[row] : a.mask_id;
+  // the first eight bf16 values of this thread are loaded before the RoPE
+  // table is formed, so the table's arithmetic overlaps the load
+  u32x4 w_first = u32x4{0u, 0u, 0u, 0u};
+  if (a.ekind == WK_BF16) w_first = *(const u32x4*)((const uint16_t*)a.E + id * a.H + min(8 * tid, a.H - 8));
+  const int half = a.rope.hd >> 1;
+  const int64_t pos = (int64_t)a.rows.pos[row] + g;
+  for (int d = tid; d < half; d += 256) {
+    float c, s;
+    rope_cs(pos, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
+    a.rt[(int64_t)m * half + d] = make_float2(c, s);
+  }
   for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
     float v[8];
     double ss = 0.0;
     if (a.ekind == WK_BF16) {
       // one 16-byte load of the eight bf16 values
-      const u32x4 w = *(const u32x4*)((const uint16_t*)a.E + id * a.H + k0);
+      const u32x4 w = k0 == 8 * tid ? w_first : *(const u32x4*)((const uint16_t*)a.E + id * a.H + k0);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         v[2 * q] = __uint_as_float(w[q] << 16);
@@ -61,13 +72,6 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
     ss += __shfl_xor(ss, 2);
     ss += __shfl_xor(ss, 4);
     if ((tid & 7) == 0) a.sums[(int64_t)(k0 >> 6) * M + m] = RowStats{0.0, 0.0, 0.0, ss};
-  }
-  const int half = a.rope.hd >> 1;
-  const int64_t pos = (int64_t)a.rows.pos[row] + g;
-  for (int d = tid; d < half; d += 256) {
-    float c, s;
-    rope_cs(pos, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
-    a.rt[(int64_t)m * half + d] = make_float2(c, s);
   }
 }
 
