@@ -989,7 +989,7 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   const bool feats = input_kind == DSPARK_INPUT_TARGET_FEATURES;
   // counters are used by fc's split-K reduction and by a context projection
   // that splits K or runs its K/V epilogue in the last-arriving workgroup
-  bool need_cnt = feats;
+  bool need_cnt = feats && p.fc.tall == TALL_NONE;
   for (int l0 = 0; l0 < c.num_hidden_layers; l0 += p.lay_per_gemm) {
     const int nl = std::min(p.lay_per_gemm, c.num_hidden_layers - l0);
     const GemmPlan gp = nl == p.lay_per_gemm ? p.kp : plan_gemm(c.weight_dtype, p.kp.xmode, M, nl * nKv * hd, H, hd,
@@ -1001,6 +1001,14 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
   tb.xop = (uint16_t*)(ws + p.xop);
   tb.T = (float*)(ws + p.T);
   NormIn nin{};
+  bool fc_planes = false;  // k_proj's input planes written by fc's epilogue
+  bool kp_all_planes = true;  // every k_proj launch reads hi / lo planes on the tiled path
+  for (int l0 = 0; l0 < c.num_hidden_layers; l0 += p.lay_per_gemm) {
+    const int nl = std::min(p.lay_per_gemm, c.num_hidden_layers - l0);
+    const GemmPlan gp = nl == p.lay_per_gemm ? p.kp : plan_gemm(c.weight_dtype, p.kp.xmode, M, nl * nKv * hd, H, hd,
+                                                                 m->tall_rows);
+    if (gp.tall == TALL_NONE || gp.np != 2) kp_all_planes = false;
+  }
   if (feats) {
     // fc rows and their statistics; k_proj reads hidden_norm(fc x)
     GemmArgs g{};
@@ -1020,7 +1028,18 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
     e.ldy = H;
     e.w1 = m->hidden_norm;
     e.sums = (RowStats*)(ws + p.sums);
-    HIPCHECK(timed("gemm.fc", stream, [&] { return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream, tb); }));
+    // both GEMMs tiled: fc's epilogue forms k_proj's input planes,
+    // hidden_norm(fc x), itself (no statistics pass, no input preparation)
+    SumsPrepArgs sp{};
+    sp.w1 = m->hidden_norm;
+    sp.act_bf16 = act_bf16(m);
+    sp.eps = (float)c.rms_norm_eps;
+    sp.xop = tb.xop;
+    sp.plane = (int64_t)M * H;
+    fc_planes = p.fc.tall != TALL_NONE && kp_all_planes && H <= SP_KMAX && H % 8 == 0;
+    HIPCHECK(timed("gemm.fc", stream, [&] {
+      return run_gemm(p.fc, g, e, EPI_SUMS, m->fc.kind, stream, tb, false, fc_planes ? &sp : nullptr);
+    }));
     nin.y = e.Y;
     nin.sums = e.sums;
     nin.ld = H;
@@ -1061,7 +1080,9 @@ dspark_status dspark_project_context_kv(const dspark_model* m, int input_kind, c
       e.kout[i] = k_out_dev ? k_out_dev[l0 + i] : nullptr;  // null: V-only cache
       e.vout[i] = v_out_dev[l0 + i];
     }
-    HIPCHECK(timed("gemm.k_proj", stream, [&] { return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream, tb); }));
+    HIPCHECK(timed("gemm.k_proj", stream, [&] {
+      return run_gemm(gp, g, e, EPI_KV, m->L[l0].k.kind, stream, tb, fc_planes);
+    }));
   }
   return DSPARK_OK;
 }

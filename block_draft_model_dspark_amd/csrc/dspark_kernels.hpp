@@ -367,7 +367,7 @@ struct SumsPrepArgs {
   const float* T;     // partial products [S][M][ldt] (slice stride tstride)
   int64_t ldt, tstride;
   int S, M, K;
-  const float* h;     // [M, ldh] residual
+  const float* h;     // [M, ldh] residual, or null (zero)
   int64_t ldh;
   const void* w1;     // [K] act dtype: norm weight of y
   const float* sc;    // [1] residual scale, or null: 1

@@ -168,8 +168,12 @@ __global__ __launch_bounds__(256) void k_sums_prep(const SumsPrepArgs a) {
     if (k < a.K) {
       float w1[8];
       cvt_act8(ld_act8(a.w1, k, bf), bf, w1);
-      const float* hp = a.h + (int64_t)m * a.ldh + k;
-      const f32x4 h0 = *(const f32x4*)hp, h1 = *(const f32x4*)(hp + 4);
+      f32x4 h0 = f32x4{0.f, 0.f, 0.f, 0.f}, h1 = h0;
+      if (a.h) {
+        const float* hp = a.h + (int64_t)m * a.ldh + k;
+        h0 = *(const f32x4*)hp;
+        h1 = *(const f32x4*)(hp + 4);
+      }
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const float hv = q < 4 ? h0[q] : h1[q - 4];
@@ -443,7 +447,7 @@ hipError_t launch_xprep(const GemmArgs& g, int xmode, uint16_t* xop, int64_t pla
 }
 
 hipError_t launch_sums_prep(const SumsPrepArgs& a, hipStream_t st) {
-  if (a.K <= 0 || a.K > SP_KMAX || a.K % 8 != 0 || a.S < 1 || a.M < 1 || !a.T || !a.h || !a.w1 || !a.xop)
+  if (a.K <= 0 || a.K > SP_KMAX || a.K % 8 != 0 || a.S < 1 || a.M < 1 || !a.T || !a.w1 || !a.xop)
     return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_sums_prep, dim3(a.M), dim3(256), 0, st, a);
   return hipGetLastError();
