@@ -38,21 +38,21 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "e8657c796f61060be6f03e8b0206a3fcd37729289899d9bb31f908c26cdbcd94",
-                  "bytes_per_step": 714371021},
+                  "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
+                  "bytes_per_step": 710093210},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "e8657c796f61060be6f03e8b0206a3fcd37729289899d9bb31f908c26cdbcd94",
-                     "bytes_per_launch": 70298195},
+                     "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
+                     "bytes_per_launch": 70296531},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "4da9ece3c2139ff7cb9dd6b97d4907b36b76ebe4c0e9837da05e0563d17ccb6d",
-                  "bytes_per_step": 387678259},
+                  "sha256": "9556050ec859c673eb3e21831f5aa593bb6a312df8ab1ac0990b1bc3e9577672",
+                  "bytes_per_step": 387674189},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "a8fb8bf2d53b1ce00e1713f95da1118b2a2ab62f59393b924a5812d9359bf7ce",
-                  "bytes_per_step": 2101769773},
+                  "sha256": "4fefc5324ed9de73ab75fa473b5f65cdfed5a233fa8b5f89b367ab8c147a6f50",
+                  "bytes_per_step": 2106861773},
 }
 
 
