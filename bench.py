@@ -357,7 +357,8 @@ def bench_prefill(args, dsp, synth, torch, sh):
         "config": {"workload": "prefill_8192: B=1, L=8192 rows of 3x2560 target features, fc 7680->2048, "
                                "hidden_norm, k_proj + k/v norms + RoPE for 4 layers (1 kv head x 256), offset 0",
                    "rows": M, "step": "one dspark_project_context_kv call over all 8192 rows"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm fc role (7680->2048 over 8192 rows)",
+        "roofline": {"bound": "mfma", "kernel": "k_tall fc role (7680->2048 over 8192 rows; tiled bf16 MFMA GEMM, "
+                                                "timed with its epilogue launch)",
                      "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_launch": flops["gemm.fc"], "us_per_launch": round(fc_us, 2)},
@@ -410,7 +411,8 @@ def bench_rows(args, dsp, synth, torch, sh, vonly=False):
                    "rows": A, "gamma": cfg.gamma, "ctx_lens_sum": sum(lens),
                    "step": "one dspark_draft_rows call",
                    "tokens_per_s": round(value * cfg.gamma, 1)},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm (bf16 MFMA GEMM, all roles over 512 block rows)",
+        "roofline": {"bound": "mfma", "kernel": "k_tall (tiled bf16 MFMA GEMM, all roles over 512 block rows, "
+                                                "timed with their epilogue and input launches)",
                      "achieved": round(g_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic("tall_rows"),
                      "flops_per_step": fl, "us_per_step": round(1e3 * g_ms, 2)},
