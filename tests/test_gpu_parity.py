@@ -385,6 +385,42 @@ def test_tiled_path_projection_small_ragged(gpu_lib, kind):
         assert rel_err(vs[li].float().cpu().numpy(), vs0[li].float().cpu().numpy()) <= 1e-2, li
 
 
+@pytest.mark.parametrize("hidden", [1024, 3072])
+def test_tiled_path_row_widths(gpu_lib, hidden):
+    """The row-owning split-K epilogue (o and down forming the next GEMM's
+    residual and input planes; fc forming k_proj's hidden_norm input) at row
+    widths other than 2048: 1024 leaves half of each workgroup's threads
+    without columns, 3072 gives some threads two items.  One layer on the
+    tiled path (threshold 1 row), 2 ragged rows, an active Markov head, and
+    the target-feature projection of 2 x 70 rows."""
+    import torch
+    cfg = synth.scaled(synth.FULL, hidden_size=hidden, num_hidden_layers=1, intermediate_size=4096,
+                       vocab_size=1024, mask_token_id=1023)
+    w = synth.Workload(f"tall_h{hidden}", cfg, rows=2, ctx_lens=(150, 33))
+    case = Case(cfg, markov_active=True, with_fc=True)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    wp = synth.Workload(f"pf_h{hidden}", cfg, rows=0, prefill_rows=70, prefill_batch=2)
+    st = synth.target_features(wp)
+    try:
+        case.gm.set_tall_rows(1)
+        toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+        ks, vs = gpu_lib.project_context_kv(case.gm, gpu_lib.act_tensor(st), [0, 9],
+                                            input_kind=gpu_lib.INPUT_TARGET_FEATURES)
+        torch.cuda.synchronize()
+    finally:
+        case.gm.set_tall_rows(256)
+    for a in range(2):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 16
+    kv = O.project_context_kv(case.om, O.project_context(case.om, O.decode(st)), [0, 9])
+    for li, (K, V) in enumerate(kv):
+        assert rel_err(ks[li].float().cpu().numpy(), K) <= 2e-2, li
+        assert rel_err(vs[li].float().cpu().numpy(), V) <= 2e-2, li
+
+
 @pytest.mark.skip(reason="4-bit path switched off: its first GPU run faulted (memory aperture violation) "
                   "and no cause has been shown yet; the library returns DSPARK_ERR_UNSUPPORTED for it")
 def test_q4_small(gpu_lib):
