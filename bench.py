@@ -39,20 +39,20 @@ TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
-                  "bytes_per_step": 710093210},
+                  "bytes_per_step": 710093440},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                      "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
-                     "bytes_per_launch": 70296531},
+                     "bytes_per_launch": 70296640},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "9556050ec859c673eb3e21831f5aa593bb6a312df8ab1ac0990b1bc3e9577672",
-                  "bytes_per_step": 387674189},
+                  "bytes_per_step": 387674880},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "4fefc5324ed9de73ab75fa473b5f65cdfed5a233fa8b5f89b367ab8c147a6f50",
-                  "bytes_per_step": 2106861773},
+                  "sha256": "6ae78dbdd3a773df635ff664ad5f3cfcee7430ae23e53b59865730ce8a59f5b2",
+                  "bytes_per_step": 2108220205},
 }
 
 
