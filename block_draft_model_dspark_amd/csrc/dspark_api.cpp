@@ -68,8 +68,11 @@ hipEvent_t prof_event() {
     g_event_pool.pop_back();
     return e;
   }
+  // timing only: no system-scope fence at the record (no cache writeback
+  // and invalidation between the timed kernels, which would slow the next
+  // one and inflate the measured durations)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   return e;
 }
 

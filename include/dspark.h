@@ -283,7 +283,8 @@ dspark_status dspark_draft_block(const dspark_model* m, const void* const* k_ctx
 
 /* Optional per-kernel timing (benchmarks and diagnostics).  While enabled,
  * each kernel launch is bracketed by two HIP events recorded on the launch
- * stream.  dspark_profile_read waits for those events, writes up to `max`
+ * stream (created with hipEventDisableSystemFence: they only time the work,
+ * so their records neither write back nor invalidate the caches).  dspark_profile_read waits for those events, writes up to `max`
  * records (one per kernel role, e.g. "gemm.lm_head", "attn"), returns the
  * number written and clears the log.  Process-wide; not for concurrent use. */
 typedef struct {
