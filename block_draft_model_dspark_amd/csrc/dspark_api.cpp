@@ -113,7 +113,7 @@ int nc_of(const dspark_model* m) { return ceil_div(m->c.vocab_size, WALK_CHUNK);
 
 RopeCfg rope_of(const dspark_model* m) {
   RopeCfg r;
-  r.theta = m->c.rope_theta;
+  r.step = std::pow((double)m->c.rope_theta, -2.0 / m->c.global_head_dim);
   r.hd = m->c.global_head_dim;
   r.nrot = m->nrot;
   return r;
@@ -1190,7 +1190,7 @@ dspark_status draft_rows_impl(const dspark_model* m, int A, const void* const* k
   const int split = wide ? attn_split_wide(total_ctx, A) : attn_split(total_ctx);
   AttnArgs at{};
   at.vonly = vonly ? 1 : 0;
-  at.theta = c.rope_theta;
+  at.rope_step = std::pow((double)c.rope_theta, -2.0 / c.global_head_dim);
   at.nrot = m->nrot;
   for (int a = 0; a < A; ++a) at.ctx_pos0[a] = ctx_pos0_host ? ctx_pos0_host[a] : 0;
   MergeArgs mg{};

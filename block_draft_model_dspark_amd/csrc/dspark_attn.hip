@@ -328,7 +328,7 @@ __device__ __forceinline__ VoCtx vo_setup(VoTables<HD, VO>& t, const AttnArgs& a
     const int tid = threadIdx.x;
     if (tid < HD / 2) {
       t.knw[tid] = ((const uint32_t*)a.kn)[tid];
-      t.inv[tid] = rope_inv(tid, HD, a.theta, a.nrot);
+      t.inv[tid] = rope_inv(tid, a.rope_step, a.nrot);
     }
     __syncthreads();  // (called by every thread of the workgroup: the split kind is uniform)
     v.knw = t.knw;

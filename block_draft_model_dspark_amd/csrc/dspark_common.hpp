@@ -247,12 +247,22 @@ __device__ __forceinline__ void block_argmax(float& u, int& i, float* redu, int*
 }
 
 // RoPE for pair k: angle = pos / theta^(2k/hd) for the first nrot pairs, 0
-// (identity) beyond.  rope_inv gives 1 / wavelength in double (once per pair);
-// rope_cs forms the angle in double, reduces it to [-pi, pi] in double
-// (positions reach 32k+, where an fp32 angle would be off by ~1e-3 rad) and
-// takes sin / cos of the reduced angle in fp32.
-__device__ __forceinline__ double rope_inv(int k, int hd, double theta, int nrot) {
-  return k < nrot ? 1.0 / pow(theta, (2.0 * k) / (double)hd) : 0.0;
+// (identity) beyond.  rope_inv gives 1 / wavelength in double (once per pair)
+// as step^k, step = theta^(-2/hd) formed on the host in double, by binary
+// powering (relative error ~1e-15; a library pow per pair was a long latency
+// chain in the kernels that build RoPE tables); rope_cs forms the angle in
+// double, reduces it to [-pi, pi] in double (positions reach 32k+, where an
+// fp32 angle would be off by ~1e-3 rad) and takes sin / cos of the reduced
+// angle in fp32.
+__device__ __forceinline__ double rope_inv(int k, double step, int nrot) {
+  if (k >= nrot) return 0.0;
+  double acc = 1.0, p = step;
+#pragma unroll
+  for (int b = 0; b < 12; ++b) {  // k < hd / 2 < 4096
+    if ((k >> b) & 1) acc *= p;
+    p *= p;
+  }
+  return acc;
 }
 __device__ __forceinline__ void rope_cs(int64_t pos, double inv, float& c, float& s) {
   const double two_pi = 6.283185307179586;

@@ -399,7 +399,7 @@ __device__ __forceinline__ void epi_kv(const GemmArgs& g, const EpiArgs& e, int 
   //    pairs.  The rows span batch rows b_first..b_last, whose starting
   //    positions are read with uniform (scalar) loads.
   if constexpr (SEP) {
-    if (tid < half) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
+    if (tid < half) rinv[tid] = rope_inv(tid, e.rope.step, e.rope.nrot);
     __syncthreads();
   }
   const int b_first = m0 / e.L, b_last = (m1 - 1) / e.L;
@@ -859,7 +859,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     load_w<WK, SMAX>(g, si, wrow, chunk_k(1), chunk_len(1) >> 5, wb);
   }
   if constexpr (EPI == EPI_KV) {
-    if (tid < (e.hd >> 1)) rinv[tid] = rope_inv(tid, e.rope.hd, e.rope.theta, e.rope.nrot);
+    if (tid < (e.hd >> 1)) rinv[tid] = rope_inv(tid, e.rope.step, e.rope.nrot);
   }
   if constexpr (XM == XM_NORM) {
     norm_finish<MT>(g, mbase, nv, sc_in, rs, vt);

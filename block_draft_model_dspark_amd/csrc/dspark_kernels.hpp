@@ -121,7 +121,7 @@ __host__ __device__ inline int wave_col(int c, int w, int N, int hd) {
 }
 
 struct RopeCfg {
-  double theta;
+  double step;        // theta^(-2 / hd): 1 / wavelength of pair k is step^k
   int hd, nrot;       // rotated pairs: k < nrot turn, the rest pass through
 };
 
@@ -287,7 +287,7 @@ struct AttnArgs {
   // K = RoPE(V * k_norm) at positions ctx_pos0[a] + j while they are staged
   int vonly;
   const void* kn;        // this layer's k_norm weight [hd], bf16
-  double theta;
+  double rope_step;      // theta^(-2 / hd)
   int nrot;
   int ctx_pos0[MAX_ROWS];
   // [nsplit, nKv, nq, hd]: fp32 unnormalised for an fp32 cache; for a bf16

@@ -41,7 +41,7 @@ __global__ __launch_bounds__(256) void k_embed(const EmbedArgs a) {
   const int64_t pos = (int64_t)a.rows.pos[row] + g;
   for (int d = tid; d < half; d += 256) {
     float c, s;
-    rope_cs(pos, rope_inv(d, a.rope.hd, a.rope.theta, a.rope.nrot), c, s);
+    rope_cs_hw(pos, rope_inv(d, a.rope.step, a.rope.nrot), c, s);
     a.rt[(int64_t)m * half + d] = make_float2(c, s);
   }
   for (int k0 = 8 * tid; k0 < a.H; k0 += 2048) {
