@@ -38,21 +38,21 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
-                  "bytes_per_step": 710093440},
+                  "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
+                  "bytes_per_step": 710038938},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "ba5da2e74d1449034cc67efbc13600f8052657bd2f123dda1405f33e5e228cd2",
-                     "bytes_per_launch": 70296640},
+                     "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
+                     "bytes_per_launch": 70297389},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "9556050ec859c673eb3e21831f5aa593bb6a312df8ab1ac0990b1bc3e9577672",
-                  "bytes_per_step": 387674880},
+                  "sha256": "db9610506219f5d257402b3724fba2ea8fe7b4c0d4851beef8a683470dcf301e",
+                  "bytes_per_step": 387622349},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "6ae78dbdd3a773df635ff664ad5f3cfcee7430ae23e53b59865730ce8a59f5b2",
-                  "bytes_per_step": 2108220205},
+                  "sha256": "701b95f6f53e83c8a3508fa8b8d62933cb32061f9eab74be45a93151310d7571",
+                  "bytes_per_step": 2106163174},
 }
 
 
