@@ -12,8 +12,8 @@
 //      sum carries the fp32 value; bf16 input rows are used as they are.
 //   2. k_tall: T[m, n] = sum over planes of X_p[m, :] . W[n, :] in fp32,
 //      BM x BN output tiles, both operands staged through LDS in 64-wide K
-//      steps (the global loads of the next two steps in flight during this
-//      step's MFMAs), four waves of (BM/2) x (BN/2).  Few output tiles split
+//      steps (the global loads of the next one or two steps in flight during
+//      this step's MFMAs), four waves of (BM/2) x (BN/2).  Few output tiles split
 //      K over blockIdx.z into partial planes that the epilogue adds.
 //   3. the GEMM's own epilogue (norm statistics, q|k RoPE, GELU gate, logit
 //      softcap, context K/V) reads T: k_gemm_epi / k_kv_epi.
@@ -214,14 +214,29 @@ __global__ __launch_bounds__(256) void k_sums_prep(const SumsPrepArgs a) {
 // ---------------------------------------------------------------------------
 // 2. T = sum_p X_p W^T, BM x BN tiles, K steps of 64
 // ---------------------------------------------------------------------------
-constexpr int TBK = 64;        // K step
-constexpr int TLD = TBK + 16;  // LDS row pitch (bf16): 160 bytes; of the 144, 160, 176
-                               // and 208-byte pitches the MFMA operand reads stall least
-                               // at this one (a round over 32 blocks of 16 rows ran
-                               // 1.4-2% faster than at 144)
+constexpr int TBK = 64;  // K step
+
+// Two forms, by the number of input planes:
+//  - two planes (hi + lo): two steps of global loads in flight in registers,
+//    rows padded to a 160-byte LDS pitch (of the 144, 160, 176 and 208-byte
+//    pitches the MFMA operand reads stall least at this one), 60 KB of LDS
+//    and ~200 VGPRs: two workgroups per CU;
+//  - one plane: one step in flight, 128-byte rows with their 16-byte chunks
+//    xor-swizzled by row (operand reads spread over the banks without
+//    padding), 32 KB of LDS and ~126 VGPRs: three to four workgroups per CU,
+//    whose waves hide each other's waits (the two-plane kernel in this form
+//    ran slower: fewer MFMAs per wait to hide).
+template <int NP>
+struct TallForm {
+  static constexpr bool one = NP == 1;
+  static constexpr int LD = one ? TBK : TBK + 16;  // LDS row pitch (bf16)
+  __device__ static constexpr int chunk(int row, int c) { return one ? (c ^ (row & 7)) : c; }
+};
 
 template <int BM, int BN, int NP>
-__global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
+__global__ __launch_bounds__(256, NP == 1 ? 3 : 2) void k_tall(const TallArgs t) {
+  using F = TallForm<NP>;
+  constexpr int TLD = F::LD;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 16, FN = WN / 16;
   constexpr int AIT = BM * (TBK / 8) / 256, BIT = BN * (TBK / 8) / 256;  // 16-byte items per thread
   static_assert(AIT >= 1 && BIT >= 1, "tile too small for 256 threads");
@@ -263,9 +278,10 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
     }
     bp[j] = (const uint16_t*)w + (int64_t)(n - nb) * t.K + 8 * c8;
   }
-  // two register sets: the steps k and k + 64 are loading while step k - 64
-  // is multiplied (a step past the slice reloads the slice's last one, so
-  // every thread always has the same loads in flight)
+  // register sets of global loads in flight: two planes, steps k and k + 64
+  // load while step k - 64 is multiplied; one plane, step k while k - 64 is
+  // (a step past the slice reloads the slice's last one, so every thread
+  // always has the same loads in flight)
   struct Stage {
     u32x4 a[NP][AIT], b[BIT];
   };
@@ -284,12 +300,12 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
     for (int j = 0; j < AIT; ++j) {
       const int it = tid + 256 * j, rr = it >> 3, c8 = it & 7;
 #pragma unroll
-      for (int p = 0; p < NP; ++p) *(u32x4*)&As[p][rr * TLD + 8 * c8] = r.a[p][j];
+      for (int p = 0; p < NP; ++p) *(u32x4*)&As[p][rr * TLD + 8 * F::chunk(rr, c8)] = r.a[p][j];
     }
 #pragma unroll
     for (int j = 0; j < BIT; ++j) {
       const int it = tid + 256 * j, rr = it >> 3, c8 = it & 7;
-      *(u32x4*)&Bs[rr * TLD + 8 * c8] = r.b[j];
+      *(u32x4*)&Bs[rr * TLD + 8 * F::chunk(rr, c8)] = r.b[j];
     }
   };
 
@@ -305,38 +321,49 @@ __global__ __launch_bounds__(256, 2) void k_tall(const TallArgs t) {
       bf16x8 bfr[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j)
-        bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&Bs[(WN * wn + 16 * j + ln) * TLD + 32 * s + 8 * gq]);
+        bfr[j] = __builtin_bit_cast(bf16x8, *(const u32x4*)&Bs[(WN * wn + 16 * j + ln) * TLD + 8 * F::chunk(ln, 4 * s + gq)]);
 #pragma unroll
       for (int p = 0; p < NP; ++p)
 #pragma unroll
         for (int i = 0; i < FM; ++i) {
           const bf16x8 afr =
-              __builtin_bit_cast(bf16x8, *(const u32x4*)&As[p][(WM * wm + 16 * i + ln) * TLD + 32 * s + 8 * gq]);
+              __builtin_bit_cast(bf16x8, *(const u32x4*)&As[p][(WM * wm + 16 * i + ln) * TLD + 8 * F::chunk(ln, 4 * s + gq)]);
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma16(afr, bfr[j], acc[i][j]);
         }
     }
   };
-  load(st0, kb);
-  load(st1, kb + TBK);
-  int k0 = kb;
-  for (; k0 + 2 * TBK <= ke; k0 += 2 * TBK) {
-    __syncthreads();  // every wave is done reading the previous step
-    store(st0);
-    __syncthreads();
-    load(st0, k0 + 2 * TBK);
-    step();
-    __syncthreads();
-    store(st1);
-    __syncthreads();
-    load(st1, k0 + 3 * TBK);
-    step();
-  }
-  if (k0 < ke) {  // an odd last step (uniform)
-    __syncthreads();
-    store(st0);
-    __syncthreads();
-    step();
+  if constexpr (F::one) {
+    load(st0, kb);
+    for (int k0 = kb; k0 < ke; k0 += TBK) {
+      __syncthreads();  // every wave is done reading the previous step
+      store(st0);
+      __syncthreads();
+      load(st0, k0 + TBK);
+      step();
+    }
+  } else {
+    load(st0, kb);
+    load(st1, kb + TBK);
+    int k0 = kb;
+    for (; k0 + 2 * TBK <= ke; k0 += 2 * TBK) {
+      __syncthreads();  // every wave is done reading the previous step
+      store(st0);
+      __syncthreads();
+      load(st0, k0 + 2 * TBK);
+      step();
+      __syncthreads();
+      store(st1);
+      __syncthreads();
+      load(st1, k0 + 3 * TBK);
+      step();
+    }
+    if (k0 < ke) {  // an odd last step (uniform)
+      __syncthreads();
+      store(st0);
+      __syncthreads();
+      step();
+    }
   }
   float* const T = t.T + blockIdx.z * t.tstride;
 
