@@ -39,20 +39,20 @@ TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
-                  "bytes_per_step": 710038938},
+                  "bytes_per_step": 710033331},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                      "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
-                     "bytes_per_launch": 70297389},
+                     "bytes_per_launch": 70295962},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "db9610506219f5d257402b3724fba2ea8fe7b4c0d4851beef8a683470dcf301e",
-                  "bytes_per_step": 387622349},
+                  "bytes_per_step": 387634355},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "701b95f6f53e83c8a3508fa8b8d62933cb32061f9eab74be45a93151310d7571",
-                  "bytes_per_step": 2106163174},
+                  "sha256": "45eaefe27568c9282d809a991285cdf7bf4cf3a67b016202b26b6bfee23625be",
+                  "bytes_per_step": 2085662899},
 }
 
 
