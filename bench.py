@@ -51,7 +51,7 @@ TRAFFIC = {
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "45eaefe27568c9282d809a991285cdf7bf4cf3a67b016202b26b6bfee23625be",
+                  "sha256": "e52ae3a0db2a66da25ffc475e4ccc2c208f1bf7f45702c39c58e46533abb1125",
                   "bytes_per_step": 2085662899},
 }
 

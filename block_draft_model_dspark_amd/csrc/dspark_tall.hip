@@ -223,9 +223,9 @@ constexpr int TBK = 64;  // K step
 //    and ~200 VGPRs: two workgroups per CU;
 //  - one plane: one step in flight, 128-byte rows with their 16-byte chunks
 //    xor-swizzled by row (operand reads spread over the banks without
-//    padding), 32 KB of LDS and ~126 VGPRs: three to four workgroups per CU,
-//    whose waves hide each other's waits (the two-plane kernel in this form
-//    ran slower: fewer MFMAs per wait to hide).
+//    padding), 32 KB of LDS and ~126 VGPRs: four workgroups per CU, whose
+//    waves hide each other's waits (the two-plane kernel in this form, at
+//    three workgroups per CU, ran 4-8% slower than in the first).
 template <int NP>
 struct TallForm {
   static constexpr bool one = NP == 1;
