@@ -230,7 +230,8 @@ def run_timed(step, args):
 class Shared:
     """The full-size bf16 model (with fc and hidden_norm) on the GPU and, for
     the CPU baselines, its float64 oracle copy: built once and used by every
-    workload of a run (C1, C2 and C3 share the model shapes)."""
+    workload of a run (the one-block round, the 8192-row projection and the
+    32-row round share the model shapes)."""
 
     def __init__(self, dsp, synth):
         self.dsp, self.synth = dsp, synth
