@@ -48,6 +48,10 @@ TRAFFIC = {
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
                   "sha256": "db9610506219f5d257402b3724fba2ea8fe7b4c0d4851beef8a683470dcf301e",
                   "bytes_per_step": 387634355},
+    # prefill_8192: one fc launch (tiled one-plane GEMM, 7680 -> 2048 over 8192 rows), per launch
+    "fc_prefill": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
+                   "sha256": "e52ae3a0db2a66da25ffc475e4ccc2c208f1bf7f45702c39c58e46533abb1125",
+                   "bytes_per_launch": 746822374},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
@@ -361,7 +365,7 @@ def bench_prefill(args, dsp, synth, torch, sh):
         "roofline": {"bound": "mfma", "kernel": "k_tall fc role (7680->2048 over 8192 rows; tiled bf16 MFMA GEMM, "
                                                 "timed with its epilogue launch)",
                      "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic("fc_prefill"),
                      "flops_per_launch": flops["gemm.fc"], "us_per_launch": round(fc_us, 2)},
         "kernels": kernels,
         "kernel_sum_us_per_step": round(sum(v["us_per_step"] for v in kernels.values()), 2),
