@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
 F32, BF16, Q4 = 0, 1, 2
 INPUT_CONTEXT_HIDDEN, INPUT_TARGET_FEATURES = 0, 1
+TALL_ROWS_DEFAULT = 48  # dspark_model_set_tall_rows's default
 _KIND = {"f32": F32, "bf16": BF16, "q4": Q4}
 
 EXPORTED = ("dspark_model_create", "dspark_model_destroy", "dspark_model_set_tall_rows", "dspark_model_aux_bytes",
             "dspark_model_prepare",
             "dspark_project_workspace_bytes", "dspark_project_context_kv", "dspark_draft_workspace_bytes",
             "dspark_draft_rows", "dspark_draft_block", "dspark_profile_enable", "dspark_profile_read",
-            "dspark_tall_tile_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
+            "dspark_tall_tile_of", "dspark_stream_block_of", "dspark_draft_rows_noalloc", "dspark_draft_noalloc_max_bytes",
             "dspark_q4_address_check",
             "dspark_draft_rows_conf", "dspark_draft_rows_ex",
             "dspark_last_error")
@@ -117,6 +118,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_tall_tile_of.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int)]
     lib.dspark_tall_tile_of.restype = ctypes.c_int
+    lib.dspark_stream_block_of.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)] * 2
+    lib.dspark_stream_block_of.restype = ctypes.c_int
     lib.dspark_q4_address_check.argtypes = [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                             I64, ctypes.c_int, ctypes.POINTER(I64)]
     lib.dspark_q4_address_check.restype = ctypes.c_int

@@ -7,7 +7,10 @@
 //
 // Work split: a 256-thread workgroup = 4 wave64s; wave w owns one 16-column
 // output tile of the workgroup's 64-column block (blockIdx.x), the workgroup
-// owns one K slice (blockIdx.y) and one block of MT*16 rows (blockIdx.z).
+// owns one K slice (blockIdx.y) and one block of MT*16 rows (blockIdx.z);
+// with 16-row tiles, one K slice and several row blocks, (x, z) is renumbered
+// so that the row blocks of a column block share its weight tile
+// (stream_block_of).
 // Each wave issues all weight loads of a K sub-slice straight from HBM into
 // registers (16 B per lane per 32-wide k step: the B operand layout needs no
 // shuffling), then the workgroup stages the activation sub-slice into LDS
@@ -37,6 +40,8 @@
 // epilogue on its 64 columns.  Only the context K/V epilogue (a head's
 // RMSNorm, which must be final in the cache) needs a second arrival per
 // head.  Counters are zero on entry and are left zero.
+#include <type_traits>
+
 #include "dspark_kernels.hpp"
 #include "dspark_common.hpp"
 
@@ -781,7 +786,7 @@ __device__ __forceinline__ void mma_w(f32x4* acc, const WRegs<WK, SMAX>& w, cons
 // first set stages, so they are read once for 128 columns.  Two waves per
 // SIMD hide one another's staging and MFMA phases behind the weight stream
 // without the cross-workgroup reduction a split K would need.
-template <int WK, int XM, int MT, int EPI, int NCH, int NW = 4>
+template <int WK, int XM, int MT, int EPI, int NCH, int NW = 4, bool RM = false>
 __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArgs e) {
   static_assert(NW == 4 || (NW == 8 && NCH > 0 &&
                               ((MT == 1 && (EPI == EPI_GELU || EPI == EPI_LM)) || (MT == 2 && EPI == EPI_KV))),
@@ -813,7 +818,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   const int ngmax = KC >> 6;
   const size_t xbuf = xbuf_bytes(WK, XM, MT, KC);
 
-  const int cb = COL2 ? 2 * blockIdx.x + half : blockIdx.x;
+  // column block (pair) and row block: RM (16-row tiles, one K slice,
+  // several row blocks) takes the XCD-aware order of stream_block_of, with
+  // the grid sizes from the arguments (a run-time choice, or gridDim, puts a
+  // scalar load ahead of the first weight address of every launch)
+  static_assert(!RM || MT == 1, "the renumbered order is for 16-row tiles");
+  int bx = blockIdx.x, bz = blockIdx.z;
+  if constexpr (RM) stream_block_of(COL2 ? g.N >> 7 : g.N >> 6, 1, (g.M + 15) >> 4, blockIdx.x, blockIdx.z, bx, bz);
+  const int cb = COL2 ? 2 * bx + half : bx;
   // wave-uniform values in scalar registers, so that the weight segment is
   // read from the kernel arguments with scalar loads (a vector load of the
   // pointer would make the first weight load wait for every earlier load)
@@ -823,10 +835,10 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     if (n0w >= g.seg[i].n0) si = i;
   si = __builtin_amdgcn_readfirstlane(si);
   const int64_t wrow = (int64_t)(n0w - g.seg[si].n0 + (lane & 15));
-  const int mbase = blockIdx.z * (MT * 16);
+  const int mbase = bz * (MT * 16);
   const int kbeg = blockIdx.y * g.kslice;
   const int kend = min(g.K, kbeg + g.kslice);
-  const bool write_h = XM == XM_NORM && g.nin.hout != nullptr && blockIdx.x == 0;
+  const bool write_h = XM == XM_NORM && g.nin.hout != nullptr && bx == 0;
   // NCH > 0: every slice is exactly NCH sub-slices of KC (fully unrolled,
   // so the loads of the next two sub-slices stay in flight with exact waits)
   const int nch = NCH > 0 ? NCH : (kend - kbeg + KC - 1) / KC;
@@ -948,13 +960,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     // (row block, column block): every store and load instruction of a wave
     // covers 256 contiguous bytes
     const int64_t tiles = (int64_t)gridDim.z * ncb;
-    const int64_t tile = (int64_t)blockIdx.z * ncb + cb;
+    const int64_t tile = (int64_t)bz * ncb + cb;
     auto pidx = [&](int sl, int t, int i) { return (((sl * tiles + tile) * MT + t) * 4 + i) * 256 + tid; };
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) st_coh(g.P + pidx(blockIdx.y, t, i), acc[t][i]);
-    if (!arrive_last(e.cnt + blockIdx.z * ncb + cb, S, &last_flag)) return;
+    if (!arrive_last(e.cnt + bz * ncb + cb, S, &last_flag)) return;
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     constexpr int PB = MT == 1 ? 8 : 4;  // partial slices loaded per batch
@@ -1021,7 +1033,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
     const int grp = (64 * cb) / gcols;
     const int ngroups = (g.N + gcols - 1) / gcols;
     const int members = (min(gcols, g.N - grp * gcols) + 63) / 64;
-    if (!arrive_last(e.cnt + gridDim.z * ncb + blockIdx.z * ngroups + grp, members, &last_flag)) return;
+    if (!arrive_last(e.cnt + gridDim.z * ncb + bz * ngroups + grp, members, &last_flag)) return;
     epi_kv<MT, 64 * NW>(g, e, mbase, min(g.M, mbase + MT * 16), grp, rinv, rcs);
   }
 }
@@ -1137,11 +1149,15 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
         }
       return hipErrorInvalidValue;
     } else {
+    // 16-row tiles: the XCD-aware block order (RM) when one K slice covers
+    // several row blocks
+    auto sel = [&](auto rm) -> hipError_t {
+    constexpr bool RM = decltype(rm)::value;
     if constexpr (unrolled && EPI == EPI_LM && MT == 1) {
       // lm_head over a whole row (no split-K): eight waves on two column
       // blocks that share one staging of the activations
       if (nch == 8 && S == 1 && (a.N / 64) % 2 == 0) {
-        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8, 8>), dim3(a.N / 128, S, grid.z), dim3(512), lds, st, a, e);
+        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8, 8, RM>), dim3(a.N / 128, S, grid.z), dim3(512), lds, st, a, e);
         return hipGetLastError();
       }
     }
@@ -1150,21 +1166,26 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
       // per K half, each half with its own two staging buffers
       if (nch == 8 && S == 1) {
         const size_t lds8 = xbuf_bytes(WK, XM, MT, 256) * 4;
-        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4, 8>), grid, dim3(512), lds8, st, a, e);
+        hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4, 8, RM>), grid, dim3(512), lds8, st, a, e);
         return hipGetLastError();
       }
     }
     if constexpr (unrolled) {
       switch (nch) {
-        case 1: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 1>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
-        case 2: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 2>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
-        case 4: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
-        case 8: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 1: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 1, 4, RM>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 2: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 2, 4, RM>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 4: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 4, 4, RM>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
+        case 8: hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 8, 4, RM>), grid, dim3(256), lds, st, a, e); return hipGetLastError();
         default: break;
       }
     }
-    hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 0>), grid, dim3(256), lds, st, a, e);
+    hipLaunchKernelGGL((k_gemm<WK, XM, MT, EPI, 0, 4, RM>), grid, dim3(256), lds, st, a, e);
     return hipGetLastError();
+    };
+    if constexpr (MT == 1) {
+      if (S == 1 && mblocks > 1) return sel(std::true_type{});
+    }
+    return sel(std::false_type{});
     }
   } else {
     return hipErrorInvalidValue;

@@ -123,8 +123,9 @@ void dspark_model_destroy(dspark_model* m);
  * theirs in the tiled kernel's store when one K slice holds the product);
  * fewer rows stream the weights once per 16-row tile.  Both compute the same product (fp32
  * activations as bf16 hi + lo planes); the context projection of bf16 rows
- * switches at four times `rows`.  rows <= 0 keeps every GEMM on the
- * weight-streaming kernel.  Default 256.  Workspace sizes depend on it: set it
+ * switches at 1024 rows or four times `rows`, whichever is more.  rows <= 0
+ * keeps every GEMM on the weight-streaming kernel.  Default 48 (draft rounds
+ * of three or more blocks of 16).  Workspace sizes depend on it: set it
  * before sizing workspaces.  DSPARK_ERR_INVALID_ARG for a null model. */
 dspark_status dspark_model_set_tall_rows(dspark_model* m, int rows);
 
@@ -302,6 +303,16 @@ int dspark_profile_read(dspark_kernel_time* out, int max);
  * of [0, gx*gy) onto the tiles.  DSPARK_ERR_INVALID_ARG for non-positive
  * sizes, w outside [0, gx*gy) or null outputs. */
 dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by);
+
+/* Diagnostic (host only, no HIP call): the column block *bx and row block
+ * *bz that workgroup (x, z) of the weight-streaming GEMM computes, in a grid
+ * of gx column blocks, S K slices and R row blocks of 16 rows.  With one K
+ * slice and several row blocks the kernel renumbers its workgroups so that the row
+ * blocks of a column block run back to back on one XCD and share its weight
+ * tile in that XCD's L2; a bijection of the (x, z) pairs.
+ * DSPARK_ERR_INVALID_ARG for non-positive sizes, (x, z) outside the grid or
+ * null outputs. */
+dspark_status dspark_stream_block_of(int gx, int S, int R, int x, int z, int* bx, int* bz);
 
 /* Diagnostic (host only, no HIP call): replays on the host every address
  * that the 4-bit branches of the kernels form for a round of A rows with

@@ -185,6 +185,32 @@ def test_tall_tile_order_keeps_a_row_tile_on_one_xcd(dsp):
             assert by.value % 8 == w % 8
 
 
+@pytest.mark.parametrize("gx,S,R", [(2048, 1, 4), (16, 1, 16), (512, 1, 4), (36, 8, 1), (32, 8, 2), (8, 1, 3),
+                                    (12, 1, 4), (64, 1, 2), (256, 1, 1), (24, 2, 5)])
+def test_stream_block_order_is_a_bijection(dsp, gx, S, R):
+    """The weight-streaming GEMM's renumbering covers every (column block,
+    row block) once; with one K slice, several row blocks and gx a multiple
+    of 8, the row blocks of a column block share one XCD (workgroup
+    x + gx z on XCD (x + gx z) mod 8) and follow each other in launch order."""
+    lib = dsp._lib
+    bx, bz = ctypes.c_int(), ctypes.c_int()
+    seen, where = set(), {}
+    for z in range(R):
+        for x in range(gx):
+            assert lib.dspark_stream_block_of(gx, S, R, x, z, ctypes.byref(bx), ctypes.byref(bz)) == 0
+            assert 0 <= bx.value < gx and 0 <= bz.value < R
+            seen.add((bx.value, bz.value))
+            where.setdefault(bx.value, []).append(x + gx * z)
+    assert len(seen) == gx * R
+    if S == 1 and R > 1 and gx % 8 == 0:
+        for cb, ws in where.items():
+            assert len({w % 8 for w in ws}) == 1
+            assert max(ws) - min(ws) == 8 * (R - 1)
+    else:
+        assert all(ws == [cb + gx * z for z in range(R)] for cb, ws in where.items())
+    assert lib.dspark_stream_block_of(gx, S, R, gx, 0, ctypes.byref(bx), ctypes.byref(bz)) == 1
+
+
 def test_draft_workspace_scales_with_context_up_to_the_split_cap(dsp):
     """Only the attention partials scale with the contexts: at most
     min(512, ceil(total / 32)) + 2A splits, so the size grows with total_ctx

@@ -185,9 +185,13 @@ def test_tiny_f32_many_ragged_rows(gpu_lib):
     assert checked >= 40
 
 
-def test_ragged_rows_small(gpu_lib):
+@pytest.mark.parametrize("path", ["default", "streaming"])
+def test_ragged_rows_small(gpu_lib, path):
     """Rows with different context lengths, including an empty context, a
-    single row and lengths off every tile boundary; Markov head active."""
+    single row and lengths off every tile boundary; Markov head active.  80
+    block rows: the tiled path by default; "streaming" keeps every GEMM on
+    the weight-streaming kernel (five 16-row blocks per column block, in the
+    XCD-aware block order where one K slice covers them)."""
     cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=4096, mask_token_id=4095)
     w = synth.Workload("ragged_small", cfg, rows=5, ctx_lens=(0, 1, 37, 300, 700))
     case = Case(cfg, markov_active=True, with_fc=False)
@@ -195,6 +199,8 @@ def test_ragged_rows_small(gpu_lib):
     o_rows, k_rows, v_rows = case.kv_rows_from_oracle([_ctx(w, a, L) for a, L in enumerate(lens)], [0] * 5)
     anchors = synth.anchors(w)
     positions = lens
+    if path == "streaming":
+        case.gm.set_tall_rows(0)
     toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, positions)
     for a in range(5):
         assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
@@ -307,7 +313,7 @@ def test_tiled_path_round_small_ragged(gpu_lib):
         case.gm.set_tall_rows(1)
         toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
     finally:
-        case.gm.set_tall_rows(256)
+        case.gm.set_tall_rows(gpu_lib.TALL_ROWS_DEFAULT)
     for a in range(3):
         assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
     checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
@@ -336,7 +342,7 @@ def test_tiled_path_fused_logits(gpu_lib):
         case.gm.set_tall_rows(1)
         toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
     finally:
-        case.gm.set_tall_rows(256)
+        case.gm.set_tall_rows(gpu_lib.TALL_ROWS_DEFAULT)
     for a in range(len(lens)):
         assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
     checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
@@ -350,12 +356,15 @@ def test_tiled_path_fused_logits(gpu_lib):
 
 @pytest.mark.parametrize("kind", ["target_features", "context_hidden"])
 def test_tiled_path_projection_small_ragged(gpu_lib, kind):
-    """The context projection on the tiled path (threshold 1 row) over 2 x 100
-    rows (a partial tile): fc + hidden_norm + k_proj from target features
-    (normed fp32 input planes), or k_proj on bf16 context rows (one plane)."""
+    """The context projection on the tiled path (threshold 1 row): fc +
+    hidden_norm + k_proj from 2 x 100 rows of target features (normed fp32
+    input planes, a partial tile), or k_proj on 2 x 520 bf16 context rows
+    (one plane; the bf16 projection takes the tiled path from 1024 rows, and
+    1040 leaves a partial 128-row tile)."""
     import torch
     cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=1024, mask_token_id=1023)
-    w = synth.Workload("pf_tall", cfg, rows=0, prefill_rows=100, prefill_batch=2)
+    L = 100 if kind == "target_features" else 520
+    w = synth.Workload("pf_tall", cfg, rows=0, prefill_rows=L, prefill_batch=2)
     case = Case(cfg)
     if kind == "target_features":
         st = synth.target_features(w)
@@ -363,7 +372,7 @@ def test_tiled_path_projection_small_ragged(gpu_lib, kind):
         ik = gpu_lib.INPUT_TARGET_FEATURES
         ctx = O.project_context(case.om, O.decode(st))
     else:
-        sts = [synth.ctx_hidden(w, b, 100) for b in range(2)]
+        sts = [synth.ctx_hidden(w, b, L) for b in range(2)]
         x = torch.stack([gpu_lib.act_tensor(s) for s in sts])
         ik = gpu_lib.INPUT_CONTEXT_HIDDEN
         ctx = np.stack([O.decode(s) for s in sts])
@@ -375,7 +384,7 @@ def test_tiled_path_projection_small_ragged(gpu_lib, kind):
         ks, vs = gpu_lib.project_context_kv(case.gm, x, [3, 500], input_kind=ik)
         torch.cuda.synchronize()
     finally:
-        case.gm.set_tall_rows(256)
+        case.gm.set_tall_rows(gpu_lib.TALL_ROWS_DEFAULT)
     ref = O.project_context_kv(case.om, ctx, [3, 500])
     for li, (K, V) in enumerate(ref):
         assert rel_err(ks[li].float().cpu().numpy(), K) <= 2e-2, li
@@ -410,7 +419,7 @@ def test_tiled_path_row_widths(gpu_lib, hidden):
                                             input_kind=gpu_lib.INPUT_TARGET_FEATURES)
         torch.cuda.synchronize()
     finally:
-        case.gm.set_tall_rows(256)
+        case.gm.set_tall_rows(gpu_lib.TALL_ROWS_DEFAULT)
     for a in range(2):
         assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
     checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
