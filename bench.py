@@ -38,25 +38,25 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
-                  "bytes_per_step": 710033331},
+                  "sha256": "942e8f7fb987acb89d398b25fc000f470def0ab78f97c0ba9827c33774500d68",
+                  "bytes_per_step": 710053299},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "4df21be53e8e9ccb8abfc986e7f02460307ae63197d6375af28bf5201522b10d",
-                     "bytes_per_launch": 70295962},
+                     "sha256": "942e8f7fb987acb89d398b25fc000f470def0ab78f97c0ba9827c33774500d68",
+                     "bytes_per_launch": 70292410},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "db9610506219f5d257402b3724fba2ea8fe7b4c0d4851beef8a683470dcf301e",
-                  "bytes_per_step": 387634355},
+                  "sha256": "b678438dc75fc08fcd27888409497b3b81987916d66e49f6973b80c49626e80f",
+                  "bytes_per_step": 387631872},
     # prefill_8192: one fc launch (tiled one-plane GEMM, 7680 -> 2048 over 8192 rows), per launch
     "fc_prefill": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                   "sha256": "e52ae3a0db2a66da25ffc475e4ccc2c208f1bf7f45702c39c58e46533abb1125",
-                   "bytes_per_launch": 746822374},
+                   "sha256": "443de4cc92fb3e934df2709c9182e964e29aa6e9ec9a889e25c20ee689f6cf61",
+                   "bytes_per_launch": 750370893},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "e52ae3a0db2a66da25ffc475e4ccc2c208f1bf7f45702c39c58e46533abb1125",
-                  "bytes_per_step": 2085662899},
+                  "sha256": "443de4cc92fb3e934df2709c9182e964e29aa6e9ec9a889e25c20ee689f6cf61",
+                  "bytes_per_step": 2085513459},
 }
 
 
