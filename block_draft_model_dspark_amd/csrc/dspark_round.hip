@@ -213,18 +213,130 @@ __global__ __launch_bounds__(256) void k_merge(const MergeArgs a) {
   *(f32x4*)(dst + d1) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
 }
 
+// Few query rows with many splits each (a long context over few draft
+// rows), fp16 partials in the wide attention's lane order: one workgroup of
+// G waves per (draft row, kv head, group of 16 query rows, tile pair); wave w
+// takes a contiguous share of the row's splits with k_merge's per-thread
+// mapping (eight dims of one query row, one 16-byte load per split, 1 KiB
+// contiguous per wave and split, MERGE_SB splits in flight), and the G
+// waves' (max, sums) are merged in LDS by wave 0.  grid A*nKv*ceil(nq/16)*(hd/32)
+template <int G>
+__global__ __launch_bounds__(64 * G) void k_merge_split(const MergeArgs a) {
+  __shared__ float sm[G][64], sden[G][64];
+  __shared__ float snum[G][8][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ng = (a.nq + 15) / 16, np2 = a.hd / 32;
+  const int64_t u = blockIdx.x;  // ((row * nKv + kvh) * ng + group) * np2 + pair
+  const int pair = (int)(u % np2);
+  const int64_t rg = u / np2;
+  const int grp = (int)(rg % ng), kvh = (int)((rg / ng) % a.nKv), row = (int)(rg / ((int64_t)ng * a.nKv));
+  const int j = grp * 16 + (lane & 15);
+  const int jc = min(j, a.nq - 1);  // rows past nq compute on row nq - 1 and store nothing
+  const int d0 = 32 * pair + 4 * (lane >> 4), d1 = d0 + 16;
+  const int64_t pbase = (((int64_t)kvh * ng + grp) * np2 + pair) * 512 + 8 * lane;
+  const int s0 = a.split_off[row], nsr = a.split_off[row + 1] - s0;
+  const int per = (nsr + G - 1) / G, gs = wave * per, gn = max(0, min(per, nsr - gs));
+  const float2* ml = (const float2*)a.ml;
+  auto mli = [&](int s) { return ((int64_t)(s0 + s) * a.nKv + kvh) * a.nq + jc; };
+  float mx = -INFINITY, den = 0.f;
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int c0 = 0; c0 < gn; c0 += MERGE_SB) {  // (per wave: no barrier inside)
+    u32x4 raw[MERGE_SB];
+    float2 wv[MERGE_SB];
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q) {
+      const int s = gs + c0 + min(q, gn - c0 - 1);
+      raw[q] = *(const u32x4*)((const uint16_t*)a.opart + (int64_t)(s0 + s) * a.nKv * ng * 16 * a.hd + pbase);
+      wv[q] = ml[mli(s)];
+    }
+    float bm = mx;
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q) bm = fmaxf(bm, wv[q].x);
+    if (bm > mx) {
+      const float r = expf(mx - bm);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] *= r;
+      den *= r;
+      mx = bm;
+    }
+#pragma unroll
+    for (int q = 0; q < MERGE_SB; ++q)
+      if (c0 + q < gn) {
+        const float wl = expf(wv[q].x - mx) * wv[q].y;
+        den += wl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          num[2 * e] += wl * f16_to_f32((uint16_t)(raw[q][e] & 0xFFFFu));
+          num[2 * e + 1] += wl * f16_to_f32((uint16_t)(raw[q][e] >> 16));
+        }
+      }
+  }
+  sm[wave][lane] = mx;
+  sden[wave][lane] = den;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) snum[wave][e][lane] = num[e];
+  __syncthreads();
+  if (wave != 0 || j >= a.nq) return;
+  // wave 0 always holds splits (per >= 1), so the common reference is finite
+  float M = sm[0][lane];
+#pragma unroll
+  for (int w = 1; w < G; ++w) M = fmaxf(M, sm[w][lane]);
+  den = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) num[e] = 0.f;
+#pragma unroll
+  for (int w = 0; w < G; ++w)
+    if (sm[w][lane] != -INFINITY) {
+      const float f = expf(sm[w][lane] - M);
+      den += sden[w][lane] * f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) num[e] += snum[w][e][lane] * f;
+    }
+  const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
+  const int h = kvh * rep + hl;
+  const float rd = 1.f / den;
+  const int64_t m = (int64_t)row * a.gamma + g;
+  // dims d0.. (values 0..3) and d1.. (values 4..7)
+  if (a.planes) {
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = num[e] * rd;
+    bf16x8 hi, lo;
+    split8(v, hi, lo);
+    const u32x4 hw = __builtin_bit_cast(u32x4, hi), lw = __builtin_bit_cast(u32x4, lo);
+    uint16_t* dst = a.planes + m * (a.nH * a.hd) + h * a.hd;
+    *(u32x2*)(dst + d0) = u32x2{hw[0], hw[1]};
+    *(u32x2*)(dst + d1) = u32x2{hw[2], hw[3]};
+    *(u32x2*)(dst + a.plane + d0) = u32x2{lw[0], lw[1]};
+    *(u32x2*)(dst + a.plane + d1) = u32x2{lw[2], lw[3]};
+    return;
+  }
+  float* dst = a.O + m * a.ldo + h * a.hd;
+  *(f32x4*)(dst + d0) = f32x4{num[0] * rd, num[1] * rd, num[2] * rd, num[3] * rd};
+  *(f32x4*)(dst + d1) = f32x4{num[4] * rd, num[5] * rd, num[6] * rd, num[7] * rd};
+}
+
 // Few query rows (a single draft row): one workgroup per query row, one
 // thread per head dim, the splits in passes of MERGE_RB with every partial
-// load of a pass in flight.  grid A*nKv*nq, block hd (>= 64)
+// load of a pass in flight.  grid A*nKv*nq, block NG*hd (hd >= 64).  NG > 1
+// (rows with many splits: long contexts over few rows) gives each of NG
+// thread groups a contiguous share of the row's splits, merged in LDS at the
+// end, so the passes run side by side instead of one after another.
 constexpr int MERGE_RB = 32;
 
-template <bool F16, bool LANE>
-__global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
-  __shared__ float2 wl[MERGE_RB];
-  __shared__ float cmax;
-  const int idx = blockIdx.x, tid = threadIdx.x;
+template <bool F16, bool LANE, int NG>
+__global__ __launch_bounds__(256 * NG) void k_merge_rows(const MergeArgs a) {
+  __shared__ float2 wl[NG][MERGE_RB];
+  __shared__ float cmax[NG];
+  __shared__ float gnum[NG > 1 ? NG : 1][NG > 1 ? 256 : 1];
+  __shared__ float gm[NG], gden[NG];
+  const int idx = blockIdx.x;
+  const int gi = NG > 1 ? (int)threadIdx.x / a.hd : 0;  // split group (wave-aligned: hd is a multiple of 64)
+  const int tid = (int)threadIdx.x - gi * a.hd;          // head-dim thread within the group
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
-  const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
+  const int s0r = a.split_off[row], nsr = a.split_off[row + 1] - s0r;  // nsr >= 1 (the block split)
+  const int per = NG > 1 ? (nsr + NG - 1) / NG : nsr;  // splits per group (the same trip count for all)
+  const int ns = NG > 1 ? max(0, min(per, nsr - gi * per)) : nsr;  // this group's splits (may be 0)
   const float2* ml = (const float2*)a.ml;
   // fp16 lane order: thread tid reads half (tid mod 8) of lane j mod 16 +
   // 16 ((tid mod 32) / 8) in tile pair tid / 32 (eight threads per 16-byte
@@ -232,13 +344,18 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
   const int pr = tid >> 5, gq8 = (tid & 31) >> 3, hv = tid & 7;
   const int dim = F16 && LANE ? 16 * (2 * pr + (hv >> 2)) + 4 * gq8 + (hv & 3) : tid;
   const int ng = (a.nq + 15) / 16;
+  // split of pass position q: clamped into the row's splits (a group with
+  // none left loads a valid split and masks it), so no load is conditional
+  auto split_at = [&](int c0, int q, int cn) {
+    return s0r + min(gi * per + c0 + min(q, max(cn, 1) - 1), nsr - 1);
+  };
   float num = 0.f, den = 0.f, mrun = -INFINITY;
-  for (int c0 = 0; c0 < ns; c0 += MERGE_RB) {
-    const int cn = min(MERGE_RB, ns - c0);
+  for (int c0 = 0; c0 < per; c0 += MERGE_RB) {
+    const int cn = min(MERGE_RB, ns - c0);  // <= 0: nothing of this group in the pass
     float o[MERGE_RB];
 #pragma unroll
     for (int q = 0; q < MERGE_RB; ++q) {
-      const int s = s0 + c0 + min(q, cn - 1);
+      const int s = split_at(c0, q, cn);
       if constexpr (F16 && LANE) {
         const int64_t i = ((((int64_t)s * a.nKv + kvh) * ng + j / 16) * (a.hd / 32) + pr) * 512 +
                           8 * ((j & 15) + 16 * gq8) + hv;
@@ -249,18 +366,19 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
         o[q] = ((const float*)a.opart)[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
       }
     }
-    const float2 v = ml[((int64_t)(s0 + c0 + min(tid, cn - 1)) * a.nKv + kvh) * a.nq + j];
+    const float2 v = ml[((int64_t)split_at(c0, tid, cn) * a.nKv + kvh) * a.nq + j];
     if (tid < 64) {
       const float mm = wave_max(tid < cn ? v.x : -INFINITY);
-      if (tid == 0) cmax = mm;
+      if (tid == 0) cmax[gi] = mm;
     }
     __syncthreads();
-    const float mnew = fmaxf(mrun, cmax);
+    const float mnew = fmaxf(mrun, cmax[gi]);
     if (tid < cn) {
       const float w = expf(v.x - mnew);
-      wl[tid] = make_float2(w, w * v.y);
+      wl[gi][tid] = make_float2(w, w * v.y);
     }
-    const float rescale = expf(mrun - mnew);
+    // (a group that has seen no split yet keeps mrun = mnew = -inf)
+    const float rescale = NG > 1 && mnew == -INFINITY ? 1.f : expf(mrun - mnew);
     num *= rescale;
     den *= rescale;
     mrun = mnew;
@@ -268,10 +386,33 @@ __global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
 #pragma unroll
     for (int q = 0; q < MERGE_RB; ++q)
       if (q < cn) {
-        num += (F16 ? wl[q].y : wl[q].x) * o[q];
-        den += wl[q].y;
+        num += (F16 ? wl[gi][q].y : wl[gi][q].x) * o[q];
+        den += wl[gi][q].y;
       }
     __syncthreads();
+  }
+  if constexpr (NG > 1) {
+    // the groups' (max, sums) merged by the first group (group 0 always has
+    // a split, so the common reference M is finite)
+    gnum[gi][tid] = num;
+    if (tid == 0) {
+      gm[gi] = mrun;
+      gden[gi] = den;
+    }
+    __syncthreads();
+    if (gi != 0) return;
+    float M = gm[0];
+#pragma unroll
+    for (int k = 1; k < NG; ++k) M = fmaxf(M, gm[k]);
+    num = 0.f;
+    den = 0.f;
+#pragma unroll
+    for (int k = 0; k < NG; ++k)
+      if (gm[k] != -INFINITY) {
+        const float f = expf(gm[k] - M);
+        num += gnum[k][tid] * f;
+        den += gden[k] * f;
+      }
   }
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
@@ -777,10 +918,24 @@ hipError_t launch_zero(unsigned* p, int64_t n, hipStream_t st) {
 hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int nrows = a.A * a.nKv * a.nq;
   if (nrows <= MERGE_FEW_ROWS) {
-    // few rows: a workgroup per row keeps enough of the chip busy
-    if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true>), dim3(nrows), dim3(a.hd), 0, st, a);
-    else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(nrows), dim3(a.hd), 0, st, a);
-    else hipLaunchKernelGGL((k_merge_rows<false, false>), dim3(nrows), dim3(a.hd), 0, st, a);
+    // few rows: a workgroup per row keeps enough of the chip busy; rows
+    // with more splits than one pass holds split them over four groups
+    int most = 0;
+    for (int r = 0; r < a.A; ++r) most = std::max(most, a.split_off[r + 1] - a.split_off[r]);
+    if (most > MERGE_RB && a.part_f16 && a.lane_order && a.hd % 32 == 0) {
+      const int64_t units = (int64_t)a.A * a.nKv * ((a.nq + 15) / 16) * (a.hd / 32);
+      hipLaunchKernelGGL((k_merge_split<16>), dim3((unsigned)units), dim3(1024), 0, st, a);
+      return hipGetLastError();
+    }
+    if (most > MERGE_RB && a.hd % 64 == 0 && a.hd <= 256) {
+      if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
+      else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
+      else hipLaunchKernelGGL((k_merge_rows<false, false, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
+      return hipGetLastError();
+    }
+    if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else hipLaunchKernelGGL((k_merge_rows<false, false, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
     return hipGetLastError();
   }
   const int per = 256 / (a.hd / 8);  // query rows per workgroup (row-major partials)

@@ -225,6 +225,25 @@ def test_wide_attention_ragged_rows(gpu_lib):
     assert checked >= 40
 
 
+@pytest.mark.parametrize("ctx_len", [1900, 6000])
+def test_merge_of_many_splits_single_row(gpu_lib, ctx_len):
+    """One row whose context splits outnumber one merge pass (more than 32):
+    the row merge spreads them over four thread groups and merges the
+    groups' (max, sums) in LDS.  1900 keys: the short-context attention (61
+    splits of 32 keys, row-major fp16 partials); 6000 keys: the wide kernel
+    (lane-order fp16 partials); Markov head active."""
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=4096, mask_token_id=4095)
+    w = synth.Workload("many_splits", cfg, rows=1, ctx_lens=(ctx_len,))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    assert rel_err(logits[0], ref["logits"][0]) <= 2e-2
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 8
+
+
 def test_wide_attention_single_row(gpu_lib):
     """One row with 2100 context keys: the attention kernel that holds every
     query row of the kv head (fp16 partials in its lanes' order) followed by
