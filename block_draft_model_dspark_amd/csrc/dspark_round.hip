@@ -318,25 +318,16 @@ __global__ __launch_bounds__(64 * G) void k_merge_split(const MergeArgs a) {
 
 // Few query rows (a single draft row): one workgroup per query row, one
 // thread per head dim, the splits in passes of MERGE_RB with every partial
-// load of a pass in flight.  grid A*nKv*nq, block NG*hd (hd >= 64).  NG > 1
-// (rows with many splits: long contexts over few rows) gives each of NG
-// thread groups a contiguous share of the row's splits, merged in LDS at the
-// end, so the passes run side by side instead of one after another.
+// load of a pass in flight.  grid A*nKv*nq, block hd (>= 64)
 constexpr int MERGE_RB = 32;
 
-template <bool F16, bool LANE, int NG>
-__global__ __launch_bounds__(256 * NG) void k_merge_rows(const MergeArgs a) {
-  __shared__ float2 wl[NG][MERGE_RB];
-  __shared__ float cmax[NG];
-  __shared__ float gnum[NG > 1 ? NG : 1][NG > 1 ? 256 : 1];
-  __shared__ float gm[NG], gden[NG];
-  const int idx = blockIdx.x;
-  const int gi = NG > 1 ? (int)threadIdx.x / a.hd : 0;  // split group (wave-aligned: hd is a multiple of 64)
-  const int tid = (int)threadIdx.x - gi * a.hd;          // head-dim thread within the group
+template <bool F16, bool LANE>
+__global__ __launch_bounds__(256) void k_merge_rows(const MergeArgs a) {
+  __shared__ float2 wl[MERGE_RB];
+  __shared__ float cmax;
+  const int idx = blockIdx.x, tid = threadIdx.x;
   const int j = idx % a.nq, kvh = (idx / a.nq) % a.nKv, row = idx / (a.nq * a.nKv);
-  const int s0r = a.split_off[row], nsr = a.split_off[row + 1] - s0r;  // nsr >= 1 (the block split)
-  const int per = NG > 1 ? (nsr + NG - 1) / NG : nsr;  // splits per group (the same trip count for all)
-  const int ns = NG > 1 ? max(0, min(per, nsr - gi * per)) : nsr;  // this group's splits (may be 0)
+  const int s0 = a.split_off[row], ns = a.split_off[row + 1] - s0;
   const float2* ml = (const float2*)a.ml;
   // fp16 lane order: thread tid reads half (tid mod 8) of lane j mod 16 +
   // 16 ((tid mod 32) / 8) in tile pair tid / 32 (eight threads per 16-byte
@@ -344,18 +335,13 @@ __global__ __launch_bounds__(256 * NG) void k_merge_rows(const MergeArgs a) {
   const int pr = tid >> 5, gq8 = (tid & 31) >> 3, hv = tid & 7;
   const int dim = F16 && LANE ? 16 * (2 * pr + (hv >> 2)) + 4 * gq8 + (hv & 3) : tid;
   const int ng = (a.nq + 15) / 16;
-  // split of pass position q: clamped into the row's splits (a group with
-  // none left loads a valid split and masks it), so no load is conditional
-  auto split_at = [&](int c0, int q, int cn) {
-    return s0r + min(gi * per + c0 + min(q, max(cn, 1) - 1), nsr - 1);
-  };
   float num = 0.f, den = 0.f, mrun = -INFINITY;
-  for (int c0 = 0; c0 < per; c0 += MERGE_RB) {
-    const int cn = min(MERGE_RB, ns - c0);  // <= 0: nothing of this group in the pass
+  for (int c0 = 0; c0 < ns; c0 += MERGE_RB) {
+    const int cn = min(MERGE_RB, ns - c0);
     float o[MERGE_RB];
 #pragma unroll
     for (int q = 0; q < MERGE_RB; ++q) {
-      const int s = split_at(c0, q, cn);
+      const int s = s0 + c0 + min(q, cn - 1);
       if constexpr (F16 && LANE) {
         const int64_t i = ((((int64_t)s * a.nKv + kvh) * ng + j / 16) * (a.hd / 32) + pr) * 512 +
                           8 * ((j & 15) + 16 * gq8) + hv;
@@ -366,19 +352,18 @@ __global__ __launch_bounds__(256 * NG) void k_merge_rows(const MergeArgs a) {
         o[q] = ((const float*)a.opart)[(((int64_t)s * a.nKv + kvh) * a.nq + j) * a.hd + tid];
       }
     }
-    const float2 v = ml[((int64_t)split_at(c0, tid, cn) * a.nKv + kvh) * a.nq + j];
+    const float2 v = ml[((int64_t)(s0 + c0 + min(tid, cn - 1)) * a.nKv + kvh) * a.nq + j];
     if (tid < 64) {
       const float mm = wave_max(tid < cn ? v.x : -INFINITY);
-      if (tid == 0) cmax[gi] = mm;
+      if (tid == 0) cmax = mm;
     }
     __syncthreads();
-    const float mnew = fmaxf(mrun, cmax[gi]);
+    const float mnew = fmaxf(mrun, cmax);
     if (tid < cn) {
       const float w = expf(v.x - mnew);
-      wl[gi][tid] = make_float2(w, w * v.y);
+      wl[tid] = make_float2(w, w * v.y);
     }
-    // (a group that has seen no split yet keeps mrun = mnew = -inf)
-    const float rescale = NG > 1 && mnew == -INFINITY ? 1.f : expf(mrun - mnew);
+    const float rescale = expf(mrun - mnew);
     num *= rescale;
     den *= rescale;
     mrun = mnew;
@@ -386,33 +371,10 @@ __global__ __launch_bounds__(256 * NG) void k_merge_rows(const MergeArgs a) {
 #pragma unroll
     for (int q = 0; q < MERGE_RB; ++q)
       if (q < cn) {
-        num += (F16 ? wl[gi][q].y : wl[gi][q].x) * o[q];
-        den += wl[gi][q].y;
+        num += (F16 ? wl[q].y : wl[q].x) * o[q];
+        den += wl[q].y;
       }
     __syncthreads();
-  }
-  if constexpr (NG > 1) {
-    // the groups' (max, sums) merged by the first group (group 0 always has
-    // a split, so the common reference M is finite)
-    gnum[gi][tid] = num;
-    if (tid == 0) {
-      gm[gi] = mrun;
-      gden[gi] = den;
-    }
-    __syncthreads();
-    if (gi != 0) return;
-    float M = gm[0];
-#pragma unroll
-    for (int k = 1; k < NG; ++k) M = fmaxf(M, gm[k]);
-    num = 0.f;
-    den = 0.f;
-#pragma unroll
-    for (int k = 0; k < NG; ++k)
-      if (gm[k] != -INFINITY) {
-        const float f = expf(gm[k] - M);
-        num += gnum[k][tid] * f;
-        den += gden[k] * f;
-      }
   }
   const int rep = a.nH / a.nKv, hl = j / a.gamma, g = j - hl * a.gamma;
   const int h = kvh * rep + hl;
@@ -919,7 +881,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
   const int nrows = a.A * a.nKv * a.nq;
   if (nrows <= MERGE_FEW_ROWS) {
     // few rows: a workgroup per row keeps enough of the chip busy; rows
-    // with more splits than one pass holds split them over four groups
+    // with more splits than one pass holds, in the wide attention's lane
+    // order, go to k_merge_split (row-major partials: the short-context
+    // kernel's at most 64 splits, where four thread groups gained nothing)
     int most = 0;
     for (int r = 0; r < a.A; ++r) most = std::max(most, a.split_off[r + 1] - a.split_off[r]);
     if (most > MERGE_RB && a.part_f16 && a.lane_order && a.hd % 32 == 0) {
@@ -927,15 +891,9 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t st) {
       hipLaunchKernelGGL((k_merge_split<16>), dim3((unsigned)units), dim3(1024), 0, st, a);
       return hipGetLastError();
     }
-    if (most > MERGE_RB && a.hd % 64 == 0 && a.hd <= 256) {
-      if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
-      else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
-      else hipLaunchKernelGGL((k_merge_rows<false, false, 4>), dim3(nrows), dim3(4 * a.hd), 0, st, a);
-      return hipGetLastError();
-    }
-    if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
-    else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
-    else hipLaunchKernelGGL((k_merge_rows<false, false, 1>), dim3(nrows), dim3(a.hd), 0, st, a);
+    if (a.part_f16 && a.lane_order) hipLaunchKernelGGL((k_merge_rows<true, true>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else if (a.part_f16) hipLaunchKernelGGL((k_merge_rows<true, false>), dim3(nrows), dim3(a.hd), 0, st, a);
+    else hipLaunchKernelGGL((k_merge_rows<false, false>), dim3(nrows), dim3(a.hd), 0, st, a);
     return hipGetLastError();
   }
   const int per = 256 / (a.hd / 8);  // query rows per workgroup (row-major partials)

@@ -227,11 +227,11 @@ def test_wide_attention_ragged_rows(gpu_lib):
 
 @pytest.mark.parametrize("ctx_len", [1900, 6000])
 def test_merge_of_many_splits_single_row(gpu_lib, ctx_len):
-    """One row whose context splits outnumber one merge pass (more than 32):
-    the row merge spreads them over four thread groups and merges the
-    groups' (max, sums) in LDS.  1900 keys: the short-context attention (61
-    splits of 32 keys, row-major fp16 partials); 6000 keys: the wide kernel
-    (lane-order fp16 partials); Markov head active."""
+    """One row whose context splits outnumber one merge pass (more than 32).
+    1900 keys: the short-context attention (61 splits of 32 keys, row-major
+    fp16 partials), merged by the row merge in two passes; 6000 keys: the
+    wide kernel (189 splits, lane-order fp16 partials), merged by sixteen
+    waves over shares of the splits combined in LDS; Markov head active."""
     cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=4096, mask_token_id=4095)
     w = synth.Workload("many_splits", cfg, rows=1, ctx_lens=(ctx_len,))
     case = Case(cfg, markov_active=True, with_fc=False)
