@@ -124,8 +124,9 @@ void dspark_model_destroy(dspark_model* m);
  * fewer rows stream the weights once per 16-row tile.  Both compute the same product (fp32
  * activations as bf16 hi + lo planes); the context projection of bf16 rows
  * switches at 1024 rows or four times `rows`, whichever is more.  rows <= 0
- * keeps every GEMM on the weight-streaming kernel.  Default 48 (draft rounds
- * of three or more blocks of 16).  Workspace sizes depend on it: set it
+ * keeps every GEMM on the weight-streaming kernel; a draft round's gate|up
+ * switches at two thirds of `rows`.  Default 48 (draft rounds of three or
+ * more blocks of 16; gate|up from two).  Workspace sizes depend on it: set it
  * before sizing workspaces.  DSPARK_ERR_INVALID_ARG for a null model. */
 dspark_status dspark_model_set_tall_rows(dspark_model* m, int rows);
 

@@ -225,6 +225,26 @@ def test_wide_attention_ragged_rows(gpu_lib):
     assert checked >= 40
 
 
+def test_two_rows_mixed_paths(gpu_lib):
+    """Two blocks (32 GEMM rows) at the default threshold: gate|up on the
+    tiled path (input planes prepared from o's streaming row statistics,
+    split over K with its separate epilogue writing the fp32 product that
+    the streaming down reads), q|k, o, down and lm_head on the streaming
+    kernel (lm_head in the XCD-aware order); ragged contexts, Markov head
+    active."""
+    cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=4096, mask_token_id=4095)
+    w = synth.Workload("two_rows", cfg, rows=2, ctx_lens=(300, 41))
+    case = Case(cfg, markov_active=True, with_fc=False)
+    lens = list(w.ctx_lens)
+    o_rows, k_rows, v_rows = case.kv_rows_from_oracle([_ctx(w, a, L) for a, L in enumerate(lens)], [0] * 2)
+    anchors = synth.anchors(w)
+    toks, logits, ref = _round(case, o_rows, k_rows, v_rows, lens, anchors, lens)
+    for a in range(2):
+        assert rel_err(logits[a], ref["logits"][a]) <= 2e-2, a
+    checked, _ = check_tokens(case.om, ref["logits"], anchors, toks)
+    assert checked >= 16
+
+
 @pytest.mark.parametrize("ctx_len", [1900, 6000])
 def test_merge_of_many_splits_single_row(gpu_lib, ctx_len):
     """One row whose context splits outnumber one merge pass (more than 32).
