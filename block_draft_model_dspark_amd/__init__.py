@@ -118,7 +118,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     lib.dspark_tall_tile_of.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
                                         ctypes.POINTER(ctypes.c_int)]
     lib.dspark_tall_tile_of.restype = ctypes.c_int
-    lib.dspark_stream_block_of.argtypes = [ctypes.c_int] * 5 + [ctypes.POINTER(ctypes.c_int)] * 2
+    lib.dspark_stream_block_of.argtypes = [ctypes.c_int] * 6 + [ctypes.POINTER(ctypes.c_int)] * 3
     lib.dspark_stream_block_of.restype = ctypes.c_int
     lib.dspark_q4_address_check.argtypes = [ctypes.POINTER(Config), ctypes.c_int, ctypes.POINTER(ctypes.c_int32),
                                             I64, ctypes.c_int, ctypes.POINTER(I64)]

@@ -591,11 +591,11 @@ extern "C" {
 
 const char* dspark_last_error(void) { return g_err.c_str(); }
 
-dspark_status dspark_stream_block_of(int gx, int S, int R, int x, int z, int* bx, int* bz) {
+dspark_status dspark_stream_block_of(int gx, int S, int R, int x, int y, int z, int* bx, int* by, int* bz) {
   g_err.clear();
-  if (gx <= 0 || S <= 0 || R <= 0 || x < 0 || x >= gx || z < 0 || z >= R || !bx || !bz)
+  if (gx <= 0 || S <= 0 || R <= 0 || x < 0 || x >= gx || y < 0 || y >= S || z < 0 || z >= R || !bx || !by || !bz)
     return fail(DSPARK_ERR_INVALID_ARG, "stream_block_of: bad grid or workgroup");
-  dsp::stream_block_of(gx, S, R, x, z, *bx, *bz);
+  dsp::stream_block_of(gx, S, R, x, y, z, *bx, *by, *bz);
   return DSPARK_OK;
 }
 

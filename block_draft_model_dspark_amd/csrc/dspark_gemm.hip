@@ -8,8 +8,8 @@
 // Work split: a 256-thread workgroup = 4 wave64s; wave w owns one 16-column
 // output tile of the workgroup's 64-column block (blockIdx.x), the workgroup
 // owns one K slice (blockIdx.y) and one block of MT*16 rows (blockIdx.z);
-// with 16-row tiles, one K slice and several row blocks, (x, z) is renumbered
-// so that the row blocks of a column block share its weight tile
+// with 16-row tiles and several row blocks, (x, y, z) is renumbered so that
+// the row blocks of a (column block, K slice) share its weight tile
 // (stream_block_of).
 // Each wave issues all weight loads of a K sub-slice straight from HBM into
 // registers (16 B per lane per 32-wide k step: the B operand layout needs no
@@ -818,13 +818,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   const int ngmax = KC >> 6;
   const size_t xbuf = xbuf_bytes(WK, XM, MT, KC);
 
-  // column block (pair) and row block: RM (16-row tiles, one K slice,
-  // several row blocks) takes the XCD-aware order of stream_block_of, with
+  // column block (pair), K slice and row block: RM (16-row tiles, several
+  // row blocks) takes the XCD-aware order of stream_block_of, with
   // the grid sizes from the arguments (a run-time choice, or gridDim, puts a
   // scalar load ahead of the first weight address of every launch)
   static_assert(!RM || MT == 1, "the renumbered order is for 16-row tiles");
-  int bx = blockIdx.x, bz = blockIdx.z;
-  if constexpr (RM) stream_block_of(COL2 ? g.N >> 7 : g.N >> 6, 1, (g.M + 15) >> 4, blockIdx.x, blockIdx.z, bx, bz);
+  int bx = blockIdx.x, by = blockIdx.y, bz = blockIdx.z;
+  if constexpr (RM)
+    stream_block_of(COL2 ? g.N >> 7 : g.N >> 6, (g.K + g.kslice - 1) / g.kslice, (g.M + 15) >> 4, blockIdx.x,
+                    blockIdx.y, blockIdx.z, bx, by, bz);
   const int cb = COL2 ? 2 * bx + half : bx;
   // wave-uniform values in scalar registers, so that the weight segment is
   // read from the kernel arguments with scalar loads (a vector load of the
@@ -836,7 +838,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
   si = __builtin_amdgcn_readfirstlane(si);
   const int64_t wrow = (int64_t)(n0w - g.seg[si].n0 + (lane & 15));
   const int mbase = bz * (MT * 16);
-  const int kbeg = blockIdx.y * g.kslice;
+  const int kbeg = by * g.kslice;
   const int kend = min(g.K, kbeg + g.kslice);
   const bool write_h = XM == XM_NORM && g.nin.hout != nullptr && bx == 0;
   // NCH > 0: every slice is exactly NCH sub-slices of KC (fully unrolled,
@@ -965,7 +967,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm(const GemmArgs g, const EpiArg
 #pragma unroll
     for (int t = 0; t < MT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) st_coh(g.P + pidx(blockIdx.y, t, i), acc[t][i]);
+      for (int i = 0; i < 4; ++i) st_coh(g.P + pidx(by, t, i), acc[t][i]);
     if (!arrive_last(e.cnt + bz * ncb + cb, S, &last_flag)) return;
 #pragma unroll
     for (int t = 0; t < MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1149,8 +1151,7 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
         }
       return hipErrorInvalidValue;
     } else {
-    // 16-row tiles: the XCD-aware block order (RM) when one K slice covers
-    // several row blocks
+    // 16-row tiles: the XCD-aware block order (RM) over several row blocks
     auto sel = [&](auto rm) -> hipError_t {
     constexpr bool RM = decltype(rm)::value;
     if constexpr (unrolled && EPI == EPI_LM && MT == 1) {
@@ -1183,7 +1184,7 @@ static hipError_t launch_one(const GemmArgs& a, const EpiArgs& e, int S, hipStre
     return hipGetLastError();
     };
     if constexpr (MT == 1) {
-      if (S == 1 && mblocks > 1) return sel(std::true_type{});
+      if (mblocks > 1) return sel(std::true_type{});
     }
     return sel(std::false_type{});
     }

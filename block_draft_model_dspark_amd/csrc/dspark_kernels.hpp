@@ -246,19 +246,25 @@ __host__ __device__ inline void tall_tile_of(int gx, int gy, int w, int& bx, int
 
 // Block order of the weight-streaming GEMM (grid: gx column blocks x S K
 // slices x R row blocks; workgroups are dealt to the 8 XCDs in launch order).
-// In launch order the R row blocks of one column block are gx * S workgroups
-// apart, so with several row blocks each weight tile would stream from HBM
-// once per row block.  With one K slice, R > 1 and gx a multiple of 8,
-// workgroup (x, z) is renumbered so that XCD x mod 8 runs the R row blocks of
-// its column blocks back to back and they share each weight tile in its L2.
-// A bijection of the (x, z) pairs in every case.
-__host__ __device__ inline void stream_block_of(int gx, int S, int R, int x, int z, int& bx, int& bz) {
+// In launch order the R row blocks of one (column block, K slice) are
+// gx * S workgroups apart, so with several row blocks each weight tile would
+// stream from HBM once per row block.  With R > 1 and gx * S a multiple of 8,
+// workgroup (x, y, z) is renumbered so that XCD (x + gx y) mod 8 runs the R
+// row blocks of its (column block, slice) pairs back to back and they share
+// each weight tile in its L2.  A bijection of the (x, y, z) triples in every
+// case.
+__host__ __device__ inline void stream_block_of(int gx, int S, int R, int x, int y, int z, int& bx, int& by,
+                                                int& bz) {
   bx = x;
+  by = y;
   bz = z;
-  if (S == 1 && R > 1 && (gx & 7) == 0) {
-    const int w = x + gx * z, s = w >> 3;
-    bx = (s / R) * 8 + (w & 7);
+  const int units = gx * S;  // (column block, K slice) pairs
+  if (R > 1 && (units & 7) == 0) {
+    const int w = x + gx * y + units * z, s = w >> 3;
+    const int u = (s / R) * 8 + (w & 7);
     bz = s % R;
+    bx = u % gx;
+    by = u / gx;
   }
 }
 

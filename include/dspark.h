@@ -305,15 +305,15 @@ int dspark_profile_read(dspark_kernel_time* out, int max);
  * sizes, w outside [0, gx*gy) or null outputs. */
 dspark_status dspark_tall_tile_of(int gx, int gy, int w, int* bx, int* by);
 
-/* Diagnostic (host only, no HIP call): the column block *bx and row block
- * *bz that workgroup (x, z) of the weight-streaming GEMM computes, in a grid
- * of gx column blocks, S K slices and R row blocks of 16 rows.  With one K
- * slice and several row blocks the kernel renumbers its workgroups so that the row
- * blocks of a column block run back to back on one XCD and share its weight
- * tile in that XCD's L2; a bijection of the (x, z) pairs.
- * DSPARK_ERR_INVALID_ARG for non-positive sizes, (x, z) outside the grid or
- * null outputs. */
-dspark_status dspark_stream_block_of(int gx, int S, int R, int x, int z, int* bx, int* bz);
+/* Diagnostic (host only, no HIP call): the column block *bx, K slice *by and
+ * row block *bz that workgroup (x, y, z) of the weight-streaming GEMM
+ * computes, in a grid of gx column blocks, S K slices and R row blocks of 16
+ * rows.  With several row blocks the kernel renumbers its workgroups so that
+ * the row blocks of a (column block, K slice) run back to back on one XCD and
+ * share its weight tile in that XCD's L2; a bijection of the (x, y, z)
+ * triples.  DSPARK_ERR_INVALID_ARG for non-positive sizes, (x, y, z) outside
+ * the grid or null outputs. */
+dspark_status dspark_stream_block_of(int gx, int S, int R, int x, int y, int z, int* bx, int* by, int* bz);
 
 /* Diagnostic (host only, no HIP call): replays on the host every address
  * that the 4-bit branches of the kernels form for a round of A rows with

@@ -185,30 +185,33 @@ def test_tall_tile_order_keeps_a_row_tile_on_one_xcd(dsp):
             assert by.value % 8 == w % 8
 
 
-@pytest.mark.parametrize("gx,S,R", [(2048, 1, 4), (16, 1, 16), (512, 1, 4), (36, 8, 1), (32, 8, 2), (8, 1, 3),
-                                    (12, 1, 4), (64, 1, 2), (256, 1, 1), (24, 2, 5)])
+@pytest.mark.parametrize("gx,S,R", [(2048, 1, 4), (16, 1, 16), (512, 1, 4), (36, 8, 1), (36, 8, 2), (32, 8, 2),
+                                    (8, 1, 3), (12, 1, 4), (64, 1, 2), (256, 1, 1), (24, 2, 5), (32, 3, 3), (7, 3, 2)])
 def test_stream_block_order_is_a_bijection(dsp, gx, S, R):
     """The weight-streaming GEMM's renumbering covers every (column block,
-    row block) once; with one K slice, several row blocks and gx a multiple
-    of 8, the row blocks of a column block share one XCD (workgroup
-    x + gx z on XCD (x + gx z) mod 8) and follow each other in launch order."""
+    K slice, row block) once; with several row blocks and gx * S a multiple
+    of 8, the row blocks of a (column block, slice) share one XCD (workgroup
+    x + gx (y + S z) on XCD (x + gx (y + S z)) mod 8) and follow each other
+    in launch order."""
     lib = dsp._lib
-    bx, bz = ctypes.c_int(), ctypes.c_int()
+    bx, by, bz = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
     seen, where = set(), {}
     for z in range(R):
-        for x in range(gx):
-            assert lib.dspark_stream_block_of(gx, S, R, x, z, ctypes.byref(bx), ctypes.byref(bz)) == 0
-            assert 0 <= bx.value < gx and 0 <= bz.value < R
-            seen.add((bx.value, bz.value))
-            where.setdefault(bx.value, []).append(x + gx * z)
-    assert len(seen) == gx * R
-    if S == 1 and R > 1 and gx % 8 == 0:
-        for cb, ws in where.items():
+        for y in range(S):
+            for x in range(gx):
+                assert lib.dspark_stream_block_of(gx, S, R, x, y, z, ctypes.byref(bx), ctypes.byref(by),
+                                                  ctypes.byref(bz)) == 0
+                assert 0 <= bx.value < gx and 0 <= by.value < S and 0 <= bz.value < R
+                seen.add((bx.value, by.value, bz.value))
+                where.setdefault((bx.value, by.value), []).append(x + gx * (y + S * z))
+    assert len(seen) == gx * S * R
+    if R > 1 and (gx * S) % 8 == 0:
+        for ws in where.values():
             assert len({w % 8 for w in ws}) == 1
             assert max(ws) - min(ws) == 8 * (R - 1)
     else:
-        assert all(ws == [cb + gx * z for z in range(R)] for cb, ws in where.items())
-    assert lib.dspark_stream_block_of(gx, S, R, gx, 0, ctypes.byref(bx), ctypes.byref(bz)) == 1
+        assert all(ws == [u[0] + gx * (u[1] + S * z) for z in range(R)] for u, ws in where.items())
+    assert lib.dspark_stream_block_of(gx, S, R, gx, 0, 0, ctypes.byref(bx), ctypes.byref(by), ctypes.byref(bz)) == 1
 
 
 def test_draft_workspace_scales_with_context_up_to_the_split_cap(dsp):
