@@ -38,25 +38,25 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "942e8f7fb987acb89d398b25fc000f470def0ab78f97c0ba9827c33774500d68",
-                  "bytes_per_step": 710053299},
+                  "sha256": "bc61176007ab868a05db290d0119492774a68a96300c947e9b50c839a4391c9b",
+                  "bytes_per_step": 710036915},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "942e8f7fb987acb89d398b25fc000f470def0ab78f97c0ba9827c33774500d68",
-                     "bytes_per_launch": 70292410},
+                     "sha256": "bc61176007ab868a05db290d0119492774a68a96300c947e9b50c839a4391c9b",
+                     "bytes_per_launch": 70296806},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "b678438dc75fc08fcd27888409497b3b81987916d66e49f6973b80c49626e80f",
-                  "bytes_per_step": 387631872},
+                  "sha256": "f358213347e558815f296d21b2f6bd8137b01ad368455678a975efac25709e5b",
+                  "bytes_per_step": 387634739},
     # prefill_8192: one fc launch (tiled one-plane GEMM, 7680 -> 2048 over 8192 rows), per launch
     "fc_prefill": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                   "sha256": "443de4cc92fb3e934df2709c9182e964e29aa6e9ec9a889e25c20ee689f6cf61",
-                   "bytes_per_launch": 750370893},
+                   "sha256": "edaa991b562c5fdd564572f964d87c11d309094507ceed7857fe0b1057c8e583",
+                   "bytes_per_launch": 754770253},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "443de4cc92fb3e934df2709c9182e964e29aa6e9ec9a889e25c20ee689f6cf61",
-                  "bytes_per_step": 2085513459},
+                  "sha256": "edaa991b562c5fdd564572f964d87c11d309094507ceed7857fe0b1057c8e583",
+                  "bytes_per_step": 2085408986},
 }
 
 
