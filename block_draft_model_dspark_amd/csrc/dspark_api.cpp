@@ -146,6 +146,17 @@ GemmPlan plan_gemm_mt(int wk, int xmode, int M, int N, int K, int group_cols, in
   if (wgs < target) S = std::min(16, ceil_div(target, wgs));
   if (xmode == XM_NORM) S = std::max(S, ceil_div(K, 2048));
   S = std::min(S, ceil_div(K, 64));
+  // prefer the fully unrolled main loop (slices of 1, 2, 4 or 8 sub-slices
+  // of 256): the fewest such slices that are at least S (K = 7680, S = 4:
+  // 15 slices of 512 rather than 4 of 1920 on the generic loop)
+  if (S > 1 && K % 256 == 0 && !(K % S == 0 && (K / S) % 256 == 0 && ((K / S / 256) & (K / S / 256 - 1)) == 0 &&
+                                  K / S / 256 <= 8)) {
+    for (int nch = 8; nch >= 1; nch /= 2)
+      if ((K / 256) % nch == 0 && K / (256 * nch) >= S && K / (256 * nch) <= 32) {
+        S = K / (256 * nch);
+        break;
+      }
+  }
   const int kslice = ceil_div(ceil_div(K, S), 64) * 64;
   p.S = ceil_div(K, kslice);
   p.kslice = kslice;
