@@ -175,11 +175,11 @@ GemmPlan plan_gemm(int wk, int xmode, int M, int N, int K, int group_cols, int t
   // many rows: the tiled path (bf16 weights; its epilogues need whole
   // 64-column blocks, head groups of at most 256 columns for the context
   // projection, and at most 256 statistics parts for normed inputs)
-  // (the context projection of bf16 rows has a 32-row-tile streaming
-  // variant that stays ahead up to about 1024 rows: 23.6 us against 38.2 us
-  // tiled at 512)
-  const int64_t min_rows =
-      group_cols > 0 && xmode == XM_BF16 ? std::max<int64_t>(4 * (int64_t)tall_rows, 1024) : tall_rows;
+  // (the context projection, whose tiled epilogue reads the product in place
+  // and so cannot split K, streams up to about 1024 rows: bf16 rows 23.6 us
+  // against 38.2 us tiled at 512; hidden_norm(fc x) rows, the projection of
+  // 64 / 256 target-feature rows 47.6 / 55.0 -> 38.3 / 51.1 us)
+  const int64_t min_rows = group_cols > 0 ? std::max<int64_t>(4 * (int64_t)tall_rows, 1024) : tall_rows;
   if (wk == WK_BF16 && tall_rows > 0 && M >= min_rows && K % 64 == 0 && N % 64 == 0 &&
       (xmode != XM_NORM || K <= 256 * 64) && (group_cols == 0 || (group_cols <= 256 && N % group_cols == 0))) {
     GemmPlan p{};

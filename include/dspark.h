@@ -122,7 +122,7 @@ void dspark_model_destroy(dspark_model* m);
  * the workspace, followed by the GEMM's epilogue (gate|up and lm_head form
  * theirs in the tiled kernel's store when one K slice holds the product);
  * fewer rows stream the weights once per 16-row tile.  Both compute the same product (fp32
- * activations as bf16 hi + lo planes); the context projection of bf16 rows
+ * activations as bf16 hi + lo planes); the context projection's k_proj
  * switches at 1024 rows or four times `rows`, whichever is more.  rows <= 0
  * keeps every GEMM on the weight-streaming kernel; a draft round's gate|up
  * switches at two thirds of `rows`.  Default 48 (draft rounds of three or

@@ -393,16 +393,16 @@ def test_tiled_path_fused_logits(gpu_lib):
     assert rel_err(logits, z0.cpu().numpy()) <= 5e-3
 
 
-@pytest.mark.parametrize("kind", ["target_features", "context_hidden"])
-def test_tiled_path_projection_small_ragged(gpu_lib, kind):
+@pytest.mark.parametrize("kind,L", [("target_features", 100), ("target_features", 520), ("context_hidden", 520)])
+def test_tiled_path_projection_small_ragged(gpu_lib, kind, L):
     """The context projection on the tiled path (threshold 1 row): fc +
-    hidden_norm + k_proj from 2 x 100 rows of target features (normed fp32
-    input planes, a partial tile), or k_proj on 2 x 520 bf16 context rows
-    (one plane; the bf16 projection takes the tiled path from 1024 rows, and
-    1040 leaves a partial 128-row tile)."""
+    hidden_norm from target features, k_proj streaming over 2 x 100 rows
+    (the projection's k_proj takes the tiled path from 1024 rows) or tiled
+    over 2 x 520 (fc's epilogue writing k_proj's input planes; 1040 rows
+    leave a partial 128-row tile); or k_proj on 2 x 520 bf16 context rows
+    (one plane)."""
     import torch
     cfg = synth.scaled(synth.FULL, num_hidden_layers=2, vocab_size=1024, mask_token_id=1023)
-    L = 100 if kind == "target_features" else 520
     w = synth.Workload("pf_tall", cfg, rows=0, prefill_rows=L, prefill_batch=2)
     case = Case(cfg)
     if kind == "target_features":
@@ -440,7 +440,7 @@ def test_tiled_path_row_widths(gpu_lib, hidden):
     widths other than 2048: 1024 leaves half of each workgroup's threads
     without columns, 3072 gives some threads two items.  One layer on the
     tiled path (threshold 1 row), 2 ragged rows, an active Markov head, and
-    the target-feature projection of 2 x 70 rows."""
+    the target-feature projection of 2 x 520 rows (k_proj tiled from 1024)."""
     import torch
     cfg = synth.scaled(synth.FULL, hidden_size=hidden, num_hidden_layers=1, intermediate_size=4096,
                        vocab_size=1024, mask_token_id=1023)
@@ -449,7 +449,7 @@ def test_tiled_path_row_widths(gpu_lib, hidden):
     lens = list(w.ctx_lens)
     o_rows, k_rows, v_rows = case.kv_rows_direct(w, lens)
     anchors = synth.anchors(w)
-    wp = synth.Workload(f"pf_h{hidden}", cfg, rows=0, prefill_rows=70, prefill_batch=2)
+    wp = synth.Workload(f"pf_h{hidden}", cfg, rows=0, prefill_rows=520, prefill_batch=2)
     st = synth.target_features(wp)
     try:
         case.gm.set_tall_rows(1)
