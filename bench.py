@@ -38,25 +38,25 @@ CSRC = "block_draft_model_dspark_amd/csrc/"
 TRAFFIC = {
     # full_bf16_a1: the 18 weight-streaming GEMM launches of one step
     "gemm_full": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "bc61176007ab868a05db290d0119492774a68a96300c947e9b50c839a4391c9b",
-                  "bytes_per_step": 710036915},
+                  "sha256": "a64370497a3b36fe9d067c37845aadce32deaa35400a53223387e16de08df138",
+                  "bytes_per_step": 710039296},
     # full_bf16_a1: one gate|up launch (the headline's dominant kernel), per launch
     "gemm_gate_up": {"sources": ("dspark_gemm.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                     "sha256": "bc61176007ab868a05db290d0119492774a68a96300c947e9b50c839a4391c9b",
-                     "bytes_per_launch": 70296806},
+                     "sha256": "a64370497a3b36fe9d067c37845aadce32deaa35400a53223387e16de08df138",
+                     "bytes_per_launch": 70297459},
     # rows_a32: the 4 wide-attention launches of one round
     "attn_rows": {"sources": ("dspark_attn.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "f358213347e558815f296d21b2f6bd8137b01ad368455678a975efac25709e5b",
-                  "bytes_per_step": 387634739},
+                  "sha256": "a9cb226a3b8521b3e3ae15357ec9549540cb9c44a122264457f1f1a93059d7b6",
+                  "bytes_per_step": 387612442},
     # prefill_8192: one fc launch (tiled one-plane GEMM, 7680 -> 2048 over 8192 rows), per launch
     "fc_prefill": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                   "sha256": "edaa991b562c5fdd564572f964d87c11d309094507ceed7857fe0b1057c8e583",
-                   "bytes_per_launch": 754770253},
+                   "sha256": "d4679a90832e8f5e29427164fea93fd17b9fd368e08a4d05cb5f9a009a308a06",
+                   "bytes_per_launch": 724636544},
     # rows_a32: the 17 tiled-GEMM launches of one round (input preparation and
     # separate epilogues excluded)
     "tall_rows": {"sources": ("dspark_tall.hip", "dspark_common.hpp", "dspark_kernels.hpp", "dspark_api.cpp"),
-                  "sha256": "edaa991b562c5fdd564572f964d87c11d309094507ceed7857fe0b1057c8e583",
-                  "bytes_per_step": 2085408986},
+                  "sha256": "d4679a90832e8f5e29427164fea93fd17b9fd368e08a4d05cb5f9a009a308a06",
+                  "bytes_per_step": 2080002765},
 }
 
 
